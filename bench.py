@@ -1,0 +1,224 @@
+"""Benchmark: one step = the whole attention hot path (forward, then backward
+from the forward's out/lse) over one batch of seeded synthetic input, timed on
+one MI355X. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--all]
+
+The default workload is the packed-varlen document-causal D=128 problem
+(T=16384, Hq=32, Hkv=8); ``--workload`` picks another of the five
+(1 small dense, 2 varlen D128, 3 dense D512, 4 varlen 192/128, 5 ring share),
+``--all`` adds per-workload numbers for every one of them to the line.
+Throughput is causal-adjusted: FLOPs count only visible (query, key) pairs,
+forward 2*pairs*(Dqk+Dv), backward 2*pairs*(3*Dqk+2*Dv).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s (causal-adjusted) and % of bf16 MFMA peak, 1 GPU"
+
+
+def _dev(t):
+    return t.to("cuda")
+
+
+class Problem:
+    """Device-resident inputs of one workload and closures for each stage."""
+
+    def __init__(self, n: int):
+        import varlen_causal_attention_amd as vca
+
+        self.vca = vca
+        self.w = w = workloads.workload(n)
+        t = w.tensors()
+        self.t = {k: _dev(v) for k, v in t.items()}
+        if w.kind == "varlen":
+            cu = torch.from_numpy(w.cu()).to("cuda")
+            self.cu, self.mx = cu, max(w.lengths)
+        elif w.kind == "ring":
+            ids = w.row_doc_ids()
+            S = w.shard
+            self.local = vca.doc_layout(ids, S, S, S, S, 0, "cuda")
+            self.cross = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
+        self.out = self.lse = None
+
+    def fwd(self):
+        v, w, t = self.vca, self.w, self.t
+        if w.kind == "dense":
+            self.out, self.lse = v.fwd_dense(t["q"], t["k"], t["v"], w.scale, w.causal)
+        elif w.kind == "varlen":
+            self.out, self.lse = v.fwd_varlen(t["q"], t["k"], t["v"], self.cu, self.cu, self.mx,
+                                              self.mx, w.scale, w.causal)
+        else:
+            cq, ck, mq, mk = self.local
+            o1, l1 = v.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
+            cq, ck, mq, mk = self.cross
+            o2, l2 = v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False)
+            _, self.lse, self.out = v.merge(o1, l1, o2, l2, bf16_copy=True)
+
+    def bwd(self):
+        v, w, t = self.vca, self.w, self.t
+        if w.kind == "dense":
+            return v.bwd_dense(t["do"], t["q"], t["k"], t["v"], self.out, self.lse, w.scale, w.causal)
+        if w.kind == "varlen":
+            return v.bwd_varlen(t["do"], t["q"], t["k"], t["v"], self.out, self.lse, self.cu,
+                                self.cu, self.mx, self.mx, w.scale, w.causal)
+        cq, ck, mq, mk = self.local
+        dq, dkl, dvl = v.bwd_varlen(t["do"], t["q"], t["k_local"], t["v_local"], self.out,
+                                    self.lse, cq, ck, mq, mk, w.scale, True)
+        cq, ck, mq, mk = self.cross
+        _, dke, dve = v.bwd_varlen(t["do"], t["q"], t["k_early"], t["v_early"], self.out,
+                                   self.lse, cq, ck, mq, mk, w.scale, False, dq_accumulate=dq)
+        return dq, dkl, dvl, dke, dve
+
+    def step(self):
+        self.fwd()
+        return self.bwd()
+
+
+def time_stage(fn, iters: int) -> float:
+    """Mean ms per call, HIP events on the current stream (the one the library
+    launches on)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def measure(n: int, steps: int, warmup: int) -> dict:
+    p = Problem(n)
+    w = p.w
+    for _ in range(warmup):
+        p.step()
+    torch.cuda.synchronize()
+    # the timed region: exactly `steps` whole steps
+    t0 = time.perf_counter()
+    step_ms_ev = time_stage(p.step, steps)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    fwd_ms = time_stage(p.fwd, steps)
+    bwd_ms = time_stage(p.bwd, steps)
+    torch.cuda.synchronize()
+    ff, bf = w.fwd_flops(), w.bwd_flops()
+    return dict(workload=w.name, ms_per_step=step_ms_ev, wall_ms_per_step=wall,
+                tflops_step=(ff + bf) / (step_ms_ev * 1e-3) / 1e12,
+                fwd_ms=fwd_ms, bwd_ms=bwd_ms,
+                fwd_tflops=ff / (fwd_ms * 1e-3) / 1e12, bwd_tflops=bf / (bwd_ms * 1e-3) / 1e12,
+                fwd_flops=ff, bwd_flops=bf, pairs=w.pairs())
+
+
+def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle on the host cores over a bounded sample of the workload:
+    whole documents of one q-head group at a time (forward then backward),
+    until the time budget is used; FLOPs counted the same causal-adjusted way."""
+    from oracle import attention as orc
+
+    w = workloads.workload(n)
+    if w.kind != "varlen":
+        w = workloads.workload(2)
+    t = w.tensors()
+    cu = w.cu()
+    G = w.Hq // w.Hkv
+    flops = 0
+    done = []
+    t0 = time.perf_counter()
+    order = np.argsort(w.lengths)  # shortest documents first keeps the sample bounded
+    for s in order:
+        a, b = int(cu[s]), int(cu[s + 1])
+        for g in range(w.Hkv):
+            hs = list(range(g * G, (g + 1) * G))
+            sl = lambda x, heads: x[a:b][:, heads]  # noqa: E731
+            qq, kk, vv, dd = sl(t["q"], hs), sl(t["k"], [g]), sl(t["v"], [g]), sl(t["do"], hs)
+            c1 = [0, b - a]
+            ro, rl = orc.fwd_varlen(qq, kk, vv, c1, c1, w.scale, True)
+            orc.bwd_varlen(dd, qq, kk, vv, ro, rl, c1, c1, w.scale, True)
+            pairs = len(hs) * workloads.causal_pairs(b - a, b - a)
+            flops += 2 * pairs * (3 * w.Dqk + 2 * w.Dv) + 2 * pairs * (w.Dqk + w.Dv)
+            done.append((b - a, g))
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{w.name}: {len(done)} (document, kv-head group) slices, forward+backward in "
+                      f"fp64 numpy, {el:.1f} s, BLAS threads = {cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--all", action="store_true", help="also report every workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    m = measure(args.workload, args.steps, args.warmup)
+    w = workloads.workload(args.workload)
+    fwd_tf = m["fwd_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(m["tflops_step"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "kind": w.kind, "Hq": w.Hq, "Hkv": w.Hkv, "Dqk": w.Dqk,
+                   "Dv": w.Dv, "tokens": w.T if w.kind == "varlen" else None,
+                   "causal": w.causal, "pairs": m["pairs"]},
+        "pct_of_peak": round(100 * m["tflops_step"] / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(m["fwd_ms"], 4), "tflops": round(fwd_tf, 2),
+                "pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
+        "bwd": {"ms": round(m["bwd_ms"], 4), "tflops": round(m["bwd_tflops"], 2),
+                "pct_of_peak": round(100 * m["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(fwd_tf, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "wall_ms_per_step": round(m["wall_ms_per_step"], 4),
+    }
+    if args.all:
+        per = {}
+        for n in range(1, 6):
+            r = measure(n, max(3, args.steps // 2), 2)
+            per[r["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                  for k, v in r.items() if k != "workload"}
+        line["workloads"] = per
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

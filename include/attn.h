@@ -1,0 +1,183 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused scaled-dot-product attention
+ * library: forward and backward, dense [B,H,N,D] and packed-THD varlen.
+ *
+ * What is computed follows the NVIDIA NeMo-Automodel API pages:
+ *  - "ffpa_attention" page, API entries of the dense forward/backward and the
+ *    varlen forward/backward wrappers: the forward returns out (query rows,
+ *    value head dim) and an fp32 log-sum-exp, handles GQA inside; the backward
+ *    takes the caller's out/lse (so a ring can feed a globally merged pair) and
+ *    returns dq, dk, dv with dk/dv reduced to the Hkv heads.
+ *  - "fa4" page, module overview (document-causal bullets): the causal mask is
+ *    aligned to the bottom-right corner of each segment, so query i of a
+ *    segment with lq queries and lk keys sees keys j <= i + (lk - lq);
+ *    zero-query segments are allowed and let key segments tile the keys.
+ *  - "gemma4_moe cp_attention" page, -inf-safe merge entry: two partial
+ *    results of the same queries combine as lse = logaddexp(lse_a, lse_b),
+ *    out = weighted mean with weights exp(lse_x - lse); a row where both are
+ *    -inf keeps out 0.
+ *
+ * Conventions shared by every entry point
+ *  - dtype: ATTN_BF16 is the only element type of q, k, v, out, dout, dq, dk,
+ *    dv. lse is always fp32.
+ *  - lse is the natural log of the sum of exp over the *scaled* scores
+ *    (scale * q.k). A query row with no visible key gets out = 0 and
+ *    lse = -inf; the backward treats lse = -inf as "row attends nothing".
+ *  - GQA: Hq must be a multiple of Hkv; q-head h reads kv-head h / (Hq/Hkv).
+ *  - Head dims: (Dqk, Dv) must be one of the pairs attn_is_supported()
+ *    accepts: (64,64), (128,128), (192,128), (256,256), (512,512).
+ *  - Strides are in elements; the innermost (head-dim) stride must be 1, every
+ *    other stride a multiple of 8, and every tensor pointer 16-byte aligned.
+ *  - Every output element is written (callers need not pre-zero): empty rows
+ *    get out 0 / lse -inf; keys no query sees get dk = dv = 0.
+ *  - Ownership: the caller allocates every buffer (inputs, outputs and the
+ *    workspace). The library allocates no device memory and keeps no state
+ *    between calls. Calls enqueue work on `stream` (a hipStream_t; NULL is
+ *    the default stream) and return; buffers must stay valid until the
+ *    stream reaches that point. Results are deterministic: the same inputs
+ *    give bitwise-identical outputs (no floating-point atomics).
+ *  - Workspace: a call with workspace == NULL and workspace_bytes != NULL is a
+ *    size query: the required size is written to *workspace_bytes and nothing
+ *    is launched. Otherwise a call that needs workspace must get a 16-byte
+ *    aligned buffer with *workspace_bytes >= the required size, else
+ *    ATTN_E_WORKSPACE. Calls that need none (the forwards) may pass NULL for
+ *    both. The workspace holds no result and may be reused once the stream
+ *    has passed the call.
+ *  - Errors: problems visible on the host return a negative status before any
+ *    launch, and attn_last_error() describes the last one on this thread.
+ *    Malformed cu_seqlens contents (not monotone, not ending at T) give
+ *    unspecified values but every access stays inside [0, T); setting the
+ *    environment variable ATTN_VALIDATE=1 makes the varlen calls copy
+ *    cu_seqlens to the host (synchronously) and reject them as ATTN_E_INVALID.
+ */
+#ifndef VCA_ATTN_H
+#define VCA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* bad argument (NULL, size, stride, alignment, GQA) */
+  ATTN_E_UNSUPPORTED = -2, /* valid but not compiled: dtype or head-dim pair */
+  ATTN_E_WORKSPACE = -3,   /* workspace smaller than required */
+  ATTN_E_HIP = -4          /* a HIP runtime call failed; text has hipGetErrorString */
+};
+
+enum { ATTN_BF16 = 0, ATTN_F32 = 1 };
+
+/* Backward flags. ATTN_DQ_ACCUMULATE: dq += this call's dq (the sum is taken
+ * in fp32 and rounded once to bf16), so per-chunk backward passes of one
+ * query shard sum their dq in place, as a ring's local dq sum does
+ * ("gemma4_moe cp_attention" page, FFPA ring backward entries). */
+enum { ATTN_DQ_ACCUMULATE = 1 };
+
+/* Text of the last non-zero status returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+/* 1 if (dtype, Dqk, Dv) is compiled in, else 0. Analogue of the readiness
+ * probes on the "ffpa_attention" page (varlen/low-level "ready" functions). */
+int attn_is_supported(int dtype, int dqk, int dv);
+
+/* Dense forward ("ffpa_attention" page, dense forward entry).
+ *  q   [B, Hq,  Nq, Dqk]   k [B, Hkv, Nk, Dqk]   v [B, Hkv, Nk, Dv]
+ *  out [B, Hq,  Nq, Dv]  (written)    lse [B, Hq, Nq] fp32 contiguous (written)
+ *  strides[12] = element strides (b, h, n) of q, k, v, out, in that order
+ *  (so both BHND- and BSHD-contiguous storage work). Nq may differ from Nk;
+ *  with causal = 1 the mask is bottom-right aligned (query i sees keys
+ *  j <= i + Nk - Nq). Dense calls need no workspace (size 0). */
+int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void* out,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv,
+                   const int64_t* strides, float scale, int causal, void* workspace,
+                   size_t* workspace_bytes, hipStream_t stream);
+
+/* Varlen forward on packed THD tensors ("ffpa_attention" page, varlen forward
+ * entry, returning out[T,Hq,D] and lse[Hq,T]).
+ *  q [Tq, Hq, Dqk]  k [Tk, Hkv, Dqk]  v [Tk, Hkv, Dv]  out [Tq, Hq, Dv]
+ *  lse [Hq, Tq] fp32 contiguous.
+ *  cu_q, cu_k: device int32 [num_segments + 1]; segment s pairs query rows
+ *  cu_q[s]..cu_q[s+1] with key rows cu_k[s]..cu_k[s+1]. Required:
+ *  cu_q[0] = cu_k[0] = 0, non-decreasing, cu_q[S] = Tq, cu_k[S] = Tk.
+ *  Zero-query and zero-key segments are allowed.
+ *  max_q, max_k: host upper bounds of the per-segment lengths (grid sizing).
+ *  strides[8] = element strides (t, h) of q, k, v, out. */
+int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* out,
+                    float* lse, const int32_t* cu_q, const int32_t* cu_k, int num_segments,
+                    int max_q, int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                    const int64_t* strides, float scale, int causal, void* workspace,
+                    size_t* workspace_bytes, hipStream_t stream);
+
+/* Dense backward from the caller's out/lse ("ffpa_attention" page, dense
+ * backward entry). dout, out [B,Hq,Nq,Dv]; lse [B,Hq,Nq] fp32 contiguous;
+ * dq [B,Hq,Nq,Dqk]; dk [B,Hkv,Nk,Dqk]; dv [B,Hkv,Nk,Dv] (dk/dv summed over the
+ * q-heads of each GQA group).
+ * strides[24] = (b, h, n) strides of q, k, v, out, dout, dq, dk, dv.
+ * Needs a workspace (query it with workspace = NULL). flags: ATTN_DQ_*. */
+int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                   const void* out, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
+                   float scale, int causal, int flags, void* workspace,
+                   size_t* workspace_bytes, hipStream_t stream);
+
+/* Varlen backward from the caller's out/lse ("ffpa_attention" page, varlen
+ * backward entry, returning (dq, dk, dv)). Shapes as in attn_fwd_varlen, with
+ * dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv].
+ * strides[16] = (t, h) strides of q, k, v, out, dout, dq, dk, dv. */
+int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                    const void* out, const float* lse, void* dq, void* dk, void* dv,
+                    const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                    int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                    const int64_t* strides, float scale, int causal, int flags,
+                    void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/* Online-softmax merge of two partial results of the same query rows
+ * ("gemma4_moe cp_attention" page, -inf-safe merge entry).
+ *  out_a, out_b: [rows, H, Dv] contiguous, element type dtype_a / dtype_b
+ *  (ATTN_BF16 or ATTN_F32); lse_a, lse_b: [H, rows] fp32.
+ *  out: [rows, H, Dv] fp32 (written); lse: [H, rows] fp32 (written);
+ *  out_bf16: optional (may be NULL) bf16 copy of out, RNE, for feeding the
+ *  backward. out may alias out_a when dtype_a is ATTN_F32, and lse may alias
+ *  lse_a (running-accumulator use). Rows where both lse are -inf get out 0 and
+ *  lse -inf. No workspace. */
+int attn_merge(const void* out_a, int dtype_a, const float* lse_a, const void* out_b,
+               int dtype_b, const float* lse_b, float* out, float* lse, void* out_bf16,
+               int rows, int H, int Dv, hipStream_t stream);
+
+/* Document-causal segment layout ("fa4" page, module overview and the
+ * _varlen_segments / _varlen_layout entries). Host-only, no GPU work.
+ *  doc_ids: host int32 [B, S] document ids of each row (1-based, 0 = padding).
+ *  Queries are the positions [q_start, q_start + q_len) of every row; keys
+ *  are the positions [k_start, k_start + k_len).
+ *  mode 0 (causal, keys cover the queries: k_start <= q_start and
+ *  q_start + q_len <= k_start + k_len): every run of equal ids is split at the
+ *  query-shard end; a piece that overlaps the shard pairs its queries with all
+ *  of its keys (bottom-right causal gives "query at p sees its document's keys
+ *  up to p"); pieces without queries become zero-query segments. Padding
+ *  (id 0) pieces become a query-only segment followed by a key-only segment,
+ *  so padding neither attends nor is attended.
+ *  mode 1 (cross, keys entirely before the queries: k_start + k_len <=
+ *  q_start; run the result with causal = 0): one segment per run in order of
+ *  position, pairing a document's queries with its keys in the key range;
+ *  unshared runs get zero queries or zero keys.
+ *  Outputs (host int32): seg_q[max_segments], seg_k[max_segments] lengths in
+ *  flattened row-major order; *num_segments receives the count. Segment
+ *  query lengths tile the B*q_len queries and key lengths the B*k_len keys.
+ *  Returns ATTN_E_INVALID on bad ranges or when max_segments is too small
+ *  (then *num_segments holds the count needed). */
+int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                      int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
+                      int max_segments, int* num_segments);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VCA_ATTN_H */

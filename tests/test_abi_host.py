@@ -1,0 +1,189 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/attn.h declares, rejects bad arguments before any launch,
+answers workspace queries, and builds document-causal segment layouts."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as orc
+from varlen_causal_attention_amd import _lib
+from varlen_causal_attention_amd.ops import doc_segments
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = set(re.findall(r"^\s*(?:const\s+char\*|int)\s+(attn_\w+)\s*\(",
+                              open(HEADER).read(), flags=re.M))
+    assert declared == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_support_table(lib):
+    assert lib.attn_version() >= 10000
+    for dqk, dv in [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]:
+        assert lib.attn_is_supported(_lib.ATTN_BF16, dqk, dv) == 1
+    assert lib.attn_is_supported(_lib.ATTN_BF16, 96, 96) == 0
+    assert lib.attn_is_supported(_lib.ATTN_F32, 128, 128) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned stand-in address; never dereferenced on these paths
+
+
+def _dense(lib, **kw):
+    a = dict(dtype=0, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Nq=8, Nk=8,
+             Dqk=128, Dv=128, strides=[8 * 128 * 4, 8 * 128, 128] * 4, scale=0.1, causal=1)
+    a.update(kw)
+    s = _lib.i64_array(a["strides"]) if a["strides"] is not None else None
+    need = C.c_size_t(12345)
+    st = lib.attn_fwd_dense(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                            a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["Dqk"], a["Dv"], s, a["scale"],
+                            a["causal"], None, C.byref(need), None)
+    return st, need.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), _lib.ATTN_E_INVALID),
+    (dict(Hkv=0), _lib.ATTN_E_INVALID),
+    (dict(Dqk=96, Dv=96), _lib.ATTN_E_UNSUPPORTED),
+    (dict(Dqk=128, Dv=64), _lib.ATTN_E_UNSUPPORTED),
+    (dict(dtype=1), _lib.ATTN_E_UNSUPPORTED),
+    (dict(q=FAKE + 2), _lib.ATTN_E_INVALID),
+    (dict(q=0), _lib.ATTN_E_INVALID),
+    (dict(lse=0), _lib.ATTN_E_INVALID),
+    (dict(strides=[8 * 128 * 4, 8 * 128, 130] * 4), _lib.ATTN_E_INVALID),
+    (dict(strides=None), _lib.ATTN_E_INVALID),
+    (dict(Nq=-1), _lib.ATTN_E_INVALID),
+    (dict(scale=float("nan")), _lib.ATTN_E_INVALID),
+])
+def test_dense_forward_rejects_bad_arguments(lib, kw, status):
+    st, _ = _dense(lib, **kw)
+    assert st == status
+    assert lib.attn_last_error().decode()
+
+
+def test_dense_forward_workspace_query(lib):
+    st, need = _dense(lib)
+    assert st == 0 and need == 0
+    assert lib.attn_last_error().decode() == ""
+
+
+def _bwd_varlen(lib, ws=None, have=None, **kw):
+    a = dict(Tq=100, Tk=120, Hq=8, Hkv=2, Dqk=192, Dv=128, nseg=3, max_q=50, max_k=60, flags=0)
+    a.update(kw)
+    strides = _lib.i64_array([8 * 256, 256] * 8)
+    need = C.c_size_t(have if have is not None else 0)
+    st = lib.attn_bwd_varlen(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             a["nseg"], a["max_q"], a["max_k"], a["Tq"], a["Tk"], a["Hq"],
+                             a["Hkv"], a["Dqk"], a["Dv"], strides, 0.1, 1, a["flags"], ws,
+                             C.byref(need), None)
+    return st, need.value
+
+
+def test_backward_workspace_query_and_shortage(lib):
+    st, need = _bwd_varlen(lib)
+    assert st == 0
+    assert need >= 4 * 8 * 100 and need % 256 == 0
+    st, _ = _bwd_varlen(lib, ws=FAKE, have=need - 1)
+    assert st == _lib.ATTN_E_WORKSPACE
+    st, _ = _bwd_varlen(lib, flags=4)
+    assert st == _lib.ATTN_E_INVALID
+    st, _ = _bwd_varlen(lib, max_k=0)
+    assert st == _lib.ATTN_E_INVALID
+
+
+def test_merge_rejects_bad_arguments(lib):
+    assert lib.attn_merge(FAKE, 2, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 4, 2, 8, None) == _lib.ATTN_E_UNSUPPORTED
+    assert lib.attn_merge(FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, -1, 2, 8, None) == _lib.ATTN_E_INVALID
+    assert lib.attn_merge(FAKE, 0, None, FAKE, 0, FAKE, FAKE, FAKE, None, 4, 2, 8, None) == _lib.ATTN_E_INVALID
+
+
+# ---------------------------------------------------------------- segments
+def _pairs_from_segments(sq, sk, q_pos, k_pos, causal):
+    """Expand a segment list into the set of visible (query pos, key pos)."""
+    vis = set()
+    qa = ka = 0
+    for lq, lk in zip(sq, sk):
+        v = orc.segment_visible(lq, lk, causal)
+        for i in range(lq):
+            for j in range(lk):
+                if v[i, j]:
+                    vis.add((int(q_pos[qa + i]), int(k_pos[ka + j])))
+        qa += lq
+        ka += lk
+    return vis
+
+
+def _pairs_from_ids(ids, q_pos, k_pos):
+    v = orc.doc_causal_visible(ids[q_pos], q_pos, ids[k_pos], k_pos)
+    return {(int(q_pos[i]), int(k_pos[j])) for i, j in zip(*np.nonzero(v))}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_causal_segments_reproduce_the_document_mask(seed):
+    rng = np.random.default_rng(seed)
+    S = 40
+    lens = []
+    while sum(lens) < S - 5:
+        lens.append(int(rng.integers(1, 9)))
+    ids = np.zeros(S, dtype=np.int32)
+    pos = 0
+    for d, n in enumerate(lens, start=1):
+        ids[pos:pos + n] = d
+        pos += n
+    q_start, q_len = int(rng.integers(0, 20)), int(rng.integers(1, 15))
+    k_start = int(rng.integers(0, q_start + 1))
+    k_len = int(rng.integers(q_start + q_len - k_start, S - k_start + 1))
+    sq, sk = doc_segments(ids[None], q_start, q_len, k_start, k_len, 0)
+    assert sum(sq) == q_len and sum(sk) == k_len
+    q_pos = np.arange(q_start, q_start + q_len)
+    k_pos = np.arange(k_start, k_start + k_len)
+    assert _pairs_from_segments(sq, sk, q_pos, k_pos, True) == _pairs_from_ids(ids, q_pos, k_pos)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cross_segments_reproduce_the_document_mask(seed):
+    rng = np.random.default_rng(100 + seed)
+    S = 48
+    ids = np.repeat(np.arange(1, 13, dtype=np.int32), rng.integers(1, 7, size=12))[:S]
+    ids = np.concatenate([ids, np.zeros(S - len(ids), dtype=np.int32)])
+    k_start, k_len = 0, int(rng.integers(5, 24))
+    q_start = int(rng.integers(k_len, S - 4))
+    q_len = int(rng.integers(1, S - q_start + 1))
+    sq, sk = doc_segments(ids[None], q_start, q_len, k_start, k_len, 1)
+    assert sum(sq) == q_len and sum(sk) == k_len
+    q_pos = np.arange(q_start, q_start + q_len)
+    k_pos = np.arange(k_start, k_start + k_len)
+    assert _pairs_from_segments(sq, sk, q_pos, k_pos, False) == _pairs_from_ids(ids, q_pos, k_pos)
+
+
+def test_ring_workload_layout():
+    """The ring workload's two chunks: local causal and earlier cross."""
+    w = workloads.workload(5)
+    ids = w.row_doc_ids()
+    sq, sk = doc_segments(ids, 4096, 4096, 4096, 4096, 0)
+    assert list(np.cumsum([0] + sq)) == [0, 2084, 2427, 3968, 4096, 4096]
+    assert list(np.cumsum([0] + sk)) == [0, 2084, 2427, 3968, 3968, 4096]
+    sq, sk = doc_segments(ids, 4096, 4096, 0, 4096, 1)
+    assert list(np.cumsum([0] + sq)) == [0, 0, 2084, 2427, 3968, 4096]
+    assert list(np.cumsum([0] + sk)) == [0, 2832, 4096, 4096, 4096, 4096]
+
+
+def test_segment_builder_rejects_bad_ranges():
+    ids = np.ones((1, 10), dtype=np.int32)
+    with pytest.raises(ValueError):
+        doc_segments(ids, 2, 4, 3, 5, 0)   # keys do not cover the queries
+    with pytest.raises(ValueError):
+        doc_segments(ids, 2, 4, 0, 5, 1)   # keys overlap the queries
+    with pytest.raises(ValueError):
+        doc_segments(ids, 8, 4, 0, 10, 0)  # queries past the row

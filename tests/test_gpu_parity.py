@@ -1,0 +1,377 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle on the
+same seeded bf16 inputs.
+
+Tolerances (fixed for N(0,1) bf16 inputs): out max-abs <= 2e-2; lse max-abs
+<= 5e-3 on finite entries with the -inf pattern matching exactly; dq, dk, dv
+relative Frobenius error <= 5e-2. The oracle computes the backward from its
+own forward (never from GPU outputs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as orc
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL, LSE_TOL, GRAD_TOL = 2e-2, 5e-3, 5e-2
+
+
+@pytest.fixture(scope="module")
+def vca():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import varlen_causal_attention_amd as m
+
+    m.load()
+    return m
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_out(out, ref, tol=OUT_TOL):
+    err = np.abs(host(out) - ref).max() if ref.size else 0.0
+    assert err <= tol, f"out max-abs {err}"
+
+
+def check_lse(lse, ref):
+    got = host(lse)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf rows differ"
+    assert not np.isnan(got).any()
+    fin = np.isfinite(ref)
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin]).max()
+        assert err <= LSE_TOL, f"lse max-abs {err}"
+
+
+def check_grad(name, g, ref):
+    g = host(g)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(g - ref)
+    if den == 0:
+        assert num == 0, f"{name}: expected zeros"
+        return
+    assert num / den <= GRAD_TOL, f"{name} rel-Frobenius {num / den}"
+
+
+def rand(shape, g):
+    return workloads.randn_bf16(shape, g)
+
+
+# ---------------------------------------------------------------- varlen
+def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed):
+    g = torch.Generator().manual_seed(seed)
+    cu_q, cu_k = workloads.cumulative(lens_q), workloads.cumulative(lens_k)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    q, k, v = rand((Tq, Hq, Dqk), g), rand((Tk, Hkv, Dqk), g), rand((Tk, Hkv, Dv), g)
+    do = rand((Tq, Hq, Dv), g)
+    scale = 1.0 / math.sqrt(Dqk)
+    ro, rl = orc.fwd_varlen(q, k, v, cu_q, cu_k, scale, causal)
+    rdq, rdk, rdv = orc.bwd_varlen(do, q, k, v, ro, rl, cu_q, cu_k, scale, causal)
+    cq, ck = dev(torch.from_numpy(cu_q)), dev(torch.from_numpy(cu_k))
+    mq, mk = max(lens_q, default=0), max(lens_k, default=0)
+    out, lse = vca.fwd_varlen(dev(q), dev(k), dev(v), cq, ck, mq, mk, scale, causal)
+    dq, dk, dv = vca.bwd_varlen(dev(do), dev(q), dev(k), dev(v), out, lse, cq, ck, mq, mk, scale,
+                                causal)
+    torch.cuda.synchronize()
+    check_out(out, ro)
+    check_lse(lse, rl)
+    check_grad("dq", dq, rdq)
+    check_grad("dk", dk, rdk)
+    check_grad("dv", dv, rdv)
+    return out, lse, (dq, dk, dv), (ro, rl)
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_every_head_dim(vca, dqk, dv, causal):
+    lens = [1, 37, 200, 129, 64, 300]
+    run_varlen(vca, lens, lens, 4, 2, dqk, dv, causal, seed=11 + dqk + dv + causal)
+
+
+def test_varlen_ragged_unequal_segments(vca):
+    # lq != lk per segment, zero-query and zero-key segments, lq > lk (empty rows)
+    lens_q = [5, 0, 130, 70, 0, 3, 33]
+    lens_k = [9, 40, 100, 70, 12, 0, 65]
+    for causal in (True, False):
+        run_varlen(vca, lens_q, lens_k, 8, 2, 128, 128, causal, seed=21 + causal)
+
+
+def test_varlen_gqa_group_sizes(vca):
+    lens = [77, 300, 5]
+    for hq, hkv in [(1, 1), (8, 1), (8, 8), (6, 2)]:
+        run_varlen(vca, lens, lens, hq, hkv, 128, 128, True, seed=31 + hq + hkv)
+
+
+def test_empty_rows_are_exact(vca):
+    out, lse, grads, (ro, rl) = run_varlen(vca, [4, 6], [0, 3], 2, 1, 128, 128, True, seed=41)
+    o, l = host(out), host(lse)
+    assert np.all(o[:4] == 0.0) and np.all(np.isneginf(l[:, :4]))
+    # second segment: lq=6 > lk=3, bottom-right leaves its first 3 rows empty
+    assert np.all(o[4:7] == 0.0) and np.all(np.isneginf(l[:, 4:7]))
+    assert np.all(host(grads[0])[:7] == 0.0)
+
+
+# ---------------------------------------------------------------- dense
+def run_dense(vca, B, Hq, Hkv, Nq, Nk, Dqk, Dv, causal, seed, layout="bhnd"):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = rand((B, Hq, Nq, Dqk), g), rand((B, Hkv, Nk, Dqk), g), rand((B, Hkv, Nk, Dv), g)
+    do = rand((B, Hq, Nq, Dv), g)
+    scale = 1.0 / math.sqrt(Dqk)
+    ro, rl = orc.fwd_dense(q, k, v, scale, causal)
+    rg = orc.bwd_dense(do, q, k, v, ro, rl, scale, causal)
+
+    def put(t):
+        if layout == "bshd":  # BSHD storage viewed as [B, H, S, D]
+            return dev(t.transpose(1, 2).contiguous()).transpose(1, 2)
+        return dev(t)
+
+    out, lse = vca.fwd_dense(put(q), put(k), put(v), scale, causal)
+    dq, dk, dv = vca.bwd_dense(put(do), put(q), put(k), put(v), out, lse, scale, causal)
+    torch.cuda.synchronize()
+    check_out(out, ro)
+    check_lse(lse, rl)
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), rg):
+        check_grad(name, a, b)
+    return out, lse
+
+
+def test_dense_small_causal_workload(vca):
+    w = workloads.workload(1)
+    t = w.tensors()
+    ro, rl = orc.fwd_dense(t["q"], t["k"], t["v"], w.scale, True)
+    rg = orc.bwd_dense(t["do"], t["q"], t["k"], t["v"], ro, rl, w.scale, True)
+    out, lse = vca.fwd_dense(dev(t["q"]), dev(t["k"]), dev(t["v"]), w.scale, True)
+    grads = vca.bwd_dense(dev(t["do"]), dev(t["q"]), dev(t["k"]), dev(t["v"]), out, lse, w.scale, True)
+    torch.cuda.synchronize()
+    check_out(out, ro)
+    check_lse(lse, rl)
+    for name, a, b in zip(("dq", "dk", "dv"), grads, rg):
+        check_grad(name, a, b)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(130, 300), (300, 130), (257, 257)])
+def test_dense_bottom_right_alignment(vca, Nq, Nk):
+    run_dense(vca, 2, 4, 2, Nq, Nk, 128, 128, True, seed=51 + Nq)
+
+
+def test_dense_bshd_views_and_d512(vca):
+    run_dense(vca, 1, 4, 2, 200, 200, 128, 128, True, seed=61, layout="bshd")
+    run_dense(vca, 1, 2, 1, 160, 160, 512, 512, True, seed=62, layout="bshd")
+    run_dense(vca, 1, 4, 4, 96, 96, 192, 128, False, seed=63)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def _segment_slice_check(vca, w, t, seg, kv_heads):
+    """Run the whole workload on the GPU; check one segment x kv-head groups
+    against the oracle, computed fully for that slice."""
+    cu = w.cu()
+    cq = dev(torch.from_numpy(cu))
+    mx = max(w.lengths)
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    out, lse = vca.fwd_varlen(q, k, v, cq, cq, mx, mx, w.scale, w.causal)
+    dq, dk, dv = vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, mx, mx, w.scale, w.causal)
+    torch.cuda.synchronize()
+    a, b = int(cu[seg]), int(cu[seg + 1])
+    G = w.Hq // w.Hkv
+    for g in kv_heads:
+        hs = list(range(g * G, (g + 1) * G))
+        sl = lambda x, heads: x[a:b][:, heads]  # noqa: E731
+        qq, kk, vv, dd = sl(t["q"], hs), sl(t["k"], [g]), sl(t["v"], [g]), sl(t["do"], hs)
+        cu1 = [0, b - a]
+        ro, rl = orc.fwd_varlen(qq, kk, vv, cu1, cu1, w.scale, w.causal)
+        rdq, rdk, rdv = orc.bwd_varlen(dd, qq, kk, vv, ro, rl, cu1, cu1, w.scale, w.causal)
+        check_out(out[a:b][:, hs], ro)
+        check_lse(lse[hs][:, a:b], rl)
+        check_grad("dq", dq[a:b][:, hs], rdq)
+        check_grad("dk", dk[a:b][:, [g]], rdk)
+        check_grad("dv", dv[a:b][:, [g]], rdv)
+    return out, lse, (dq, dk, dv)
+
+
+def test_varlen_d128_workload_full_size(vca):
+    w = workloads.workload(2)
+    t = w.tensors()
+    out, lse, grads = _segment_slice_check(vca, w, t, seg=0, kv_heads=[0, 7])
+    _segment_slice_check(vca, w, t, seg=7, kv_heads=[3])
+    # properties at full size: finite everywhere, no empty row in causal self-attention
+    assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
+    for gtn in grads:
+        assert torch.isfinite(gtn.float()).all()
+
+
+def test_varlen_192_128_workload_full_size(vca):
+    w = workloads.workload(4)
+    t = w.tensors()
+    _segment_slice_check(vca, w, t, seg=4, kv_heads=[13])
+
+
+def test_dense_d512_workload_full_size(vca):
+    w = workloads.workload(3)
+    t = w.tensors()
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    out, lse = vca.fwd_dense(q, k, v, w.scale, True)
+    dq, dk, dv = vca.bwd_dense(do, q, k, v, out, lse, w.scale, True)
+    torch.cuda.synchronize()
+    b, g = 1, 5
+    G = w.Hq // w.Hkv
+    hs = list(range(g * G, (g + 1) * G))
+    qq, kk, vv, dd = t["q"][b:b + 1, hs], t["k"][b:b + 1, [g]], t["v"][b:b + 1, [g]], t["do"][b:b + 1, hs]
+    ro, rl = orc.fwd_dense(qq, kk, vv, w.scale, True)
+    rdq, rdk, rdv = orc.bwd_dense(dd, qq, kk, vv, ro, rl, w.scale, True)
+    check_out(out[b:b + 1, hs], ro)
+    check_lse(lse[b:b + 1, hs], rl)
+    check_grad("dq", dq[b:b + 1, hs], rdq)
+    check_grad("dk", dk[b:b + 1, [g]], rdk)
+    check_grad("dv", dv[b:b + 1, [g]], rdv)
+    assert torch.isfinite(lse).all()
+
+
+def ring_share(vca, w, t):
+    """One rank's ring share on the GPU: local causal chunk, earlier cross chunk,
+    lse merge, then both chunk backwards from the merged out/lse (dq summed)."""
+    ids = w.row_doc_ids()
+    S = w.shard
+    lq_cu, lk_cu, lmq, lmk = vca.doc_layout(ids, S, S, S, S, 0, "cuda")
+    xq_cu, xk_cu, xmq, xmk = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
+    q, do = dev(t["q"]), dev(t["do"])
+    kl, vl, ke, ve = (dev(t[n]) for n in ("k_local", "v_local", "k_early", "v_early"))
+    o1, l1 = vca.fwd_varlen(q, kl, vl, lq_cu, lk_cu, lmq, lmk, w.scale, True)
+    o2, l2 = vca.fwd_varlen(q, ke, ve, xq_cu, xk_cu, xmq, xmk, w.scale, False)
+    mo, ml, mob = vca.merge(o1, l1, o2, l2, bf16_copy=True)
+    dq, dkl, dvl = vca.bwd_varlen(do, q, kl, vl, mob, ml, lq_cu, lk_cu, lmq, lmk, w.scale, True)
+    _, dke, dve = vca.bwd_varlen(do, q, ke, ve, mob, ml, xq_cu, xk_cu, xmq, xmk, w.scale, False,
+                                 dq_accumulate=dq)
+    return (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve)
+
+
+def test_ring_share_workload(vca):
+    w = workloads.workload(5)
+    t = w.tensors()
+    (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve) = ring_share(vca, w, t)
+    torch.cuda.synchronize()
+    ids = w.row_doc_ids()[0]
+    S = w.shard
+    q_pos, loc_pos, early_pos = np.arange(S, 2 * S), np.arange(S, 2 * S), np.arange(0, S)
+    G = w.Hq // w.Hkv
+    for g in (0, 6):
+        hs = list(range(g * G, (g + 1) * G))
+        q, do = t["q"][:, hs], t["do"][:, hs]
+        kl, vl = t["k_local"][:, [g]], t["v_local"][:, [g]]
+        ke, ve = t["k_early"][:, [g]], t["v_early"][:, [g]]
+        k_all, v_all = torch.cat([ke, kl]), torch.cat([ve, vl])
+        all_pos = np.arange(0, 2 * S)
+        ro, rl = orc.fwd_doc_causal(q, k_all, v_all, ids[q_pos], q_pos, ids[all_pos], all_pos, w.scale)
+        # per-chunk results and the merge
+        r1 = orc.fwd_doc_causal(q, kl, vl, ids[q_pos], q_pos, ids[loc_pos], loc_pos, w.scale)
+        r2 = orc.fwd_doc_causal(q, ke, ve, ids[q_pos], q_pos, ids[early_pos], early_pos, w.scale)
+        check_out(o1[:, hs], r1[0])
+        check_lse(l1[hs], r1[1])
+        check_out(o2[:, hs], r2[0])
+        check_lse(l2[hs], r2[1])
+        check_out(mo[:, hs], ro)
+        check_lse(ml[hs], rl)
+        rdq, rdk, rdv = orc.bwd_doc_causal(do, q, k_all, v_all, ro, rl, ids[q_pos], q_pos,
+                                           ids[all_pos], all_pos, w.scale)
+        check_grad("dq", dq[:, hs], rdq)
+        check_grad("dk_early", dke[:, [g]], rdk[:S])
+        check_grad("dv_early", dve[:, [g]], rdv[:S])
+        check_grad("dk_local", dkl[:, [g]], rdk[S:])
+        check_grad("dv_local", dvl[:, [g]], rdv[S:])
+    # padding queries: out 0, lse -inf, dq 0
+    pad = np.nonzero(ids[q_pos] == 0)[0]
+    assert len(pad) == w.pad_tail
+    assert torch.all(mo[pad] == 0) and torch.all(torch.isneginf(ml[:, pad]))
+    assert torch.all(dq[pad] == 0)
+
+
+def test_merge_kernel_against_oracle(vca):
+    g = torch.Generator().manual_seed(71)
+    rows, H, Dv = 300, 4, 512
+    oa, ob = rand((rows, H, Dv), g), rand((rows, H, Dv), g).float()
+    la = torch.randn((H, rows), generator=g) * 3
+    lb = torch.randn((H, rows), generator=g) * 3
+    la[0, :50] = -math.inf
+    lb[0, 25:75] = -math.inf
+    lb[1, :10] = -math.inf
+    ro, rl = orc.merge(oa, la, ob, lb)
+    mo, ml, mob = vca.merge(dev(oa), dev(la), dev(ob), dev(lb), bf16_copy=True)
+    torch.cuda.synchronize()
+    assert np.abs(host(mo) - ro).max() < 1e-5
+    check_lse(ml, rl)
+    assert torch.equal(mob, mo.to(torch.bfloat16))
+    # running-accumulator use: out aliases out_a, lse aliases lse_a
+    acc, lacc = dev(oa.float()), dev(la.clone())
+    vca.merge(acc, lacc, dev(ob), dev(lb), out=acc, lse=lacc)
+    torch.cuda.synchronize()
+    assert np.abs(host(acc) - ro).max() < 1e-5
+    check_lse(lacc, rl)
+
+
+# ---------------------------------------------------------------- robustness
+def test_results_are_bitwise_deterministic(vca):
+    w = workloads.small_varlen(81, [500, 33, 700], 8, 2, 128, 128)
+    t = w.tensors()
+    cq = dev(torch.from_numpy(w.cu()))
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    res = []
+    for _ in range(2):
+        out, lse = vca.fwd_varlen(q, k, v, cq, cq, 700, 700, w.scale, True)
+        grads = vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, 700, 700, w.scale, True)
+        res.append([x.clone() for x in (out, lse, *grads)])
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+def test_outputs_stay_inside_their_views(vca):
+    """Guard bands: outputs written through strided views of larger NaN-filled
+    buffers leave every element outside the view untouched."""
+    import ctypes as C
+    from varlen_causal_attention_amd import _lib
+
+    lib = _lib.load()
+    g = torch.Generator().manual_seed(91)
+    B, Hq, Hkv, N, D = 2, 4, 2, 150, 128
+    q, k, v = (dev(rand(s, g)) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D)))
+    big = torch.full((B, Hq + 1, N + 16, D + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = big[:, 1:, 8:8 + N, 32:32 + D]
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    strides = _lib.i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
+                             + list(out.stride()[:3]))
+    st = lib.attn_fwd_dense(0, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                            C.c_void_p(v.data_ptr()), C.c_void_p(out.data_ptr()),
+                            C.c_void_p(lse.data_ptr()), B, Hq, Hkv, N, N, D, D, strides,
+                            1 / math.sqrt(D), 1, None, None,
+                            C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, lib.attn_last_error()
+    torch.cuda.synchronize()
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, 1:, 8:8 + N, 32:32 + D] = False
+    assert torch.isnan(big[mask].float()).all()
+    assert torch.isfinite(out.float()).all()
+    ref, _ = vca.fwd_dense(q, k, v, 1 / math.sqrt(D), True)
+    assert torch.equal(ref, out)
+
+
+def test_dq_accumulate_adds(vca):
+    w = workloads.small_varlen(93, [90, 200], 4, 2, 128, 128)
+    t = w.tensors()
+    cq = dev(torch.from_numpy(w.cu()))
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    out, lse = vca.fwd_varlen(q, k, v, cq, cq, 200, 200, w.scale, True)
+    dq1, _, _ = vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, 200, 200, w.scale, True)
+    acc = dq1.clone()
+    vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, 200, 200, w.scale, True, dq_accumulate=acc)
+    torch.cuda.synchronize()
+    ref = dq1.float() * 2
+    assert (acc.float() - ref).abs().max().item() <= 2 ** -7 * ref.abs().max().item() + 1e-6

@@ -1,0 +1,89 @@
+"""ctypes loader for libvca_attn.so: signatures and status handling only.
+
+The library must have been built in-tree (``python -m
+varlen_causal_attention_amd.build``); there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvca_attn.so")
+
+ATTN_OK = 0
+ATTN_E_INVALID = -1
+ATTN_E_UNSUPPORTED = -2
+ATTN_E_WORKSPACE = -3
+ATTN_E_HIP = -4
+ATTN_BF16 = 0
+ATTN_F32 = 1
+ATTN_DQ_ACCUMULATE = 1
+
+EXPORTED = (
+    "attn_last_error", "attn_version", "attn_is_supported", "attn_fwd_dense", "attn_fwd_varlen",
+    "attn_bwd_dense", "attn_bwd_varlen", "attn_merge", "attn_doc_segments",
+)
+
+_P = C.c_void_p
+_I = C.c_int
+_F = C.c_float
+_I64P = C.POINTER(C.c_int64)
+_SZP = C.POINTER(C.c_size_t)
+_I32P = C.POINTER(C.c_int32)
+
+_SIGS = {
+    "attn_last_error": (C.c_char_p, []),
+    "attn_version": (_I, []),
+    "attn_is_supported": (_I, [_I, _I, _I]),
+    "attn_fwd_dense": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64P, _F, _I,
+                            _P, _SZP, _P]),
+    "attn_fwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                             _I64P, _F, _I, _P, _SZP, _P]),
+    "attn_bwd_dense": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                            _I64P, _F, _I, _I, _P, _SZP, _P]),
+    "attn_bwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                             _I, _I, _I, _I, _I64P, _F, _I, _I, _P, _SZP, _P]),
+    "attn_merge": (_I, [_P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "attn_doc_segments": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,
+                               C.POINTER(C.c_int)]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A HIP runtime failure reported by the library."""
+
+
+def load() -> C.CDLL:
+    """Load the built library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m varlen_causal_attention_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(status: int, what: str) -> None:
+    """Map a status code to an exception (ValueError for argument problems)."""
+    if status == ATTN_OK:
+        return
+    msg = load().attn_last_error().decode()
+    if status == ATTN_E_HIP:
+        raise AttnError(f"{what}: {msg}")
+    kind = {ATTN_E_INVALID: "invalid", ATTN_E_UNSUPPORTED: "unsupported",
+            ATTN_E_WORKSPACE: "workspace"}.get(status, f"status {status}")
+    raise ValueError(f"{what}: {kind}: {msg}")
+
+
+def i64_array(values) -> C.Array:
+    arr = (C.c_int64 * len(values))(*[int(x) for x in values])
+    return arr

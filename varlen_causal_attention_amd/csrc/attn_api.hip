@@ -1,0 +1,332 @@
+// C ABI of the attention library: argument validation, workspace sizing,
+// cu_seqlens checking on request, and kernel dispatch. Every check that can be
+// made on the host runs before any HIP call, so invalid calls fail without a
+// GPU and without launching anything.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "attn_error.hpp"
+#include "attn_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int ok() { return ATTN_OK; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int dtype, int Hq, int Hkv, int Dqk, int Dv, float scale) {
+  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "dtype must be ATTN_BF16");
+  if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID, "Hq and Hkv must be positive");
+  if (Hq % Hkv != 0) return fail(ATTN_E_INVALID, "Hq must be a multiple of Hkv (GQA)");
+  if (!vca::head_dims_supported(Dqk, Dv))
+    return fail(ATTN_E_UNSUPPORTED, "head dims (" + std::to_string(Dqk) + "," +
+                                        std::to_string(Dv) + ") not compiled in");
+  if (!std::isfinite(scale)) return fail(ATTN_E_INVALID, "scale must be finite");
+  return ATTN_OK;
+}
+
+int check_tensor(const char* name, const void* p, bool nonempty, const int64_t* strides, int n) {
+  if (nonempty && p == nullptr) return fail(ATTN_E_INVALID, std::string(name) + " is NULL");
+  if (p && !aligned16(p)) return fail(ATTN_E_INVALID, std::string(name) + " is not 16-byte aligned");
+  for (int i = 0; i < n; ++i) {
+    if (strides[i] < 0 || strides[i] % 8 != 0)
+      return fail(ATTN_E_INVALID, std::string(name) + " strides must be non-negative multiples of 8");
+  }
+  return ATTN_OK;
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// workspace protocol: (workspace == NULL && workspace_bytes != NULL) is a size
+// query; otherwise a call that needs `need` bytes must be given them.
+int workspace_step(size_t need, void* ws, size_t* ws_bytes, bool* query) {
+  *query = false;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    *query = true;
+    return ATTN_OK;
+  }
+  if (need == 0) return ATTN_OK;
+  if (ws == nullptr || ws_bytes == nullptr || *ws_bytes < need)
+    return fail(ATTN_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes required");
+  if (!aligned16(ws)) return fail(ATTN_E_INVALID, "workspace is not 16-byte aligned");
+  return ATTN_OK;
+}
+
+bool validate_env() {
+  const char* e = std::getenv("ATTN_VALIDATE");
+  return e && e[0] == '1';
+}
+
+// Host copy of cu_seqlens and a full contract check (ATTN_VALIDATE=1 only).
+int validate_cu(const int32_t* cu_q, const int32_t* cu_k, int S, int Tq, int Tk, int max_q,
+                int max_k, hipStream_t st) {
+  std::vector<int32_t> hq(S + 1), hk(S + 1);
+  hipError_t e = hipMemcpyAsync(hq.data(), cu_q, sizeof(int32_t) * (S + 1), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(hk.data(), cu_k, sizeof(int32_t) * (S + 1), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("cu_seqlens copy: ") + hipGetErrorString(e));
+  if (hq[0] != 0 || hk[0] != 0) return fail(ATTN_E_INVALID, "cu_seqlens must start at 0");
+  if (hq[S] != Tq || hk[S] != Tk) return fail(ATTN_E_INVALID, "cu_seqlens must end at Tq / Tk");
+  for (int s = 0; s < S; ++s) {
+    const int lq = hq[s + 1] - hq[s], lk = hk[s + 1] - hk[s];
+    if (lq < 0 || lk < 0) return fail(ATTN_E_INVALID, "cu_seqlens must be non-decreasing");
+    if (lq > max_q || lk > max_k) return fail(ATTN_E_INVALID, "segment longer than max_q / max_k");
+  }
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+vca::View view(const void* p, int64_t sb, int64_t sh, int64_t sn) {
+  return vca::View{static_cast<const uint16_t*>(p), sb, sh, sn};
+}
+vca::ViewW vieww(void* p, int64_t sb, int64_t sh, int64_t sn) {
+  return vca::ViewW{static_cast<uint16_t*>(p), sb, sh, sn};
+}
+
+}  // namespace
+
+void vca::set_last_error(const std::string& msg) { g_last_error = msg; }
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_version(void) { return 10000; }
+
+int attn_is_supported(int dtype, int dqk, int dv) {
+  return dtype == ATTN_BF16 && vca::head_dims_supported(dqk, dv) ? 1 : 0;
+}
+
+int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
+                   float scale, int causal, void* workspace, size_t* workspace_bytes,
+                   hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  if (st) return st;
+  if (B < 0 || Nq < 0 || Nk < 0) return fail(ATTN_E_INVALID, "B, Nq, Nk must be >= 0");
+  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
+  const bool has_q = (int64_t)B * Nq > 0, has_k = (int64_t)B * Nk > 0;
+  if ((st = check_tensor("q", q, has_q, strides + 0, 3))) return st;
+  if ((st = check_tensor("k", k, has_k, strides + 3, 3))) return st;
+  if ((st = check_tensor("v", v, has_k, strides + 6, 3))) return st;
+  if ((st = check_tensor("out", out, has_q, strides + 9, 3))) return st;
+  if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  bool query = false;
+  if ((st = workspace_step(0, workspace, workspace_bytes, &query))) return st;
+  if (query || !has_q) return ok();
+
+  vca::FwdArgs a{};
+  a.q = view(q, strides[0], strides[1], strides[2]);
+  a.k = view(k, strides[3], strides[4], strides[5]);
+  a.v = view(v, strides[6], strides[7], strides[8]);
+  a.o = vieww(out, strides[9], strides[10], strides[11]);
+  a.lse = lse;
+  a.lse_sb = (int64_t)Hq * Nq;
+  a.lse_sh = Nq;
+  a.cu_q = a.cu_k = nullptr;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Tq = Nq;
+  a.Tk = Nk;
+  a.G = Hq / Hkv;
+  a.scale_log2 = scale * vca::kLog2e;
+  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, B, Hq, Nq, stream), "attn_fwd_dense launch");
+}
+
+int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                    int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                    const int64_t* strides, float scale, int causal, void* workspace,
+                    size_t* workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  if (st) return st;
+  if (num_segments < 0 || Tq < 0 || Tk < 0 || max_q < 0 || max_k < 0)
+    return fail(ATTN_E_INVALID, "sizes must be >= 0");
+  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
+  if (num_segments > 0 && (!cu_q || !cu_k)) return fail(ATTN_E_INVALID, "cu_seqlens is NULL");
+  if (num_segments == 0 && (Tq > 0 || Tk > 0))
+    return fail(ATTN_E_INVALID, "tokens given but no segments");
+  if (Tq > 0 && max_q < 1) return fail(ATTN_E_INVALID, "max_q must be >= 1 when Tq > 0");
+  if ((st = check_tensor("q", q, Tq > 0, strides + 0, 2))) return st;
+  if ((st = check_tensor("k", k, Tk > 0, strides + 2, 2))) return st;
+  if ((st = check_tensor("v", v, Tk > 0, strides + 4, 2))) return st;
+  if ((st = check_tensor("out", out, Tq > 0, strides + 6, 2))) return st;
+  if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  bool query = false;
+  if ((st = workspace_step(0, workspace, workspace_bytes, &query))) return st;
+  if (query || Tq == 0) return ok();
+  if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
+    return st;
+
+  vca::FwdArgs a{};
+  a.q = view(q, 0, strides[1], strides[0]);
+  a.k = view(k, 0, strides[3], strides[2]);
+  a.v = view(v, 0, strides[5], strides[4]);
+  a.o = vieww(out, 0, strides[7], strides[6]);
+  a.lse = lse;
+  a.lse_sb = 0;
+  a.lse_sh = Tq;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.Nq = a.Nk = 0;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.G = Hq / Hkv;
+  a.scale_log2 = scale * vca::kLog2e;
+  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, max_q, stream),
+                    "attn_fwd_varlen launch");
+}
+
+int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                   const void* out, const float* lse, void* dq, void* dk, void* dv, int B, int Hq,
+                   int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides, float scale,
+                   int causal, int flags, void* workspace, size_t* workspace_bytes,
+                   hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  if (st) return st;
+  if (B < 0 || Nq < 0 || Nk < 0) return fail(ATTN_E_INVALID, "B, Nq, Nk must be >= 0");
+  if (flags & ~ATTN_DQ_ACCUMULATE) return fail(ATTN_E_INVALID, "unknown flags");
+  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
+  const bool has_q = (int64_t)B * Nq > 0, has_k = (int64_t)B * Nk > 0;
+  const char* names[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+  const void* ptrs[8] = {q, k, v, out, dout, dq, dk, dv};
+  const bool need[8] = {has_q, has_k, has_k, has_q, has_q, has_q, has_k, has_k};
+  for (int i = 0; i < 8; ++i)
+    if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 3 * i, 3))) return st;
+  if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  const size_t need_ws = round_up(sizeof(float) * (size_t)B * Hq * Nq);
+  bool query = false;
+  if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
+  if (query || (!has_q && !has_k)) return ok();
+
+  vca::BwdArgs a{};
+  a.q = view(q, strides[0], strides[1], strides[2]);
+  a.k = view(k, strides[3], strides[4], strides[5]);
+  a.v = view(v, strides[6], strides[7], strides[8]);
+  a.o = view(out, strides[9], strides[10], strides[11]);
+  a.dout = view(dout, strides[12], strides[13], strides[14]);
+  a.dq = vieww(dq, strides[15], strides[16], strides[17]);
+  a.dk = vieww(dk, strides[18], strides[19], strides[20]);
+  a.dv = vieww(dv, strides[21], strides[22], strides[23]);
+  a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.lse_sb = (int64_t)Hq * Nq;
+  a.lse_sh = Nq;
+  a.cu_q = a.cu_k = nullptr;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Tq = Nq;
+  a.Tk = Nk;
+  a.G = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * vca::kLog2e;
+  a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
+  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, Nk, stream),
+                    "attn_bwd_dense launch");
+}
+
+int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                    const void* out, const float* lse, void* dq, void* dk, void* dv,
+                    const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                    int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                    const int64_t* strides, float scale, int causal, int flags, void* workspace,
+                    size_t* workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  if (st) return st;
+  if (num_segments < 0 || Tq < 0 || Tk < 0 || max_q < 0 || max_k < 0)
+    return fail(ATTN_E_INVALID, "sizes must be >= 0");
+  if (flags & ~ATTN_DQ_ACCUMULATE) return fail(ATTN_E_INVALID, "unknown flags");
+  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
+  if (num_segments > 0 && (!cu_q || !cu_k)) return fail(ATTN_E_INVALID, "cu_seqlens is NULL");
+  if (num_segments == 0 && (Tq > 0 || Tk > 0))
+    return fail(ATTN_E_INVALID, "tokens given but no segments");
+  if (Tq > 0 && max_q < 1) return fail(ATTN_E_INVALID, "max_q must be >= 1 when Tq > 0");
+  if (Tk > 0 && max_k < 1) return fail(ATTN_E_INVALID, "max_k must be >= 1 when Tk > 0");
+  const char* names[8] = {"q", "k", "v", "out", "dout", "dq", "dk", "dv"};
+  const void* ptrs[8] = {q, k, v, out, dout, dq, dk, dv};
+  const bool need[8] = {Tq > 0, Tk > 0, Tk > 0, Tq > 0, Tq > 0, Tq > 0, Tk > 0, Tk > 0};
+  for (int i = 0; i < 8; ++i)
+    if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 2 * i, 2))) return st;
+  if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  const size_t need_ws = round_up(sizeof(float) * (size_t)Hq * Tq);
+  bool query = false;
+  if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
+  if (query || (Tq == 0 && Tk == 0)) return ok();
+  if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
+    return st;
+
+  vca::BwdArgs a{};
+  a.q = view(q, 0, strides[1], strides[0]);
+  a.k = view(k, 0, strides[3], strides[2]);
+  a.v = view(v, 0, strides[5], strides[4]);
+  a.o = view(out, 0, strides[7], strides[6]);
+  a.dout = view(dout, 0, strides[9], strides[8]);
+  a.dq = vieww(dq, 0, strides[11], strides[10]);
+  a.dk = vieww(dk, 0, strides[13], strides[12]);
+  a.dv = vieww(dv, 0, strides[15], strides[14]);
+  a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.lse_sb = 0;
+  a.lse_sh = Tq;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.Nq = a.Nk = 0;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.G = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * vca::kLog2e;
+  a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
+  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, max_k,
+                                    stream),
+                    "attn_bwd_varlen launch");
+}
+
+int attn_merge(const void* out_a, int dtype_a, const float* lse_a, const void* out_b, int dtype_b,
+               const float* lse_b, float* out, float* lse, void* out_bf16, int rows, int H, int Dv,
+               hipStream_t stream) {
+  g_last_error.clear();
+  if (rows < 0 || H <= 0 || Dv <= 0) return fail(ATTN_E_INVALID, "rows >= 0, H > 0, Dv > 0 required");
+  if ((dtype_a != ATTN_BF16 && dtype_a != ATTN_F32) || (dtype_b != ATTN_BF16 && dtype_b != ATTN_F32))
+    return fail(ATTN_E_UNSUPPORTED, "merge inputs must be ATTN_BF16 or ATTN_F32");
+  if (rows == 0) return ok();
+  if (!out_a || !out_b || !lse_a || !lse_b || !out || !lse)
+    return fail(ATTN_E_INVALID, "merge pointer is NULL");
+  vca::MergeArgs a{};
+  a.out_a = out_a;
+  a.out_b = out_b;
+  a.a_f32 = dtype_a == ATTN_F32;
+  a.b_f32 = dtype_b == ATTN_F32;
+  a.lse_a = lse_a;
+  a.lse_b = lse_b;
+  a.out = out;
+  a.lse = lse;
+  a.out_bf16 = static_cast<uint16_t*>(out_bf16);
+  a.rows = rows;
+  a.H = H;
+  a.Dv = Dv;
+  return hip_status(vca::launch_merge(a, stream), "attn_merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,406 @@
+// Backward kernels, recomputing from the caller's out/lse (NeMo-Automodel
+// "ffpa_attention" page, dense and varlen backward entries: the ring feeds a
+// globally merged out/lse, so the backward never uses a chunk-local one).
+//
+//   delta[i]  = sum_d dO[i,d] * O[i,d]                       (delta kernel)
+//   P[i,j]    = exp(scale * q_i.k_j - lse_i) on visible (i,j), 0 elsewhere and
+//               on rows with lse = -inf
+//   dV[j]    += sum_i P[i,j] dO[i]                            (dK/dV kernel)
+//   dS[i,j]   = P[i,j] * (dO[i].v_j - delta[i])
+//   dK[j]    += scale * sum_i dS[i,j] q_i                     (dK/dV kernel)
+//   dQ[i]     = scale * sum_j dS[i,j] k_j                     (dQ kernel)
+// dK/dV sum over the q-heads of each GQA group inside the dK/dV kernel.
+//
+// Both main kernels split a 32-row block across DS waves by head-dim range:
+// each wave of the group computes a partial score tile over its share of Dqk
+// (and of Dv for dP), the partials are summed through LDS, and each wave then
+// accumulates its own share of the output columns. DS = 1 needs no exchange;
+// larger head dims use DS = 2 or 4 to keep the accumulators in registers.
+#pragma once
+
+#include "attn_common.hpp"
+#include "attn_fwd.hpp"
+
+namespace vca {
+
+struct BwdArgs {
+  View q, k, v, o, dout;
+  ViewW dq, dk, dv;
+  const float* lse;
+  float* delta;            // workspace, same indexing as lse
+  int64_t lse_sb, lse_sh;  // index = b*lse_sb + h*lse_sh + (q_row0 + i)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int Nq, Nk, Tq, Tk;
+  int G;
+  float scale, scale_log2;
+  int dq_accumulate;
+};
+
+// Rows [r0, r0 + R) of a [rows][D] bf16 view (row stride sn; rows >= nrows
+// read as zero) stored transposed into LDS dst[D][R + 8], the row index placed
+// by vt_pos so the tile can serve as the A operand against a C tile used as B.
+template <int D, int R>
+__device__ __forceinline__ void load_transposed(uint16_t* dst, const uint16_t* src, int64_t sn,
+                                                int r0, int nrows, int tid, int nthreads) {
+  constexpr int TS = R + 8;
+  for (int c = tid; c < (R / 4) * (D / 8); c += nthreads) {
+    const int rq = c / (D / 8), dc = c % (D / 8);
+    u32x4 rv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + rq * 4 + i;
+      rv[i] = r < nrows ? ldg16(src + (int64_t)r * sn + dc * 8) : zero_u32x4();
+    }
+    const int pos = vt_pos(rq * 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x2 pk;
+      pk[0] = bf16_at(rv[0], e) | (bf16_at(rv[1], e) << 16);
+      pk[1] = bf16_at(rv[2], e) | (bf16_at(rv[3], e) << 16);
+      sts8(&dst[(dc * 8 + e) * TS + pos], pk);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O) in fp32. blockIdx = (row block, head, segment); a row
+// is covered by DV/8 lanes (at most 64), each reading 16-byte chunks.
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
+  constexpr int LPR = DV / 8 >= 64 ? 64 : DV / 8;  // lanes per row
+  constexpr int RPW = 64 / LPR;                     // rows per wave
+  constexpr int CPL = DV / 8 / LPR;                 // 16-byte chunks per lane
+  const int s = blockIdx.z, h = blockIdx.y;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int row = (blockIdx.x * 4 + w) * RPW + sub;
+  float acc = 0.f;
+  const bool ok = row < sg.lq;
+  if (ok) {
+    const int64_t r = sg.q_row0 + row;
+    const uint16_t* op = a.o.p + s * a.o.sb + r * a.o.sn + h * a.o.sh;
+    const uint16_t* dp = a.dout.p + s * a.dout.sb + r * a.dout.sn + h * a.dout.sh;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int d0 = (c * LPR + li) * 8;
+      const u32x4 ov = ldg16(op + d0), dv = ldg16(dp + d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc += __uint_as_float(bf16_at(ov, e) << 16) * __uint_as_float(bf16_at(dv, e) << 16);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (ok && li == 0) a.delta[s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: one workgroup = (segment, kv-head, block of 32*(4/DS) keys)
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int DS, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int KG = 4 / DS;           // 32-key groups per workgroup
+  constexpr int DR = DQK / DS;         // this wave's share of Dqk
+  constexpr int VR = DV / DS;          // this wave's share of Dv
+  static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
+  constexpr int NKS = DR / 16, NVS = VR / 16;
+  constexpr int NDB = DR / 32, NVB = VR / 32;
+  constexpr int TS = 40;               // transposed tile row stride (32 rows + pad)
+  __shared__ __attribute__((aligned(16))) uint16_t sqt[DQK * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sdot[DV * TS];
+  __shared__ __attribute__((aligned(16))) float slse[32];
+  __shared__ __attribute__((aligned(16))) float sdel[32];
+  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? KG * DS * 2 * 16 * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int kg = w / DS, ds = w % DS;
+  const int s = blockIdx.z, g = blockIdx.y;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int kb0 = blockIdx.x * (32 * KG);
+  if (kb0 >= sg.lk) return;
+  const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
+  const int key = kb0 + kg * 32 + col;  // this lane's key (output column)
+
+  const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
+  const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
+
+  // K and V fragments of this lane's key over this wave's d ranges (B operands)
+  bf16x8 kf[NKS], vf[NVS];
+  {
+    const bool ok = key < lk;
+    const uint16_t* kp = kbp + (int64_t)(ok ? key : 0) * a.k.sn + ds * DR + half * 8;
+    const uint16_t* vp = vbp + (int64_t)(ok ? key : 0) * a.v.sn + ds * VR + half * 8;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) kf[i] = as_frag(ok ? ldg16(kp + i * 16) : zero_u32x4());
+#pragma unroll
+    for (int i = 0; i < NVS; ++i) vf[i] = as_frag(ok ? ldg16(vp + i * 16) : zero_u32x4());
+  }
+
+  f32x16 dka[NDB], dva[NVB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dka[i] = zero16();
+#pragma unroll
+  for (int i = 0; i < NVB; ++i) dva[i] = zero16();
+
+  // queries that can see any key of this block
+  int q_begin = 0;
+  if (CAUSAL) q_begin = max(0, kb0 - shift);
+  q_begin &= ~31;
+
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int h = g * a.G + hh;
+    const uint16_t* qbp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+    const uint16_t* dobp = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
+    const int64_t lbase = s * a.lse_sb + h * a.lse_sh + sg.q_row0;
+    for (int q0 = q_begin; q0 < lq; q0 += 32) {
+      __syncthreads();
+      load_transposed<DQK, 32>(sqt, qbp, a.q.sn, q0, lq, tid, 256);
+      load_transposed<DV, 32>(sdot, dobp, a.dout.sn, q0, lq, tid, 256);
+      if (tid < 32) {
+        const int i = q0 + tid;
+        float l2 = __builtin_inff();
+        float dl = 0.f;
+        if (i < lq) {
+          const float l = a.lse[lbase + i];
+          l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+          dl = a.delta[lbase + i];
+        }
+        slse[tid] = l2;
+        sdel[tid] = dl;
+      }
+      __syncthreads();
+      // this 32-query step is hidden from every key of this wave's group?
+      const int gk0 = kb0 + kg * 32;
+      const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + 31 + shift);
+      f32x16 sacc = zero16(), pacc = zero16();
+      if (live) {
+        // partial S[q][key] = Q K^T and dP[q][key] = dO V^T over this wave's d ranges
+        const int qi = q0 + col;
+        const bool qok = qi < lq;
+        const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
+        const uint16_t* dop = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + ds * VR + half * 8;
+#pragma unroll
+        for (int i = 0; i < NKS; ++i)
+          sacc = mfma32(as_frag(qok ? ldg16(qp + i * 16) : zero_u32x4()), kf[i], sacc);
+#pragma unroll
+        for (int i = 0; i < NVS; ++i)
+          pacc = mfma32(as_frag(qok ? ldg16(dop + i * 16) : zero_u32x4()), vf[i], pacc);
+      }
+      if constexpr (DS > 1) {
+        float* mine = &sx[((kg * DS + ds) * 2) * 16 * 64];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          mine[r * 64 + lane] = sacc[r];
+          mine[16 * 64 + r * 64 + lane] = pacc[r];
+        }
+        __syncthreads();
+        sacc = zero16();
+        pacc = zero16();
+#pragma unroll
+        for (int o = 0; o < DS; ++o) {
+          const float* src = &sx[((kg * DS + o) * 2) * 16 * 64];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[r] += src[r * 64 + lane];
+            pacc[r] += src[16 * 64 + r * 64 + lane];
+          }
+        }
+      }
+      if (!live) continue;
+      // P and dS (rows q = q0 + 8*(r/4) + 4*half + r%4, column = key)
+      float p[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
+        const int qi = q0 + qr;
+        bool vis = key < lk && qi < lq;
+        if (CAUSAL) vis = vis && key <= qi + shift;
+        const float x = fast_exp2(sacc[r] * a.scale_log2 - slse[qr]);
+        p[r] = vis ? x : 0.f;
+        dsv[r] = p[r] * (pacc[r] - sdel[qr]);
+      }
+      const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
+      const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+      // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
+#pragma unroll
+      for (int b = 0; b < NVB; ++b) {
+        const uint16_t* src = &sdot[(ds * VR + b * 32 + col) * TS + half * 8];
+        dva[b] = mfma32(lds_frag(src), p0, dva[b]);
+        dva[b] = mfma32(lds_frag(src + 16), p1, dva[b]);
+      }
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const uint16_t* src = &sqt[(ds * DR + b * 32 + col) * TS + half * 8];
+        dka[b] = mfma32(lds_frag(src), s0, dka[b]);
+        dka[b] = mfma32(lds_frag(src + 16), s1, dka[b]);
+      }
+    }
+  }
+
+  if (key < lk) {
+    const int64_t r = sg.k_row0 + key;
+    uint16_t* dkp = a.dk.p + s * a.dk.sb + r * a.dk.sn + g * a.dk.sh + ds * DR;
+    uint16_t* dvp = a.dv.p + s * a.dv.sb + r * a.dv.sn + g * a.dv.sh + ds * VR;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(dka[b][rr * 4 + c] * a.scale);
+        *reinterpret_cast<bf16x4*>(dkp + b * 32 + rr * 8 + half * 4) = v4;
+      }
+#pragma unroll
+    for (int b = 0; b < NVB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)dva[b][rr * 4 + c];
+        *reinterpret_cast<bf16x4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = (segment, q-head, block of 32*(4/DS) queries)
+// ---------------------------------------------------------------------------
+template <int DQK, int DV, int DS, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int QG = 4 / DS;
+  constexpr int DR = DQK / DS;
+  constexpr int VR = DV / DS;
+  static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
+  constexpr int NKS = DR / 16, NVS = VR / 16, NDB = DR / 32;
+  constexpr int TS = 40;
+  __shared__ __attribute__((aligned(16))) uint16_t skt[DQK * TS];
+  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * 16 * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int qg = w / DS, ds = w % DS;
+  const int s = blockIdx.z, h = blockIdx.y, g = h / a.G;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int tile = gridDim.x - 1 - blockIdx.x;
+  const int m0 = tile * (32 * QG);
+  if (m0 >= sg.lq) return;
+  const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
+  const int wq0 = m0 + qg * 32;
+  const int qi = wq0 + col;  // this lane's query (output column)
+  const bool qok = qi < lq;
+
+  const uint16_t* qbp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+  const uint16_t* dobp = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
+  const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
+  const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
+
+  bf16x8 qf[NKS], df[NVS];
+  {
+    const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
+    const uint16_t* dp = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + ds * VR + half * 8;
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) qf[i] = as_frag(qok ? ldg16(qp + i * 16) : zero_u32x4());
+#pragma unroll
+    for (int i = 0; i < NVS; ++i) df[i] = as_frag(qok ? ldg16(dp + i * 16) : zero_u32x4());
+  }
+  const int64_t lidx = s * a.lse_sb + h * a.lse_sh + sg.q_row0 + (qok ? qi : 0);
+  float l2 = __builtin_inff(), dl = 0.f;
+  if (qok) {
+    const float l = a.lse[lidx];
+    l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    dl = a.delta[lidx];
+  }
+
+  f32x16 dqa[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqa[i] = zero16();
+
+  int kv_end = lk;
+  if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
+  for (int k0 = 0; k0 < kv_end; k0 += 32) {
+    __syncthreads();
+    load_transposed<DQK, 32>(skt, kbp, a.k.sn, k0, lk, tid, 256);
+    __syncthreads();
+    const bool live = wq0 < lq && !(CAUSAL && k0 > wq0 + 31 + shift);
+    f32x16 sacc = zero16(), pacc = zero16();
+    if (live) {
+      // partial S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T over this wave's d ranges
+      const int kj = k0 + col;
+      const bool kok = kj < lk;
+      const uint16_t* kp = kbp + (int64_t)(kok ? kj : 0) * a.k.sn + ds * DR + half * 8;
+      const uint16_t* vp = vbp + (int64_t)(kok ? kj : 0) * a.v.sn + ds * VR + half * 8;
+#pragma unroll
+      for (int i = 0; i < NKS; ++i)
+        sacc = mfma32(as_frag(kok ? ldg16(kp + i * 16) : zero_u32x4()), qf[i], sacc);
+#pragma unroll
+      for (int i = 0; i < NVS; ++i)
+        pacc = mfma32(as_frag(kok ? ldg16(vp + i * 16) : zero_u32x4()), df[i], pacc);
+    }
+    if constexpr (DS > 1) {
+      float* mine = &sx[((qg * DS + ds) * 2) * 16 * 64];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mine[r * 64 + lane] = sacc[r];
+        mine[16 * 64 + r * 64 + lane] = pacc[r];
+      }
+      __syncthreads();
+      sacc = zero16();
+      pacc = zero16();
+#pragma unroll
+      for (int o = 0; o < DS; ++o) {
+        const float* src = &sx[((qg * DS + o) * 2) * 16 * 64];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] += src[r * 64 + lane];
+          pacc[r] += src[16 * 64 + r * 64 + lane];
+        }
+      }
+    }
+    if (!live) continue;
+    float dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = k0 + (r >> 2) * 8 + half * 4 + (r & 3);
+      bool vis = kj < lk && qok;
+      if (CAUSAL) vis = vis && kj <= qi + shift;
+      const float p = vis ? fast_exp2(sacc[r] * a.scale_log2 - l2) : 0.f;
+      dsv[r] = p * (pacc[r] - dl);
+    }
+    const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+    // dQ^T[d][q] += K^T dS^T
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) {
+      const uint16_t* src = &skt[(ds * DR + b * 32 + col) * TS + half * 8];
+      dqa[b] = mfma32(lds_frag(src), s0, dqa[b]);
+      dqa[b] = mfma32(lds_frag(src + 16), s1, dqa[b]);
+    }
+  }
+
+  if (qok) {
+    uint16_t* dqp = a.dq.p + s * a.dq.sb + (int64_t)(sg.q_row0 + qi) * a.dq.sn + h * a.dq.sh + ds * DR;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint16_t* dst = dqp + b * 32 + rr * 8 + half * 4;
+        float add[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.dq_accumulate) {
+          const u32x2 old = *reinterpret_cast<const u32x2*>(dst);
+          add[0] = __uint_as_float(old[0] << 16);
+          add[1] = __uint_as_float(old[0] & 0xffff0000u);
+          add[2] = __uint_as_float(old[1] << 16);
+          add[3] = __uint_as_float(old[1] & 0xffff0000u);
+        }
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(dqa[b][rr * 4 + c] * a.scale + add[c]);
+        *reinterpret_cast<bf16x4*>(dst) = v4;
+      }
+  }
+}
+
+}  // namespace vca

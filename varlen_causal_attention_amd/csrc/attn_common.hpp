@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   A operand: lane l supplies row (l % 32), 8 contraction elements chosen by
+//              the lane half (l / 32);
+//   B operand: lane l supplies column (l % 32), 8 contraction elements chosen
+//              by the lane half;
+//   C/D:       lane l, register r holds row 8*(r/4) + 4*(l/32) + (r%4) and
+//              column (l % 32).
+// Which 8 contraction indices a lane half carries is free, as long as the A
+// and B fragments of one product agree; the kernels use that freedom to feed
+// a C tile back as a B operand without any lane exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vca {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void sts16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void sts8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 as_frag(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// Element e (0..7) of eight packed bf16 values.
+__device__ __forceinline__ uint32_t bf16_at(u32x4 v, int e) {
+  return (v[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+}
+
+// Partner lane across the two wave halves (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Eight fp32 values -> eight bf16 (round to nearest even) as one MFMA fragment.
+__device__ __forceinline__ bf16x8 to_frag(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+// Segment geometry: query rows [q_row0, q_row0 + lq) and key rows
+// [k_row0, k_row0 + lk) of the packed tensors. cu arrays are clamped into
+// [0, T] so a malformed table can never index outside the tensors.
+struct SegGeom {
+  int q_row0, lq, k_row0, lk;
+};
+
+__device__ __forceinline__ SegGeom seg_geom(const int32_t* cu_q, const int32_t* cu_k, int s,
+                                            int Nq, int Nk, int Tq, int Tk) {
+  SegGeom g;
+  if (cu_q) {
+    int qa = min(max(cu_q[s], 0), Tq);
+    int qb = min(max(cu_q[s + 1], qa), Tq);
+    int ka = min(max(cu_k[s], 0), Tk);
+    int kb = min(max(cu_k[s + 1], ka), Tk);
+    g.q_row0 = qa;
+    g.lq = qb - qa;
+    g.k_row0 = ka;
+    g.lk = kb - ka;
+  } else {
+    g.q_row0 = 0;
+    g.lq = Nq;
+    g.k_row0 = 0;
+    g.lk = Nk;
+  }
+  return g;
+}
+
+// Tensor view: element (seg-or-batch b, row, head h, d) lives at
+// base + b*sb + row*sn + h*sh + d. Varlen views have sb = 0 and rows offset by
+// the segment's first row.
+struct View {
+  const uint16_t* p;
+  int64_t sb, sh, sn;
+};
+struct ViewW {
+  uint16_t* p;
+  int64_t sb, sh, sn;
+};
+
+}  // namespace vca

@@ -1,0 +1,247 @@
+// Forward kernel: fused S = scale * Q K^T -> online softmax -> O = P V, with
+// out (bf16) and the fp32 natural-log log-sum-exp per query row.
+//
+// Operation (NeMo-Automodel "ffpa_attention" page, dense and varlen forward
+// entries; "fa4" page overview for the bottom-right causal corner): query i of
+// a segment with lq queries and lk keys sees keys j < lk with, when causal,
+// j <= i + (lk - lq). A row that sees nothing gets out 0 and lse -inf.
+//
+// Work item: one workgroup = one (segment or batch, q-head, 128-row q tile);
+// four 32-row query blocks, each owned by DS waves (DS = 1 below Dqk 512).
+// Per key tile:
+//   * K tile [BN][Dqk] and V tile stored transposed [Dv][BN] in LDS;
+//   * each wave computes S^T = K Q^T with Q held in registers, so a lane owns
+//     one query (its column) and the row max / row sum are lane-local except
+//     for one exchange with the partner lane of the other wave half;
+//   * softmax in base 2 with scale*log2(e) folded in; the running max is only
+//     moved when it grows by more than 2^8 (lazy rescale, exact either way);
+//   * O^T += V^T P^T takes the S^T accumulators directly as the B operand (the
+//     V^T tile is stored with the matching key permutation).
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace vca {
+
+struct FwdArgs {
+  View q, k, v;
+  ViewW o;
+  float* lse;
+  int64_t lse_sb, lse_sh;  // lse index = b*lse_sb + h*lse_sh + (q_row0 + i)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int Nq, Nk, Tq, Tk;
+  int G;            // Hq / Hkv
+  float scale_log2; // scale * log2(e)
+};
+
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBM = 32 * kFwdWaves;
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+// Position of key kk (0..BN-1) inside a row of the transposed V tile. The PV
+// product contracts 16 keys per MFMA; lane half h supplies the S^T registers
+// that hold keys {16g + 4h + c, 16g + 8 + 4h + c : c < 4}, so those eight keys
+// are stored contiguously at 16g + 8h.
+__device__ __forceinline__ int vt_pos(int kk) {
+  const int grp = kk >> 4, a = (kk >> 3) & 1, h = (kk >> 2) & 1, c = kk & 3;
+  return grp * 16 + h * 8 + a * 4 + c;
+}
+
+template <int DQK, int DV, int BN, int DS, bool CAUSAL>
+__global__ void __launch_bounds__(256 * DS, 1) attn_fwd_kernel(const FwdArgs a) {
+  // DS waves share one 32-row query block: wave `ds` of the group holds the
+  // Q fragments of Dqk range [ds*DR, (ds+1)*DR) and accumulates O^T for Dv
+  // range [ds*VR, (ds+1)*VR); the partial score tiles are summed through LDS
+  // in a fixed order, so every wave of the group sees bitwise-identical scores.
+  static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
+  constexpr int NT = 256 * DS;      // threads
+  constexpr int DR = DQK / DS, VR = DV / DS;
+  constexpr int KS = DQK + 8;       // K row stride in LDS (elements), padded
+  constexpr int VS = BN + 8;        // V^T row stride
+  constexpr int NKB = BN / 32;
+  constexpr int NDB = VR / 32;
+  constexpr int NKS = DR / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t svt[DV * VS];
+  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int qg = w / DS, ds = w % DS;
+  const int col = lane & 31, half = lane >> 5;
+  const int s = blockIdx.z, h = blockIdx.y, kvh = h / a.G;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int tile = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
+  const int m0 = tile * kFwdBM;
+  if (m0 >= sg.lq) return;
+  const int lq = sg.lq, lk = sg.lk;
+  const int shift = lk - lq;
+
+  const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+  const uint16_t* kb = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + kvh * a.k.sh;
+  const uint16_t* vb = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + kvh * a.v.sh;
+
+  const int wrow0 = m0 + 32 * qg;  // first query row of this wave
+  const int row = wrow0 + col;     // this lane's query row
+  int kv_end = lk;
+  if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  bf16x8 qf[NKS];
+  {
+    const bool ok = row < lq;
+    const uint16_t* src = qb + (int64_t)(ok ? row : 0) * a.q.sn + ds * DR + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_frag(ok ? ldg16(src + ks * 16) : zero_u32x4());
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = zero16();
+  float m_ref = kNegInf;  // base-2 running reference max of this row
+  float lsum = 0.f;       // this lane half's share of the row sum
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    __syncthreads();
+    // K tile -> LDS, row-major
+    for (int c = tid; c < BN * DQK / 8; c += NT) {
+      const int r = c / (DQK / 8), cc = c % (DQK / 8);
+      const int key = k0 + r;
+      u32x4 val = key < lk ? ldg16(kb + (int64_t)key * a.k.sn + cc * 8) : zero_u32x4();
+      sts16(&sk[r * KS + cc * 8], val);
+    }
+    // V tile -> LDS, transposed with the PV key permutation
+    for (int c = tid; c < (BN / 4) * (DV / 8); c += NT) {
+      const int kq = c / (DV / 8), dc = c % (DV / 8);
+      u32x4 rv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kq * 4 + i;
+        rv[i] = key < lk ? ldg16(vb + (int64_t)key * a.v.sn + dc * 8) : zero_u32x4();
+      }
+      const int pos = vt_pos(kq * 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u32x2 pk;
+        pk[0] = bf16_at(rv[0], e) | (bf16_at(rv[1], e) << 16);
+        pk[1] = bf16_at(rv[2], e) | (bf16_at(rv[3], e) << 16);
+        sts8(&svt[(dc * 8 + e) * VS + pos], pk);
+      }
+    }
+    __syncthreads();
+    // the DS waves of a group take every branch below together
+    const bool live = wrow0 < lq && !(CAUSAL && k0 > wrow0 + 31 + shift);
+
+    // S^T = K Q^T (partial over this wave's Dqk range when DS > 1)
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) {
+      f32x16 acc = zero16();
+      if (live) {
+        const uint16_t* src = &sk[(kbk * 32 + col) * KS + ds * DR + half * 8];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = mfma32(lds_frag(src + ks * 16), qf[ks], acc);
+      }
+      sacc[kbk] = acc;
+    }
+    if constexpr (DS > 1) {
+      float* mine = &sx[(w * NKB) * 16 * 64];
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(kbk * 16 + r) * 64 + lane] = sacc[kbk][r];
+      __syncthreads();
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = 0.f;
+#pragma unroll
+          for (int o2 = 0; o2 < DS; ++o2) v += sx[((qg * DS + o2) * NKB + kbk) * 16 * 64 + r * 64 + lane];
+          sacc[kbk][r] = v;
+        }
+    }
+    if (!live) continue;
+
+    // scale, mask, row max
+    const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift);
+    float mx = kNegInf;
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[kbk][r] * a.scale_log2;
+        if (need_mask) {
+          const int key = k0 + kbk * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          const bool vis = key < lk && (!CAUSAL || key <= row + shift);
+          x = vis ? x : kNegInf;
+        }
+        sacc[kbk][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, xor32(mx));
+
+    // lazy rescale of the running reference
+    const float m_new = fmaxf(m_ref, mx);
+    const bool need = m_new > m_ref + kLazyRescale;
+    if (__any(need)) {
+      const float m_set = need ? m_new : m_ref;
+      const float alpha = need ? fast_exp2(m_ref - m_set) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_ref = m_set;
+    }
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+
+    // P = exp2(x - m), row sum, pack to bf16 fragments
+    bf16x8 pf[2 * NKB];
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(sacc[kbk][r] - m_use);
+        lsum += p[r];
+      }
+      pf[2 * kbk] = to_frag(p);
+      pf[2 * kbk + 1] = to_frag(p + 8);
+    }
+
+    // O^T += V^T P^T over this wave's Dv range
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint16_t* src = &svt[(ds * VR + db * 32 + col) * VS + half * 8];
+#pragma unroll
+      for (int kk = 0; kk < 2 * NKB; ++kk) o[db] = mfma32(lds_frag(src + kk * 16), pf[kk], o[db]);
+    }
+  }
+
+  // epilogue: O / l, lse = ln(sum exp(scaled scores))
+  const float ltot = lsum + xor32(lsum);
+  if (row < lq) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    uint16_t* ob = a.o.p + s * a.o.sb + (int64_t)(sg.q_row0 + row) * a.o.sn + h * a.o.sh + ds * VR;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[db][rr * 4 + c] * inv);
+        *reinterpret_cast<bf16x4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
+      }
+    }
+    if (half == 0 && ds == 0) {
+      const float l = ltot > 0.f ? (m_ref + log2f(ltot)) * kLn2 : kNegInf;
+      a.lse[s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row] = l;
+    }
+  }
+}
+
+}  // namespace vca

@@ -1,0 +1,118 @@
+// Document-causal segment layout on the host ("fa4" page: module overview of
+// document-causal attention and the _varlen_segments / _varlen_layout entries;
+// "gemma4_moe cp_attention" page: ring segments pair a document's queries of
+// one shard with its keys in one KV chunk, cu_q[i] pairing cu_k[i]).
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "attn_error.hpp"
+
+namespace {
+
+struct Run {
+  int begin, end, id;  // positions [begin, end) of one row carrying document id
+};
+
+// Maximal runs of equal id inside positions [a, b) of one row.
+std::vector<Run> runs_of(const int32_t* ids, int a, int b) {
+  std::vector<Run> out;
+  int p = a;
+  while (p < b) {
+    int e = p + 1;
+    while (e < b && ids[e] == ids[p]) ++e;
+    out.push_back(Run{p, e, ids[p]});
+    p = e;
+  }
+  return out;
+}
+
+}  // namespace
+
+extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                                 int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
+                                 int max_segments, int* num_segments) {
+  vca::set_last_error("");
+  if (!doc_ids || !num_segments || B < 0 || S < 0 || q_len < 0 || k_len < 0 || q_start < 0 ||
+      k_start < 0 || q_start + q_len > S || k_start + k_len > S || (mode != 0 && mode != 1)) {
+    vca::set_last_error("attn_doc_segments: invalid arguments");
+    return ATTN_E_INVALID;
+  }
+  const int q_end = q_start + q_len, k_end = k_start + k_len;
+  if (mode == 0 && !(k_start <= q_start && q_end <= k_end)) {
+    vca::set_last_error("attn_doc_segments: causal mode needs the key range to cover the query range");
+    return ATTN_E_INVALID;
+  }
+  if (mode == 1 && k_end > q_start) {
+    vca::set_last_error("attn_doc_segments: cross mode needs every key before every query");
+    return ATTN_E_INVALID;
+  }
+  std::vector<int32_t> sq, sk;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* ids = doc_ids + (size_t)b * S;
+    if (mode == 0) {
+      // split every run of the key range at the query-shard end; a piece that
+      // ends inside the shard carries its queries (the part inside the shard)
+      // and all of its keys; other pieces only keys.
+      for (const Run& r0 : runs_of(ids, k_start, k_end)) {
+        Run pieces[2] = {r0, r0};
+        int np = 1;
+        if (r0.begin < q_end && q_end < r0.end) {
+          pieces[0].end = q_end;
+          pieces[1].begin = q_end;
+          np = 2;
+        }
+        for (int i = 0; i < np; ++i) {
+          const Run& r = pieces[i];
+          const int qa = r.begin > q_start ? r.begin : q_start;
+          const int qb = r.end < q_end ? r.end : q_end;
+          const int nq = qb > qa ? qb - qa : 0;
+          const int nk = r.end - r.begin;
+          if (r.id == 0 && nq > 0) {
+            // padding: queries attend nothing, keys are seen by nobody
+            sq.push_back(nq);
+            sk.push_back(0);
+            sq.push_back(0);
+            sk.push_back(nk);
+          } else {
+            sq.push_back(r.id == 0 ? 0 : nq);
+            sk.push_back(nk);
+          }
+        }
+      }
+    } else {
+      // cross chunk: merge the runs of the key range and of the query range in
+      // position order; a document present in both pairs up, others stand alone.
+      std::vector<Run> kr = runs_of(ids, k_start, k_end);
+      std::vector<Run> qr = runs_of(ids, q_start, q_end);
+      size_t i = 0, j = 0;
+      while (i < kr.size() || j < qr.size()) {
+        if (i < kr.size() && j < qr.size() && kr[i].id == qr[j].id && kr[i].id != 0) {
+          sq.push_back(qr[j].end - qr[j].begin);
+          sk.push_back(kr[i].end - kr[i].begin);
+          ++i;
+          ++j;
+        } else if (i < kr.size() && (j >= qr.size() || kr[i].begin < qr[j].begin)) {
+          sq.push_back(0);
+          sk.push_back(kr[i].end - kr[i].begin);
+          ++i;
+        } else {
+          sq.push_back(qr[j].end - qr[j].begin);
+          sk.push_back(0);
+          ++j;
+        }
+      }
+    }
+  }
+  *num_segments = (int)sq.size();
+  if ((int)sq.size() > max_segments || !seg_q || !seg_k) {
+    vca::set_last_error("attn_doc_segments: max_segments too small, " + std::to_string(sq.size()) +
+                        " needed");
+    return ATTN_E_INVALID;
+  }
+  for (size_t i = 0; i < sq.size(); ++i) {
+    seg_q[i] = sq[i];
+    seg_k[i] = sk[i];
+  }
+  return ATTN_OK;
+}

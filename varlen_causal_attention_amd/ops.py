@@ -1,0 +1,252 @@
+"""Torch-facing binding of the C ABI: shape checks, output allocation and
+argument marshalling. Every step of the computation runs in the HIP library;
+torch only provides device memory and the current stream.
+
+Names and call shapes follow the dense / varlen forward and backward wrappers
+of the NeMo-Automodel "ffpa_attention" page.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from ._lib import ATTN_BF16, ATTN_DQ_ACCUMULATE, ATTN_F32, check, i64_array, load
+
+
+def _stream(t: torch.Tensor) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else C.c_void_p(0)
+
+
+def _need_gpu_bf16(**tensors):
+    dev = None
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if t.numel() > 0 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _workspace(size: int, device) -> torch.Tensor:
+    return torch.empty(max(size, 16), dtype=torch.uint8, device=device)
+
+
+def is_supported(dqk: int, dv: int) -> bool:
+    return bool(load().attn_is_supported(ATTN_BF16, dqk, dv))
+
+
+def version() -> int:
+    return int(load().attn_version())
+
+
+# ---------------------------------------------------------------------------
+# dense [B, H, N, D]
+# ---------------------------------------------------------------------------
+def fwd_dense(q, k, v, scale: float, causal: bool):
+    """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log)."""
+    dev = _need_gpu_bf16(q=q, k=k, v=v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("dense tensors are [B, H, N, D]")
+    B, Hq, Nq, Dqk = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != Dqk or v.shape[:3] != k.shape[:3]:
+        raise ValueError("q/k/v shapes disagree")
+    Dv = v.shape[3]
+    out = torch.empty((B, Hq, Nq, Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    strides = i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
+                        + list(out.stride()[:3]))
+    st = load().attn_fwd_dense(ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq,
+                               Hkv, Nq, Nk, Dqk, Dv, strides, float(scale), int(bool(causal)),
+                               None, None, _stream(q))
+    check(st, "attn_fwd_dense")
+    return out, lse
+
+
+def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate=None):
+    """(dq, dk, dv) from the caller's out/lse; dk/dv have Hkv heads.
+    dq_accumulate: an existing dq tensor to add this call's dq into."""
+    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
+    B, Hq, Nq, Dqk = q.shape
+    _, Hkv, Nk, _ = k.shape
+    Dv = v.shape[3]
+    if tuple(out.shape) != (B, Hq, Nq, Dv) or tuple(dout.shape) != (B, Hq, Nq, Dv):
+        raise ValueError("out/dout must be [B, Hq, Nq, Dv]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, Hq, Nq]")
+    if lse.device != dev:
+        raise ValueError("lse must be on the GPU with the other tensors")
+    flags = 0
+    if dq_accumulate is not None:
+        _need_gpu_bf16(dq=dq_accumulate)
+        if tuple(dq_accumulate.shape) != tuple(q.shape):
+            raise ValueError("dq_accumulate must have q's shape")
+        dq = dq_accumulate
+        flags |= ATTN_DQ_ACCUMULATE
+    else:
+        dq = torch.empty((B, Hq, Nq, Dqk), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((B, Hkv, Nk, Dqk), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((B, Hkv, Nk, Dv), dtype=torch.bfloat16, device=dev)
+    strides = i64_array(sum((list(t.stride()[:3]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
+    lib = load()
+    args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, Dqk, Dv, strides, float(scale),
+            int(bool(causal)), flags)
+    need = C.c_size_t(0)
+    check(lib.attn_bwd_dense(*args, None, C.byref(need), _stream(q)), "attn_bwd_dense")
+    ws = _workspace(need.value, dev)
+    have = C.c_size_t(ws.numel())
+    check(lib.attn_bwd_dense(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_bwd_dense")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# packed varlen THD [T, H, D]
+# ---------------------------------------------------------------------------
+def _cu(cu, dev):
+    if cu.dtype != torch.int32 or cu.device != dev or cu.dim() != 1 or not cu.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous int32 [segments + 1] on the GPU")
+    return C.c_void_p(cu.data_ptr())
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool):
+    """out [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 (natural log)."""
+    dev = _need_gpu_bf16(q=q, k=k, v=v)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("varlen tensors are [T, H, D]")
+    Tq, Hq, Dqk = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Dk != Dqk or v.shape[:2] != k.shape[:2]:
+        raise ValueError("q/k/v shapes disagree")
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    Dv = v.shape[2]
+    out = torch.empty((Tq, Hq, Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
+                        + list(out.stride()[:2]))
+    st = load().attn_fwd_varlen(ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                _cu(cu_q, dev), _cu(cu_k, dev), cu_q.numel() - 1, int(max_q),
+                                int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale),
+                                int(bool(causal)), None, None, _stream(q))
+    check(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float,
+               causal: bool, dq_accumulate=None):
+    """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse."""
+    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
+    Tq, Hq, Dqk = q.shape
+    Tk, Hkv, _ = k.shape
+    Dv = v.shape[2]
+    if tuple(out.shape) != (Tq, Hq, Dv) or tuple(dout.shape) != (Tq, Hq, Dv):
+        raise ValueError("out/dout must be [Tq, Hq, Dv]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [Hq, Tq]")
+    if lse.device != dev:
+        raise ValueError("lse must be on the GPU with the other tensors")
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    flags = 0
+    if dq_accumulate is not None:
+        _need_gpu_bf16(dq=dq_accumulate)
+        if tuple(dq_accumulate.shape) != tuple(q.shape):
+            raise ValueError("dq_accumulate must have q's shape")
+        dq = dq_accumulate
+        flags |= ATTN_DQ_ACCUMULATE
+    else:
+        dq = torch.empty((Tq, Hq, Dqk), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((Tk, Hkv, Dqk), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((Tk, Hkv, Dv), dtype=torch.bfloat16, device=dev)
+    strides = i64_array(sum((list(t.stride()[:2]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
+    lib = load()
+    args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _cu(cu_q, dev), _cu(cu_k, dev), cu_q.numel() - 1, int(max_q),
+            int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale), int(bool(causal)), flags)
+    need = C.c_size_t(0)
+    check(lib.attn_bwd_varlen(*args, None, C.byref(need), _stream(q)), "attn_bwd_varlen")
+    ws = _workspace(need.value, dev)
+    have = C.c_size_t(ws.numel())
+    check(lib.attn_bwd_varlen(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_bwd_varlen")
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# lse merge of two partial results of the same rows
+# ---------------------------------------------------------------------------
+def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, bf16_copy: bool = False):
+    """fp32 (out [rows, H, Dv], lse [H, rows]) of two partial results; with
+    bf16_copy also a bf16 rounding of out (to feed the backward). out/lse may
+    be given (e.g. aliasing fp32 out_a / lse_a as running accumulators)."""
+    rows, H, Dv = out_a.shape
+    for name, t in (("out_a", out_a), ("out_b", out_b)):
+        if t.device.type != "cuda" or t.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"{name} must be a bf16 or fp32 GPU tensor")
+        if tuple(t.shape) != (rows, H, Dv) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [rows, H, Dv]")
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (H, rows) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 [H, rows]")
+        if t.device != out_a.device:
+            raise ValueError("all merge tensors must be on one device")
+    dev = out_a.device
+    if out is None:
+        out = torch.empty((rows, H, Dv), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((H, rows), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or tuple(out.shape) != (rows, H, Dv) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [rows, H, Dv]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, rows) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [H, rows]")
+    ob = torch.empty((rows, H, Dv), dtype=torch.bfloat16, device=dev) if bf16_copy else None
+    dt = lambda t: ATTN_F32 if t.dtype == torch.float32 else ATTN_BF16  # noqa: E731
+    st = load().attn_merge(_ptr(out_a), dt(out_a), _ptr(lse_a), _ptr(out_b), dt(out_b),
+                           _ptr(lse_b), _ptr(out), _ptr(lse), _ptr(ob), rows, H, Dv,
+                           _stream(out_a))
+    check(st, "attn_merge")
+    return out, lse, ob
+
+
+# ---------------------------------------------------------------------------
+# document-causal segment layout (host)
+# ---------------------------------------------------------------------------
+def doc_segments(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int):
+    """Per-segment (query lengths, key lengths) of the document-causal layout
+    (mode 0: causal, keys cover the queries; mode 1: keys before queries)."""
+    ids = np.ascontiguousarray(np.asarray(doc_ids, dtype=np.int32))
+    if ids.ndim != 2:
+        raise ValueError("doc_ids is [B, S]")
+    B, S = ids.shape
+    lib = load()
+    n = C.c_int(0)
+    cap = 2 * S * max(B, 1) + 2
+    sq = (C.c_int32 * cap)()
+    sk = (C.c_int32 * cap)()
+    st = lib.attn_doc_segments(ids.ctypes.data_as(C.POINTER(C.c_int32)), B, S, q_start, q_len,
+                               k_start, k_len, mode, sq, sk, cap, C.byref(n))
+    check(st, "attn_doc_segments")
+    return list(sq[:n.value]), list(sk[:n.value])
+
+
+def doc_layout(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int, device):
+    """(cu_q, cu_k int32 on device, max_q, max_k) of doc_segments' layout."""
+    sq, sk = doc_segments(doc_ids, q_start, q_len, k_start, k_len, mode)
+    cu_q = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    return (torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_k).to(device),
+            int(max(sq, default=0)), int(max(sk, default=0)))

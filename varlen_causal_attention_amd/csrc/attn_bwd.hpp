@@ -37,32 +37,6 @@ struct BwdArgs {
   int dq_accumulate;
 };
 
-// Rows [r0, r0 + R) of a [rows][D] bf16 view (row stride sn; rows >= nrows
-// read as zero) stored transposed into LDS dst[D][R + 8], the row index placed
-// by vt_pos so the tile can serve as the A operand against a C tile used as B.
-template <int D, int R>
-__device__ __forceinline__ void load_transposed(uint16_t* dst, const uint16_t* src, int64_t sn,
-                                                int r0, int nrows, int tid, int nthreads) {
-  constexpr int TS = R + 8;
-  for (int c = tid; c < (R / 4) * (D / 8); c += nthreads) {
-    const int rq = c / (D / 8), dc = c % (D / 8);
-    u32x4 rv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + rq * 4 + i;
-      rv[i] = r < nrows ? ldg16(src + (int64_t)r * sn + dc * 8) : zero_u32x4();
-    }
-    const int pos = vt_pos(rq * 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x2 pk;
-      pk[0] = bf16_at(rv[0], e) | (bf16_at(rv[1], e) << 16);
-      pk[1] = bf16_at(rv[2], e) | (bf16_at(rv[3], e) << 16);
-      sts8(&dst[(dc * 8 + e) * TS + pos], pk);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O) in fp32. blockIdx = (row block, head, segment); a row
 // is covered by DV/8 lanes (at most 64), each reading 16-byte chunks.
@@ -98,21 +72,28 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup = (segment, kv-head, block of 32*(4/DS) keys)
+// dK / dV: one workgroup = (segment, kv-head, block of 32*(4/DS) keys). The
+// workgroup walks every (q-head of the group, 32-row query step) that can see
+// its keys; each step's Q and dO rows are staged row-major in LDS (the next
+// step's global loads issued a step ahead when PF), read row-wise as the A
+// operand of S = Q K^T and dP = dO V^T, and column-wise (transposing LDS read)
+// as the A operand of dK^T += Q^T dS and dV^T += dO^T P.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, bool CAUSAL>
+template <int DQK, int DV, int DS, int NBUF, bool PF, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) {
+  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int KG = 4 / DS;           // 32-key groups per workgroup
   constexpr int DR = DQK / DS;         // this wave's share of Dqk
   constexpr int VR = DV / DS;          // this wave's share of Dv
   static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
   constexpr int NKS = DR / 16, NVS = VR / 16;
   constexpr int NDB = DR / 32, NVB = VR / 32;
-  constexpr int TS = 40;               // transposed tile row stride (32 rows + pad)
-  __shared__ __attribute__((aligned(16))) uint16_t sqt[DQK * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t sdot[DV * TS];
-  __shared__ __attribute__((aligned(16))) float slse[32];
-  __shared__ __attribute__((aligned(16))) float sdel[32];
+  constexpr int BQ = 32;
+  constexpr int QS = DQK + 16, OS = DV + 16;  // LDS row strides (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t sq[NBUF][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t sdo[NBUF][BQ * OS];
+  __shared__ __attribute__((aligned(16))) float slse[NBUF][BQ];
+  __shared__ __attribute__((aligned(16))) float sdel[NBUF][BQ];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? KG * DS * 2 * 16 * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -123,7 +104,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
   const int kb0 = blockIdx.x * (32 * KG);
   if (kb0 >= sg.lk) return;
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
-  const int key = kb0 + kg * 32 + col;  // this lane's key (output column)
+  const int gk0 = kb0 + kg * 32;        // first key of this wave's group
+  const int key = gk0 + col;            // this lane's key (output column)
 
   const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
   const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
@@ -146,98 +128,133 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
 #pragma unroll
   for (int i = 0; i < NVB; ++i) dva[i] = zero16();
 
-  // queries that can see any key of this block
+  // query steps that can see any key of this block
   int q_begin = 0;
   if (CAUSAL) q_begin = max(0, kb0 - shift);
-  q_begin &= ~31;
+  q_begin &= ~(BQ - 1);
+  const int nq = lq > q_begin ? (lq - q_begin + BQ - 1) / BQ : 0;
+  const int total = a.G * nq;
 
-  for (int hh = 0; hh < a.G; ++hh) {
+  using QStage = TileStage<BQ, DQK, 256>;
+  using OStage = TileStage<BQ, DV, 256>;
+  QStage qst;
+  OStage ost;
+  float lse_r = 0.f, del_r = 0.f;  // threads < BQ carry one row's lse / delta
+
+  auto step_ptrs = [&](int it, const uint16_t*& qp, const uint16_t*& dop, int64_t& lb, int& q0) {
+    const int hh = it / nq;
+    q0 = q_begin + (it - hh * nq) * BQ;
     const int h = g * a.G + hh;
-    const uint16_t* qbp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
-    const uint16_t* dobp = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
-    const int64_t lbase = s * a.lse_sb + h * a.lse_sh + sg.q_row0;
-    for (int q0 = q_begin; q0 < lq; q0 += 32) {
-      __syncthreads();
-      load_transposed<DQK, 32>(sqt, qbp, a.q.sn, q0, lq, tid, 256);
-      load_transposed<DV, 32>(sdot, dobp, a.dout.sn, q0, lq, tid, 256);
-      if (tid < 32) {
-        const int i = q0 + tid;
-        float l2 = __builtin_inff();
-        float dl = 0.f;
-        if (i < lq) {
-          const float l = a.lse[lbase + i];
-          l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-          dl = a.delta[lbase + i];
-        }
-        slse[tid] = l2;
-        sdel[tid] = dl;
+    qp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+    dop = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
+    lb = s * a.lse_sb + h * a.lse_sh + sg.q_row0;
+  };
+  auto load_rows = [&](int it) {
+    const uint16_t *qp, *dop;
+    int64_t lb;
+    int q0;
+    step_ptrs(it, qp, dop, lb, q0);
+    qst.load(qp, a.q.sn, q0, lq, tid);
+    ost.load(dop, a.dout.sn, q0, lq, tid);
+    if (tid < BQ) {
+      const int i = q0 + tid;
+      lse_r = __builtin_inff();
+      del_r = 0.f;
+      if (i < lq) {
+        const float l = a.lse[lb + i];
+        lse_r = l == kNegInf ? __builtin_inff() : l * kLog2e;
+        del_r = a.delta[lb + i];
+      }
+    }
+  };
+  auto store_rows = [&](int b) {
+    qst.template store<QS>(sq[b], tid);
+    ost.template store<OS>(sdo[b], tid);
+    if (tid < BQ) {
+      slse[b][tid] = lse_r;
+      sdel[b][tid] = del_r;
+    }
+  };
+
+  if (total > 0) {
+    load_rows(0);
+    store_rows(0);
+    if (PF && total > 1) load_rows(1);
+  }
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = NBUF == 2 ? (it & 1) : 0;
+    const int q0 = q_begin + (it % nq) * BQ;
+    __syncthreads();  // step `it` is in LDS; nobody still reads the other buffer
+    if (NBUF == 2 && it + 1 < total) {
+      store_rows(buf ^ 1);
+      if (it + 2 < total) load_rows(it + 2);
+    }
+    // this 32-query step is hidden from every key of this wave's group?
+    const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + BQ - 1 + shift);
+    f32x16 sacc = zero16(), pacc = zero16();
+    if (live) {
+      // partial S[q][key] = Q K^T and dP[q][key] = dO V^T over this wave's d ranges
+#pragma unroll
+      for (int i = 0; i < NKS; ++i)
+        sacc = mfma32(lds_frag(&sq[buf][col * QS + ds * DR + half * 8 + i * 16]), kf[i], sacc);
+#pragma unroll
+      for (int i = 0; i < NVS; ++i)
+        pacc = mfma32(lds_frag(&sdo[buf][col * OS + ds * VR + half * 8 + i * 16]), vf[i], pacc);
+    }
+    if constexpr (DS > 1) {
+      float* mine = &sx[((kg * DS + ds) * 2) * 16 * 64];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mine[r * 64 + lane] = sacc[r];
+        mine[16 * 64 + r * 64 + lane] = pacc[r];
       }
       __syncthreads();
-      // this 32-query step is hidden from every key of this wave's group?
-      const int gk0 = kb0 + kg * 32;
-      const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + 31 + shift);
-      f32x16 sacc = zero16(), pacc = zero16();
-      if (live) {
-        // partial S[q][key] = Q K^T and dP[q][key] = dO V^T over this wave's d ranges
-        const int qi = q0 + col;
-        const bool qok = qi < lq;
-        const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
-        const uint16_t* dop = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + ds * VR + half * 8;
+      sacc = zero16();
+      pacc = zero16();
 #pragma unroll
-        for (int i = 0; i < NKS; ++i)
-          sacc = mfma32(as_frag(qok ? ldg16(qp + i * 16) : zero_u32x4()), kf[i], sacc);
-#pragma unroll
-        for (int i = 0; i < NVS; ++i)
-          pacc = mfma32(as_frag(qok ? ldg16(dop + i * 16) : zero_u32x4()), vf[i], pacc);
-      }
-      if constexpr (DS > 1) {
-        float* mine = &sx[((kg * DS + ds) * 2) * 16 * 64];
+      for (int o = 0; o < DS; ++o) {
+        const float* src = &sx[((kg * DS + o) * 2) * 16 * 64];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          mine[r * 64 + lane] = sacc[r];
-          mine[16 * 64 + r * 64 + lane] = pacc[r];
-        }
-        __syncthreads();
-        sacc = zero16();
-        pacc = zero16();
-#pragma unroll
-        for (int o = 0; o < DS; ++o) {
-          const float* src = &sx[((kg * DS + o) * 2) * 16 * 64];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sacc[r] += src[r * 64 + lane];
-            pacc[r] += src[16 * 64 + r * 64 + lane];
-          }
+          sacc[r] += src[r * 64 + lane];
+          pacc[r] += src[16 * 64 + r * 64 + lane];
         }
       }
-      if (!live) continue;
+    }
+    if (live) {
       // P and dS (rows q = q0 + 8*(r/4) + 4*half + r%4, column = key)
       float p[16], dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
         const int qi = q0 + qr;
-        bool vis = key < lk && qi < lq;
+        bool vis = key < lk;
         if (CAUSAL) vis = vis && key <= qi + shift;
-        const float x = fast_exp2(sacc[r] * a.scale_log2 - slse[qr]);
+        // rows past the segment end carry lse = +inf, so their P is 0
+        const float x = fast_exp2(sacc[r] * a.scale_log2 - slse[buf][qr]);
         p[r] = vis ? x : 0.f;
-        dsv[r] = p[r] * (pacc[r] - sdel[qr]);
+        dsv[r] = p[r] * (pacc[r] - sdel[buf][qr]);
       }
       const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
       const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
       // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
 #pragma unroll
       for (int b = 0; b < NVB; ++b) {
-        const uint16_t* src = &sdot[(ds * VR + b * 32 + col) * TS + half * 8];
-        dva[b] = mfma32(lds_frag(src), p0, dva[b]);
-        dva[b] = mfma32(lds_frag(src + 16), p1, dva[b]);
+        dva[b] = mfma32(tr_frag(sdo[buf], OS, 0, ds * VR + b * 32, lane), p0, dva[b]);
+        dva[b] = mfma32(tr_frag(sdo[buf], OS, 16, ds * VR + b * 32, lane), p1, dva[b]);
       }
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
-        const uint16_t* src = &sqt[(ds * DR + b * 32 + col) * TS + half * 8];
-        dka[b] = mfma32(lds_frag(src), s0, dka[b]);
-        dka[b] = mfma32(lds_frag(src + 16), s1, dka[b]);
+        dka[b] = mfma32(tr_frag(sq[buf], QS, 0, ds * DR + b * 32, lane), s0, dka[b]);
+        dka[b] = mfma32(tr_frag(sq[buf], QS, 16, ds * DR + b * 32, lane), s1, dka[b]);
       }
+    }
+    if (NBUF == 1 && it + 1 < total) {
+      __syncthreads();  // everyone is done reading the single buffer
+      if (!PF) load_rows(it + 1);
+      store_rows(0);
+      if (PF && it + 2 < total) load_rows(it + 2);
     }
   }
 
@@ -267,18 +284,22 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = (segment, q-head, block of 32*(4/DS) queries)
+// dQ: one workgroup = (segment, q-head, block of 32*(4/DS) queries). Per
+// BN-key tile, K and V are staged row-major in LDS; S^T = K Q^T and
+// dP^T = V dO^T read them row-wise, dQ^T += K^T dS^T column-wise.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdArgs a) {
+template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, bool CAUSAL>
+__global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) {
+  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int QG = 4 / DS;
   constexpr int DR = DQK / DS;
   constexpr int VR = DV / DS;
-  static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
-  constexpr int NKS = DR / 16, NVS = VR / 16, NDB = DR / 32;
-  constexpr int TS = 40;
-  __shared__ __attribute__((aligned(16))) uint16_t skt[DQK * TS];
-  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * 16 * 64 : 1];
+  static_assert(DR % 32 == 0 && VR % 32 == 0 && BN % 32 == 0, "head-dim split");
+  constexpr int NKS = DR / 16, NVS = VR / 16, NDB = DR / 32, NKB = BN / 32;
+  constexpr int KS = DQK + 16, VS = DV + 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
+  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -297,6 +318,30 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdArgs a) {
   const uint16_t* dobp = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
   const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
   const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
+
+  int kv_end = lk;
+  if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  using KStage = TileStage<BN, DQK, 256>;
+  using VStage = TileStage<BN, DV, 256>;
+  KStage kst;
+  VStage vst;
+  if (ntiles > 0) {
+    if (PF) {
+      kst.load(kbp, a.k.sn, 0, lk, tid);
+      vst.load(vbp, a.v.sn, 0, lk, tid);
+      kst.template store<KS>(sk[0], tid);
+      vst.template store<VS>(sv[0], tid);
+      if (ntiles > 1) {
+        kst.load(kbp, a.k.sn, BN, lk, tid);
+        vst.load(vbp, a.v.sn, BN, lk, tid);
+      }
+    } else {
+      KStage::template copy<KS>(sk[0], kbp, a.k.sn, 0, lk, tid);
+      VStage::template copy<VS>(sv[0], vbp, a.v.sn, 0, lk, tid);
+    }
+  }
 
   bf16x8 qf[NKS], df[NVS];
   {
@@ -319,64 +364,103 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqa[i] = zero16();
 
-  int kv_end = lk;
-  if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
-  for (int k0 = 0; k0 < kv_end; k0 += 32) {
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BN;
+    const int buf = NBUF == 2 ? (t & 1) : 0;
     __syncthreads();
-    load_transposed<DQK, 32>(skt, kbp, a.k.sn, k0, lk, tid, 256);
-    __syncthreads();
+    if (NBUF == 2 && t + 1 < ntiles) {
+      kst.template store<KS>(sk[buf ^ 1], tid);
+      vst.template store<VS>(sv[buf ^ 1], tid);
+      if (t + 2 < ntiles) {
+        kst.load(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
+        vst.load(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
+      }
+    }
     const bool live = wq0 < lq && !(CAUSAL && k0 > wq0 + 31 + shift);
-    f32x16 sacc = zero16(), pacc = zero16();
+    f32x16 sacc[NKB], pacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = zero16();
+      pacc[kb] = zero16();
+    }
     if (live) {
       // partial S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T over this wave's d ranges
-      const int kj = k0 + col;
-      const bool kok = kj < lk;
-      const uint16_t* kp = kbp + (int64_t)(kok ? kj : 0) * a.k.sn + ds * DR + half * 8;
-      const uint16_t* vp = vbp + (int64_t)(kok ? kj : 0) * a.v.sn + ds * VR + half * 8;
 #pragma unroll
       for (int i = 0; i < NKS; ++i)
-        sacc = mfma32(as_frag(kok ? ldg16(kp + i * 16) : zero_u32x4()), qf[i], sacc);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc[kb] = mfma32(lds_frag(&sk[buf][(kb * 32 + col) * KS + ds * DR + half * 8 + i * 16]),
+                            qf[i], sacc[kb]);
 #pragma unroll
       for (int i = 0; i < NVS; ++i)
-        pacc = mfma32(as_frag(kok ? ldg16(vp + i * 16) : zero_u32x4()), df[i], pacc);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          pacc[kb] = mfma32(lds_frag(&sv[buf][(kb * 32 + col) * VS + ds * VR + half * 8 + i * 16]),
+                            df[i], pacc[kb]);
     }
     if constexpr (DS > 1) {
-      float* mine = &sx[((qg * DS + ds) * 2) * 16 * 64];
+      float* mine = &sx[((qg * DS + ds) * 2 * NKB) * 16 * 64];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        mine[r * 64 + lane] = sacc[r];
-        mine[16 * 64 + r * 64 + lane] = pacc[r];
-      }
-      __syncthreads();
-      sacc = zero16();
-      pacc = zero16();
-#pragma unroll
-      for (int o = 0; o < DS; ++o) {
-        const float* src = &sx[((qg * DS + o) * 2) * 16 * 64];
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sacc[r] += src[r * 64 + lane];
-          pacc[r] += src[16 * 64 + r * 64 + lane];
+          mine[(kb * 16 + r) * 64 + lane] = sacc[kb][r];
+          mine[((NKB + kb) * 16 + r) * 64 + lane] = pacc[kb][r];
         }
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = zero16();
+        pacc[kb] = zero16();
+      }
+#pragma unroll
+      for (int o = 0; o < DS; ++o) {
+        const float* src = &sx[((qg * DS + o) * 2 * NKB) * 16 * 64];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sacc[kb][r] += src[(kb * 16 + r) * 64 + lane];
+            pacc[kb][r] += src[((NKB + kb) * 16 + r) * 64 + lane];
+          }
       }
     }
-    if (!live) continue;
-    float dsv[16];
+    if (live) {
+      bf16x8 sf[2 * NKB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kj = k0 + (r >> 2) * 8 + half * 4 + (r & 3);
-      bool vis = kj < lk && qok;
-      if (CAUSAL) vis = vis && kj <= qi + shift;
-      const float p = vis ? fast_exp2(sacc[r] * a.scale_log2 - l2) : 0.f;
-      dsv[r] = p * (pacc[r] - dl);
+      for (int kb = 0; kb < NKB; ++kb) {
+        float dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          bool vis = kj < lk && qok;
+          if (CAUSAL) vis = vis && kj <= qi + shift;
+          const float p = vis ? fast_exp2(sacc[kb][r] * a.scale_log2 - l2) : 0.f;
+          dsv[r] = p * (pacc[kb][r] - dl);
+        }
+        sf[2 * kb] = to_frag(dsv);
+        sf[2 * kb + 1] = to_frag(dsv + 8);
+      }
+      // dQ^T[d][q] += K^T dS^T (K^T read down the K tile's columns)
+#pragma unroll
+      for (int kk = 0; kk < 2 * NKB; ++kk)
+#pragma unroll
+        for (int b = 0; b < NDB; ++b)
+          dqa[b] = mfma32(tr_frag(sk[buf], KS, kk * 16, ds * DR + b * 32, lane), sf[kk], dqa[b]);
     }
-    const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
-    // dQ^T[d][q] += K^T dS^T
-#pragma unroll
-    for (int b = 0; b < NDB; ++b) {
-      const uint16_t* src = &skt[(ds * DR + b * 32 + col) * TS + half * 8];
-      dqa[b] = mfma32(lds_frag(src), s0, dqa[b]);
-      dqa[b] = mfma32(lds_frag(src + 16), s1, dqa[b]);
+    if (NBUF == 1 && t + 1 < ntiles) {
+      __syncthreads();
+      if (PF) {
+        kst.template store<KS>(sk[0], tid);
+        vst.template store<VS>(sv[0], tid);
+        if (t + 2 < ntiles) {
+          kst.load(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
+          vst.load(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
+        }
+      } else {
+        KStage::template copy<KS>(sk[0], kbp, a.k.sn, k0 + BN, lk, tid);
+        VStage::template copy<VS>(sv[0], vbp, a.v.sn, k0 + BN, lk, tid);
+      }
     }
   }
 

@@ -73,6 +73,72 @@ __device__ __forceinline__ bf16x8 to_frag(const float* x) {
   return r;
 }
 
+// Rows [row0, row0 + R) x D bf16 columns of a row-major global view, staged
+// through registers (16-byte chunks; rows >= nrows read as zero) into a
+// row-major LDS tile with row stride LS elements. load() may be issued a step
+// ahead so the global latency overlaps other work; copy() goes straight
+// through with few registers live.
+template <int R, int D, int NT>
+struct TileStage {
+  static constexpr int CH = R * D / 8;
+  static constexpr int PT = (CH + NT - 1) / NT;
+  u32x4 r[PT];
+
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t sn, int row0, int nrows,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), cc = c % (D / 8);
+      r[i] = (c < CH && row0 + row < nrows) ? ldg16(base + (int64_t)(row0 + row) * sn + cc * 8)
+                                            : zero_u32x4();
+    }
+  }
+  template <int LS>
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = tid + i * NT;
+      if (c < CH) sts16(&dst[(c / (D / 8)) * LS + (c % (D / 8)) * 8], r[i]);
+    }
+  }
+  template <int LS>
+  __device__ __forceinline__ static void copy(uint16_t* dst, const uint16_t* base, int64_t sn,
+                                              int row0, int nrows, int tid) {
+    for (int c = tid; c < CH; c += NT) {
+      const int row = c / (D / 8), cc = c % (D / 8);
+      sts16(&dst[row * LS + cc * 8], row0 + row < nrows
+                                         ? ldg16(base + (int64_t)(row0 + row) * sn + cc * 8)
+                                         : zero_u32x4());
+    }
+  }
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// MFMA A-operand fragment read down the columns of a row-major LDS tile
+// X[k][n] (row stride LS elements) with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16). Within each 16-lane group, lane s points at row
+// k0 + s/4 and columns 4*(s%4)..+3; the hardware hands lane i of the group
+// column i of those four rows. Result: lane l gets column n0 + (l % 32) and
+// rows {k0 + 4h + j, k0 + 8 + 4h + j : j < 4} (h = l / 32), the key/query
+// order in which a 32x32 C tile holds its rows, so the fragment pairs with a
+// C tile reused as the B operand.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* X, int LS, int k0, int n0, int lane) {
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
+  const int row = k0 + 4 * h + (s >> 2);
+  const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
+  const uint16_t* p = X + row * LS + c;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 8 * LS)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Segment geometry: query rows [q_row0, q_row0 + lq) and key rows
 // [k_row0, k_row0 + lk) of the packed tensors. cu arrays are clamped into
 // [0, T] so a malformed table can never index outside the tensors.

@@ -9,14 +9,15 @@
 // Work item: one workgroup = one (segment or batch, q-head, 128-row q tile);
 // four 32-row query blocks, each owned by DS waves (DS = 1 below Dqk 512).
 // Per key tile:
-//   * K tile [BN][Dqk] and V tile stored transposed [Dv][BN] in LDS;
+//   * K tile [BN][Dqk] and V tile [BN][Dv] row-major in LDS;
 //   * each wave computes S^T = K Q^T with Q held in registers, so a lane owns
 //     one query (its column) and the row max / row sum are lane-local except
 //     for one exchange with the partner lane of the other wave half;
 //   * softmax in base 2 with scale*log2(e) folded in; the running max is only
 //     moved when it grows by more than 2^8 (lazy rescale, exact either way);
-//   * O^T += V^T P^T takes the S^T accumulators directly as the B operand (the
-//     V^T tile is stored with the matching key permutation).
+//   * O^T += V^T P^T takes the S^T accumulators directly as the B operand; the
+//     V^T fragments come from the row-major V tile through the transposing
+//     LDS read, in the key order the S^T registers hold.
 #pragma once
 
 #include "attn_common.hpp"
@@ -39,31 +40,27 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdBM = 32 * kFwdWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-// Position of key kk (0..BN-1) inside a row of the transposed V tile. The PV
-// product contracts 16 keys per MFMA; lane half h supplies the S^T registers
-// that hold keys {16g + 4h + c, 16g + 8 + 4h + c : c < 4}, so those eight keys
-// are stored contiguously at 16g + 8h.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int grp = kk >> 4, a = (kk >> 3) & 1, h = (kk >> 2) & 1, c = kk & 3;
-  return grp * 16 + h * 8 + a * 4 + c;
-}
-
-template <int DQK, int DV, int BN, int DS, bool CAUSAL>
-__global__ void __launch_bounds__(256 * DS, 1) attn_fwd_kernel(const FwdArgs a) {
+template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL>
+__global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a) {
   // DS waves share one 32-row query block: wave `ds` of the group holds the
   // Q fragments of Dqk range [ds*DR, (ds+1)*DR) and accumulates O^T for Dv
   // range [ds*VR, (ds+1)*VR); the partial score tiles are summed through LDS
   // in a fixed order, so every wave of the group sees bitwise-identical scores.
+  // NBUF = 2 double-buffers the K/V tiles in LDS (one barrier per tile);
+  // NBUF = 1 keeps one buffer (two barriers per tile) to fit Dqk = 512.
+  // PF = the next tile's global loads are issued a tile ahead into registers
+  // (off where the registers are needed for the accumulators).
   static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
+  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 256 * DS;      // threads
   constexpr int DR = DQK / DS, VR = DV / DS;
-  constexpr int KS = DQK + 8;       // K row stride in LDS (elements), padded
-  constexpr int VS = BN + 8;        // V^T row stride
+  constexpr int KS = DQK + 16;      // K row stride in LDS (elements), padded
+  constexpr int VS = DV + 16;       // V row stride
   constexpr int NKB = BN / 32;
   constexpr int NDB = VR / 32;
   constexpr int NKS = DR / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[DV * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -88,6 +85,26 @@ __global__ void __launch_bounds__(256 * DS, 1) attn_fwd_kernel(const FwdArgs a) 
   if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
+  using KStage = TileStage<BN, DQK, NT>;
+  using VStage = TileStage<BN, DV, NT>;
+  KStage kst;
+  VStage vst;
+  if (ntiles > 0) {
+    if (PF) {
+      kst.load(kb, a.k.sn, 0, lk, tid);
+      vst.load(vb, a.v.sn, 0, lk, tid);
+      kst.template store<KS>(sk[0], tid);
+      vst.template store<VS>(sv[0], tid);
+      if (ntiles > 1) {
+        kst.load(kb, a.k.sn, BN, lk, tid);
+        vst.load(vb, a.v.sn, BN, lk, tid);
+      }
+    } else {
+      KStage::template copy<KS>(sk[0], kb, a.k.sn, 0, lk, tid);
+      VStage::template copy<VS>(sv[0], vb, a.v.sn, 0, lk, tid);
+    }
+  }
+
   bf16x8 qf[NKS];
   {
     const bool ok = row < lq;
@@ -104,47 +121,30 @@ __global__ void __launch_bounds__(256 * DS, 1) attn_fwd_kernel(const FwdArgs a) 
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    __syncthreads();
-    // K tile -> LDS, row-major
-    for (int c = tid; c < BN * DQK / 8; c += NT) {
-      const int r = c / (DQK / 8), cc = c % (DQK / 8);
-      const int key = k0 + r;
-      u32x4 val = key < lk ? ldg16(kb + (int64_t)key * a.k.sn + cc * 8) : zero_u32x4();
-      sts16(&sk[r * KS + cc * 8], val);
-    }
-    // V tile -> LDS, transposed with the PV key permutation
-    for (int c = tid; c < (BN / 4) * (DV / 8); c += NT) {
-      const int kq = c / (DV / 8), dc = c % (DV / 8);
-      u32x4 rv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kq * 4 + i;
-        rv[i] = key < lk ? ldg16(vb + (int64_t)key * a.v.sn + dc * 8) : zero_u32x4();
-      }
-      const int pos = vt_pos(kq * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2 pk;
-        pk[0] = bf16_at(rv[0], e) | (bf16_at(rv[1], e) << 16);
-        pk[1] = bf16_at(rv[2], e) | (bf16_at(rv[3], e) << 16);
-        sts8(&svt[(dc * 8 + e) * VS + pos], pk);
+    const int buf = NBUF == 2 ? (t & 1) : 0;
+    __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
+    if (NBUF == 2 && t + 1 < ntiles) {
+      kst.template store<KS>(sk[buf ^ 1], tid);
+      vst.template store<VS>(sv[buf ^ 1], tid);
+      if (t + 2 < ntiles) {
+        kst.load(kb, a.k.sn, k0 + 2 * BN, lk, tid);
+        vst.load(vb, a.v.sn, k0 + 2 * BN, lk, tid);
       }
     }
-    __syncthreads();
     // the DS waves of a group take every branch below together
     const bool live = wrow0 < lq && !(CAUSAL && k0 > wrow0 + 31 + shift);
 
     // S^T = K Q^T (partial over this wave's Dqk range when DS > 1)
     f32x16 sacc[NKB];
 #pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) {
-      f32x16 acc = zero16();
-      if (live) {
-        const uint16_t* src = &sk[(kbk * 32 + col) * KS + ds * DR + half * 8];
+    for (int kbk = 0; kbk < NKB; ++kbk) sacc[kbk] = zero16();
+    if (live) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) acc = mfma32(lds_frag(src + ks * 16), qf[ks], acc);
-      }
-      sacc[kbk] = acc;
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kbk = 0; kbk < NKB; ++kbk)
+          sacc[kbk] = mfma32(lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 + ks * 16]),
+                             qf[ks], sacc[kbk]);
     }
     if constexpr (DS > 1) {
       float* mine = &sx[(w * NKB) * 16 * 64];
@@ -163,62 +163,75 @@ __global__ void __launch_bounds__(256 * DS, 1) attn_fwd_kernel(const FwdArgs a) 
           sacc[kbk][r] = v;
         }
     }
-    if (!live) continue;
-
-    // scale, mask, row max
-    const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift);
-    float mx = kNegInf;
+    if (live) {
+      // scale, mask, row max
+      const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift);
+      float mx = kNegInf;
 #pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) {
+      for (int kbk = 0; kbk < NKB; ++kbk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kbk][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = k0 + kbk * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          const bool vis = key < lk && (!CAUSAL || key <= row + shift);
-          x = vis ? x : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kbk][r] * a.scale_log2;
+          if (need_mask) {
+            const int key = k0 + kbk * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            const bool vis = key < lk && (!CAUSAL || key <= row + shift);
+            x = vis ? x : kNegInf;
+          }
+          sacc[kbk][r] = x;
+          mx = fmaxf(mx, x);
         }
-        sacc[kbk][r] = x;
-        mx = fmaxf(mx, x);
       }
-    }
-    mx = fmaxf(mx, xor32(mx));
+      mx = fmaxf(mx, xor32(mx));
 
-    // lazy rescale of the running reference
-    const float m_new = fmaxf(m_ref, mx);
-    const bool need = m_new > m_ref + kLazyRescale;
-    if (__any(need)) {
-      const float m_set = need ? m_new : m_ref;
-      const float alpha = need ? fast_exp2(m_ref - m_set) : 1.f;
-      lsum *= alpha;
+      // lazy rescale of the running reference
+      const float m_new = fmaxf(m_ref, mx);
+      const bool need = m_new > m_ref + kLazyRescale;
+      if (__any(need)) {
+        const float m_set = need ? m_new : m_ref;
+        const float alpha = need ? fast_exp2(m_ref - m_set) : 1.f;
+        lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_ref = m_set;
-    }
-    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-
-    // P = exp2(x - m), row sum, pack to bf16 fragments
-    bf16x8 pf[2 * NKB];
-#pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(sacc[kbk][r] - m_use);
-        lsum += p[r];
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_ref = m_set;
       }
-      pf[2 * kbk] = to_frag(p);
-      pf[2 * kbk + 1] = to_frag(p + 8);
-    }
+      const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
-    // O^T += V^T P^T over this wave's Dv range
+      // P = exp2(x - m), row sum, pack to bf16 fragments
+      bf16x8 pf[2 * NKB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint16_t* src = &svt[(ds * VR + db * 32 + col) * VS + half * 8];
+      for (int kbk = 0; kbk < NKB; ++kbk) {
+        float p[16];
 #pragma unroll
-      for (int kk = 0; kk < 2 * NKB; ++kk) o[db] = mfma32(lds_frag(src + kk * 16), pf[kk], o[db]);
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(sacc[kbk][r] - m_use);
+          lsum += p[r];
+        }
+        pf[2 * kbk] = to_frag(p);
+        pf[2 * kbk + 1] = to_frag(p + 8);
+      }
+
+      // O^T += V^T P^T over this wave's Dv range (V^T read down V's columns)
+#pragma unroll
+      for (int kk = 0; kk < 2 * NKB; ++kk)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          o[db] = mfma32(tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane), pf[kk], o[db]);
+    }
+    if (NBUF == 1 && t + 1 < ntiles) {
+      __syncthreads();  // everyone is done reading the single buffer
+      if (PF) {
+        kst.template store<KS>(sk[0], tid);
+        vst.template store<VS>(sv[0], tid);
+        if (t + 2 < ntiles) {
+          kst.load(kb, a.k.sn, k0 + 2 * BN, lk, tid);
+          vst.load(vb, a.v.sn, k0 + 2 * BN, lk, tid);
+        }
+      } else {
+        KStage::template copy<KS>(sk[0], kb, a.k.sn, k0 + BN, lk, tid);
+        VStage::template copy<VS>(sv[0], vb, a.v.sn, k0 + BN, lk, tid);
+      }
     }
   }
 

@@ -22,8 +22,13 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "attn_api.hip"]
 CXX_SOURCES = ["attn_segments.cpp"]
+# -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in VGPRs. The kernels keep
+# their working set under the unified register budget; left to choose, the
+# compiler parks accumulators in AGPRs and then shuttles hundreds of values
+# per loop iteration between the two register files.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-command-line-argument", "-Wno-unused-result"]
 
 

@@ -121,6 +121,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
 #pragma unroll
     for (int i = 0; i < NVS; ++i) vf[i] = as_frag(ok ? ldg16(vp + i * 16) : zero_u32x4());
   }
+  wait_global_loads();
 
   f32x16 dka[NDB], dva[NVB];
 #pragma unroll
@@ -140,6 +141,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
   QStage qst;
   OStage ost;
   float lse_r = 0.f, del_r = 0.f;  // threads < BQ carry one row's lse / delta
+  bool row_ok = false;
 
   auto step_ptrs = [&](int it, const uint16_t*& qp, const uint16_t*& dop, int64_t& lb, int& q0) {
     const int hh = it / nq;
@@ -154,25 +156,24 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
     int64_t lb;
     int q0;
     step_ptrs(it, qp, dop, lb, q0);
-    qst.load(qp, a.q.sn, q0, lq, tid);
-    ost.load(dop, a.dout.sn, q0, lq, tid);
+    qst.load_clamped(qp, a.q.sn, q0, lq, tid);
+    ost.load_clamped(dop, a.dout.sn, q0, lq, tid);
+    // raw values only: using a loaded value here would make the wave wait for
+    // every earlier load, the prefetched tiles included
     if (tid < BQ) {
-      const int i = q0 + tid;
-      lse_r = __builtin_inff();
-      del_r = 0.f;
-      if (i < lq) {
-        const float l = a.lse[lb + i];
-        lse_r = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        del_r = a.delta[lb + i];
-      }
+      const int i = min(q0 + tid, lq - 1);
+      lse_r = a.lse[lb + i];
+      del_r = a.delta[lb + i];
+      row_ok = q0 + tid < lq;
     }
   };
   auto store_rows = [&](int b) {
     qst.template store<QS>(sq[b], tid);
     ost.template store<OS>(sdo[b], tid);
     if (tid < BQ) {
-      slse[b][tid] = lse_r;
-      sdel[b][tid] = del_r;
+      // base-2 lse; rows past the segment end or with lse = -inf get +inf (P = 0)
+      slse[b][tid] = (row_ok && lse_r != kNegInf) ? lse_r * kLog2e : __builtin_inff();
+      sdel[b][tid] = row_ok ? del_r : 0.f;
     }
   };
 
@@ -223,18 +224,23 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
       }
     }
     if (live) {
-      // P and dS (rows q = q0 + 8*(r/4) + 4*half + r%4, column = key)
+      // P and dS (rows q = q0 + 8*(r/4) + 4*half + r%4, column = key). Rows
+      // past the segment end carry lse = +inf, so their P is 0 without a mask;
+      // the key mask is only needed on steps that cross the causal diagonal
+      // or hold keys past the segment end.
+      const bool need_mask = gk0 + 31 >= lk || (CAUSAL && gk0 + 31 > q0 + shift);
       float p[16], dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-        const int qi = q0 + qr;
-        bool vis = key < lk;
-        if (CAUSAL) vis = vis && key <= qi + shift;
-        // rows past the segment end carry lse = +inf, so their P is 0
-        const float x = fast_exp2(sacc[r] * a.scale_log2 - slse[buf][qr]);
-        p[r] = vis ? x : 0.f;
-        dsv[r] = p[r] * (pacc[r] - sdel[buf][qr]);
+        float x = fast_exp2(sacc[r] * a.scale_log2 - slse[buf][qr]);
+        if (need_mask) {
+          bool vis = key < lk;
+          if (CAUSAL) vis = vis && key <= q0 + qr + shift;
+          x = vis ? x : 0.f;
+        }
+        p[r] = x;
+        dsv[r] = x * (pacc[r] - sdel[buf][qr]);
       }
       const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
       const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
@@ -323,26 +329,6 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
   if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  using KStage = TileStage<BN, DQK, 256>;
-  using VStage = TileStage<BN, DV, 256>;
-  KStage kst;
-  VStage vst;
-  if (ntiles > 0) {
-    if (PF) {
-      kst.load(kbp, a.k.sn, 0, lk, tid);
-      vst.load(vbp, a.v.sn, 0, lk, tid);
-      kst.template store<KS>(sk[0], tid);
-      vst.template store<VS>(sv[0], tid);
-      if (ntiles > 1) {
-        kst.load(kbp, a.k.sn, BN, lk, tid);
-        vst.load(vbp, a.v.sn, BN, lk, tid);
-      }
-    } else {
-      KStage::template copy<KS>(sk[0], kbp, a.k.sn, 0, lk, tid);
-      VStage::template copy<VS>(sv[0], vbp, a.v.sn, 0, lk, tid);
-    }
-  }
-
   bf16x8 qf[NKS], df[NVS];
   {
     const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
@@ -359,6 +345,28 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
     l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
     dl = a.delta[lidx];
   }
+  wait_global_loads();
+
+  using KStage = TileStage<BN, DQK, 256>;
+  using VStage = TileStage<BN, DV, 256>;
+  KStage kst;
+  VStage vst;
+  if (ntiles > 0) {
+    if (PF) {
+      kst.load_clamped(kbp, a.k.sn, 0, lk, tid);
+      vst.load_clamped(vbp, a.v.sn, 0, lk, tid);
+      kst.template store<KS>(sk[0], tid);
+      vst.template store<VS>(sv[0], tid);
+      if (ntiles > 1) {
+        kst.load_clamped(kbp, a.k.sn, BN, lk, tid);
+        vst.load_clamped(vbp, a.v.sn, BN, lk, tid);
+      }
+    } else {
+      KStage::template copy<KS>(sk[0], kbp, a.k.sn, 0, lk, tid);
+      VStage::template copy<VS>(sv[0], vbp, a.v.sn, 0, lk, tid);
+    }
+  }
+
 
   f32x16 dqa[NDB];
 #pragma unroll
@@ -372,8 +380,8 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
-        kst.load(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
-        vst.load(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
+        kst.load_clamped(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
+        vst.load_clamped(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
       }
     }
     const bool live = wq0 < lq && !(CAUSAL && k0 > wq0 + 31 + shift);
@@ -426,16 +434,22 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
       }
     }
     if (live) {
+      // rows past the segment end carry l2 = +inf (P = 0); the key mask is only
+      // needed on tiles that cross the diagonal or the segment end
+      const bool need_mask = k0 + BN > lk || (CAUSAL && k0 + BN - 1 > wq0 + shift);
       bf16x8 sf[2 * NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          bool vis = kj < lk && qok;
-          if (CAUSAL) vis = vis && kj <= qi + shift;
-          const float p = vis ? fast_exp2(sacc[kb][r] * a.scale_log2 - l2) : 0.f;
+          float p = fast_exp2(sacc[kb][r] * a.scale_log2 - l2);
+          if (need_mask) {
+            const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            bool vis = kj < lk;
+            if (CAUSAL) vis = vis && kj <= qi + shift;
+            p = vis ? p : 0.f;
+          }
           dsv[r] = p * (pacc[kb][r] - dl);
         }
         sf[2 * kb] = to_frag(dsv);
@@ -454,8 +468,8 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
         kst.template store<KS>(sk[0], tid);
         vst.template store<VS>(sv[0], tid);
         if (t + 2 < ntiles) {
-          kst.load(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
-          vst.load(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
+          kst.load_clamped(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
+          vst.load_clamped(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
         }
       } else {
         KStage::template copy<KS>(sk[0], kbp, a.k.sn, k0 + BN, lk, tid);

@@ -62,6 +62,12 @@ __device__ __forceinline__ uint32_t bf16_at(u32x4 v, int e) {
 // Partner lane across the two wave halves (l ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Wait until every outstanding global load of this wave has landed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at "no wait"). Used once,
+// after the loads of values that stay live across a loop, so the loop's
+// own prefetches are never waited on before they are needed.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -92,6 +98,18 @@ struct TileStage {
       const int row = c / (D / 8), cc = c % (D / 8);
       r[i] = (c < CH && row0 + row < nrows) ? ldg16(base + (int64_t)(row0 + row) * sn + cc * 8)
                                             : zero_u32x4();
+    }
+  }
+  // Branch-free variant: rows past the end re-read row nrows - 1 (nrows >= 1),
+  // which stays inside the segment; callers mask those rows out of every
+  // result (their scores are hidden / their P is zero).
+  __device__ __forceinline__ void load_clamped(const uint16_t* base, int64_t sn, int row0,
+                                               int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = min(tid + i * NT, CH - 1);
+      const int row = min(row0 + c / (D / 8), nrows - 1), cc = c % (D / 8);
+      r[i] = ldg16(base + (int64_t)row * sn + cc * 8);
     }
   }
   template <int LS>

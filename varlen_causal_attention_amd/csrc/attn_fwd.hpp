@@ -85,26 +85,6 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  using KStage = TileStage<BN, DQK, NT>;
-  using VStage = TileStage<BN, DV, NT>;
-  KStage kst;
-  VStage vst;
-  if (ntiles > 0) {
-    if (PF) {
-      kst.load(kb, a.k.sn, 0, lk, tid);
-      vst.load(vb, a.v.sn, 0, lk, tid);
-      kst.template store<KS>(sk[0], tid);
-      vst.template store<VS>(sv[0], tid);
-      if (ntiles > 1) {
-        kst.load(kb, a.k.sn, BN, lk, tid);
-        vst.load(vb, a.v.sn, BN, lk, tid);
-      }
-    } else {
-      KStage::template copy<KS>(sk[0], kb, a.k.sn, 0, lk, tid);
-      VStage::template copy<VS>(sv[0], vb, a.v.sn, 0, lk, tid);
-    }
-  }
-
   bf16x8 qf[NKS];
   {
     const bool ok = row < lq;
@@ -112,6 +92,28 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_frag(ok ? ldg16(src + ks * 16) : zero_u32x4());
   }
+  wait_global_loads();
+
+  using KStage = TileStage<BN, DQK, NT>;
+  using VStage = TileStage<BN, DV, NT>;
+  KStage kst;
+  VStage vst;
+  if (ntiles > 0) {
+    if (PF) {
+      kst.load_clamped(kb, a.k.sn, 0, lk, tid);
+      vst.load_clamped(vb, a.v.sn, 0, lk, tid);
+      kst.template store<KS>(sk[0], tid);
+      vst.template store<VS>(sv[0], tid);
+      if (ntiles > 1) {
+        kst.load_clamped(kb, a.k.sn, BN, lk, tid);
+        vst.load_clamped(vb, a.v.sn, BN, lk, tid);
+      }
+    } else {
+      KStage::template copy<KS>(sk[0], kb, a.k.sn, 0, lk, tid);
+      VStage::template copy<VS>(sv[0], vb, a.v.sn, 0, lk, tid);
+    }
+  }
+
 
   f32x16 o[NDB];
 #pragma unroll
@@ -127,8 +129,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
-        kst.load(kb, a.k.sn, k0 + 2 * BN, lk, tid);
-        vst.load(vb, a.v.sn, k0 + 2 * BN, lk, tid);
+        kst.load_clamped(kb, a.k.sn, k0 + 2 * BN, lk, tid);
+        vst.load_clamped(vb, a.v.sn, k0 + 2 * BN, lk, tid);
       }
     }
     // the DS waves of a group take every branch below together
@@ -225,8 +227,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
         kst.template store<KS>(sk[0], tid);
         vst.template store<VS>(sv[0], tid);
         if (t + 2 < ntiles) {
-          kst.load(kb, a.k.sn, k0 + 2 * BN, lk, tid);
-          vst.load(vb, a.v.sn, k0 + 2 * BN, lk, tid);
+          kst.load_clamped(kb, a.k.sn, k0 + 2 * BN, lk, tid);
+          vst.load_clamped(vb, a.v.sn, k0 + 2 * BN, lk, tid);
         }
       } else {
         KStage::template copy<KS>(sk[0], kb, a.k.sn, k0 + BN, lk, tid);

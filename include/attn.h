@@ -40,9 +40,8 @@
  *    size query: the required size is written to *workspace_bytes and nothing
  *    is launched. Otherwise a call that needs workspace must get a 16-byte
  *    aligned buffer with *workspace_bytes >= the required size, else
- *    ATTN_E_WORKSPACE. Calls that need none (the forwards) may pass NULL for
- *    both. The workspace holds no result and may be reused once the stream
- *    has passed the call.
+ *    ATTN_E_WORKSPACE. The workspace holds no result and may be reused once
+ *    the stream has passed the call.
  *  - Errors: problems visible on the host return a negative status before any
  *    launch, and attn_last_error() describes the last one on this thread.
  *    Malformed cu_seqlens contents (not monotone, not ending at T) give
@@ -93,7 +92,8 @@ int attn_is_supported(int dtype, int dqk, int dv);
  *  strides[12] = element strides (b, h, n) of q, k, v, out, in that order
  *  (so both BHND- and BSHD-contiguous storage work). Nq may differ from Nk;
  *  with causal = 1 the mask is bottom-right aligned (query i sees keys
- *  j <= i + Nk - Nq). Dense calls need no workspace (size 0). */
+ *  j <= i + Nk - Nq). Needs a small workspace (the work list the call
+ *  orders heaviest tile first); query its size with workspace = NULL. */
 int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void* out,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv,
                    const int64_t* strides, float scale, int causal, void* workspace,
@@ -107,8 +107,10 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
  *  cu_q[s]..cu_q[s+1] with key rows cu_k[s]..cu_k[s+1]. Required:
  *  cu_q[0] = cu_k[0] = 0, non-decreasing, cu_q[S] = Tq, cu_k[S] = Tk.
  *  Zero-query and zero-key segments are allowed.
- *  max_q, max_k: host upper bounds of the per-segment lengths (grid sizing).
- *  strides[8] = element strides (t, h) of q, k, v, out. */
+ *  max_q, max_k: host upper bounds of the per-segment lengths.
+ *  strides[8] = element strides (t, h) of q, k, v, out.
+ *  Needs a workspace (the heavy-first work list built on the device from
+ *  cu_seqlens); query its size with workspace = NULL. */
 int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* out,
                     float* lse, const int32_t* cu_q, const int32_t* cu_k, int num_segments,
                     int max_q, int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,

@@ -74,8 +74,14 @@ def test_dense_forward_rejects_bad_arguments(lib, kw, status):
 
 def test_dense_forward_workspace_query(lib):
     st, need = _dense(lib)
-    assert st == 0 and need == 0
+    # the forward's workspace holds its heavy-first work list
+    assert st == 0 and need >= 256 + 8 and need % 256 == 0
     assert lib.attn_last_error().decode() == ""
+    # no workspace and no size pointer: a workspace error, nothing launched
+    s = _lib.i64_array([8 * 128 * 4, 8 * 128, 128] * 4)
+    st = lib.attn_fwd_dense(0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 8, 8, 128, 128, s, 0.1, 1,
+                            None, None, None)
+    assert st == _lib.ATTN_E_WORKSPACE
 
 
 def _bwd_varlen(lib, ws=None, have=None, **kw):

@@ -348,11 +348,15 @@ def test_outputs_stay_inside_their_views(vca):
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
     strides = _lib.i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
                              + list(out.stride()[:3]))
-    st = lib.attn_fwd_dense(0, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
-                            C.c_void_p(v.data_ptr()), C.c_void_p(out.data_ptr()),
-                            C.c_void_p(lse.data_ptr()), B, Hq, Hkv, N, N, D, D, strides,
-                            1 / math.sqrt(D), 1, None, None,
-                            C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    args = (0, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()), C.c_void_p(v.data_ptr()),
+            C.c_void_p(out.data_ptr()), C.c_void_p(lse.data_ptr()), B, Hq, Hkv, N, N, D, D, strides,
+            1 / math.sqrt(D), 1)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    need = C.c_size_t(0)
+    assert lib.attn_fwd_dense(*args, None, C.byref(need), stream) == 0
+    ws = torch.empty(need.value, dtype=torch.uint8, device="cuda")
+    have = C.c_size_t(need.value)
+    st = lib.attn_fwd_dense(*args, C.c_void_p(ws.data_ptr()), C.byref(have), stream)
     assert st == 0, lib.attn_last_error()
     torch.cuda.synchronize()
     mask = torch.ones_like(big, dtype=torch.bool)

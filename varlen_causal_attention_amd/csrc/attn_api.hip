@@ -46,8 +46,6 @@ int check_tensor(const char* name, const void* p, bool nonempty, const int64_t* 
   return ATTN_OK;
 }
 
-size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
-
 // workspace protocol: (workspace == NULL && workspace_bytes != NULL) is a size
 // query; otherwise a call that needs `need` bytes must be given them.
 int workspace_step(size_t need, void* ws, size_t* ws_bytes, bool* query) {
@@ -130,7 +128,8 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
   if ((st = check_tensor("out", out, has_q, strides + 9, 3))) return st;
   if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
   bool query = false;
-  if ((st = workspace_step(0, workspace, workspace_bytes, &query))) return st;
+  const size_t need_ws = vca::fwd_workspace_bytes((int64_t)B * Nq, B);
+  if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || !has_q) return ok();
 
   vca::FwdArgs a{};
@@ -148,7 +147,8 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
   a.Tk = Nk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
-  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, B, Hq, Nq, stream), "attn_fwd_dense launch");
+  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, B, Hq, (int64_t)B * Nq, workspace, stream),
+                    "attn_fwd_dense launch");
 }
 
 int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
@@ -172,7 +172,8 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
   if ((st = check_tensor("out", out, Tq > 0, strides + 6, 2))) return st;
   if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
   bool query = false;
-  if ((st = workspace_step(0, workspace, workspace_bytes, &query))) return st;
+  const size_t need_ws = vca::fwd_workspace_bytes(Tq, num_segments);
+  if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || Tq == 0) return ok();
   if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
     return st;
@@ -192,7 +193,7 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
   a.Tk = Tk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
-  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, max_q, stream),
+  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, workspace, stream),
                     "attn_fwd_varlen launch");
 }
 
@@ -214,7 +215,8 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   for (int i = 0; i < 8; ++i)
     if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 3 * i, 3))) return st;
   if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
-  const size_t need_ws = round_up(sizeof(float) * (size_t)B * Hq * Nq);
+  const size_t need_ws =
+      vca::bwd_workspace_bytes((int64_t)B * Hq * Nq, (int64_t)B * Nq, (int64_t)B * Nk, B);
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (!has_q && !has_k)) return ok();
@@ -241,7 +243,8 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   a.scale = scale;
   a.scale_log2 = scale * vca::kLog2e;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
-  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, Nk, stream),
+  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
+                                    (int64_t)B * Nk, workspace, stream),
                     "attn_bwd_dense launch");
 }
 
@@ -269,7 +272,7 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   for (int i = 0; i < 8; ++i)
     if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 2 * i, 2))) return st;
   if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
-  const size_t need_ws = round_up(sizeof(float) * (size_t)Hq * Tq);
+  const size_t need_ws = vca::bwd_workspace_bytes((int64_t)Hq * Tq, Tq, Tk, num_segments);
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (Tq == 0 && Tk == 0)) return ok();
@@ -298,8 +301,8 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   a.scale = scale;
   a.scale_log2 = scale * vca::kLog2e;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
-  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, max_k,
-                                    stream),
+  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq, Tk,
+                                    workspace, stream),
                     "attn_bwd_varlen launch");
 }
 

@@ -10,24 +10,72 @@ namespace {
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
 template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE>
-hipError_t bwd_dims(const BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
-                    int max_k, hipStream_t st) {
+hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
+                    int64_t k_rows, void* ws, hipStream_t st) {
+  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
+  constexpr int key_block = kPipe ? 128 : 32 * (4 / DS);
+  constexpr int q_tile = 32 * (4 / DS);
+  char* w = static_cast<char*>(ws);
+  const size_t delta_bytes = align256(sizeof(float) * (size_t)Hq * q_rows);
+  int* counts = reinterpret_cast<int*>(w + delta_bytes);
+  int2* list_q = reinterpret_cast<int2*>(w + delta_bytes + 256);
+  const size_t cap_q = list_capacity(q_rows, nseg), cap_k = list_capacity(k_rows, nseg);
+  int2* list_k = reinterpret_cast<int2*>(w + delta_bytes + 256 + align256(sizeof(int2) * cap_q));
+  SchedArgs sa{};
+  sa.cu_q = a.cu_q;
+  sa.cu_k = a.cu_k;
+  sa.nseg = nseg;
+  sa.Nq = a.Nq;
+  sa.Nk = a.Nk;
+  sa.Tq = a.Tq;
+  sa.Tk = a.Tk;
+  sa.causal = causal;
+  // query tiles of the dQ pass, cost = key tiles walked
+  sa.by_keys = 0;
+  sa.tile = q_tile;
+  sa.step = BN;
+  sa.list = list_q;
+  sa.count = counts;
+  sa.max_items = (int)cap_q;
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  // key blocks of the dK/dV pass, cost = query steps walked
+  sa.by_keys = 1;
+  sa.tile = key_block;
+  sa.step = 32;
+  sa.list = list_k;
+  sa.count = counts + 1;
+  sa.max_items = (int)cap_k;
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  a.items_q = list_q;
+  a.count_q = counts;
+  a.items_k = list_k;
+  a.count_k = counts + 1;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+
   constexpr int LPR = DV / 8 >= 64 ? 64 : DV / 8;
   constexpr int rows_per_block = 4 * (64 / LPR);
   if (max_q > 0) {
     const dim3 g((max_q + rows_per_block - 1) / rows_per_block, Hq, nseg);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<DV>), g, dim3(256), 0, st, a);
   }
-  constexpr int blk = 32 * (4 / DS);
-  if (max_k > 0) {
-    const dim3 g((max_k + blk - 1) / blk, Hkv, nseg);
-    if (causal)
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, true>), g, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, false>), g, dim3(256), 0, st, a);
+  if (k_rows > 0) {
+    const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
+    if constexpr (kPipe) {
+      if (causal)
+        hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, true>), g, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, false>), g, dim3(256), 0, st, a);
+    } else {
+      if (causal)
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, true>), g, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, false>), g, dim3(256), 0, st,
+                           a);
+    }
   }
-  if (max_q > 0) {
-    const dim3 g((max_q + blk - 1) / blk, Hq, nseg);
+  if (q_rows > 0) {
+    const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
     if (causal)
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, true>), g, dim3(256), 0,
                          st, a);
@@ -40,11 +88,12 @@ hipError_t bwd_dims(const BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, in
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
-                      int max_q, int max_k, hipStream_t st) {
+hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                      int64_t q_rows, int64_t k_rows, void* ws, hipStream_t st) {
   if (nseg == 0 || Hq == 0) return hipSuccess;
-#define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE) \
-  bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE>(a, causal, nseg, Hq, Hkv, max_q, max_k, st)
+#define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE)                                      \
+  bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE>(a, causal, nseg, Hq, Hkv, max_q, q_rows, \
+                                                 k_rows, ws, st)
   if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2);
   if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2);
   if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 2, 2, true, 32, 2, true, 1);

@@ -35,6 +35,11 @@ struct BwdArgs {
   int G;
   float scale, scale_log2;
   int dq_accumulate;
+  int Hq, Hkv;
+  const int2* items_q;    // (segment, query tile) for the dQ pass, heavy first
+  const int* count_q;
+  const int2* items_k;    // (segment, key block) for the dK/dV pass, heavy first
+  const int* count_k;
 };
 
 // ---------------------------------------------------------------------------
@@ -99,9 +104,12 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int kg = w / DS, ds = w % DS;
-  const int s = blockIdx.z, g = blockIdx.y;
+  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  if (item >= *a.count_k) return;
+  const int2 st = a.items_k[item];
+  const int s = st.x;
   const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
-  const int kb0 = blockIdx.x * (32 * KG);
+  const int kb0 = st.y * (32 * KG);
   if (kb0 >= sg.lk) return;
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
   const int gk0 = kb0 + kg * 32;        // first key of this wave's group
@@ -202,6 +210,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < NVS; ++i)
         pacc = mfma32(lds_frag(&sdo[buf][col * OS + ds * VR + half * 8 + i * 16]), vf[i], pacc);
+      pipeline_mfma_reads<NKS + NVS, 4>();
     }
     if constexpr (DS > 1) {
       float* mine = &sx[((kg * DS + ds) * 2) * 16 * 64];
@@ -255,6 +264,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
         dka[b] = mfma32(tr_frag(sq[buf], QS, 0, ds * DR + b * 32, lane), s0, dka[b]);
         dka[b] = mfma32(tr_frag(sq[buf], QS, 16, ds * DR + b * 32, lane), s1, dka[b]);
       }
+      pipeline_mfma_reads<2 * (NVB + NDB), 4, 2>();
     }
     if (NBUF == 1 && it + 1 < total) {
       __syncthreads();  // everyone is done reading the single buffer
@@ -290,6 +300,181 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV for head dims that need no split (Dqk = Dv <= 128), software
+// pipelined: one workgroup = (segment, kv-head, 128 keys), four waves of 32
+// keys. The workgroup's K and V rows stay in LDS for its whole life, so the
+// registers hold only the dK^T/dV^T accumulators and two generations of the
+// score tiles. Each iteration issues the S/dP MFMAs of query step it+1 and
+// computes P/dS of step it between them (the matrix pipe and the vector ALU
+// run at the same time), then accumulates dV^T/dK^T of step it.
+// The score accumulators start from -lse/scale and -delta instead of zero:
+// P = exp2(scale*log2(e)*acc) and dS = P*acc then need no per-row operands,
+// and rows past the segment end (lse = +inf there) come out as P = 0.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArgs a) {
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int BQ = 32, BK = 128;
+  constexpr int KS = D + 8;   // K/V rows: row-wise reads only
+  constexpr int QS = D + 16;  // Q/dO rows: row-wise and transposing reads
+  __shared__ __attribute__((aligned(16))) uint16_t sk[BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[BK * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t sdo[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) float slse[2][BQ];  // -lse * log2(e) / (scale*log2(e))
+  __shared__ __attribute__((aligned(16))) float sdel[2][BQ];  // -delta
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  if (item >= *a.count_k) return;
+  const int2 st = a.items_k[item];
+  const int s = st.x;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int kb0 = st.y * BK;
+  if (kb0 >= sg.lk) return;
+  const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
+  const int gk0 = kb0 + w * 32;
+  const int key = gk0 + col;
+  // first query row that sees this lane's key (keys past the segment: none)
+  const int qmin = key < lk ? (CAUSAL ? key - shift : INT_MIN) : INT_MAX;
+
+  const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
+  const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
+  TileStage<BK, D, 256>::template copy<KS>(sk, kbp, a.k.sn, kb0, lk, tid);
+  TileStage<BK, D, 256>::template copy<KS>(sv, vbp, a.v.sn, kb0, lk, tid);
+  wait_global_loads();
+
+  int q_begin = 0;
+  if (CAUSAL) q_begin = max(0, kb0 - shift);
+  q_begin &= ~(BQ - 1);
+  const int nq = lq > q_begin ? (lq - q_begin + BQ - 1) / BQ : 0;
+  const int total = a.G * nq;
+  const float inv_c = 1.f / a.scale_log2;
+
+  using QStage = TileStage<BQ, D, 256>;
+  QStage qst, ost;
+  float lse_r = 0.f, del_r = 0.f;
+  bool row_ok = false;
+  auto load_rows = [&](int it) {
+    const int hh = it / nq;
+    const int q0 = q_begin + (it - hh * nq) * BQ;
+    const int h = g * a.G + hh;
+    const uint16_t* qp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+    const uint16_t* dop = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
+    qst.load_clamped(qp, a.q.sn, q0, lq, tid);
+    ost.load_clamped(dop, a.dout.sn, q0, lq, tid);
+    if (tid < BQ) {
+      const int64_t lb = s * a.lse_sb + h * a.lse_sh + sg.q_row0;
+      const int i = min(q0 + tid, lq - 1);
+      lse_r = a.lse[lb + i];
+      del_r = a.delta[lb + i];
+      row_ok = q0 + tid < lq;
+    }
+  };
+  auto store_rows = [&](int b) {
+    qst.template store<QS>(sq[b], tid);
+    ost.template store<QS>(sdo[b], tid);
+    if (tid < BQ) {
+      // rows past the segment end or with lse = -inf: -inf, so P = 0
+      slse[b][tid] = (row_ok && lse_r != kNegInf) ? -lse_r * kLog2e * inv_c : kNegInf;
+      sdel[b][tid] = row_ok ? -del_r : 0.f;
+    }
+  };
+  // score tiles of step in buffer b: C starts at -lse/c (S) and -delta (dP)
+  auto scores = [&](int b, f32x16& sacc, f32x16& pacc) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&slse[b][r4 * 8 + half * 4]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sdel[b][r4 * 8 + half * 4]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sacc[r4 * 4 + c] = l4[c];
+        pacc[r4 * 4 + c] = d4[c];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      sacc = mfma32(lds_frag(&sq[b][col * QS + half * 8 + i * 16]),
+                    lds_frag(&sk[(w * 32 + col) * KS + half * 8 + i * 16]), sacc);
+      pacc = mfma32(lds_frag(&sdo[b][col * QS + half * 8 + i * 16]),
+                    lds_frag(&sv[(w * 32 + col) * KS + half * 8 + i * 16]), pacc);
+    }
+  };
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dka[i] = zero16();
+    dva[i] = zero16();
+  }
+  f32x16 sacc, pacc;
+  if (total > 0) {
+    load_rows(0);
+    store_rows(0);
+    if (total > 1) load_rows(1);
+    __syncthreads();
+    scores(0, sacc, pacc);
+  }
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1, nb = buf ^ 1;
+    const int q0 = q_begin + (it % nq) * BQ;
+    __syncthreads();  // every wave is done with step it-1 (its buffer is nb)
+    if (it + 1 < total) {
+      store_rows(nb);
+      if (it + 2 < total) load_rows(it + 2);
+    }
+    __syncthreads();  // step it+1 is visible
+    // scores of step it+1 (its buffer holds stale rows after the last step;
+    // those results are never used)
+    f32x16 sacc_n, pacc_n;
+    scores(nb, sacc_n, pacc_n);
+    // P and dS of step it: rows q = q0 + 8*(r/4) + 4*half + r%4
+    float p[16], dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = q0 + (r >> 2) * 8 + half * 4 + (r & 3);
+      float x = fast_exp2(sacc[r] * a.scale_log2);
+      x = qi >= qmin ? x : 0.f;
+      p[r] = x;
+      dsv[r] = x * pacc[r];
+    }
+    const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
+    const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+    // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) {
+      dva[b] = mfma32(tr_frag(sdo[buf], QS, 0, b * 32, lane), p0, dva[b]);
+      dva[b] = mfma32(tr_frag(sdo[buf], QS, 16, b * 32, lane), p1, dva[b]);
+      dka[b] = mfma32(tr_frag(sq[buf], QS, 0, b * 32, lane), s0, dka[b]);
+      dka[b] = mfma32(tr_frag(sq[buf], QS, 16, b * 32, lane), s1, dka[b]);
+    }
+    sacc = sacc_n;
+    pacc = pacc_n;
+  }
+
+  if (key < lk) {
+    const int64_t r = sg.k_row0 + key;
+    uint16_t* dkp = a.dk.p + s * a.dk.sb + r * a.dk.sn + g * a.dk.sh;
+    uint16_t* dvp = a.dv.p + s * a.dv.sb + r * a.dv.sn + g * a.dv.sh;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          k4[c] = (__bf16)(dka[b][rr * 4 + c] * a.scale);
+          v4[c] = (__bf16)dva[b][rr * 4 + c];
+        }
+        *reinterpret_cast<bf16x4*>(dkp + b * 32 + rr * 8 + half * 4) = k4;
+        *reinterpret_cast<bf16x4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup = (segment, q-head, block of 32*(4/DS) queries). Per
 // BN-key tile, K and V are staged row-major in LDS; S^T = K Q^T and
 // dP^T = V dO^T read them row-wise, dQ^T += K^T dS^T column-wise.
@@ -302,7 +487,10 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
   constexpr int VR = DV / DS;
   static_assert(DR % 32 == 0 && VR % 32 == 0 && BN % 32 == 0, "head-dim split");
   constexpr int NKS = DR / 16, NVS = VR / 16, NDB = DR / 32, NKB = BN / 32;
-  constexpr int KS = DQK + 16, VS = DV + 16;
+  // K is read both row-wise and through the transposing read: a stride of
+  // 32 bytes mod 256 is the compromise (2-way on the row reads, none on the
+  // transposing reads); V is only read row-wise (16 bytes mod 256).
+  constexpr int KS = DQK + 16, VS = DV + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * NKB * 16 * 64 : 1];
@@ -310,10 +498,12 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int qg = w / DS, ds = w % DS;
-  const int s = blockIdx.z, h = blockIdx.y, g = h / a.G;
+  const int item = blockIdx.x / a.Hq, h = blockIdx.x - item * a.Hq, g = h / a.G;
+  if (item >= *a.count_q) return;
+  const int2 st = a.items_q[item];
+  const int s = st.x;
   const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
-  const int tile = gridDim.x - 1 - blockIdx.x;
-  const int m0 = tile * (32 * QG);
+  const int m0 = st.y * (32 * QG);
   if (m0 >= sg.lq) return;
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
   const int wq0 = m0 + qg * 32;
@@ -405,6 +595,7 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
         for (int kb = 0; kb < NKB; ++kb)
           pacc[kb] = mfma32(lds_frag(&sv[buf][(kb * 32 + col) * VS + ds * VR + half * 8 + i * 16]),
                             df[i], pacc[kb]);
+      pipeline_mfma_reads<(NKS + NVS) * NKB, 4>();
     }
     if constexpr (DS > 1) {
       float* mine = &sx[((qg * DS + ds) * 2 * NKB) * 16 * 64];
@@ -461,6 +652,7 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
           dqa[b] = mfma32(tr_frag(sk[buf], KS, kk * 16, ds * DR + b * 32, lane), sf[kk], dqa[b]);
+      pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
     }
     if (NBUF == 1 && t + 1 < ntiles) {
       __syncthreads();

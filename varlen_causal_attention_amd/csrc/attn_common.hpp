@@ -13,6 +13,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace vca {
@@ -57,6 +58,26 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
 // Element e (0..7) of eight packed bf16 values.
 __device__ __forceinline__ uint32_t bf16_at(u32x4 v, int e) {
   return (v[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+}
+
+// Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Ask the scheduler to run N MFMAs, each fed by one LDS read, with LEAD reads
+// issued ahead of the first MFMA: reads, then (MFMA, read) pairs, then the
+// last MFMAs. Keeps LEAD fragment reads in flight so the LDS latency hides
+// behind the MFMA pipe instead of stalling every MFMA.
+template <int N, int LEAD, int READS_PER_MFMA = 1>
+__device__ __forceinline__ void pipeline_mfma_reads() {
+  static_assert(LEAD <= N, "lead");
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD * READS_PER_MFMA, 0);
+#pragma unroll
+  for (int i = 0; i < N - LEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS_PER_MFMA, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, LEAD, 0);
 }
 
 // Partner lane across the two wave halves (l ^ 32).

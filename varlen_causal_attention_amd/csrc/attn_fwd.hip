@@ -24,17 +24,38 @@ hipError_t fwd_dims(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
 }
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int dqk, int dv, bool causal, int nseg, int Hq,
-                      int max_q, hipStream_t st) {
-  const int tiles = (max_q + kFwdBM - 1) / kFwdBM;
-  if (tiles == 0 || nseg == 0 || Hq == 0) return hipSuccess;
-  const dim3 grid(tiles, Hq, nseg);
+hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int64_t q_rows,
+                      void* ws, hipStream_t st) {
+  if (nseg == 0 || Hq == 0 || q_rows == 0) return hipSuccess;
+  if (!head_dims_supported(dqk, dv)) return hipErrorInvalidValue;
+  char* w = static_cast<char*>(ws);
+  SchedArgs sa{};
+  sa.cu_q = a.cu_q;
+  sa.cu_k = a.cu_k;
+  sa.nseg = nseg;
+  sa.Nq = a.Nq;
+  sa.Nk = a.Nk;
+  sa.Tq = a.Tq;
+  sa.Tk = a.Tk;
+  sa.by_keys = 0;
+  sa.tile = kFwdBM;
+  sa.step = 64;
+  sa.causal = causal;
+  sa.count = reinterpret_cast<int*>(w);
+  sa.list = reinterpret_cast<int2*>(w + 256);
+  sa.max_items = (int)list_capacity(q_rows, nseg);
+  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  a.items = sa.list;
+  a.item_count = sa.count;
+  a.H = Hq;
+  // at most ceil(q_rows / 128) + nseg query tiles exist
+  const int64_t items = (q_rows + kFwdBM - 1) / kFwdBM + nseg;
+  const dim3 grid((unsigned)(items * Hq));
   if (dqk == 64 && dv == 64) return fwd_dims<64, 64, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 128 && dv == 128) return fwd_dims<128, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 256 && dv == 256) return fwd_dims<256, 256, 64, 1, 2, 1, true>(a, causal, grid, st);
-  if (dqk == 512 && dv == 512) return fwd_dims<512, 512, 32, 2, 1, 1, false>(a, causal, grid, st);
-  return hipErrorInvalidValue;
+  return fwd_dims<512, 512, 32, 2, 1, 1, false>(a, causal, grid, st);
 }
 
 }  // namespace vca

@@ -33,7 +33,10 @@ struct FwdArgs {
   const int32_t* cu_k;
   int Nq, Nk, Tq, Tk;
   int G;            // Hq / Hkv
+  int H;            // q-heads: blockIdx.x = item * H + head
   float scale_log2; // scale * log2(e)
+  const int2* items;      // (segment, q tile) heavy first
+  const int* item_count;
 };
 
 constexpr int kFwdWaves = 4;
@@ -54,8 +57,13 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 256 * DS;      // threads
   constexpr int DR = DQK / DS, VR = DV / DS;
-  constexpr int KS = DQK + 16;      // K row stride in LDS (elements), padded
-  constexpr int VS = DV + 16;       // V row stride
+  // LDS row strides (elements). K is only read row-wise (b128 per lane, 16
+  // lanes per LDS cycle): a stride of 16 bytes mod 256 puts 16 consecutive
+  // rows on distinct banks. V is only read through the transposing read (4
+  // rows x 32 bytes per 16-lane group): 64 bytes mod 256 keeps the two
+  // groups served together on distinct banks.
+  constexpr int KS = DQK + 8;
+  constexpr int VS = DV + 32;
   constexpr int NKB = BN / 32;
   constexpr int NDB = VR / 32;
   constexpr int NKS = DR / 16;
@@ -67,9 +75,11 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   const int lane = tid & 63, w = tid >> 6;
   const int qg = w / DS, ds = w % DS;
   const int col = lane & 31, half = lane >> 5;
-  const int s = blockIdx.z, h = blockIdx.y, kvh = h / a.G;
+  const int item = blockIdx.x / a.H, h = blockIdx.x - item * a.H, kvh = h / a.G;
+  if (item >= *a.item_count) return;
+  const int2 st = a.items[item];
+  const int s = st.x, tile = st.y;
   const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
-  const int tile = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
   const int m0 = tile * kFwdBM;
   if (m0 >= sg.lq) return;
   const int lq = sg.lq, lk = sg.lk;
@@ -147,6 +157,7 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
         for (int kbk = 0; kbk < NKB; ++kbk)
           sacc[kbk] = mfma32(lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 + ks * 16]),
                              qf[ks], sacc[kbk]);
+      pipeline_mfma_reads<NKS * NKB, 4>();
     }
     if constexpr (DS > 1) {
       float* mine = &sx[(w * NKB) * 16 * 64];
@@ -220,6 +231,7 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           o[db] = mfma32(tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane), pf[kk], o[db]);
+      pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
     }
     if (NBUF == 1 && t + 1 < ntiles) {
       __syncthreads();  // everyone is done reading the single buffer

@@ -5,6 +5,7 @@
 
 #include "attn_bwd.hpp"
 #include "attn_fwd.hpp"
+#include "attn_sched.hpp"
 
 namespace vca {
 
@@ -28,13 +29,31 @@ struct MergeArgs {
 // Head-dim pairs compiled into the library.
 bool head_dims_supported(int dqk, int dv);
 
-// Grid: (q tiles of the longest segment, Hq, segments-or-batches).
-hipError_t launch_fwd(const FwdArgs& a, int dqk, int dv, bool causal, int nseg, int Hq,
-                      int max_q, hipStream_t stream);
+// Work lists: every pass orders its (segment, tile) items heaviest first.
+// The list capacity is bounded with 32-row tiles, the smallest any pass uses.
+constexpr int kListRows = 32;
+inline size_t list_capacity(int64_t rows, int nseg) { return (size_t)((rows + kListRows - 1) / kListRows) + nseg; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// forward workspace: [count][list]
+inline size_t fwd_workspace_bytes(int64_t q_rows, int nseg) {
+  return 256 + align256(sizeof(int2) * list_capacity(q_rows, nseg));
+}
+// backward workspace: [delta fp32, one per (q-head, query row)][counts][query list][key list]
+inline size_t bwd_workspace_bytes(int64_t delta_elems, int64_t q_rows, int64_t k_rows, int nseg) {
+  return align256(sizeof(float) * delta_elems) + 256 +
+         align256(sizeof(int2) * list_capacity(q_rows, nseg)) +
+         align256(sizeof(int2) * list_capacity(k_rows, nseg));
+}
+
+// Scheduler launch + forward kernel. ws: the forward workspace. q_rows: Tq
+// (varlen) or B * Nq (dense), used for the list capacity.
+hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int64_t q_rows,
+                      void* ws, hipStream_t stream);
 
 // delta pre-pass, dK/dV pass, dQ pass, in that order on one stream.
-hipError_t launch_bwd(const BwdArgs& a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
-                      int max_q, int max_k, hipStream_t stream);
+// ws: the backward workspace (delta first).
+hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
+                      int max_q, int64_t q_rows, int64_t k_rows, void* ws, hipStream_t stream);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

@@ -1,0 +1,104 @@
+// Work decomposition: turns the segment table into a list of (segment, tile)
+// work items ordered heaviest first, so the long causal tiles of every
+// segment start early and the short ones fill the tail.
+//
+// Causal tiles differ widely in cost: the last query tile of a long document
+// walks all of its keys, the first one a single key tile (and the other way
+// round for key blocks in the dK/dV pass). Dispatching in grid order leaves
+// the heavy tiles of late segments for the end; longest-processing-time-first
+// ordering bounds the makespan by the average load plus one tile.
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace vca {
+
+constexpr int kSchedBuckets = 2048;  // cost classes (costs clamp into the last one)
+
+struct SchedArgs {
+  const int32_t* cu_q;  // NULL: dense, every segment has Nq queries and Nk keys
+  const int32_t* cu_k;
+  int nseg, Nq, Nk, Tq, Tk;
+  int by_keys;   // 0: tiles of `tile` query rows; 1: blocks of `tile` keys
+  int tile;      // rows per work item
+  int step;      // rows per inner step: keys per tile (by_keys = 0) or queries (1)
+  int causal;
+  int2* list;    // out: (segment, tile) in heavy-first order
+  int* count;    // out: number of items
+  int max_items; // capacity of list (a malformed table may ask for more)
+};
+
+__device__ __forceinline__ int sched_cost(const SchedArgs& a, const SegGeom& g, int t) {
+  const int shift = g.lk - g.lq;
+  if (!a.by_keys) {
+    int kv_end = g.lk;
+    if (a.causal) kv_end = min(g.lk, (t + 1) * a.tile + shift);
+    return kv_end > 0 ? (kv_end + a.step - 1) / a.step : 0;
+  }
+  int q_begin = 0;
+  if (a.causal) q_begin = max(0, t * a.tile - shift);
+  return g.lq > q_begin ? (g.lq - q_begin + a.step - 1) / a.step : 0;
+}
+
+// One workgroup of 16 waves: histogram of item costs, descending exclusive
+// scan, scatter. Wave w takes segments w, w+16, ...; its lanes split the
+// segment's tiles. Items of equal cost land in an arbitrary order; every item
+// writes only its own outputs, so the order never changes a result.
+static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedArgs a) {
+  constexpr int NT = 1024, PER = kSchedBuckets / NT;  // buckets per thread
+  __shared__ int hist[kSchedBuckets];
+  __shared__ int wave_sum[NT / 64];
+  __shared__ int total;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kSchedBuckets; i += NT) hist[i] = 0;
+  if (tid == 0) total = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int s = w; s < a.nseg; s += NT / 64) {
+    const SegGeom g = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+    const int len = a.by_keys ? g.lk : g.lq;
+    const int nt = (len + a.tile - 1) / a.tile;
+    for (int t = lane; t < nt; t += 64) {
+      atomicAdd(&hist[min(sched_cost(a, g, t), kSchedBuckets - 1)], 1);
+      ++mine;
+    }
+  }
+  atomicAdd(&total, mine);
+  __syncthreads();
+  // descending exclusive scan: bucket c starts after all buckets > c.
+  // Thread i owns buckets kSchedBuckets-1-(i*PER .. i*PER+PER-1).
+  int vals[PER], run = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    vals[j] = hist[kSchedBuckets - 1 - (tid * PER + j)];
+    run += vals[j];
+  }
+  int incl = run;  // inclusive scan of per-thread sums within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int n = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += n;
+  }
+  if (lane == 63) wave_sum[w] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int i = 0; i < w; ++i) base += wave_sum[i];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    hist[kSchedBuckets - 1 - (tid * PER + j)] = base;
+    base += vals[j];
+  }
+  if (tid == 0) *a.count = min(total, a.max_items);
+  __syncthreads();
+  for (int s = w; s < a.nseg; s += NT / 64) {
+    const SegGeom g = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+    const int len = a.by_keys ? g.lk : g.lq;
+    const int nt = (len + a.tile - 1) / a.tile;
+    for (int t = lane; t < nt; t += 64) {
+      const int pos = atomicAdd(&hist[min(sched_cost(a, g, t), kSchedBuckets - 1)], 1);
+      if (pos < a.max_items) a.list[pos] = make_int2(s, t);
+    }
+  }
+}
+
+}  // namespace vca

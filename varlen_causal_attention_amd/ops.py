@@ -70,10 +70,14 @@ def fwd_dense(q, k, v, scale: float, causal: bool):
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     strides = i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
                         + list(out.stride()[:3]))
-    st = load().attn_fwd_dense(ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq,
-                               Hkv, Nq, Nk, Dqk, Dv, strides, float(scale), int(bool(causal)),
-                               None, None, _stream(q))
-    check(st, "attn_fwd_dense")
+    lib = load()
+    args = (ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, Dqk, Dv,
+            strides, float(scale), int(bool(causal)))
+    need = C.c_size_t(0)
+    check(lib.attn_fwd_dense(*args, None, C.byref(need), _stream(q)), "attn_fwd_dense")
+    ws = _workspace(need.value, dev)
+    have = C.c_size_t(ws.numel())
+    check(lib.attn_fwd_dense(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_fwd_dense")
     return out, lse
 
 
@@ -139,11 +143,15 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
     strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
                         + list(out.stride()[:2]))
-    st = load().attn_fwd_varlen(ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                _cu(cu_q, dev), _cu(cu_k, dev), cu_q.numel() - 1, int(max_q),
-                                int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale),
-                                int(bool(causal)), None, None, _stream(q))
-    check(st, "attn_fwd_varlen")
+    lib = load()
+    args = (ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev),
+            _cu(cu_k, dev), cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv,
+            strides, float(scale), int(bool(causal)))
+    need = C.c_size_t(0)
+    check(lib.attn_fwd_varlen(*args, None, C.byref(need), _stream(q)), "attn_fwd_varlen")
+    ws = _workspace(need.value, dev)
+    have = C.c_size_t(ws.numel())
+    check(lib.attn_fwd_varlen(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_fwd_varlen")
     return out, lse
 
 

@@ -115,12 +115,71 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     fwd_ms = time_stage(p.fwd, steps)
     bwd_ms = time_stage(p.bwd, steps)
     torch.cuda.synchronize()
+    kernels = kernel_times(p, steps)
     ff, bf = w.fwd_flops(), w.bwd_flops()
     return dict(workload=w.name, ms_per_step=step_ms_ev, wall_ms_per_step=wall,
                 tflops_step=(ff + bf) / (step_ms_ev * 1e-3) / 1e12,
                 fwd_ms=fwd_ms, bwd_ms=bwd_ms,
                 fwd_tflops=ff / (fwd_ms * 1e-3) / 1e12, bwd_tflops=bf / (bwd_ms * 1e-3) / 1e12,
-                fwd_flops=ff, bwd_flops=bf, pairs=w.pairs())
+                fwd_flops=ff, bwd_flops=bf, pairs=w.pairs(), kernels=kernels)
+
+
+def kernel_times(p: "Problem", steps: int) -> dict:
+    """Per-kernel mean launch duration (ms) and launches per step, from HIP
+    events the library records around each of its launches on their stream."""
+    vca = p.vca
+    vca.timing_read()  # drop anything recorded earlier
+    vca.timing_enable(True)
+    try:
+        for _ in range(steps):
+            p.step()
+        recs = vca.timing_read(1 << 16)
+    finally:
+        vca.timing_enable(False)
+    agg: dict = {}
+    for name, ms in recs:
+        t, n = agg.get(name, (0.0, 0))
+        agg[name] = (t + ms, n + 1)
+    return {k: {"mean_ms": t / n, "per_step": n / steps} for k, (t, n) in agg.items()}
+
+
+def kernel_work(w: "workloads.Workload", name: str):
+    """(bound, algorithmic units per launch, unit) of one library kernel.
+    Forward: 2*pairs*(Dqk+Dv) FLOPs. dK/dV pass: S, dP, dV, dK products,
+    2*pairs*(2*Dqk+2*Dv). dQ pass: the dQ product only, 2*pairs*Dqk (its S/dP
+    recomputation is not algorithmic work). delta pass: bytes of O and dO read
+    plus delta written. Merge: bytes of both inputs read and the output written."""
+    pairs = w.pairs()
+    rows = w.T if w.kind == "varlen" else (w.shard if w.kind == "ring" else w.B * w.Nq)
+    chunks = 2 if w.kind == "ring" else 1
+    if name == "attn_fwd":
+        return "mfma", 2 * pairs * (w.Dqk + w.Dv) / chunks, "FLOP"
+    if name == "attn_bwd_dkdv":
+        return "mfma", 2 * pairs * (2 * w.Dqk + 2 * w.Dv) / chunks, "FLOP"
+    if name == "attn_bwd_dq":
+        return "mfma", 2 * pairs * w.Dqk / chunks, "FLOP"
+    if name == "attn_bwd_delta":
+        return "hbm", rows * w.Hq * (2 * w.Dv * 2 + 4), "B"
+    if name == "attn_merge":
+        return "hbm", rows * w.Hq * (w.Dv * (2 + 2 + 4 + 2) + 4 * 3), "B"
+    return None
+
+
+def roofline(w: "workloads.Workload", kernels: dict) -> dict:
+    """Roofline entry of the kernel that takes the most time per step."""
+    name = max(kernels, key=lambda k: kernels[k]["mean_ms"] * kernels[k]["per_step"])
+    bound, units, unit = kernel_work(w, name)
+    sec = kernels[name]["mean_ms"] * 1e-3
+    if bound == "mfma":
+        achieved = units / sec / 1e12
+        peak, u = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = units / sec / 1e9
+        peak, u = PEAK_HBM_GBS, "GB/s"
+    return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": round(peak, 1),
+            "unit": u, "frac": round(achieved / peak, 4), "traffic": None,
+            "launch_ms": round(kernels[name]["mean_ms"], 4),
+            "per_unit": "2*pairs*(2*Dqk+2*Dv) FLOP" if name == "attn_bwd_dkdv" else unit}
 
 
 def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
@@ -203,9 +262,8 @@ def main():
                 "pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(m["bwd_ms"], 4), "tflops": round(m["bwd_tflops"], 2),
                 "pct_of_peak": round(100 * m["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel", "achieved": round(fwd_tf, 2),
-                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "roofline": roofline(w, m["kernels"]),
+        "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in m["kernels"].items()},
         "wall_ms_per_step": round(m["wall_ms_per_step"], 4),
     }
     if args.all:
@@ -213,7 +271,9 @@ def main():
         for n in range(1, 6):
             r = measure(n, max(3, args.steps // 2), 2)
             per[r["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
-                                  for k, v in r.items() if k != "workload"}
+                                  for k, v in r.items() if k not in ("workload", "kernels")}
+            per[r["workload"]]["kernels_ms"] = {k: round(v["mean_ms"], 4)
+                                                for k, v in r["kernels"].items()}
         line["workloads"] = per
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.workload)

@@ -178,6 +178,20 @@ int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_l
                       int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
                       int max_segments, int* num_segments);
 
+/* Opt-in kernel timing, for profiling on the caller's own streams. While
+ * enabled (per calling thread), every kernel this library launches from that
+ * thread is bracketed by two HIP events recorded on its stream. Returns the
+ * previous setting. Disabled by default; adds two event records per launch. */
+int attn_timing_enable(int enable);
+
+/* Waits for and reads the recorded launches (in launch order) of the calling
+ * thread, then clears the record. Up to max_records entries: names receives
+ * NUL-terminated kernel labels in slots of name_len bytes ("attn_fwd",
+ * "attn_schedule", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq",
+ * "attn_merge"), ms the elapsed milliseconds; *count receives the total number
+ * recorded. Returns ATTN_E_HIP if an event could not be read. */
+int attn_timing_read(int max_records, char* names, int name_len, float* ms, int* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,3 +193,13 @@ def test_segment_builder_rejects_bad_ranges():
         doc_segments(ids, 2, 4, 0, 5, 1)   # keys overlap the queries
     with pytest.raises(ValueError):
         doc_segments(ids, 8, 4, 0, 10, 0)  # queries past the row
+
+
+def test_timing_toggle_and_empty_read(lib):
+    assert lib.attn_timing_enable(1) == 0
+    assert lib.attn_timing_enable(0) == 1
+    n = C.c_int(-1)
+    names = C.create_string_buffer(64)
+    ms = (C.c_float * 2)()
+    assert lib.attn_timing_read(2, names, 32, ms, C.byref(n)) == 0 and n.value == 0
+    assert lib.attn_timing_read(2, names, 1, ms, C.byref(n)) == _lib.ATTN_E_INVALID

@@ -7,9 +7,10 @@ this package only marshals torch tensors into its C ABI.
 """
 from ._lib import EXPORTED, LIB_PATH, AttnError, load
 from .ops import (bwd_dense, bwd_varlen, doc_layout, doc_segments, fwd_dense, fwd_varlen,
-                  is_supported, merge, version)
+                  is_supported, merge, timing_enable, timing_read, version)
 
 __all__ = [
     "AttnError", "EXPORTED", "LIB_PATH", "load", "fwd_dense", "fwd_varlen", "bwd_dense",
     "bwd_varlen", "merge", "doc_segments", "doc_layout", "is_supported", "version",
+    "timing_enable", "timing_read",
 ]

@@ -2,6 +2,7 @@
 // compiled head-dim pair. DS = number of waves that split one 32-row block by
 // head-dim range (1 for Dqk <= 128, 2 up to 256, 4 for 512).
 #include "attn_launch.hpp"
+#include "attn_timing.hpp"
 
 namespace vca {
 namespace {
@@ -37,7 +38,10 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   sa.list = list_q;
   sa.count = counts;
   sa.max_items = (int)cap_q;
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  {
+    TimedLaunch timer("attn_schedule", st);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  }
   // key blocks of the dK/dV pass, cost = query steps walked
   sa.by_keys = 1;
   sa.tile = key_block;
@@ -45,7 +49,10 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   sa.list = list_k;
   sa.count = counts + 1;
   sa.max_items = (int)cap_k;
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  {
+    TimedLaunch timer("attn_schedule", st);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  }
   a.items_q = list_q;
   a.count_q = counts;
   a.items_k = list_k;
@@ -56,10 +63,12 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   constexpr int LPR = DV / 8 >= 64 ? 64 : DV / 8;
   constexpr int rows_per_block = 4 * (64 / LPR);
   if (max_q > 0) {
+    TimedLaunch timer("attn_bwd_delta", st);
     const dim3 g((max_q + rows_per_block - 1) / rows_per_block, Hq, nseg);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<DV>), g, dim3(256), 0, st, a);
   }
   if (k_rows > 0) {
+    TimedLaunch timer("attn_bwd_dkdv", st);
     const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
     if constexpr (kPipe) {
       if (causal)
@@ -75,6 +84,7 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
     }
   }
   if (q_rows > 0) {
+    TimedLaunch timer("attn_bwd_dq", st);
     const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
     if (causal)
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, true>), g, dim3(256), 0,

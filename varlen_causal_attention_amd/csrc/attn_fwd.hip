@@ -1,6 +1,7 @@
 // Forward launcher: instantiates the forward kernel for every compiled
 // head-dim pair and both mask modes.
 #include "attn_launch.hpp"
+#include "attn_timing.hpp"
 
 namespace vca {
 
@@ -14,6 +15,7 @@ namespace {
 // buffers for the K/V tiles, WPE = waves per SIMD the register budget targets.
 template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF>
 hipError_t fwd_dims(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
+  TimedLaunch timer("attn_fwd", st);
   if (causal)
     hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true>), grid, dim3(256 * DS),
                        0, st, a);
@@ -44,7 +46,10 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   sa.count = reinterpret_cast<int*>(w);
   sa.list = reinterpret_cast<int2*>(w + 256);
   sa.max_items = (int)list_capacity(q_rows, nseg);
-  hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  {
+    TimedLaunch timer("attn_schedule", st);
+    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+  }
   a.items = sa.list;
   a.item_count = sa.count;
   a.H = Hq;

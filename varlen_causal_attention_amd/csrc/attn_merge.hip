@@ -1,5 +1,6 @@
 // Merge launcher and kernel.
 #include "attn_launch.hpp"
+#include "attn_timing.hpp"
 
 namespace vca {
 
@@ -41,6 +42,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int64_t pairs = (int64_t)a.rows * a.H;
   if (pairs == 0) return hipSuccess;
   const dim3 grid((unsigned)((pairs + 3) / 4));
+  TimedLaunch timer("attn_merge", st);
   hipLaunchKernelGGL(attn_merge_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -258,3 +258,27 @@ def doc_layout(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode
     cu_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
     return (torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_k).to(device),
             int(max(sq, default=0)), int(max(sk, default=0)))
+
+
+# ---------------------------------------------------------------------------
+# kernel timing (profiling aid)
+# ---------------------------------------------------------------------------
+def timing_enable(enable: bool = True) -> bool:
+    """Record HIP events around every library kernel launched from this thread."""
+    return bool(load().attn_timing_enable(int(bool(enable))))
+
+
+def timing_read(max_records: int = 4096):
+    """[(kernel label, ms)] of the launches recorded since the last read."""
+    lib = load()
+    name_len = 32
+    names = C.create_string_buffer(max_records * name_len)
+    ms = (C.c_float * max_records)()
+    n = C.c_int(0)
+    check(lib.attn_timing_read(max_records, names, name_len, ms, C.byref(n)), "attn_timing_read")
+    raw = names.raw
+    out = []
+    for i in range(min(n.value, max_records)):
+        label = raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out.append((label, float(ms[i])))
+    return out

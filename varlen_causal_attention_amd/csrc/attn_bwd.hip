@@ -10,12 +10,12 @@ namespace {
 // DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
-template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE>
+template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE, int NWK, int NWQ>
 hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
                     int64_t k_rows, void* ws, hipStream_t st) {
   constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
-  constexpr int key_block = kPipe ? 128 : 32 * (4 / DS);
-  constexpr int q_tile = 32 * (4 / DS);
+  constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
+  constexpr int q_tile = 32 * (NWQ / DS);
   char* w = static_cast<char*>(ws);
   const size_t delta_bytes = align256(sizeof(float) * (size_t)Hq * q_rows);
   int* counts = reinterpret_cast<int*>(w + delta_bytes);
@@ -77,21 +77,22 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
         hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, false>), g, dim3(256), 0, st, a);
     } else {
       if (causal)
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, true>), g, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true>), g, dim3(64 * NWK), 0,
+                           st, a);
       else
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, false>), g, dim3(256), 0, st,
-                           a);
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false>), g, dim3(64 * NWK),
+                           0, st, a);
     }
   }
   if (q_rows > 0) {
     TimedLaunch timer("attn_bwd_dq", st);
     const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
     if (causal)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, true>), g, dim3(256), 0,
-                         st, a);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true>), g,
+                         dim3(64 * NWQ), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, false>), g, dim3(256), 0,
-                         st, a);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false>), g,
+                         dim3(64 * NWQ), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -101,14 +102,16 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
 hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                       int64_t q_rows, int64_t k_rows, void* ws, hipStream_t st) {
   if (nseg == 0 || Hq == 0) return hipSuccess;
-#define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE)                                      \
-  bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE>(a, causal, nseg, Hq, Hkv, max_q, q_rows, \
-                                                 k_rows, ws, st)
-  if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2);
-  if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2);
-  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 2, 2, true, 32, 2, true, 1);
-  if (dqk == 256 && dv == 256) return VCA_BWD(256, 256, 2, 2, true, 32, 2, true, 1);
-  if (dqk == 512 && dv == 512) return VCA_BWD(512, 512, 4, 1, false, 32, 1, false, 1);
+// arguments: DQK, DV, DS, dK/dV buffers + prefetch, dQ key tile, dQ buffers + prefetch, dQ waves
+// per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
+#define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \
+  bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ>(a, causal, nseg, Hq, Hkv, max_q, \
+                                                           q_rows, k_rows, ws, st)
+  if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
+  if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
+  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 2, 2, true, 32, 2, true, 2, 8, 8);
+  if (dqk == 256 && dv == 256) return VCA_BWD(256, 256, 2, 2, true, 32, 2, true, 2, 4, 8);
+  if (dqk == 512 && dv == 512) return VCA_BWD(512, 512, 4, 1, false, 32, 1, false, 1, 4, 4);
 #undef VCA_BWD
   return hipErrorInvalidValue;
 }

@@ -84,10 +84,11 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
 // operand of S = Q K^T and dP = dO V^T, and column-wise (transposing LDS read)
 // as the A operand of dK^T += Q^T dS and dV^T += dO^T P.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int NBUF, bool PF, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) {
+template <int DQK, int DV, int DS, int NBUF, bool PF, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const BwdArgs a) {
   static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
-  constexpr int KG = 4 / DS;           // 32-key groups per workgroup
+  constexpr int NT = 64 * NW;          // threads
+  constexpr int KG = NW / DS;          // 32-key groups per workgroup
   constexpr int DR = DQK / DS;         // this wave's share of Dqk
   constexpr int VR = DV / DS;          // this wave's share of Dv
   static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
@@ -144,8 +145,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const BwdArgs a) 
   const int nq = lq > q_begin ? (lq - q_begin + BQ - 1) / BQ : 0;
   const int total = a.G * nq;
 
-  using QStage = TileStage<BQ, DQK, 256>;
-  using OStage = TileStage<BQ, DV, 256>;
+  using QStage = TileStage<BQ, DQK, NT>;
+  using OStage = TileStage<BQ, DV, NT>;
   QStage qst;
   OStage ost;
   float lse_r = 0.f, del_r = 0.f;  // threads < BQ carry one row's lse / delta
@@ -479,10 +480,11 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
 // BN-key tile, K and V are staged row-major in LDS; S^T = K Q^T and
 // dP^T = V dO^T read them row-wise, dQ^T += K^T dS^T column-wise.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, bool CAUSAL>
-__global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) {
+template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs a) {
   static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
-  constexpr int QG = 4 / DS;
+  constexpr int NT = 64 * NW;
+  constexpr int QG = NW / DS;
   constexpr int DR = DQK / DS;
   constexpr int VR = DV / DS;
   static_assert(DR % 32 == 0 && VR % 32 == 0 && BN % 32 == 0, "head-dim split");
@@ -537,8 +539,8 @@ __global__ void __launch_bounds__(256, WPE) attn_bwd_dq_kernel(const BwdArgs a) 
   }
   wait_global_loads();
 
-  using KStage = TileStage<BN, DQK, 256>;
-  using VStage = TileStage<BN, DV, 256>;
+  using KStage = TileStage<BN, DQK, NT>;
+  using VStage = TileStage<BN, DV, NT>;
   KStage kst;
   VStage vst;
   if (ntiles > 0) {

@@ -215,8 +215,9 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   for (int i = 0; i < 8; ++i)
     if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 3 * i, 3))) return st;
   if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  const vca::TileGeom tg = vca::tile_geom_dense(B, Nq, Nk);
   const size_t need_ws =
-      vca::bwd_workspace_bytes((int64_t)B * Hq * Nq, (int64_t)B * Nq, (int64_t)B * Nk, B);
+      vca::bwd_workspace(Dqk, Dv, Hq, (int64_t)B * Nq, (int64_t)B * Nk, B, tg).total;
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (!has_q && !has_k)) return ok();
@@ -244,7 +245,7 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   a.scale_log2 = scale * vca::kLog2e;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
   return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
-                                    (int64_t)B * Nk, workspace, stream),
+                                    (int64_t)B * Nk, tg, workspace, stream),
                     "attn_bwd_dense launch");
 }
 
@@ -272,7 +273,8 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   for (int i = 0; i < 8; ++i)
     if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 2 * i, 2))) return st;
   if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
-  const size_t need_ws = vca::bwd_workspace_bytes((int64_t)Hq * Tq, Tq, Tk, num_segments);
+  const vca::TileGeom tg = vca::tile_geom_varlen(Tq, num_segments, max_k);
+  const size_t need_ws = vca::bwd_workspace(Dqk, Dv, Hq, Tq, Tk, num_segments, tg).total;
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (Tq == 0 && Tk == 0)) return ok();
@@ -302,7 +304,7 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   a.scale_log2 = scale * vca::kLog2e;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
   return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq, Tk,
-                                    workspace, stream),
+                                    tg, workspace, stream),
                     "attn_bwd_varlen launch");
 }
 

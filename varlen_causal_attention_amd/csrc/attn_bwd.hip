@@ -1,6 +1,7 @@
-// Backward launcher: delta pre-pass, then the dK/dV and dQ passes, for every
-// compiled head-dim pair. DS = number of waves that split one 32-row block by
-// head-dim range (1 for Dqk <= 128, 2 up to 256, 4 for 512).
+// Backward launcher: delta pre-pass, then for every compiled head-dim pair
+// either the fused dK/dV and dQ passes (DS = number of waves that split one
+// 32-row block by head-dim range) or the two-phase scores + products passes.
+#include "attn_bwd_tiles.hpp"
 #include "attn_launch.hpp"
 #include "attn_timing.hpp"
 
@@ -10,18 +11,17 @@ namespace {
 // DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
-template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE, int NWK, int NWQ>
-hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
-                    int64_t k_rows, void* ws, hipStream_t st) {
-  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
-  constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
-  constexpr int q_tile = 32 * (NWQ / DS);
+// Work lists (query tiles of q_tile rows with key steps of q_step, key blocks
+// of k_tile keys with query steps of k_step) and the delta pre-pass.
+template <int DV>
+void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
+                  int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step, int k_tile,
+                  int k_step, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  const size_t delta_bytes = align256(sizeof(float) * (size_t)Hq * q_rows);
+  const size_t delta_bytes = wl.list_q - 256;
   int* counts = reinterpret_cast<int*>(w + delta_bytes);
-  int2* list_q = reinterpret_cast<int2*>(w + delta_bytes + 256);
-  const size_t cap_q = list_capacity(q_rows, nseg), cap_k = list_capacity(k_rows, nseg);
-  int2* list_k = reinterpret_cast<int2*>(w + delta_bytes + 256 + align256(sizeof(int2) * cap_q));
+  int2* list_q = reinterpret_cast<int2*>(w + wl.list_q);
+  int2* list_k = reinterpret_cast<int2*>(w + wl.list_k);
   SchedArgs sa{};
   sa.cu_q = a.cu_q;
   sa.cu_k = a.cu_k;
@@ -31,24 +31,24 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   sa.Tq = a.Tq;
   sa.Tk = a.Tk;
   sa.causal = causal;
-  // query tiles of the dQ pass, cost = key tiles walked
+  // query tiles, cost = key steps walked
   sa.by_keys = 0;
   sa.tile = q_tile;
-  sa.step = BN;
+  sa.step = q_step;
   sa.list = list_q;
   sa.count = counts;
-  sa.max_items = (int)cap_q;
+  sa.max_items = (int)list_capacity(q_rows, nseg);
   {
     TimedLaunch timer("attn_schedule", st);
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
   }
-  // key blocks of the dK/dV pass, cost = query steps walked
+  // key blocks, cost = query steps walked
   sa.by_keys = 1;
-  sa.tile = key_block;
-  sa.step = 32;
+  sa.tile = k_tile;
+  sa.step = k_step;
   sa.list = list_k;
   sa.count = counts + 1;
-  sa.max_items = (int)cap_k;
+  sa.max_items = (int)list_capacity(k_rows, nseg);
   {
     TimedLaunch timer("attn_schedule", st);
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
@@ -67,6 +67,19 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
     const dim3 g((max_q + rows_per_block - 1) / rows_per_block, Hq, nseg);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<DV>), g, dim3(256), 0, st, a);
   }
+}
+
+// DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
+// and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
+// BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
+template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE, int NWK, int NWQ>
+hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
+                    int64_t k_rows, const BwdWorkspace& wl, void* ws, hipStream_t st) {
+  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
+  constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
+  constexpr int q_tile = 32 * (NWQ / DS);
+  bwd_prologue<DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, BN, key_block, 32,
+                   ws, st);
   if (k_rows > 0) {
     TimedLaunch timer("attn_bwd_dkdv", st);
     const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
@@ -97,21 +110,78 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   return hipGetLastError();
 }
 
+// Two-phase backward: scores (P, dS tiles), then dV, dK and dQ products.
+// WRV / WRK / WRQ: wave rows of the 8-wave grid of each product kernel.
+template <int DQK, int DV, int WRV, int WRK, int WRQ, bool CAUSAL>
+hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows, int64_t k_rows,
+                     const TileGeom& tg, const BwdWorkspace& wl, void* ws, hipStream_t st) {
+  bwd_prologue<DV>(a, CAUSAL, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, kTile, kTile, kTile, kTile,
+                   ws, st);
+  char* w = static_cast<char*>(ws);
+  a.tile_p = reinterpret_cast<uint16_t*>(w + wl.tile_p);
+  a.tile_ds = reinterpret_cast<uint16_t*>(w + wl.tile_ds);
+  a.tile_nkb = tg.nkb;
+  a.tile_nqb_dense = tg.nqb_dense;
+  const unsigned q_items = (unsigned)((q_rows + kTile - 1) / kTile + nseg);
+  const unsigned k_items = (unsigned)((k_rows + kTile - 1) / kTile + nseg);
+  if (q_rows > 0 && k_rows > 0) {
+    TimedLaunch timer("attn_bwd_scores", st);
+    hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>), dim3(q_items * Hq), dim3(512), 0,
+                       st, a);
+  }
+  if (k_rows > 0) {
+    {
+      TimedLaunch timer("attn_bwd_dv_tiles", st);
+      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, WRV, CAUSAL, false>), dim3(k_items * Hkv),
+                         dim3(512), 0, st, a);
+    }
+    {
+      TimedLaunch timer("attn_bwd_dk_tiles", st);
+      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DQK, WRK, CAUSAL, true>), dim3(k_items * Hkv),
+                         dim3(512), 0, st, a);
+    }
+  }
+  if (q_rows > 0) {
+    TimedLaunch timer("attn_bwd_dq_tiles", st);
+    hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<DQK, WRQ, CAUSAL>), dim3(q_items * Hq), dim3(512), 0,
+                       st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DQK, int DV, int WRV, int WRK, int WRQ>
+hipError_t bwd_tiles_any(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                         int64_t q_rows, int64_t k_rows, const TileGeom& tg,
+                         const BwdWorkspace& wl, void* ws, hipStream_t st) {
+  return causal ? bwd_tiles<DQK, DV, WRV, WRK, WRQ, true>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows,
+                                                          tg, wl, ws, st)
+                : bwd_tiles<DQK, DV, WRV, WRK, WRQ, false>(a, nseg, Hq, Hkv, max_q, q_rows,
+                                                           k_rows, tg, wl, ws, st);
+}
+
 }  // namespace
 
 hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
-                      int64_t q_rows, int64_t k_rows, void* ws, hipStream_t st) {
+                      int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws, hipStream_t st) {
   if (nseg == 0 || Hq == 0) return hipSuccess;
+  const BwdWorkspace wl = bwd_workspace(dqk, dv, Hq, q_rows, k_rows, nseg, tg);
+  if (bwd_uses_tiles(dqk, dv)) {
+    if (dqk == 256 && dv == 256)
+      return bwd_tiles_any<256, 256, 2, 2, 2>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg,
+                                              wl, ws, st);
+    if (dqk == 512 && dv == 512)
+      return bwd_tiles_any<512, 512, 2, 2, 2>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg,
+                                              wl, ws, st);
+    return hipErrorInvalidValue;
+  }
 // arguments: DQK, DV, DS, dK/dV buffers + prefetch, dQ key tile, dQ buffers + prefetch, dQ waves
 // per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
 #define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \
   bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ>(a, causal, nseg, Hq, Hkv, max_q, \
-                                                           q_rows, k_rows, ws, st)
+                                                           q_rows, k_rows, wl, ws, st)
   if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
   if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
   if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 2, 2, true, 32, 2, true, 2, 8, 8);
-  if (dqk == 256 && dv == 256) return VCA_BWD(256, 256, 2, 2, true, 32, 2, true, 2, 4, 8);
-  if (dqk == 512 && dv == 512) return VCA_BWD(512, 512, 4, 1, false, 32, 1, false, 1, 4, 4);
 #undef VCA_BWD
   return hipErrorInvalidValue;
 }

@@ -40,6 +40,11 @@ struct BwdArgs {
   const int* count_q;
   const int2* items_k;    // (segment, key block) for the dK/dV pass, heavy first
   const int* count_k;
+  // two-phase backward only: bf16 P and dS tiles (workspace) and their layout
+  uint16_t* tile_p;
+  uint16_t* tile_ds;
+  int tile_nkb;        // key tiles per row slot
+  int tile_nqb_dense;  // dense: query tiles per batch; 0 for varlen
 };
 
 // ---------------------------------------------------------------------------

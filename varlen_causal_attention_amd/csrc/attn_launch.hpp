@@ -38,11 +38,42 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t fwd_workspace_bytes(int64_t q_rows, int nseg) {
   return 256 + align256(sizeof(int2) * list_capacity(q_rows, nseg));
 }
-// backward workspace: [delta fp32, one per (q-head, query row)][counts][query list][key list]
-inline size_t bwd_workspace_bytes(int64_t delta_elems, int64_t q_rows, int64_t k_rows, int nseg) {
-  return align256(sizeof(float) * delta_elems) + 256 +
-         align256(sizeof(int2) * list_capacity(q_rows, nseg)) +
-         align256(sizeof(int2) * list_capacity(k_rows, nseg));
+// Backward workspace: [delta fp32, one per (q-head, query row)][counts]
+// [query list][key list], then for the two-phase backward the P and dS tile
+// stores (bf16, 128x128 per (row slot, key tile, q-head)).
+struct TileGeom {
+  int64_t slots;  // query-tile row slots
+  int nkb;        // key tiles per slot
+  int nqb_dense;  // dense: query tiles per batch (slot = b*nqb + qb); 0: varlen
+};
+inline TileGeom tile_geom_dense(int B, int Nq, int Nk) {
+  const int nqb = (Nq + 127) / 128;
+  return TileGeom{(int64_t)B * nqb, (Nk + 127) / 128, nqb};
+}
+inline TileGeom tile_geom_varlen(int Tq, int nseg, int max_k) {
+  return TileGeom{(int64_t)Tq / 128 + nseg + 1, (max_k + 127) / 128, 0};
+}
+// Head-dim pairs whose backward runs in two phases through stored tiles.
+inline bool bwd_uses_tiles(int dqk, int dv) { return dqk == dv && dqk >= 256; }
+struct BwdWorkspace {
+  size_t list_q, list_k, tile_p, tile_ds, total;
+};
+inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64_t k_rows, int nseg,
+                                  const TileGeom& tg) {
+  BwdWorkspace w{};
+  const size_t delta = align256(sizeof(float) * (size_t)Hq * (size_t)q_rows);
+  w.list_q = delta + 256;
+  w.list_k = w.list_q + align256(sizeof(int2) * list_capacity(q_rows, nseg));
+  w.tile_p = w.list_k + align256(sizeof(int2) * list_capacity(k_rows, nseg));
+  w.tile_ds = w.tile_p;
+  if (bwd_uses_tiles(dqk, dv)) {
+    const size_t tiles = sizeof(uint16_t) * 128 * 128 * (size_t)tg.slots * (size_t)tg.nkb * (size_t)Hq;
+    w.tile_ds = w.tile_p + tiles;
+    w.total = w.tile_ds + tiles;
+  } else {
+    w.total = w.tile_p;
+  }
+  return w;
 }
 
 // Scheduler launch + forward kernel. ws: the forward workspace. q_rows: Tq
@@ -50,10 +81,12 @@ inline size_t bwd_workspace_bytes(int64_t delta_elems, int64_t q_rows, int64_t k
 hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int64_t q_rows,
                       void* ws, hipStream_t stream);
 
-// delta pre-pass, dK/dV pass, dQ pass, in that order on one stream.
-// ws: the backward workspace (delta first).
+// delta pre-pass, then either the fused dK/dV and dQ passes or the two-phase
+// scores + products passes, in that order on one stream. ws: the backward
+// workspace laid out by bwd_workspace (delta first).
 hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
-                      int max_q, int64_t q_rows, int64_t k_rows, void* ws, hipStream_t stream);
+                      int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws,
+                      hipStream_t stream);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

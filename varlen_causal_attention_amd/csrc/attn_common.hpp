@@ -89,6 +89,53 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 // own prefetches are never waited on before they are needed.
 __device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wave are outstanding (they complete in issue order); other counters free.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// gfx950 direct global -> LDS load (global_load_lds_dwordx4): lane l's 16
+// bytes from g land at LDS byte address lds_base + 16*l; the data never
+// passes through VGPRs. Issued as inline assembly on purpose: the compiler
+// treats any outstanding LDS DMA as aliasing every later LDS read and every
+// barrier and drains vmcnt in front of them, which would serialize a
+// multi-stage pipeline. Callers therefore own the synchronization: a stage is
+// read only after wait_vmcnt<> (own loads) and a barrier (everyone's). M0 is
+// restored afterwards; the s_nops separate the M0 writes from the LDS DMA.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void* lds_ptr(const void* p) { return (lds_void*)p; }
+// The LDS destination also goes into the asm as a pointer operand: the
+// compiler then knows the asm writes that LDS object and keeps later reads of
+// it, instead of treating never-stored LDS as undefined.
+__device__ __forceinline__ void dma16(const uint16_t* g, lds_void* lds_base) {
+  uint32_t saved;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m0), "v"(lds_base)
+      : "memory");
+}
+// Global stores whose vmcnt footprint is exactly one operation each (used
+// where a wave counts its outstanding memory operations by hand). A store of
+// more than 8 bytes reads its data VGPRs after issue: a VALU write to them in
+// the next cycle would change what is stored. The compiler pads its own
+// stores; these carry their own wait states.
+__device__ __forceinline__ void stg16(uint16_t* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void stg8(uint16_t* p, u32x2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

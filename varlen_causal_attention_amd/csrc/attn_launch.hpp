@@ -39,22 +39,23 @@ inline size_t fwd_workspace_bytes(int64_t q_rows, int nseg) {
   return 256 + align256(sizeof(int2) * list_capacity(q_rows, nseg));
 }
 // Backward workspace: [delta fp32, one per (q-head, query row)][counts]
-// [query list][key list], then for the two-phase backward the P and dS tile
-// stores (bf16, 128x128 per (row slot, key tile, q-head)).
+// [query list][key list], then for the two-phase backward the P and dS block
+// stores (bf16, 256x256 per (row slot, key block, q-head)).
+constexpr int kBlockRows = 256;
 struct TileGeom {
-  int64_t slots;  // query-tile row slots
-  int nkb;        // key tiles per slot
-  int nqb_dense;  // dense: query tiles per batch (slot = b*nqb + qb); 0: varlen
+  int64_t slots;  // 256-query row slots
+  int nkb;        // 256-key blocks per slot
+  int nqb_dense;  // dense: query blocks per batch (slot = b*nqb + qb); 0: varlen
 };
 inline TileGeom tile_geom_dense(int B, int Nq, int Nk) {
-  const int nqb = (Nq + 127) / 128;
-  return TileGeom{(int64_t)B * nqb, (Nk + 127) / 128, nqb};
+  const int nqb = (Nq + kBlockRows - 1) / kBlockRows;
+  return TileGeom{(int64_t)B * nqb, (Nk + kBlockRows - 1) / kBlockRows, nqb};
 }
 inline TileGeom tile_geom_varlen(int Tq, int nseg, int max_k) {
-  return TileGeom{(int64_t)Tq / 128 + nseg + 1, (max_k + 127) / 128, 0};
+  return TileGeom{(int64_t)Tq / kBlockRows + nseg + 1, (max_k + kBlockRows - 1) / kBlockRows, 0};
 }
-// Head-dim pairs whose backward runs in two phases through stored tiles.
-inline bool bwd_uses_tiles(int dqk, int dv) { return dqk == dv && dqk >= 256; }
+// Head-dim pairs whose backward runs in two phases through stored blocks.
+inline bool bwd_uses_tiles(int dqk, int dv) { return dqk == dv && (dqk == 256 || dqk == 512); }
 struct BwdWorkspace {
   size_t list_q, list_k, tile_p, tile_ds, total;
 };
@@ -67,9 +68,10 @@ inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64
   w.tile_p = w.list_k + align256(sizeof(int2) * list_capacity(k_rows, nseg));
   w.tile_ds = w.tile_p;
   if (bwd_uses_tiles(dqk, dv)) {
-    const size_t tiles = sizeof(uint16_t) * 128 * 128 * (size_t)tg.slots * (size_t)tg.nkb * (size_t)Hq;
-    w.tile_ds = w.tile_p + tiles;
-    w.total = w.tile_ds + tiles;
+    const size_t blocks = sizeof(uint16_t) * kBlockRows * kBlockRows * (size_t)tg.slots *
+                          (size_t)tg.nkb * (size_t)Hq;
+    w.tile_ds = w.tile_p + blocks;
+    w.total = w.tile_ds + blocks;
   } else {
     w.total = w.tile_p;
   }

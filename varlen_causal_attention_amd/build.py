@@ -20,7 +20,8 @@ LIB = os.path.join(HERE, "libvca_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_merge.hip", "attn_api.hip", "attn_timing.hip"]
+HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_merge.hip",
+               "attn_api.hip", "attn_timing.hip"]
 CXX_SOURCES = ["attn_segments.cpp"]
 # -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in VGPRs. The kernels keep
 # their working set under the unified register budget; left to choose, the

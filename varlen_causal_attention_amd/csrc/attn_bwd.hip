@@ -1,7 +1,7 @@
 // Backward launcher: delta pre-pass, then for every compiled head-dim pair
 // either the fused dK/dV and dQ passes (DS = number of waves that split one
-// 32-row block by head-dim range) or the two-phase scores + products passes.
-#include "attn_bwd_tiles.hpp"
+// 32-row block by head-dim range) or the two-phase scores + products passes
+// (their own translation unit, attn_bwd_tiles.hip).
 #include "attn_launch.hpp"
 #include "attn_timing.hpp"
 
@@ -110,68 +110,33 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   return hipGetLastError();
 }
 
-// Two-phase backward: scores (P, dS blocks), then the dV/dK and dQ products.
-template <int D, bool CAUSAL>
-hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows, int64_t k_rows,
-                     const TileGeom& tg, const BwdWorkspace& wl, void* ws, hipStream_t st) {
-  bwd_prologue<D>(a, CAUSAL, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, kBlk, kBlk, kBlk, kBlk, ws,
-                  st);
-  char* w = static_cast<char*>(ws);
-  a.tile_p = reinterpret_cast<uint16_t*>(w + wl.tile_p);
-  a.tile_ds = reinterpret_cast<uint16_t*>(w + wl.tile_ds);
-  a.tile_nkb = tg.nkb;
-  a.tile_nqb_dense = tg.nqb_dense;
-  const unsigned q_items = (unsigned)((q_rows + kBlk - 1) / kBlk + nseg);
-  const unsigned k_items = (unsigned)((k_rows + kBlk - 1) / kBlk + nseg);
-  if (q_rows > 0 && k_rows > 0) {
-    // The score kernel counts its outstanding memory operations by hand;
-    // register spills (scratch traffic) would break that count.
-    static const hipError_t no_scratch = [] {
-      hipFuncAttributes attr{};
-      const hipError_t e =
-          hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&attn_bwd_scores_kernel<D, D, CAUSAL>));
-      if (e != hipSuccess) return e;
-      return attr.localSizeBytes == 0 ? hipSuccess : hipErrorInvalidDeviceFunction;
-    }();
-    if (no_scratch != hipSuccess) return no_scratch;
-    TimedLaunch timer("attn_bwd_scores", st);
-    hipLaunchKernelGGL((attn_bwd_scores_kernel<D, D, CAUSAL>),
-                       dim3(xcd_grid<kScoreSplit>(q_items * Hq)), dim3(512), 0, st, a);
-  }
-  if (k_rows > 0) {
-    TimedLaunch timer("attn_bwd_dkdv_tiles", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<D, CAUSAL>),
-                       dim3(xcd_grid<2 * (D / kBlk)>(k_items * Hkv)), dim3(512), 0, st, a);
-  }
-  if (q_rows > 0) {
-    TimedLaunch timer("attn_bwd_dq_tiles", st);
-    hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<D, CAUSAL>),
-                       dim3(xcd_grid<D / kBlk>(q_items * Hq)), dim3(512), 0, st, a);
-  }
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t bwd_tiles_any(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q,
-                         int64_t q_rows, int64_t k_rows, const TileGeom& tg,
-                         const BwdWorkspace& wl, void* ws, hipStream_t st) {
-  return causal ? bwd_tiles<D, true>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st)
-                : bwd_tiles<D, false>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
-}
-
 }  // namespace
+
+void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                 int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
+                 int k_tile, int k_step, void* ws, hipStream_t st) {
+  switch (dv) {
+    case 64:
+      return bwd_prologue<64>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, q_step,
+                              k_tile, k_step, ws, st);
+    case 128:
+      return bwd_prologue<128>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, q_step,
+                               k_tile, k_step, ws, st);
+    case 256:
+      return bwd_prologue<256>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, q_step,
+                               k_tile, k_step, ws, st);
+    default:
+      return bwd_prologue<512>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, q_step,
+                               k_tile, k_step, ws, st);
+  }
+}
 
 hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                       int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws, hipStream_t st) {
   if (nseg == 0 || Hq == 0) return hipSuccess;
   const BwdWorkspace wl = bwd_workspace(dqk, dv, Hq, q_rows, k_rows, nseg, tg);
-  if (bwd_uses_tiles(dqk, dv)) {
-    if (dqk == 256)
-      return bwd_tiles_any<256>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
-    if (dqk == 512)
-      return bwd_tiles_any<512>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
-    return hipErrorInvalidValue;
-  }
+  if (bwd_uses_tiles(dqk, dv))
+    return launch_bwd_tiles(a, dqk, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
 // arguments: DQK, DV, DS, dK/dV buffers + prefetch, dQ key tile, dQ buffers + prefetch, dQ waves
 // per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
 #define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \

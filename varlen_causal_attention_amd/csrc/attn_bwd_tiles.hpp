@@ -43,6 +43,7 @@ constexpr int kChunk = 64;                           // contraction elements per
 constexpr int kOpElems = kBlk * kChunk;              // one staged operand (32 KB)
 constexpr int64_t kBlkElems = (int64_t)kBlk * kBlk;  // one stored block
 constexpr int kXcds = 8;
+constexpr int kNT = 512;                             // threads per workgroup (8 waves)
 
 __device__ __forceinline__ int64_t blk_slot(const BwdArgs& a, const SegGeom& g, int s, int qb) {
   return a.tile_nqb_dense ? (int64_t)s * a.tile_nqb_dense + qb
@@ -144,7 +145,7 @@ typedef const __attribute__((address_space(1))) float gfloat;
 constexpr int kScoreSplit = 4;
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) attn_bwd_scores_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a) {
   constexpr int NCQ = DQK / kChunk, NCV = DV / kChunk, NCT = NCQ + NCV;
   static_assert(DQK % kChunk == 0 && DV % kChunk == 0, "head dims stream in 64-element chunks");
   constexpr int NST = 16;  // hand-issued block stores per lane per epilogue
@@ -213,9 +214,11 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_scores_kernel(const BwdArgs a
 
   const int total = nkt * NCT;
   issue(0, 0);
-  // Every vector memory operation in the loop is issued by hand, so a wave
-  // knows what it has in flight when it waits for stage it: only the block
-  // stores of the previous iteration's epilogue (if any) came after it.
+  // The loop's loads and stores are issued by hand, so a wave knows what it
+  // has in flight when it waits for stage it: only the block stores of the
+  // previous iteration's epilogue (if any) came after it. Operations retire
+  // in issue order, so anything the compiler adds (register spills) only
+  // makes such a wait stricter, never too weak.
   bool stored = false;
   for (int it = 0; it < total; ++it) {
     const int kt = it / NCT, c = it - kt * NCT, stage = it & 1;
@@ -317,7 +320,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_scores_kernel(const BwdArgs a
 // side stream the same X rows at the same time.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_tiles_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdArgs a) {
   constexpr int NDH = D / kBlk, PARTS = 2 * NDH, CPB = kBlk / kChunk;
   static_assert(D % kBlk == 0, "output columns in blocks of 256");
   __shared__ __attribute__((aligned(1024))) uint16_t stg[2][2 * kOpElems];
@@ -418,7 +421,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
 // each lane its eight keys as one 16-byte piece.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) attn_bwd_dq_tiles_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs a) {
   constexpr int NDH = D / kBlk, CPB = kBlk / kChunk;
   static_assert(D % kBlk == 0, "output columns in blocks of 256");
   __shared__ __attribute__((aligned(1024))) uint16_t stg[2][2 * kOpElems];

@@ -90,6 +90,19 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
                       int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws,
                       hipStream_t stream);
 
+// Work lists of the backward (query tiles of q_tile rows costed in q_step
+// keys, key blocks of k_tile keys costed in k_step queries) and the delta
+// pre-pass; fills the list fields of a.
+void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                 int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
+                 int k_tile, int k_step, void* ws, hipStream_t st);
+
+// Two-phase backward (Dqk == Dv == d, d in {256, 512}): lists, delta, scores,
+// products.
+hipError_t launch_bwd_tiles(BwdArgs a, int d, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                            int64_t q_rows, int64_t k_rows, const TileGeom& tg,
+                            const BwdWorkspace& wl, void* ws, hipStream_t st);
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace vca

@@ -23,6 +23,7 @@
  *  - lse is the natural log of the sum of exp over the *scaled* scores
  *    (scale * q.k). A query row with no visible key gets out = 0 and
  *    lse = -inf; the backward treats lse = -inf as "row attends nothing".
+ *  - scale must be finite and non-zero (ATTN_E_INVALID otherwise).
  *  - GQA: Hq must be a multiple of Hkv; q-head h reads kv-head h / (Hq/Hkv).
  *  - Head dims: (Dqk, Dv) must be one of the pairs attn_is_supported()
  *    accepts: (64,64), (128,128), (192,128), (256,256), (512,512).

@@ -65,6 +65,7 @@ def _dense(lib, **kw):
     (dict(strides=None), _lib.ATTN_E_INVALID),
     (dict(Nq=-1), _lib.ATTN_E_INVALID),
     (dict(scale=float("nan")), _lib.ATTN_E_INVALID),
+    (dict(scale=0.0), _lib.ATTN_E_INVALID),
 ])
 def test_dense_forward_rejects_bad_arguments(lib, kw, status):
     st, _ = _dense(lib, **kw)

@@ -32,7 +32,8 @@ int check_heads(int dtype, int Hq, int Hkv, int Dqk, int Dv, float scale) {
   if (!vca::head_dims_supported(Dqk, Dv))
     return fail(ATTN_E_UNSUPPORTED, "head dims (" + std::to_string(Dqk) + "," +
                                         std::to_string(Dv) + ") not compiled in");
-  if (!std::isfinite(scale)) return fail(ATTN_E_INVALID, "scale must be finite");
+  if (!std::isfinite(scale) || scale == 0.f)
+    return fail(ATTN_E_INVALID, "scale must be finite and non-zero");
   return ATTN_OK;
 }
 
@@ -243,6 +244,7 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   a.G = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * vca::kLog2e;
+  a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
   return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
                                     (int64_t)B * Nk, tg, workspace, stream),
@@ -302,6 +304,7 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   a.G = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * vca::kLog2e;
+  a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
   return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq, Tk,
                                     tg, workspace, stream),

@@ -136,7 +136,8 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   if (nseg == 0 || Hq == 0) return hipSuccess;
   const BwdWorkspace wl = bwd_workspace(dqk, dv, Hq, q_rows, k_rows, nseg, tg);
   if (bwd_uses_tiles(dqk, dv))
-    return launch_bwd_tiles(a, dqk, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
+    return launch_bwd_tiles(a, dqk, dv, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws,
+                            st);
 // arguments: DQK, DV, DS, dK/dV buffers + prefetch, dQ key tile, dQ buffers + prefetch, dQ waves
 // per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
 #define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \
@@ -144,7 +145,6 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
                                                            q_rows, k_rows, wl, ws, st)
   if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
   if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
-  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 2, 2, true, 32, 2, true, 2, 8, 8);
 #undef VCA_BWD
   return hipErrorInvalidValue;
 }

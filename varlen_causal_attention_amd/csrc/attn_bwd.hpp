@@ -33,7 +33,7 @@ struct BwdArgs {
   const int32_t* cu_k;
   int Nq, Nk, Tq, Tk;
   int G;
-  float scale, scale_log2;
+  float scale, scale_log2, inv_scale;  // inv_scale = 1 / scale (scale != 0)
   int dq_accumulate;
   int Hq, Hkv;
   const int2* items_q;    // (segment, query tile) for the dQ pass, heavy first

@@ -6,10 +6,12 @@
 namespace vca {
 namespace {
 
-template <int D, bool CAUSAL>
+template <int DQK, int DV, bool CAUSAL>
 hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows, int64_t k_rows,
                      const TileGeom& tg, const BwdWorkspace& wl, void* ws, hipStream_t st) {
-  bwd_prepare(a, D, CAUSAL, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, kBlk, kBlk, kBlk, kBlk, ws, st);
+  constexpr int OBQ = prod_block(DQK), OBV = prod_block(DV);
+  bwd_prepare(a, DV, CAUSAL, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, kBlk, kBlk, kBlk, kBlk, ws,
+              st);
   char* w = static_cast<char*>(ws);
   a.tile_p = reinterpret_cast<uint16_t*>(w + wl.tile_p);
   a.tile_ds = reinterpret_cast<uint16_t*>(w + wl.tile_ds);
@@ -19,39 +21,51 @@ hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_
   const unsigned k_items = (unsigned)((k_rows + kBlk - 1) / kBlk + nseg);
   if (q_rows > 0 && k_rows > 0) {
     TimedLaunch timer("attn_bwd_scores", st);
-    hipLaunchKernelGGL((attn_bwd_scores_kernel<D, D, CAUSAL>),
+    hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>),
                        dim3(xcd_grid<kScoreSplit>(q_items * Hq)), dim3(kNT), 0, st, a);
   }
   if (k_rows > 0) {
     TimedLaunch timer("attn_bwd_dkdv_tiles", st);
-    hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<D, CAUSAL>),
-                       dim3(xcd_grid<2 * (D / kBlk)>(k_items * Hkv)), dim3(kNT), 0, st, a);
+    if constexpr (DQK == DV) {
+      // dV and dK blocks of one launch, side by side
+      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 2>),
+                         dim3(xcd_grid<2 * (DV / OBV)>(k_items * Hkv)), dim3(kNT), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 0>),
+                         dim3(xcd_grid<DV / OBV>(k_items * Hkv)), dim3(kNT), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DQK, OBQ, CAUSAL, 1>),
+                         dim3(xcd_grid<DQK / OBQ>(k_items * Hkv)), dim3(kNT), 0, st, a);
+    }
   }
   if (q_rows > 0) {
     TimedLaunch timer("attn_bwd_dq_tiles", st);
-    hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<D, CAUSAL>),
-                       dim3(xcd_grid<D / kBlk>(q_items * Hq)), dim3(kNT), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<DQK, OBQ, CAUSAL>),
+                       dim3(xcd_grid<DQK / OBQ>(q_items * Hq)), dim3(kNT), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int DQK, int DV>
 hipError_t bwd_tiles_any(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q,
                          int64_t q_rows, int64_t k_rows, const TileGeom& tg,
                          const BwdWorkspace& wl, void* ws, hipStream_t st) {
-  return causal ? bwd_tiles<D, true>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st)
-                : bwd_tiles<D, false>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
+  return causal
+             ? bwd_tiles<DQK, DV, true>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st)
+             : bwd_tiles<DQK, DV, false>(a, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_tiles(BwdArgs a, int d, bool causal, int nseg, int Hq, int Hkv, int max_q,
-                            int64_t q_rows, int64_t k_rows, const TileGeom& tg,
+hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
+                            int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg,
                             const BwdWorkspace& wl, void* ws, hipStream_t st) {
-  if (d == 256)
-    return bwd_tiles_any<256>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
-  if (d == 512)
-    return bwd_tiles_any<512>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
+#define VCA_TILES(DQK, DV)                                                                       \
+  if (dqk == DQK && dv == DV)                                                                    \
+    return bwd_tiles_any<DQK, DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
+  VCA_TILES(192, 128)
+  VCA_TILES(256, 256)
+  VCA_TILES(512, 512)
+#undef VCA_TILES
   return hipErrorInvalidValue;
 }
 

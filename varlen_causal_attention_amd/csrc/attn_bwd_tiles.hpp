@@ -14,11 +14,11 @@
 // bytes per visible (query, key, head)) turns every matrix product into a
 // plain block GEMM whose accumulators fit, at the price of that traffic.
 //
-// Every pass is the same 256x256 block GEMM: 8 waves, each owning 64 rows x
-// 128 columns of C (2x4 MFMA tiles: two A and four B fragments per eight
-// MFMAs); the contraction streams through two LDS stages of 64 elements per
-// operand, loaded straight from global memory into LDS one stage ahead, with
-// one barrier per stage.
+// Every pass is a block GEMM of 8 waves (scores: 256x256 C, each wave 64 rows
+// x 128 columns; products: OB output columns, each wave 64 rows x OB/2 or
+// OB/4 columns); the contraction streams through two LDS stages of 64
+// elements per operand, loaded straight from global memory into LDS one
+// stage ahead, with one barrier per stage.
 //
 // Block store: query block qb of segment s owns row slot
 // floor(q_row0/256) + s + qb (varlen; injective because a segment adds at
@@ -93,21 +93,31 @@ inline unsigned xcd_grid(unsigned groups) {
 __device__ __forceinline__ bf16x8 row_frag(const uint16_t* X, int r, int piece) {
   return lds_frag(X + r * kChunk + ((piece ^ ((r >> 1) & 7)) << 3));
 }
-// Column mode: kChunk contraction rows x kBlk columns, 512-byte rows. The
-// 16-byte unit u of row r sits at position u ^ ((r & 3) << 2), so the four
-// rows one transposing read covers per 32 lanes use four different 64-byte
-// bank groups. Same result as tr_frag: lane l gets column n0 + l%32 and rows
-// {k0 + 4h + j, k0 + 8 + 4h + j} (h = l/32).
+// Column mode: kChunk contraction rows x W columns (W = 128, 192 or 256).
+// The 16-byte unit u of row r sits at position col_pos<W>(r, u), chosen so
+// the four rows one transposing read covers per 32 lanes land in four
+// different 64-byte bank groups: rows of 256 or 512 bytes all start on the
+// same bank, so 64-byte windows are XORed with r & 3; rows of 384 bytes
+// alternate between the two bank halves, so the window is XORed with bit 1
+// of r. col_frag gives the same result as tr_frag: lane l gets column
+// n0 + l%32 and rows {k0 + 4h + j, k0 + 8 + 4h + j} (h = l/32).
+template <int W>
+__device__ __forceinline__ int col_pos(int r, int u) {
+  static_assert(W == 128 || W == 192 || W == 256, "column-mode widths");
+  if constexpr (W == 192) return u ^ (((r >> 1) & 1) << 2);
+  else return u ^ ((r & 3) << 2);
+}
+template <int W>
 __device__ __forceinline__ bf16x8 col_frag(const uint16_t* X, int k0, int n0, int lane) {
   const int g = lane >> 4, s = lane & 15, h = lane >> 5;
   const int row = k0 + 4 * h + (s >> 2);
   const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
-  const uint16_t* p = X + row * kBlk + ((((c >> 3) ^ ((row & 3) << 2))) << 3) + (c & 7);
+  // rows row and row + 8 share the swizzle
+  const uint16_t* p = X + row * W + (col_pos<W>(row, c >> 3) << 3) + (c & 7);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 8 * kBlk)));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 8 * W)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // Fill a row-mode operand: rp(r) points at the stage's first element of row
@@ -121,15 +131,18 @@ __device__ __forceinline__ void fill_rows(const uint16_t* X, int w, int lane, Ro
     dma16(rp(r) + piece * 8, lds_ptr(X + (32 * w + 8 * j) * kChunk));
   }
 }
-// Fill a column-mode operand: rp(r) points at the first of the 256 columns of
-// contraction row r (r < 64). Wave w issues four 2-row loads.
-template <class RowPtr>
+// Fill a column-mode operand of width W: rp(r) points at the first of the W
+// columns of contraction row r (r < 64). The operand is W/8 contiguous 1 KB
+// loads; wave w issues W/64 of them, each lane placing one 16-byte unit.
+template <int W, class RowPtr>
 __device__ __forceinline__ void fill_cols(const uint16_t* X, int w, int lane, RowPtr rp) {
+  constexpr int NL = W / 64, RB = 2 * W;  // loads per wave, bytes per row
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * w + 2 * j + (lane >> 5);
-    const int unit = (lane & 31) ^ ((r & 3) << 2);
-    dma16(rp(r) + unit * 8, lds_ptr(X + (8 * w + 2 * j) * kBlk));
+  for (int j = 0; j < NL; ++j) {
+    const int blk = w * NL + j;                        // 1 KB block of the operand
+    const int pos = blk * 1024 + 16 * lane;            // this lane's byte offset
+    const int r = pos / RB, su = (pos % RB) / 16;      // row, stored unit
+    dma16(rp(r) + col_pos<W>(r, su) * 8, lds_ptr(X + blk * 512));
   }
 }
 
@@ -138,9 +151,10 @@ typedef const __attribute__((address_space(1))) float gfloat;
 // ---------------------------------------------------------------------------
 // Phase 1. One workgroup = (segment, q-head, query block, part); it takes key
 // blocks part, part + kScoreSplit, ... of the row. Per key block it runs the
-// S^T = K Q^T loop, writes P, then the dP^T = V dO^T loop and writes dS
-// (re-reading its own P). Wave (wm, wn) owns keys 64*wm.. and queries
-// 128*wn.. of the block.
+// S^T = K Q^T loop, writes P, then the dP^T = V dO^T loop (accumulators
+// seeded with -delta) and writes dS = P * (dP - delta), re-reading its own P.
+// Wave (wm, wn) owns keys 64*wm.. and queries 128*wn.. of the block. Masks
+// are evaluated only for blocks that are not entirely visible.
 // ---------------------------------------------------------------------------
 constexpr int kScoreSplit = 4;
 
@@ -252,27 +266,35 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
     const int64_t base = blk_base(a, slot, kb, h);
     if (c == NCQ - 1) {
       uint16_t* pb = a.tile_p + base;
+      auto pstore = [&](auto masked) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int qr = 128 * wn + 32 * u + col, qi = q0 + qr;
+          for (int u = 0; u < 4; ++u) {
+            const int qr = 128 * wn + 32 * u + col, qi = q0 + qr;
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            bf16x8 p8;
+            for (int m = 0; m < 2; ++m) {
+              bf16x8 p8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * m + e;
-              const int kj = k0 + 64 * wm + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-              bool vis = qi < lq && kj < lk;
-              if (CAUSAL) vis = vis && kj <= qi + shift;
-              const float p = fast_exp2(acc[t][u][r] * a.scale_log2 - l2[u]);
-              p8[e] = (__bf16)(vis ? p : 0.f);
+              for (int e = 0; e < 8; ++e) {
+                const int r = 8 * m + e;
+                float p = fast_exp2(acc[t][u][r] * a.scale_log2 - l2[u]);
+                if constexpr (decltype(masked)::value) {
+                  const int kj = k0 + 64 * wm + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+                  bool vis = qi < lq && kj < lk;
+                  if (CAUSAL) vis = vis && kj <= qi + shift;
+                  p = vis ? p : 0.f;
+                }
+                p8[e] = (__bf16)p;
+              }
+              stg16(pb + qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half,
+                    __builtin_bit_cast(u32x4, p8));
             }
-            stg16(pb + qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half,
-                  __builtin_bit_cast(u32x4, p8));
           }
-        }
+      };
+      const bool full = q0 + kBlk <= lq && k0 + kBlk <= lk && (!CAUSAL || k0 + kBlk - 1 <= q0 + shift);
+      if (full) pstore(std::false_type{});
+      else pstore(std::true_type{});
     } else {
       const uint16_t* pb = a.tile_p + base;
       uint16_t* db = a.tile_ds + base;
@@ -296,44 +318,61 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
             bf16x8 d8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              d8[e] = (__bf16)((float)p8[e] * (acc[t][u][8 * m + e] - dl[u]));
+              d8[e] = (__bf16)((float)p8[e] * acc[t][u][8 * m + e]);
             stg16(db + off, __builtin_bit_cast(u32x4, d8));
           }
         }
       }
     }
     stored = true;
+    // the dP loop starts from -delta (dS = P * dP then needs no row operand)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 4; ++u) {
+      float x = c == NCQ - 1 ? -dl[u] : 0.f;
+      asm volatile("" : "+v"(x));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][u] = zero16();
+      for (int t = 0; t < 2; ++t) acc[t][u] = splat16(x);
+    }
   }
 }
 
+// Products run 8 waves over an (OB output columns) x (256 keys or queries)
+// result: a WM x WN wave grid with RT x CT MFMA tiles per wave.
+template <int OB>
+struct ProdShape {
+  static constexpr int WM = OB == 256 ? 4 : 2, WN = 8 / WM;
+  static constexpr int RM = OB / WM, RN = kBlk / WN;  // rows / columns per wave
+  static constexpr int RT = RM / 32, CT = RN / 32;
+  static_assert(RM % 32 == 0 && RN % 32 == 0, "wave grid");
+};
+// output block width for a head dim: whole when it fits, else 256 at a time
+constexpr int prod_block(int d) { return d > kBlk ? kBlk : d; }
+
 // ---------------------------------------------------------------------------
-// Phase 2a. dV (part even) or dK (part odd) of one (segment, kv-head, key
-// block) and 256 of its output columns (part / 2):
+// Phase 2a. dV (WHICH 0), dK (WHICH 1) or both (WHICH 2, part parity) of one
+// (segment, kv-head, key block) and OB of its DOUT output columns:
 //   C^T[d][key] = sum over (q-head of the group, visible query block, 64-row
 //   chunk) of X^T[d][q] T[q][key],  X = dO or Q, T = P or dS.
 // Both operands are staged in column mode and read down their columns. Query
 // blocks run last to first, so the key blocks of one kv-head working side by
 // side stream the same X rows at the same time.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int DOUT, int OB, bool CAUSAL, int WHICH>
 __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdArgs a) {
-  constexpr int NDH = D / kBlk, PARTS = 2 * NDH, CPB = kBlk / kChunk;
-  static_assert(D % kBlk == 0, "output columns in blocks of 256");
+  using S = ProdShape<OB>;
+  constexpr int NDH = DOUT / OB, PARTS = (WHICH == 2 ? 2 : 1) * NDH, CPB = kBlk / kChunk;
+  static_assert(DOUT % OB == 0, "output columns in whole blocks");
   __shared__ __attribute__((aligned(1024))) uint16_t stg[2][2 * kOpElems];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / S::WN, wn = w % S::WN;
   int grp, part;
   xcd_work<PARTS>(blockIdx.x, grp, part);
   const int item = grp / a.Hkv, hk = grp - item * a.Hkv;
   if (item >= *a.count_k) return;
-  const bool is_dk = part & 1;
-  const int dh = part >> 1;
+  const bool is_dk = WHICH == 2 ? (part & 1) != 0 : WHICH == 1;
+  const int dh = WHICH == 2 ? part >> 1 : part;
   const int2 st = a.items_k[item];
   const int s = st.x, kb = st.y;
   const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
@@ -350,7 +389,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   const uint16_t* xp = is_dk ? a.q.p : a.dout.p;
   const int64_t xsb = is_dk ? a.q.sb : a.dout.sb, xsh = is_dk ? a.q.sh : a.dout.sh;
   const int64_t xsn = is_dk ? a.q.sn : a.dout.sn;
-  xp += s * xsb + (int64_t)sg.q_row0 * xsn + dh * kBlk;
+  xp += s * xsb + (int64_t)sg.q_row0 * xsn + dh * OB;
   const uint16_t* T = is_dk ? a.tile_ds : a.tile_p;
   auto issue = [&](int it, int stage) {
     const int hh = it / per, rem = it - hh * per;
@@ -358,17 +397,17 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
     const int h = hk * a.G + hh;
     const int r0 = qb * kBlk + c * kChunk;
     const uint16_t* xh = xp + h * xsh;
-    fill_cols(stg[stage], w, lane,
-              [&](int r) { return xh + (int64_t)min(r0 + r, lq - 1) * xsn; });
+    fill_cols<OB>(stg[stage], w, lane,
+                  [&](int r) { return xh + (int64_t)min(r0 + r, lq - 1) * xsn; });
     const uint16_t* tb = T + blk_base(a, blk_slot(a, sg, s, qb), kb, h) + c * kChunk * kBlk;
-    fill_cols(stg[stage] + kOpElems, w, lane, [&](int r) { return tb + r * kBlk; });
+    fill_cols<kBlk>(stg[stage] + kOpElems, w, lane, [&](int r) { return tb + r * kBlk; });
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[S::RT][S::CT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < S::RT; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[t][u] = zero16();
+    for (int u = 0; u < S::CT; ++u) acc[t][u] = zero16();
 
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; ++it) {
@@ -380,15 +419,16 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
     const uint16_t* B = stg[stage] + kOpElems;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
-      bf16x8 af[2], bf[4];
+      bf16x8 af[S::RT], bf[S::CT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) af[t] = col_frag(A, 16 * ks, 64 * wm + 32 * t, lane);
+      for (int t = 0; t < S::RT; ++t) af[t] = col_frag<OB>(A, 16 * ks, S::RM * wm + 32 * t, lane);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bf[u] = col_frag(B, 16 * ks, 128 * wn + 32 * u, lane);
+      for (int u = 0; u < S::CT; ++u)
+        bf[u] = col_frag<kBlk>(B, 16 * ks, S::RN * wn + 32 * u, lane);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < S::RT; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[t][u] = mfma32(af[t], bf[u], acc[t][u]);
+        for (int u = 0; u < S::CT; ++u) acc[t][u] = mfma32(af[t], bf[u], acc[t][u]);
     }
   }
 
@@ -397,38 +437,39 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   const int64_t osb = is_dk ? a.dk.sb : a.dv.sb, osh = is_dk ? a.dk.sh : a.dv.sh;
   const int64_t osn = is_dk ? a.dk.sn : a.dv.sn;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int key = k0 + key_perm(128 * wn + 32 * u + col);
+  for (int u = 0; u < S::CT; ++u) {
+    const int key = k0 + key_perm(S::RN * wn + 32 * u + col);
     if (key >= sg.lk) continue;
-    uint16_t* orow = op + s * osb + (int64_t)(sg.k_row0 + key) * osn + hk * osh + dh * kBlk;
+    uint16_t* orow = op + s * osb + (int64_t)(sg.k_row0 + key) * osn + hk * osh + dh * OB;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < S::RT; ++t)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[t][u][rr * 4 + e] * mul);
-        *reinterpret_cast<bf16x4*>(orow + 64 * wm + 32 * t + rr * 8 + half * 4) = v4;
+        *reinterpret_cast<bf16x4*>(orow + S::RM * wm + 32 * t + rr * 8 + half * 4) = v4;
       }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 2b. dQ of one (segment, q-head, query block) and 256 of its output
+// Phase 2b. dQ of one (segment, q-head, query block) and OB of its DQK output
 // columns (part):  dQ^T[d][q] = sum over (visible key block, 64-key chunk) of
 // K^T[d][key] dS^T[key][q]. K is staged in column mode and read down its
 // columns; dS rows are staged in row mode, where the stored key order gives
 // each lane its eight keys as one 16-byte piece.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int DQK, int OB, bool CAUSAL>
 __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs a) {
-  constexpr int NDH = D / kBlk, CPB = kBlk / kChunk;
-  static_assert(D % kBlk == 0, "output columns in blocks of 256");
+  using S = ProdShape<OB>;
+  constexpr int NDH = DQK / OB, CPB = kBlk / kChunk;
+  static_assert(DQK % OB == 0, "output columns in whole blocks");
   __shared__ __attribute__((aligned(1024))) uint16_t stg[2][2 * kOpElems];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / S::WN, wn = w % S::WN;
   int grp, dh;
   xcd_work<NDH>(blockIdx.x, grp, dh);
   const int item = grp / a.Hq, h = grp - item * a.Hq, g = h / a.G;
@@ -442,21 +483,21 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
   const int total = blk_row_extent(a, sg, q0, CAUSAL) * CPB;
   const int64_t slot = blk_slot(a, sg, s, st.y);
   const uint16_t* kbp =
-      a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh + dh * kBlk;
+      a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh + dh * OB;
   auto issue = [&](int it, int stage) {
     const int kb = it / CPB, c = it % CPB;
     const int r0 = kb * kBlk + c * kChunk;
-    fill_cols(stg[stage], w, lane,
-              [&](int r) { return kbp + (int64_t)min(r0 + r, lk - 1) * a.k.sn; });
+    fill_cols<OB>(stg[stage], w, lane,
+                  [&](int r) { return kbp + (int64_t)min(r0 + r, lk - 1) * a.k.sn; });
     const uint16_t* db = a.tile_ds + blk_base(a, slot, kb, h) + c * kChunk;
     fill_rows(stg[stage] + kOpElems, w, lane, [&](int r) { return db + r * kBlk; });
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[S::RT][S::CT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < S::RT; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[t][u] = zero16();
+    for (int u = 0; u < S::CT; ++u) acc[t][u] = zero16();
 
   if (total > 0) issue(0, 0);
   for (int it = 0; it < total; ++it) {
@@ -468,29 +509,30 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
     const uint16_t* B = stg[stage] + kOpElems;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
-      bf16x8 af[2], bf[4];
+      bf16x8 af[S::RT], bf[S::CT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) af[t] = col_frag(A, 16 * ks, 64 * wm + 32 * t, lane);
+      for (int t = 0; t < S::RT; ++t) af[t] = col_frag<OB>(A, 16 * ks, S::RM * wm + 32 * t, lane);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) bf[u] = row_frag(B, 128 * wn + 32 * u + col, 2 * ks + half);
+      for (int u = 0; u < S::CT; ++u)
+        bf[u] = row_frag(B, S::RN * wn + 32 * u + col, 2 * ks + half);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < S::RT; ++t)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[t][u] = mfma32(af[t], bf[u], acc[t][u]);
+        for (int u = 0; u < S::CT; ++u) acc[t][u] = mfma32(af[t], bf[u], acc[t][u]);
     }
   }
 
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int qi = q0 + 128 * wn + 32 * u + col;
+  for (int u = 0; u < S::CT; ++u) {
+    const int qi = q0 + S::RN * wn + 32 * u + col;
     if (qi >= sg.lq) continue;
     uint16_t* dqp = a.dq.p + s * a.dq.sb + (int64_t)(sg.q_row0 + qi) * a.dq.sn + h * a.dq.sh +
-                    dh * kBlk;
+                    dh * OB;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < S::RT; ++t)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        uint16_t* dst = dqp + 64 * wm + 32 * t + rr * 8 + half * 4;
+        uint16_t* dst = dqp + S::RM * wm + 32 * t + rr * 8 + half * 4;
         float add[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.dq_accumulate) {
           const u32x2 old = *reinterpret_cast<const u32x2*>(dst);

@@ -39,6 +39,12 @@ __device__ __forceinline__ f32x16 zero16() {
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
 }
+__device__ __forceinline__ f32x16 splat16(float x) {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = x;
+  return z;
+}
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -107,12 +113,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // restored afterwards; the s_nops separate the M0 writes from the LDS DMA.
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void* lds_ptr(const void* p) { return (lds_void*)p; }
-// The LDS destination also goes into the asm as a pointer operand: the
-// compiler then knows the asm writes that LDS object and keeps later reads of
-// it, instead of treating never-stored LDS as undefined.
+// The LDS address reaches the asm as an integer taken from the array's
+// address, so the array counts as escaped and the compiler keeps every later
+// read of it (the "memory" clobber covers the write).
 __device__ __forceinline__ void dma16(const uint16_t* g, lds_void* lds_base) {
   uint32_t saved;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
@@ -121,7 +127,7 @@ __device__ __forceinline__ void dma16(const uint16_t* g, lds_void* lds_base) {
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(m0), "v"(lds_base)
+      : "v"(g), "s"(m0)
       : "memory");
 }
 // Global stores whose vmcnt footprint is exactly one operation each (used

@@ -55,7 +55,9 @@ inline TileGeom tile_geom_varlen(int Tq, int nseg, int max_k) {
   return TileGeom{(int64_t)Tq / kBlockRows + nseg + 1, (max_k + kBlockRows - 1) / kBlockRows, 0};
 }
 // Head-dim pairs whose backward runs in two phases through stored blocks.
-inline bool bwd_uses_tiles(int dqk, int dv) { return dqk == dv && (dqk == 256 || dqk == 512); }
+inline bool bwd_uses_tiles(int dqk, int dv) {
+  return (dqk == dv && (dqk == 256 || dqk == 512)) || (dqk == 192 && dv == 128);
+}
 struct BwdWorkspace {
   size_t list_q, list_k, tile_p, tile_ds, total;
 };
@@ -97,10 +99,10 @@ void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int
                  int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
                  int k_tile, int k_step, void* ws, hipStream_t st);
 
-// Two-phase backward (Dqk == Dv == d, d in {256, 512}): lists, delta, scores,
-// products.
-hipError_t launch_bwd_tiles(BwdArgs a, int d, bool causal, int nseg, int Hq, int Hkv, int max_q,
-                            int64_t q_rows, int64_t k_rows, const TileGeom& tg,
+// Two-phase backward (the head-dim pairs bwd_uses_tiles names): lists,
+// delta, scores, products.
+hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
+                            int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg,
                             const BwdWorkspace& wl, void* ws, hipStream_t st);
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -147,7 +147,9 @@ def kernel_work(w: "workloads.Workload", name: str):
     """(bound, algorithmic units per launch, unit) of one library kernel.
     Forward: 2*pairs*(Dqk+Dv) FLOPs. dK/dV pass: S, dP, dV, dK products,
     2*pairs*(2*Dqk+2*Dv). dQ pass: the dQ product only, 2*pairs*Dqk (its S/dP
-    recomputation is not algorithmic work). delta pass: bytes of O and dO read
+    recomputation is not algorithmic work). Two-phase backward: scores S and
+    dP, 2*pairs*(Dqk+Dv); products dV and dK, 2*pairs*(Dqk+Dv); dQ,
+    2*pairs*Dqk. delta pass: bytes of O and dO read
     plus delta written. Merge: bytes of both inputs read and the output written."""
     pairs = w.pairs()
     rows = w.T if w.kind == "varlen" else (w.shard if w.kind == "ring" else w.B * w.Nq)
@@ -157,6 +159,13 @@ def kernel_work(w: "workloads.Workload", name: str):
     if name == "attn_bwd_dkdv":
         return "mfma", 2 * pairs * (2 * w.Dqk + 2 * w.Dv) / chunks, "FLOP"
     if name == "attn_bwd_dq":
+        return "mfma", 2 * pairs * w.Dqk / chunks, "FLOP"
+    # two-phase backward (large head dims): scores S and dP, then products
+    if name == "attn_bwd_scores":
+        return "mfma", 2 * pairs * (w.Dqk + w.Dv) / chunks, "FLOP"
+    if name == "attn_bwd_dkdv_tiles":
+        return "mfma", 2 * pairs * (w.Dqk + w.Dv) / chunks, "FLOP"
+    if name == "attn_bwd_dq_tiles":
         return "mfma", 2 * pairs * w.Dqk / chunks, "FLOP"
     if name == "attn_bwd_delta":
         return "hbm", rows * w.Hq * (2 * w.Dv * 2 + 4), "B"
@@ -177,9 +186,69 @@ def roofline(w: "workloads.Workload", kernels: dict) -> dict:
         achieved = units / sec / 1e9
         peak, u = PEAK_HBM_GBS, "GB/s"
     return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": round(peak, 1),
-            "unit": u, "frac": round(achieved / peak, 4), "traffic": None,
+            "unit": u, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(name, w.name),
             "launch_ms": round(kernels[name]["mean_ms"], 4),
-            "per_unit": "2*pairs*(2*Dqk+2*Dv) FLOP" if name == "attn_bwd_dkdv" else unit}
+            "per_unit": PER_UNIT.get(name, unit)}
+
+
+PER_UNIT = {
+    "attn_fwd": "2*pairs*(Dqk+Dv) FLOP",
+    "attn_bwd_dkdv": "2*pairs*(2*Dqk+2*Dv) FLOP",
+    "attn_bwd_dq": "2*pairs*Dqk FLOP",
+    "attn_bwd_scores": "2*pairs*(Dqk+Dv) FLOP",
+    "attn_bwd_dkdv_tiles": "2*pairs*(Dqk+Dv) FLOP",
+    "attn_bwd_dq_tiles": "2*pairs*Dqk FLOP",
+}
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.md")
+
+
+def sources_digest() -> str:
+    """sha256 over the library's kernel sources: counter figures taken from an
+    older build stop applying as soon as any of them changes."""
+    import hashlib
+    csrc = os.path.join(HERE, "varlen_causal_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy),
+    or None when there is none for the current sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = sources_digest()
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if not line.startswith("kernel="):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split())
+            if kv.get("kernel") == kernel and kv.get("workload") == workload \
+                    and kv.get("sources") == want:
+                return float(kv["bytes"])
+    return None
+
+
+def copy_calibration(gib: int = 1) -> None:
+    """A plain elementwise copy of known size (reads and writes `gib` GiB),
+    the reference the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "dispatches": 3}), flush=True)
 
 
 def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
@@ -229,6 +298,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--all", action="store_true", help="also report every workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB elementwise copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -238,6 +309,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     m = measure(args.workload, args.steps, args.warmup)
     w = workloads.workload(args.workload)
     fwd_tf = m["fwd_tflops"]

@@ -20,8 +20,8 @@ LIB = os.path.join(HERE, "libvca_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_merge.hip",
-               "attn_api.hip", "attn_timing.hip"]
+HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_bwd_roles.hip",
+               "attn_merge.hip", "attn_api.hip", "attn_timing.hip"]
 CXX_SOURCES = ["attn_segments.cpp"]
 # -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in VGPRs. The kernels keep
 # their working set under the unified register budget; left to choose, the
@@ -29,14 +29,16 @@ CXX_SOURCES = ["attn_segments.cpp"]
 # per loop iteration between the two register files.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-command-line-argument", "-Wno-unused-result"]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_SOURCES: set = set()
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    form = [] if src in AGPR_SOURCES else VGPR_FORM
+    cmd = [HIPCC, *COMMON, *form, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)

@@ -53,6 +53,7 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
     TimedLaunch timer("attn_schedule", st);
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
   }
+  a.lse2 = reinterpret_cast<float*>(w + wl.lse2);
   a.items_q = list_q;
   a.count_q = counts;
   a.items_k = list_k;
@@ -83,7 +84,10 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   if (k_rows > 0) {
     TimedLaunch timer("attn_bwd_dkdv", st);
     const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
-    if constexpr (kPipe) {
+    if constexpr (kPipe && DQK == 128) {
+      const hipError_t e = launch_dkdv_roles(a, causal, g.x, st);
+      if (e != hipSuccess) return e;
+    } else if constexpr (kPipe) {
       if (causal)
         hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, true>), g, dim3(256), 0, st, a);
       else

@@ -28,6 +28,7 @@ struct BwdArgs {
   ViewW dq, dk, dv;
   const float* lse;
   float* delta;            // workspace, same indexing as lse
+  float* lse2;             // workspace: lse * log2(e), same indexing
   int64_t lse_sb, lse_sh;  // index = b*lse_sb + h*lse_sh + (q_row0 + i)
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -78,7 +79,11 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (ok && li == 0) a.delta[s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row] = acc;
+  if (ok && li == 0) {
+    const int64_t idx = s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row;
+    a.delta[idx] = acc;
+    a.lse2[idx] = a.lse[idx] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,434 @@
+// dK / dV pass for head dim 128 (Dqk = Dv = 128) with split wave roles
+// (NeMo-Automodel "ffpa_attention" page, dense and varlen backward entries;
+// same quantities as the other backward kernels):
+//
+//   P  = exp(scale * Q K^T - lse),  dV += P^T dO
+//   dS = P * (dO V^T - delta),      dK += scale * dS^T Q
+//
+// One workgroup = (segment, kv-head, 128 keys): two wave pairs of 64 keys.
+// In a pair, wave A computes S -> P -> dV and wave B computes dP -> dS -> dK;
+// A hands P to B through LDS. Each wave keeps its 64 keys' K (A) or V (B)
+// rows in registers as MFMA operands for the whole kernel, and its 64 x 128
+// dV (A) or dK (B) accumulators in the accumulation registers. So a Q or dO
+// fragment read from LDS feeds two MFMAs (one per 32-key half), half the LDS
+// traffic per MFMA of one wave doing all four products for 32 keys.
+//
+// The workgroup walks every (q-head of the GQA group, 32-query step) that
+// can see its keys. Q, dO, lse*log2(e) and delta of a step are loaded
+// straight from global memory into LDS three steps ahead (six stages). Each
+// iteration issues 32 MFMAs per wave, one VALU element of the softmax work
+// after each: wave A runs S of step i+1 and dV of step i-1 while it computes
+// P of step i (exp of S of step i); wave B runs dP of step i and dK of step
+// i-2 while it computes dS of step i-1 (P of step i-1 arrives from A across
+// the iteration's single barrier). The matrix pipe and the VALU stay busy
+// together instead of taking turns.
+#pragma once
+
+#include "attn_bwd.hpp"
+
+namespace vca {
+
+constexpr int kRD = 128;              // head dim
+constexpr int kRBQ = 32;              // queries per step
+constexpr int kRKP = 64;              // keys per wave pair
+constexpr int kRBK = 2 * kRKP;        // keys per workgroup
+constexpr int kRStages = 6;           // Q/dO/lse/delta stages in LDS
+constexpr int kRTile = kRBQ * kRD;    // elements of one staged Q or dO tile (8 KB)
+
+// Staged tiles are row-major with 256-byte rows; the 16-byte piece u of row r
+// sits at position u ^ (4*(r%4) + (r/4)%4). A row read (ds_read_b128, 16
+// consecutive rows per LDS cycle) then covers all 16 piece positions, and a
+// transposing read (4 consecutive rows x 64 bytes per 32 lanes) covers all 16
+// as well: both are free of bank conflicts.
+__device__ __forceinline__ int rtile_off(int r, int u) {
+  return r * kRD + ((u ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3);
+}
+// A operand of S / dP: lane l gets row l%32 and the 8 head-dim elements of
+// piece `piece` (= 2*ks + l/32).
+__device__ __forceinline__ bf16x8 rtile_row(const uint16_t* X, int r, int piece) {
+  return lds_frag(X + rtile_off(r, piece));
+}
+// A operand of dV^T / dK^T: lane l gets head-dim column n0 + l%32 and query
+// rows {k0 + 4h + j, k0 + 8 + 4h + j : j < 4} (h = l/32) through the
+// transposing read; the row order matches a 32x32 C tile reused as B.
+__device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, int lane) {
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
+  const int row = k0 + 4 * h + (s >> 2);
+  const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint16_t* p0 = X + rtile_off(row, c >> 3) + (c & 7);
+  const uint16_t* p1 = X + rtile_off(row + 8, c >> 3) + (c & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// gfx950 direct global -> LDS load of one dword per lane (lane l's 4 bytes
+// land at lds_base + 4*l); same contract as dma16.
+__device__ __forceinline__ void dma4(const float* g, lds_void* lds_base) {
+  uint32_t saved;
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m0)
+      : "memory");
+}
+
+// Every MFMA of this kernel is written out, so operands can sit in the
+// accumulation registers (AGPRs): the K/V fragments (B operands of S / dP)
+// and the 64x128 dV/dK accumulators live there, leaving the VGPRs to the
+// score tiles, staged fragments and softmax. The compiler does not see these
+// as MFMAs, so they carry their own wait states: mfma_a's s_nop gives the 2 a
+// VALU write of an A/B operand needs before the MFMA reads it (back-to-back
+// MFMAs on one accumulator need none), and mfma_results_ready() waits out an
+// MFMA before anything else reads or overwrites its result or C operand.
+// S / dP: A from an LDS read, B from AGPRs (no VALU-written operand, so no
+// wait states); C starts at zero (mfma_v0) or accumulates (mfma_v).
+__device__ __forceinline__ void mfma_v0(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_a(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Orders the wait after the MFMAs that produced `x` (an asm with x as an
+// in/out operand cannot move above them).
+__device__ __forceinline__ void mfma_results_ready(f32x16& x0, f32x16& x1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
+}
+// The accumulators are in/out operands, so their reads stay below the wait.
+__device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]),
+                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[3][0]), "+a"(acc[3][1]));
+}
+// Move a value into AGPRs at its definition, so the loop-carried value is
+// allocated there (instead of living in VGPRs and being copied around every
+// MFMA that takes it from an AGPR).
+__device__ __forceinline__ f32x16 in_agprs(f32x16 x) {
+  f32x16 r;
+  asm volatile("; in agprs" : "=a"(r) : "0"(x));
+  return r;
+}
+__device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
+  bf16x8 r;
+  asm volatile("; in agprs" : "=a"(r) : "0"(x));
+  return r;
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdArgs a) {
+  constexpr int NKS = kRD / 16;  // contraction steps of S / dP
+  constexpr int NDB = kRD / 32;  // 32-wide head-dim blocks of dV / dK
+  constexpr int NDMA = 5;        // hand-issued loads per wave per step
+  constexpr int NS = kRStages;
+  __shared__ __attribute__((aligned(1024))) uint16_t sq[NS][kRTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdo[NS][kRTile];
+  __shared__ __attribute__((aligned(256))) float sld[NS][2 * kRBQ];  // lse*log2e | delta
+  __shared__ __attribute__((aligned(16))) u32x4 sp[2][2][2][2][64];  // [parity][pair][kt][j][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, h = lane >> 5;
+  const int pair = w >> 1, role = w & 1;  // role 0: S, P, dV; role 1: dP, dS, dK
+  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  if (item >= *a.count_k) return;
+  const int2 st = a.items_k[item];
+  const int s = st.x;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int kb0 = st.y * kRBK;
+  if (kb0 >= sg.lk) return;
+  const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
+  const int kp0 = kb0 + pair * kRKP;  // first key of this wave pair
+
+  int q_begin = 0;
+  if (CAUSAL) q_begin = max(0, kb0 - shift);
+  q_begin &= ~(kRBQ - 1);
+  const int nq = lq > q_begin ? (lq - q_begin + kRBQ - 1) / kRBQ : 0;
+  const int total = a.G * nq;
+
+  // this wave's K (role 0) or V (role 1) rows as B fragments (kept in AGPRs):
+  // kf[kt][ks] = row kp0 + 32*kt + l%32, head-dim elements 16*ks + 8*h ..+7
+  bf16x8 kf[2][NKS];
+  {
+    // field-wise selects (a runtime select of a whole View goes to scratch)
+    const uint16_t* base = (role == 0 ? a.k.p : a.v.p) + s * (role == 0 ? a.k.sb : a.v.sb) +
+                           (int64_t)sg.k_row0 * (role == 0 ? a.k.sn : a.v.sn) +
+                           g * (role == 0 ? a.k.sh : a.v.sh);
+    const int64_t sn = role == 0 ? a.k.sn : a.v.sn;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = min(kp0 + 32 * kt + col, lk - 1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        kf[kt][ks] = in_agprs(as_frag(ldg16(base + key * sn + 16 * ks + 8 * h)));
+    }
+  }
+  // The lagging products of the first iterations read Q of "steps" -2 and -1
+  // (stages NS-2, NS-1), dO and delta of step -1 and P parity 1 before any
+  // load reaches them: those must hold zeros, not stale bits (stage NS-2's
+  // first load is issued after the first barrier).
+  {
+    const u32x4 z = zero_u32x4();
+    u32x4* q4 = reinterpret_cast<u32x4*>(&sq[NS - 2][0]);
+    for (int i = tid; i < 2 * kRTile / 8; i += 256) q4[i] = z;
+    u32x4* d4 = reinterpret_cast<u32x4*>(&sdo[NS - 1][0]);
+    for (int i = tid; i < kRTile / 8; i += 256) d4[i] = z;
+    if (tid < 2 * kRBQ) sld[NS - 1][tid] = 0.f;
+    u32x4* p1 = &sp[1][0][0][0][0];
+    for (int i = tid; i < 2 * 2 * 2 * 64; i += 256) p1[i] = z;
+  }
+  wait_global_loads();
+
+  // step it -> (q-head, first query); stage of step it (it >= -2)
+  auto step_head = [&](int it) { return g * a.G + it / nq; };
+  auto step_q0 = [&](int it) { return q_begin + (it % nq) * kRBQ; };
+  auto stage = [](int it) { return (it + NS) % NS; };
+  // Hand-issued loads of step it: 2 of the Q tile's 8 four-row slices, 2 of
+  // dO's, and 16 of the 64 lse*log2(e) | delta values. Lane l of slice j
+  // loads row 4j + l/16, stored piece l%16 (global piece l%16 ^ swizzle).
+  int srow[2], spiece[2];
+  int64_t qoff[2], doff[2];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2) {
+    const int r = 4 * (2 * w + j2) + (lane >> 4);
+    srow[j2] = r;
+    spiece[j2] = ((lane & 15) ^ (((r & 3) << 2) | ((r >> 2) & 3))) * 8;
+    qoff[j2] = (int64_t)r * a.q.sn + spiece[j2];
+    doff[j2] = (int64_t)r * a.dout.sn + spiece[j2];
+  }
+  const float* ldsrc = (w < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + 16 * (w & 1) + lane;
+  auto issue = [&](int it) {
+    const int b = stage(it);
+    const int hh = step_head(it), q0 = step_q0(it);
+    const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + hh * a.q.sh;
+    const uint16_t* db = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + hh * a.dout.sh;
+    if (q0 + kRBQ <= lq) {
+      const uint16_t* qs = qb + (int64_t)q0 * a.q.sn;
+      const uint16_t* ds = db + (int64_t)q0 * a.dout.sn;
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        dma16(qs + qoff[j2], lds_ptr(&sq[b][(2 * w + j2) * 512]));
+        dma16(ds + doff[j2], lds_ptr(&sdo[b][(2 * w + j2) * 512]));
+      }
+      if (lane < 16) dma4(ldsrc + hh * a.lse_sh + q0, lds_ptr(&sld[b][16 * w]));
+    } else {
+      // last step of the segment: rows past its end re-read its last row
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int qi = min(q0 + srow[j2], lq - 1);
+        dma16(qb + (int64_t)qi * a.q.sn + spiece[j2], lds_ptr(&sq[b][(2 * w + j2) * 512]));
+        dma16(db + (int64_t)qi * a.dout.sn + spiece[j2], lds_ptr(&sdo[b][(2 * w + j2) * 512]));
+      }
+      if (lane < 16) {
+        const int qi = min(q0 + 16 * (w & 1) + lane, lq - 1) - (16 * (w & 1) + lane);
+        dma4(ldsrc + hh * a.lse_sh + qi, lds_ptr(&sld[b][16 * w]));
+      }
+    }
+  };
+
+  f32x16 acc[NDB][2];  // dV^T (role 0) or dK^T (role 1): [head-dim block][key half]
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    acc[d][0] = in_agprs(zero16());
+    acc[d][1] = in_agprs(zero16());
+  }
+  // P (role 0) or dS (role 1) fragments [kt][j] of two consecutive steps
+  bf16x8 tf0[2][2], tf1[2][2];
+  // score tiles S (role 0) or dP (role 1) of two consecutive steps
+  f32x16 sc0[2], sc1[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    sc0[kt] = zero16();
+    sc1[kt] = zero16();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      tf0[kt][j] = as_frag(zero_u32x4());
+      tf1[kt][j] = as_frag(zero_u32x4());
+    }
+  }
+
+  // One iteration's 32 MFMAs: 16 of a score tile out = Xs K^T (8 head-dim
+  // steps x 2 key halves) and 16 of the product acc += Xp^T T (4 head-dim
+  // blocks x 2 query halves x 2 key halves), alternating, each followed by
+  // one VALU element valu(e), e = 0..31. Fragments are read two MFMA pairs
+  // ahead; sched_barrier pins the interleave.
+  auto pipe = [&](const uint16_t* Xs, f32x16 (&out)[2], const uint16_t* Xp,
+                  const bf16x8 (&T)[2][2], auto&& valu) {
+    bf16x8 af[NKS];
+    bf16x8 cf[2 * NDB];
+    af[0] = rtile_row(Xs, col, h);
+    af[1] = rtile_row(Xs, col, 2 + h);
+    cf[0] = rtile_col(Xp, 0, 0, lane);
+    cf[1] = rtile_col(Xp, 16, 0, lane);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int ks = c >> 1, kt = c & 1, f = c >> 1;  // f = 2*d + j
+      if (kt == 0 && ks + 2 < NKS) af[ks + 2] = rtile_row(Xs, col, 2 * (ks + 2) + h);
+      if (kt == 0 && f + 2 < 2 * NDB)
+        cf[f + 2] = rtile_col(Xp, 16 * ((f + 2) & 1), 32 * ((f + 2) >> 1), lane);
+      if (ks == 0) mfma_v0(out[kt], af[0], kf[kt][0]);
+      else mfma_v(out[kt], af[ks], kf[kt][ks]);
+      valu(2 * c);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_a(acc[f >> 1][kt], cf[f], T[kt][f & 1]);
+      valu(2 * c + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Role 0, iteration i: S of step i+1 (into nxt) and dV of step i-1 (Pold),
+  // with P of step i from cur (into Pnew, and to role 1 through LDS).
+  auto step_a = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Pold)[2][2],
+                    bf16x8 (&Pnew)[2][2]) {
+    const int q0 = step_q0(i);
+    float l2[16];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][8 * rr + 4 * h]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l2[4 * rr + c] = v[c];
+    }
+    float p[2][16];
+    const uint16_t* Xs = sq[stage(i + 1)];  // stale past the last step: unused
+    const uint16_t* Xp = sdo[stage(i - 1)];
+    pipe(Xs, nxt, Xp, Pold, [&](int e) {
+      const int kt = e >> 4, r = e & 15;
+      p[kt][r] = fast_exp2(cur[kt][r] * a.scale_log2 - l2[r]);
+    });
+    // diagonal blocks and segment tails (a few steps per key block): zero
+    // what the mask hides (a select: hidden entries may be inf, e.g. on rows
+    // with lse = -inf)
+    if (q0 + kRBQ > lq || (CAUSAL && kp0 + kRKP - 1 > q0 + shift)) {
+      const int qh = q0 + 4 * h;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int kmin = kp0 + 32 * kt + col - shift;  // first query that sees the key
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qh + 8 * (r >> 2) + (r & 3);
+          bool vis = qi < lq;
+          if (CAUSAL) vis = vis && qi >= kmin;
+          p[kt][r] = vis ? p[kt][r] : 0.f;
+        }
+      }
+    }
+    const int par = i & 1;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        Pnew[kt][j] = to_frag(&p[kt][8 * j]);
+        sp[par][pair][kt][j][lane] = __builtin_bit_cast(u32x4, Pnew[kt][j]);
+      }
+  };
+  // Role 1, iteration i: dP of step i (into nxt) and dK of step i-2 (Dold),
+  // with dS of step i-1 from cur and role 0's P (into Dnew).
+  auto step_b = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Dold)[2][2],
+                    bf16x8 (&Dnew)[2][2]) {
+    float dl[16];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][kRBQ + 8 * rr + 4 * h]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dl[4 * rr + c] = v[c];
+    }
+    const int par = (i + 1) & 1;  // parity of step i-1
+    u32x4 pv[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) pv[kt][j] = sp[par][pair][kt][j][lane];
+    float d[2][16];
+    pipe(sdo[stage(i)], nxt, sq[stage(i - 2)], Dold, [&](int e) {
+      const int kt = e >> 4, r = e & 15;
+      const uint32_t wv = pv[kt][r >> 3][(r & 7) >> 1];
+      const float pe = __uint_as_float(r & 1 ? (wv & 0xffff0000u) : (wv << 16));
+      d[kt][r] = pe * (cur[kt][r] - dl[r]);
+    });
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) Dnew[kt][j] = to_frag(&d[kt][8 * j]);
+  };
+
+  // Prologue: steps 0..2 in flight; role 0 computes S of step 0.
+  if (total > 0) issue(0);
+  if (total > 1) issue(1);
+  if (total > 2) issue(2);
+  if (total > 2) wait_vmcnt<2 * NDMA>();
+  else if (total > 1) wait_vmcnt<NDMA>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  if (role == 0 && total > 0) {
+    bf16x8 af[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) af[ks] = rtile_row(sq[0], col, 2 * ks + h);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      mfma_v0(sc0[kt], af[0], kf[kt][0]);
+#pragma unroll
+      for (int ks = 1; ks < NKS; ++ks) mfma_v(sc0[kt], af[ks], kf[kt][ks]);
+    }
+    mfma_results_ready(sc0[0], sc0[1]);
+  }
+  // Iteration i (0..total+1): wait for step i+1's loads, one barrier, issue
+  // step i+3's. Role 0 works for i <= total (its dV lags one step), role 1
+  // for every i (its dK lags two). Tiles and fragments of consecutive steps
+  // alternate between the 0 and 1 copies. Each role runs its own copy of the
+  // loop (same barriers), so values hoisted out of one role's loop do not
+  // stay live in the other's.
+  auto run = [&](auto&& body) {
+    auto iteration = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
+                         bf16x8 (&Tnew)[2][2]) {
+      if (i + 2 < total) wait_vmcnt<NDMA>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (i + 3 < total) issue(i + 3);
+      body(i, cur, nxt, Told, Tnew);
+    };
+    for (int i = 0; i <= total + 1; i += 2) {
+      iteration(i, sc0, sc1, tf0, tf1);
+      if (i + 1 <= total + 1) iteration(i + 1, sc1, sc0, tf1, tf0);
+    }
+  };
+  if (role == 0)
+    run([&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
+            bf16x8 (&Tnew)[2][2]) {
+      if (i <= total) step_a(i, cur, nxt, Told, Tnew);
+    });
+  else
+    run([&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
+            bf16x8 (&Tnew)[2][2]) { step_b(i, cur, nxt, Told, Tnew); });
+
+  // dV (role 0) or dK * scale (role 1) of keys kp0 + 32*kt + l%32
+  agpr_results_ready(acc);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kp0 + 32 * kt + col;
+    if (key >= lk) continue;
+    const int64_t r = sg.k_row0 + key;
+    const float mul = role == 0 ? 1.f : a.scale;
+    uint16_t* out = role == 0 ? a.dv.p + s * a.dv.sb + r * a.dv.sn + g * a.dv.sh
+                              : a.dk.p + s * a.dk.sb + r * a.dk.sn + g * a.dk.sh;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(acc[d][kt][4 * rr + c] * mul);
+        *reinterpret_cast<bf16x4*>(out + 32 * d + 8 * rr + 4 * h) = v4;
+      }
+  }
+}
+
+}  // namespace vca

@@ -39,8 +39,9 @@ inline size_t fwd_workspace_bytes(int64_t q_rows, int nseg) {
   return 256 + align256(sizeof(int2) * list_capacity(q_rows, nseg));
 }
 // Backward workspace: [delta fp32, one per (q-head, query row)][counts]
-// [query list][key list], then for the two-phase backward the P and dS block
-// stores (bf16, 256x256 per (row slot, key block, q-head)).
+// [query list][key list][lse*log2(e), like delta], then for the two-phase
+// backward the P and dS block stores (bf16, 256x256 per (row slot, key block,
+// q-head)).
 constexpr int kBlockRows = 256;
 struct TileGeom {
   int64_t slots;  // 256-query row slots
@@ -59,7 +60,7 @@ inline bool bwd_uses_tiles(int dqk, int dv) {
   return (dqk == dv && (dqk == 256 || dqk == 512)) || (dqk == 192 && dv == 128);
 }
 struct BwdWorkspace {
-  size_t list_q, list_k, tile_p, tile_ds, total;
+  size_t list_q, list_k, lse2, tile_p, tile_ds, total;
 };
 inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64_t k_rows, int nseg,
                                   const TileGeom& tg) {
@@ -67,7 +68,8 @@ inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64
   const size_t delta = align256(sizeof(float) * (size_t)Hq * (size_t)q_rows);
   w.list_q = delta + 256;
   w.list_k = w.list_q + align256(sizeof(int2) * list_capacity(q_rows, nseg));
-  w.tile_p = w.list_k + align256(sizeof(int2) * list_capacity(k_rows, nseg));
+  w.lse2 = w.list_k + align256(sizeof(int2) * list_capacity(k_rows, nseg));
+  w.tile_p = w.lse2 + delta;
   w.tile_ds = w.tile_p;
   if (bwd_uses_tiles(dqk, dv)) {
     const size_t blocks = sizeof(uint16_t) * kBlockRows * kBlockRows * (size_t)tg.slots *
@@ -98,6 +100,10 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
 void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                  int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
                  int k_tile, int k_step, void* ws, hipStream_t st);
+
+// dK/dV pass of head dim 128 with split wave roles (attn_bwd_roles.hip);
+// grid = (128-key blocks + segments) * Hkv.
+hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
 
 // Two-phase backward (the head-dim pairs bwd_uses_tiles names): lists,
 // delta, scores, products.

@@ -31,14 +31,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument", "-Wno-unused-result"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-AGPR_SOURCES: set = set()
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    form = [] if src in AGPR_SOURCES else VGPR_FORM
-    cmd = [HIPCC, *COMMON, *form, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *VGPR_FORM, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)

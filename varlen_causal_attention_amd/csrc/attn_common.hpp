@@ -177,8 +177,22 @@ struct TileStage {
   // Branch-free variant: rows past the end re-read row nrows - 1 (nrows >= 1),
   // which stays inside the segment; callers mask those rows out of every
   // result (their scores are hidden / their P is zero).
+  // Head dims up to 128: a tile wholly inside the rows (every tile but a
+  // segment's last) takes the scalar tile base plus a per-thread offset that
+  // does not depend on the tile, so the compiler keeps it out of the loop.
+  // (Wider tiles keep the plain form: the hoisted offsets cost registers
+  // their kernels do not have.)
   __device__ __forceinline__ void load_clamped(const uint16_t* base, int64_t sn, int row0,
                                                int nrows, int tid) {
+    if (D <= 128 && row0 + R <= nrows) {
+      const uint16_t* b = base + (int64_t)row0 * sn;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int c = min(tid + i * NT, CH - 1);
+        r[i] = ldg16(b + (int64_t)(c / (D / 8)) * sn + (c % (D / 8)) * 8);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int c = min(tid + i * NT, CH - 1);

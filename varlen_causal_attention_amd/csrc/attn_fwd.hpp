@@ -72,7 +72,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int qg = w / DS, ds = w % DS;
   const int col = lane & 31, half = lane >> 5;
   const int item = blockIdx.x / a.H, h = blockIdx.x - item * a.H, kvh = h / a.G;

@@ -335,7 +335,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
   __shared__ __attribute__((aligned(16))) float slse[2][BQ];  // -lse * log2(e) / (scale*log2(e))
   __shared__ __attribute__((aligned(16))) float sdel[2][BQ];  // -delta
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
   const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
   if (item >= *a.count_k) return;
@@ -507,7 +508,8 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * NKB * 16 * 64 : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
   const int qg = w / DS, ds = w % DS;
   const int item = blockIdx.x / a.Hq, h = blockIdx.x - item * a.Hq, g = h / a.G;

@@ -245,6 +245,40 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* X, int LS, int k0, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---- swizzled 128-wide tiles ---------------------------------------------
+// Rows of kTileD = 128 bf16 elements (256 bytes), loaded straight into LDS
+// by global_load_lds, four rows per 1 KB load (lane l: row 4j + l/16, stored
+// piece l%16).
+constexpr int kTileD = 128;
+// Staged tiles are row-major with 256-byte rows; the 16-byte piece u of row r
+// sits at position u ^ (4*(r%4) + (r/4)%4). A row read (ds_read_b128, 16
+// consecutive rows per LDS cycle) then covers all 16 piece positions, and a
+// transposing read (4 consecutive rows x 64 bytes per 32 lanes) covers all 16
+// as well: both are free of bank conflicts.
+__device__ __forceinline__ int rtile_off(int r, int u) {
+  return r * kTileD + ((u ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 3);
+}
+// A operand of S / dP: lane l gets row l%32 and the 8 head-dim elements of
+// piece `piece` (= 2*ks + l/32).
+__device__ __forceinline__ bf16x8 rtile_row(const uint16_t* X, int r, int piece) {
+  return lds_frag(X + rtile_off(r, piece));
+}
+// A operand of dV^T / dK^T: lane l gets head-dim column n0 + l%32 and query
+// rows {k0 + 4h + j, k0 + 8 + 4h + j : j < 4} (h = l/32) through the
+// transposing read; the row order matches a 32x32 C tile reused as B.
+__device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, int lane) {
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
+  const int row = k0 + 4 * h + (s >> 2);
+  const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint16_t* p0 = X + rtile_off(row, c >> 3) + (c & 7);
+  const uint16_t* p1 = X + rtile_off(row + 8, c >> 3) + (c & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Segment geometry: query rows [q_row0, q_row0 + lq) and key rows
 // [k_row0, k_row0 + lk) of the packed tensors. cu arrays are clamped into
 // [0, T] so a malformed table can never index outside the tensors.

@@ -67,8 +67,13 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   constexpr int NKB = BN / 32;
   constexpr int NDB = VR / 32;
   constexpr int NKS = DR / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
+  // Head dim 128 (one wave per 32-row block, 64-key tiles, two buffers): K
+  // and V tiles go straight from global memory into LDS (global_load_lds),
+  // 256-byte rows in the swizzled layout of rtile_off, one tile ahead;
+  // no staging through registers and no LDS stores.
+  constexpr bool DMA = DQK == kTileD && DV == kTileD && DS == 1 && NBUF == 2 && BN == 64;
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * kTileD : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * kTileD : BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -105,11 +110,41 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   }
   wait_global_loads();
 
+  // DMA: wave w loads K and V rows 16w..16w+15 of a tile (4 loads each):
+  // load jj covers rows 16w + 4jj + l/16; stored piece l%16 of row r holds
+  // global piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ jj.
+  const int dl = lane >> 4, p0 = (lane & 15) ^ (dl << 2);
+  const int64_t kr0 = (int64_t)(16 * w + dl) * a.k.sn, vr0 = (int64_t)(16 * w + dl) * a.v.sn;
+  auto issue_kv = [&](int tt) {
+    const int b = tt & 1, kt0 = tt * BN;
+    if (kt0 + BN <= lk) {
+      const uint16_t* kt = kb + (int64_t)kt0 * a.k.sn + kr0;
+      const uint16_t* vt = vb + (int64_t)kt0 * a.v.sn + vr0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int pc = (p0 ^ jj) * 8;
+        dma16(kt + (int64_t)(4 * jj) * a.k.sn + pc, lds_ptr(&sk[b][(4 * w + jj) * 512]));
+        dma16(vt + (int64_t)(4 * jj) * a.v.sn + pc, lds_ptr(&sv[b][(4 * w + jj) * 512]));
+      }
+    } else {
+      // the segment's last tile: rows past its end re-read its last row
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rr = min(kt0 + 16 * w + 4 * jj + dl, lk - 1);
+        const int pc = (p0 ^ jj) * 8;
+        dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][(4 * w + jj) * 512]));
+        dma16(vb + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][(4 * w + jj) * 512]));
+      }
+    }
+  };
+
   using KStage = TileStage<BN, DQK, NT>;
   using VStage = TileStage<BN, DV, NT>;
   KStage kst;
   VStage vst;
-  if (ntiles > 0) {
+  if constexpr (DMA) {
+    if (ntiles > 0) issue_kv(0);
+  } else if (ntiles > 0) {
     if (PF) {
       kst.load_clamped(kb, a.k.sn, 0, lk, tid);
       vst.load_clamped(vb, a.v.sn, 0, lk, tid);
@@ -135,8 +170,11 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = NBUF == 2 ? (t & 1) : 0;
+    if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
     __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
-    if (NBUF == 2 && t + 1 < ntiles) {
+    if constexpr (DMA) {
+      if (t + 1 < ntiles) issue_kv(t + 1);
+    } else if (NBUF == 2 && t + 1 < ntiles) {
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
@@ -156,7 +194,9 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int kbk = 0; kbk < NKB; ++kbk)
-          sacc[kbk] = mfma32(lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 + ks * 16]),
+          sacc[kbk] = mfma32(DMA ? rtile_row(sk[buf], kbk * 32 + col, 2 * ks + half)
+                                 : lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 +
+                                                     ks * 16]),
                              qf[ks], sacc[kbk]);
       pipeline_mfma_reads<NKS * NKB, 4>();
     }
@@ -231,7 +271,9 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          o[db] = mfma32(tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane), pf[kk], o[db]);
+          o[db] = mfma32(DMA ? rtile_col(sv[buf], kk * 16, db * 32, lane)
+                             : tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane),
+                         pf[kk], o[db]);
       pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
     }
     if (NBUF == 1 && t + 1 < ntiles) {

@@ -504,8 +504,12 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   // 32 bytes mod 256 is the compromise (2-way on the row reads, none on the
   // transposing reads); V is only read row-wise (16 bytes mod 256).
   constexpr int KS = DQK + 16, VS = DV + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF][BN * VS];
+  // Head dim 128 (DS 1, 32-key tiles, two buffers): K and V tiles go straight
+  // from global memory into LDS (global_load_lds) in the swizzled layout of
+  // rtile_off, one tile ahead, instead of through registers.
+  constexpr bool DMA = DQK == kTileD && DV == kTileD && DS == 1 && NBUF == 2 && BN == 32 && NW == 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * kTileD : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * kTileD : BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -551,11 +555,28 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   }
   wait_global_loads();
 
+  // DMA: wave w loads K and V rows 8w..8w+7 of a tile (2 loads each): load
+  // jj covers rows 8w + 4jj + l/16; stored piece l%16 of row r holds global
+  // piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ ((2w + jj) % 4).
+  const int dl4 = lane >> 4, p0 = (lane & 15) ^ (dl4 << 2);
+  auto issue_kv = [&](int tt) {
+    const int b = tt & 1, kt0 = tt * BN;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int rr = min(kt0 + 8 * w + 4 * jj + dl4, lk - 1);  // past the end: its last row
+      const int pc = (p0 ^ ((2 * w + jj) & 3)) * 8;
+      dma16(kbp + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][(2 * w + jj) * 512]));
+      dma16(vbp + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][(2 * w + jj) * 512]));
+    }
+  };
+
   using KStage = TileStage<BN, DQK, NT>;
   using VStage = TileStage<BN, DV, NT>;
   KStage kst;
   VStage vst;
-  if (ntiles > 0) {
+  if constexpr (DMA) {
+    if (ntiles > 0) issue_kv(0);
+  } else if (ntiles > 0) {
     if (PF) {
       kst.load_clamped(kbp, a.k.sn, 0, lk, tid);
       vst.load_clamped(vbp, a.v.sn, 0, lk, tid);
@@ -579,8 +600,11 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = NBUF == 2 ? (t & 1) : 0;
+    if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
     __syncthreads();
-    if (NBUF == 2 && t + 1 < ntiles) {
+    if constexpr (DMA) {
+      if (t + 1 < ntiles) issue_kv(t + 1);
+    } else if (NBUF == 2 && t + 1 < ntiles) {
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
@@ -601,13 +625,17 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
       for (int i = 0; i < NKS; ++i)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          sacc[kb] = mfma32(lds_frag(&sk[buf][(kb * 32 + col) * KS + ds * DR + half * 8 + i * 16]),
+          sacc[kb] = mfma32(DMA ? rtile_row(sk[buf], kb * 32 + col, 2 * i + half)
+                                : lds_frag(&sk[buf][(kb * 32 + col) * KS + ds * DR + half * 8 +
+                                                    i * 16]),
                             qf[i], sacc[kb]);
 #pragma unroll
       for (int i = 0; i < NVS; ++i)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-          pacc[kb] = mfma32(lds_frag(&sv[buf][(kb * 32 + col) * VS + ds * VR + half * 8 + i * 16]),
+          pacc[kb] = mfma32(DMA ? rtile_row(sv[buf], kb * 32 + col, 2 * i + half)
+                                : lds_frag(&sv[buf][(kb * 32 + col) * VS + ds * VR + half * 8 +
+                                                    i * 16]),
                             df[i], pacc[kb]);
       pipeline_mfma_reads<(NKS + NVS) * NKB, 4>();
     }
@@ -665,7 +693,9 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
       for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
-          dqa[b] = mfma32(tr_frag(sk[buf], KS, kk * 16, ds * DR + b * 32, lane), sf[kk], dqa[b]);
+          dqa[b] = mfma32(DMA ? rtile_col(sk[buf], kk * 16, b * 32, lane)
+                              : tr_frag(sk[buf], KS, kk * 16, ds * DR + b * 32, lane),
+                          sf[kk], dqa[b]);
       pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
     }
     if (NBUF == 1 && t + 1 < ntiles) {

@@ -4,11 +4,15 @@
 
 namespace vca {
 
+// 32-key tiles per wave: 1 -> eight waves (two per SIMD), 2 -> four
+constexpr int kRolesKT = 2;
+
 hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st) {
+  constexpr int NT = 512 / kRolesKT;
   if (causal)
-    hipLaunchKernelGGL(attn_bwd_dkdv_roles_kernel<true>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_roles_kernel<true, kRolesKT>), dim3(grid), dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_roles_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_roles_kernel<false, kRolesKT>), dim3(grid), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -74,13 +74,18 @@ __device__ __forceinline__ void mfma_a(f32x16& acc, bf16x8 a, bf16x8 b) {
 // Orders the wait after the MFMAs that produced `x` (an asm with x as an
 // in/out operand cannot move above them).
 __device__ __forceinline__ void mfma_results_ready(f32x16& x0, f32x16& x1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
+  if (&x0 == &x1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0));
+  else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
 }
 // The accumulators are in/out operands, so their reads stay below the wait.
 __device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[4][2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]),
                  "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[3][0]), "+a"(acc[3][1]));
+}
+__device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[4][1]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0][0]), "+a"(acc[1][0]), "+a"(acc[2][0]), "+a"(acc[3][0]));
 }
 // Move a value into AGPRs at its definition, so the loop-carried value is
 // allocated there (instead of living in VGPRs and being copied around every
@@ -96,16 +101,26 @@ __device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
   return r;
 }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdArgs a) {
+// KT: 32-key tiles per wave (2: four waves, one per SIMD; 1: eight waves,
+// two per SIMD, whose softmax work then overlaps the other wave's MFMAs).
+template <bool CAUSAL, int KT>
+__global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const BwdArgs a) {
   constexpr int NKS = kRD / 16;  // contraction steps of S / dP
   constexpr int NDB = kRD / 32;  // 32-wide head-dim blocks of dV / dK
-  constexpr int NDMA = 5;        // hand-issued loads per wave per step
+  constexpr int NW = 8 / KT;     // waves
+  constexpr int NT = 64 * NW;    // threads
+  constexpr int NP = NW / 2;     // wave pairs
+  constexpr int KP = 32 * KT;    // keys per pair
+  constexpr int SPW = 8 / NW;    // Q (and dO) four-row slices per wave and step
+  constexpr int NDMA = 2 * SPW + 1;  // hand-issued loads per wave per step
   constexpr int NS = kRStages;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[NS][kRTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sdo[NS][kRTile];
-  __shared__ __attribute__((aligned(256))) float sld[NS][2 * kRBQ];  // lse*log2e | delta
-  __shared__ __attribute__((aligned(16))) u32x4 sp[2][2][2][2][64];  // [parity][pair][kt][j][lane]
+  // lse*log2(e) (waves 0, 1: query rows 0-15, 16-31) | delta (waves 2, 3); a
+  // wave's load fills 64 values of which the first 16 are used (waves 4-7
+  // load stand-ins, keeping every wave's load count the same)
+  __shared__ __attribute__((aligned(256))) float sld[NS][NW][64];
+  __shared__ __attribute__((aligned(16))) u32x4 sp[2][NP][KT][2][64];  // [parity][pair][kt][j][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, h = lane >> 5;
@@ -118,7 +133,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   const int kb0 = st.y * kRBK;
   if (kb0 >= sg.lk) return;
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
-  const int kp0 = kb0 + pair * kRKP;  // first key of this wave pair
+  const int kp0 = kb0 + pair * KP;  // first key of this wave pair
 
   int q_begin = 0;
   if (CAUSAL) q_begin = max(0, kb0 - shift);
@@ -128,7 +143,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
 
   // this wave's K (role 0) or V (role 1) rows as B fragments (kept in AGPRs):
   // kf[kt][ks] = row kp0 + 32*kt + l%32, head-dim elements 16*ks + 8*h ..+7
-  bf16x8 kf[2][NKS];
+  bf16x8 kf[KT][NKS];
   {
     // field-wise selects (a runtime select of a whole View goes to scratch)
     const uint16_t* base = (role == 0 ? a.k.p : a.v.p) + s * (role == 0 ? a.k.sb : a.v.sb) +
@@ -136,7 +151,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
                            g * (role == 0 ? a.k.sh : a.v.sh);
     const int64_t sn = role == 0 ? a.k.sn : a.v.sn;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int key = min(kp0 + 32 * kt + col, lk - 1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -150,12 +165,12 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   {
     const u32x4 z = zero_u32x4();
     u32x4* q4 = reinterpret_cast<u32x4*>(&sq[NS - 2][0]);
-    for (int i = tid; i < 2 * kRTile / 8; i += 256) q4[i] = z;
+    for (int i = tid; i < 2 * kRTile / 8; i += NT) q4[i] = z;
     u32x4* d4 = reinterpret_cast<u32x4*>(&sdo[NS - 1][0]);
-    for (int i = tid; i < kRTile / 8; i += 256) d4[i] = z;
-    if (tid < 2 * kRBQ) sld[NS - 1][tid] = 0.f;
+    for (int i = tid; i < kRTile / 8; i += NT) d4[i] = z;
+    for (int i = tid; i < NW * 64; i += NT) (&sld[NS - 1][0][0])[i] = 0.f;
     u32x4* p1 = &sp[1][0][0][0][0];
-    for (int i = tid; i < 2 * 2 * 2 * 64; i += 256) p1[i] = z;
+    for (int i = tid; i < NP * KT * 2 * 64; i += NT) p1[i] = z;
   }
   wait_global_loads();
 
@@ -163,20 +178,21 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   auto step_head = [&](int it) { return g * a.G + it / nq; };
   auto step_q0 = [&](int it) { return q_begin + (it % nq) * kRBQ; };
   auto stage = [](int it) { return (it + NS) % NS; };
-  // Hand-issued loads of step it: 2 of the Q tile's 8 four-row slices, 2 of
-  // dO's, and 16 of the 64 lse*log2(e) | delta values. Lane l of slice j
+  // Hand-issued loads of step it: SPW of the Q tile's 8 four-row slices, SPW
+  // of dO's, and 16 of the 64 lse*log2(e) | delta values. Lane l of slice j
   // loads row 4j + l/16, stored piece l%16 (global piece l%16 ^ swizzle).
-  int srow[2], spiece[2];
-  int64_t qoff[2], doff[2];
+  int srow[SPW], spiece[SPW];
+  int64_t qoff[SPW], doff[SPW];
 #pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int r = 4 * (2 * w + j2) + (lane >> 4);
+  for (int j2 = 0; j2 < SPW; ++j2) {
+    const int r = 4 * (SPW * w + j2) + (lane >> 4);
     srow[j2] = r;
     spiece[j2] = ((lane & 15) ^ (((r & 3) << 2) | ((r >> 2) & 3))) * 8;
     qoff[j2] = (int64_t)r * a.q.sn + spiece[j2];
     doff[j2] = (int64_t)r * a.dout.sn + spiece[j2];
   }
-  const float* ldsrc = (w < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + 16 * (w & 1) + lane;
+  const float* ldsrc =
+      ((w & 3) < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + 16 * (w & 1) + (lane & 15);
   auto issue = [&](int it) {
     const int b = stage(it);
     const int hh = step_head(it), q0 = step_q0(it);
@@ -186,38 +202,37 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
       const uint16_t* qs = qb + (int64_t)q0 * a.q.sn;
       const uint16_t* ds = db + (int64_t)q0 * a.dout.sn;
 #pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) {
-        dma16(qs + qoff[j2], lds_ptr(&sq[b][(2 * w + j2) * 512]));
-        dma16(ds + doff[j2], lds_ptr(&sdo[b][(2 * w + j2) * 512]));
+      for (int j2 = 0; j2 < SPW; ++j2) {
+        dma16(qs + qoff[j2], lds_ptr(&sq[b][(SPW * w + j2) * 512]));
+        dma16(ds + doff[j2], lds_ptr(&sdo[b][(SPW * w + j2) * 512]));
       }
-      if (lane < 16) dma4(ldsrc + hh * a.lse_sh + q0, lds_ptr(&sld[b][16 * w]));
+      dma4(ldsrc + hh * a.lse_sh + q0, lds_ptr(&sld[b][w][0]));
     } else {
       // last step of the segment: rows past its end re-read its last row
 #pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) {
+      for (int j2 = 0; j2 < SPW; ++j2) {
         const int qi = min(q0 + srow[j2], lq - 1);
-        dma16(qb + (int64_t)qi * a.q.sn + spiece[j2], lds_ptr(&sq[b][(2 * w + j2) * 512]));
-        dma16(db + (int64_t)qi * a.dout.sn + spiece[j2], lds_ptr(&sdo[b][(2 * w + j2) * 512]));
+        dma16(qb + (int64_t)qi * a.q.sn + spiece[j2], lds_ptr(&sq[b][(SPW * w + j2) * 512]));
+        dma16(db + (int64_t)qi * a.dout.sn + spiece[j2], lds_ptr(&sdo[b][(SPW * w + j2) * 512]));
       }
-      if (lane < 16) {
-        const int qi = min(q0 + 16 * (w & 1) + lane, lq - 1) - (16 * (w & 1) + lane);
-        dma4(ldsrc + hh * a.lse_sh + qi, lds_ptr(&sld[b][16 * w]));
+      {
+        const int r = 16 * (w & 1) + (lane & 15);
+        dma4(ldsrc + hh * a.lse_sh + (min(q0 + r, lq - 1) - r), lds_ptr(&sld[b][w][0]));
       }
     }
   };
 
-  f32x16 acc[NDB][2];  // dV^T (role 0) or dK^T (role 1): [head-dim block][key half]
+  f32x16 acc[NDB][KT];  // dV^T (role 0) or dK^T (role 1): [head-dim block][key tile]
 #pragma unroll
-  for (int d = 0; d < NDB; ++d) {
-    acc[d][0] = in_agprs(zero16());
-    acc[d][1] = in_agprs(zero16());
-  }
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[d][kt] = in_agprs(zero16());
   // P (role 0) or dS (role 1) fragments [kt][j] of two consecutive steps
-  bf16x8 tf0[2][2], tf1[2][2];
+  bf16x8 tf0[KT][2], tf1[KT][2];
   // score tiles S (role 0) or dP (role 1) of two consecutive steps
-  f32x16 sc0[2], sc1[2];
+  f32x16 sc0[KT], sc1[KT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     sc0[kt] = zero16();
     sc1[kt] = zero16();
 #pragma unroll
@@ -232,8 +247,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   // blocks x 2 query halves x 2 key halves), alternating, each followed by
   // one VALU element valu(e), e = 0..31. Fragments are read two MFMA pairs
   // ahead; sched_barrier pins the interleave.
-  auto pipe = [&](const uint16_t* Xs, f32x16 (&out)[2], const uint16_t* Xp,
-                  const bf16x8 (&T)[2][2], auto&& valu) {
+  auto pipe = [&](const uint16_t* Xs, f32x16 (&out)[KT], const uint16_t* Xp,
+                  const bf16x8 (&T)[KT][2], auto&& valu) {
     bf16x8 af[NKS];
     bf16x8 cf[2 * NDB];
     af[0] = rtile_row(Xs, col, h);
@@ -241,8 +256,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
     cf[0] = rtile_col(Xp, 0, 0, lane);
     cf[1] = rtile_col(Xp, 16, 0, lane);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int ks = c >> 1, kt = c & 1, f = c >> 1;  // f = 2*d + j
+    for (int c = 0; c < 8 * KT; ++c) {
+      const int ks = c / KT, kt = c % KT, f = c / KT;  // f = 2*d + j
       if (kt == 0 && ks + 2 < NKS) af[ks + 2] = rtile_row(Xs, col, 2 * (ks + 2) + h);
       if (kt == 0 && f + 2 < 2 * NDB)
         cf[f + 2] = rtile_col(Xp, 16 * ((f + 2) & 1), 32 * ((f + 2) >> 1), lane);
@@ -258,17 +273,18 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
 
   // Role 0, iteration i: S of step i+1 (into nxt) and dV of step i-1 (Pold),
   // with P of step i from cur (into Pnew, and to role 1 through LDS).
-  auto step_a = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Pold)[2][2],
-                    bf16x8 (&Pnew)[2][2]) {
+  auto step_a = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Pold)[KT][2],
+                    bf16x8 (&Pnew)[KT][2]) {
     const int q0 = step_q0(i);
     float l2[16];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][8 * rr + 4 * h]);
+      const int qo = 8 * rr + 4 * h;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][qo >> 4][qo & 15]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) l2[4 * rr + c] = v[c];
     }
-    float p[2][16];
+    float p[KT][16];
     const uint16_t* Xs = sq[stage(i + 1)];  // stale past the last step: unused
     const uint16_t* Xp = sdo[stage(i - 1)];
     pipe(Xs, nxt, Xp, Pold, [&](int e) {
@@ -278,10 +294,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
     // diagonal blocks and segment tails (a few steps per key block): zero
     // what the mask hides (a select: hidden entries may be inf, e.g. on rows
     // with lse = -inf)
-    if (q0 + kRBQ > lq || (CAUSAL && kp0 + kRKP - 1 > q0 + shift)) {
+    if (q0 + kRBQ > lq || (CAUSAL && kp0 + KP - 1 > q0 + shift)) {
       const int qh = q0 + 4 * h;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         const int kmin = kp0 + 32 * kt + col - shift;  // first query that sees the key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -294,7 +310,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
     }
     const int par = i & 1;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         Pnew[kt][j] = to_frag(&p[kt][8 * j]);
@@ -303,22 +319,23 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   };
   // Role 1, iteration i: dP of step i (into nxt) and dK of step i-2 (Dold),
   // with dS of step i-1 from cur and role 0's P (into Dnew).
-  auto step_b = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Dold)[2][2],
-                    bf16x8 (&Dnew)[2][2]) {
+  auto step_b = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Dold)[KT][2],
+                    bf16x8 (&Dnew)[KT][2]) {
     float dl[16];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][kRBQ + 8 * rr + 4 * h]);
+      const int qo = 8 * rr + 4 * h;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][2 + (qo >> 4)][qo & 15]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) dl[4 * rr + c] = v[c];
     }
     const int par = (i + 1) & 1;  // parity of step i-1
-    u32x4 pv[2][2];
+    u32x4 pv[KT][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) pv[kt][j] = sp[par][pair][kt][j][lane];
-    float d[2][16];
+    float d[KT][16];
     pipe(sdo[stage(i)], nxt, sq[stage(i - 2)], Dold, [&](int e) {
       const int kt = e >> 4, r = e & 15;
       const uint32_t wv = pv[kt][r >> 3][(r & 7) >> 1];
@@ -326,7 +343,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
       d[kt][r] = pe * (cur[kt][r] - dl[r]);
     });
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int j = 0; j < 2; ++j) Dnew[kt][j] = to_frag(&d[kt][8 * j]);
   };
@@ -344,12 +361,12 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) af[ks] = rtile_row(sq[0], col, 2 * ks + h);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       mfma_v0(sc0[kt], af[0], kf[kt][0]);
 #pragma unroll
       for (int ks = 1; ks < NKS; ++ks) mfma_v(sc0[kt], af[ks], kf[kt][ks]);
     }
-    mfma_results_ready(sc0[0], sc0[1]);
+    mfma_results_ready(sc0[0], sc0[KT - 1]);
   }
   // Iteration i (0..total+1): wait for step i+1's loads, one barrier, issue
   // step i+3's. Role 0 works for i <= total (its dV lags one step), role 1
@@ -358,8 +375,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
   // loop (same barriers), so values hoisted out of one role's loop do not
   // stay live in the other's.
   auto run = [&](auto&& body) {
-    auto iteration = [&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
-                         bf16x8 (&Tnew)[2][2]) {
+    auto iteration = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
+                         bf16x8 (&Tnew)[KT][2]) {
       if (i + 2 < total) wait_vmcnt<NDMA>();
       else wait_vmcnt<0>();
       __syncthreads();
@@ -372,18 +389,18 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_kernel(const BwdAr
     }
   };
   if (role == 0)
-    run([&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
-            bf16x8 (&Tnew)[2][2]) {
+    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
+            bf16x8 (&Tnew)[KT][2]) {
       if (i <= total) step_a(i, cur, nxt, Told, Tnew);
     });
   else
-    run([&](int i, f32x16 (&cur)[2], f32x16 (&nxt)[2], bf16x8 (&Told)[2][2],
-            bf16x8 (&Tnew)[2][2]) { step_b(i, cur, nxt, Told, Tnew); });
+    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
+            bf16x8 (&Tnew)[KT][2]) { step_b(i, cur, nxt, Told, Tnew); });
 
   // dV (role 0) or dK * scale (role 1) of keys kp0 + 32*kt + l%32
   agpr_results_ready(acc);
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = kp0 + 32 * kt + col;
     if (key >= lk) continue;
     const int64_t r = sg.k_row0 + key;

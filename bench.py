@@ -68,6 +68,15 @@ class Problem:
             o2, l2 = v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False)
             _, self.lse, self.out = v.merge(o1, l1, o2, l2, bf16_copy=True)
 
+    def partials(self):
+        """Ring share: the two partial forward results the merge combines."""
+        v, w, t = self.vca, self.w, self.t
+        cq, ck, mq, mk = self.local
+        o1, l1 = v.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
+        cq, ck, mq, mk = self.cross
+        o2, l2 = v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False)
+        return o1, l1, o2, l2
+
     def bwd(self):
         v, w, t = self.vca, self.w, self.t
         if w.kind == "dense":
@@ -101,7 +110,42 @@ def time_stage(fn, iters: int) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def measure(n: int, steps: int, warmup: int) -> dict:
+def time_calls(fn, min_iters: int = 20, min_ms: float = 200.0, flush=None) -> dict:
+    """Per-call HIP-event times (ms) of fn: at least min_iters calls and
+    min_ms in total; flush (if given) runs between calls, outside the timed
+    events (an L2/MALL flush for the HBM-bound cases)."""
+    s = torch.cuda.current_stream()
+    times = []
+    total = 0.0
+    while len(times) < min_iters or total < min_ms:
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        t = e0.elapsed_time(e1)
+        times.append(t)
+        total += t
+        if len(times) >= 10000:
+            break
+    times.sort()
+    return {"median_ms": round(times[len(times) // 2], 4), "min_ms": round(times[0], 4),
+            "iters": len(times)}
+
+
+class L2Flush:
+    """Writes a 512 MiB scratch buffer: evicts L2 and MALL between calls."""
+
+    def __init__(self):
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1)
+
+
+def measure(n: int, steps: int, warmup: int, per_call: bool = True, flush=None) -> dict:
     p = Problem(n)
     w = p.w
     for _ in range(warmup):
@@ -117,11 +161,27 @@ def measure(n: int, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     kernels = kernel_times(p, steps)
     ff, bf = w.fwd_flops(), w.bwd_flops()
-    return dict(workload=w.name, ms_per_step=step_ms_ev, wall_ms_per_step=wall,
-                tflops_step=(ff + bf) / (step_ms_ev * 1e-3) / 1e12,
-                fwd_ms=fwd_ms, bwd_ms=bwd_ms,
-                fwd_tflops=ff / (fwd_ms * 1e-3) / 1e12, bwd_tflops=bf / (bwd_ms * 1e-3) / 1e12,
-                fwd_flops=ff, bwd_flops=bf, pairs=w.pairs(), kernels=kernels)
+    r = dict(workload=w.name, ms_per_step=step_ms_ev, wall_ms_per_step=wall,
+             tflops_step=(ff + bf) / (step_ms_ev * 1e-3) / 1e12,
+             fwd_ms=fwd_ms, bwd_ms=bwd_ms,
+             fwd_tflops=ff / (fwd_ms * 1e-3) / 1e12, bwd_tflops=bf / (bwd_ms * 1e-3) / 1e12,
+             fwd_flops=ff, bwd_flops=bf, pairs=w.pairs(), kernels=kernels)
+    if per_call:
+        # one forward call / one backward call: median and min over >= 20 calls
+        # and >= 200 ms
+        r["fwd_calls"] = time_calls(p.fwd)
+        r["bwd_calls"] = time_calls(p.bwd)
+        if w.kind == "ring":
+            # the lse merge alone (HBM-bound elementwise)
+            parts = p.partials()
+            r["merge_calls"] = time_calls(lambda: p.vca.merge(*parts, bf16_copy=True))
+            if flush is not None:
+                r["merge_calls_l2_flushed"] = time_calls(
+                    lambda: p.vca.merge(*parts, bf16_copy=True), flush=flush)
+        elif flush is not None:
+            r["fwd_calls_l2_flushed"] = time_calls(p.fwd, flush=flush)
+            r["bwd_calls_l2_flushed"] = time_calls(p.bwd, flush=flush)
+    return r
 
 
 def kernel_times(p: "Problem", steps: int) -> dict:
@@ -264,6 +324,8 @@ def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
     cu = w.cu()
     G = w.Hq // w.Hkv
     flops = 0
+    ffl = bfl = 0
+    tf = tb = 0.0
     done = []
     t0 = time.perf_counter()
     order = np.argsort(w.lengths)  # shortest documents first keeps the sample bounded
@@ -274,10 +336,16 @@ def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
             sl = lambda x, heads: x[a:b][:, heads]  # noqa: E731
             qq, kk, vv, dd = sl(t["q"], hs), sl(t["k"], [g]), sl(t["v"], [g]), sl(t["do"], hs)
             c1 = [0, b - a]
+            t1 = time.perf_counter()
             ro, rl = orc.fwd_varlen(qq, kk, vv, c1, c1, w.scale, True)
+            t2 = time.perf_counter()
             orc.bwd_varlen(dd, qq, kk, vv, ro, rl, c1, c1, w.scale, True)
+            tf += t2 - t1
+            tb += time.perf_counter() - t2
             pairs = len(hs) * workloads.causal_pairs(b - a, b - a)
-            flops += 2 * pairs * (3 * w.Dqk + 2 * w.Dv) + 2 * pairs * (w.Dqk + w.Dv)
+            ffl += 2 * pairs * (w.Dqk + w.Dv)
+            bfl += 2 * pairs * (3 * w.Dqk + 2 * w.Dv)
+            flops = ffl + bfl
             done.append((b - a, g))
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -286,8 +354,21 @@ def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
     el = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "fwd_gflops": round(ffl / tf / 1e9, 3) if tf else None,
+            "bwd_gflops": round(bfl / tb / 1e9, 3) if tb else None,
+            "fwd_s": round(tf, 3), "bwd_s": round(tb, 3), "blas": blas_name(),
             "sample": f"{w.name}: {len(done)} (document, kv-head group) slices, forward+backward in "
                       f"fp64 numpy, {el:.1f} s, BLAS threads = {cores}"}
+
+
+def blas_name() -> str:
+    """The BLAS numpy was built against (reported with the CPU baseline)."""
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version', '')}".strip()
+    except Exception:  # older numpy: no dict mode
+        return "unknown"
 
 
 def main():
@@ -333,17 +414,21 @@ def main():
                    "causal": w.causal, "pairs": m["pairs"]},
         "pct_of_peak": round(100 * m["tflops_step"] / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(m["fwd_ms"], 4), "tflops": round(fwd_tf, 2),
-                "pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2)},
+                "pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2), **m["fwd_calls"]},
         "bwd": {"ms": round(m["bwd_ms"], 4), "tflops": round(m["bwd_tflops"], 2),
-                "pct_of_peak": round(100 * m["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)},
+                "pct_of_peak": round(100 * m["bwd_tflops"] / PEAK_BF16_TFLOPS, 2),
+                **m["bwd_calls"]},
         "roofline": roofline(w, m["kernels"]),
         "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in m["kernels"].items()},
         "wall_ms_per_step": round(m["wall_ms_per_step"], 4),
     }
     if args.all:
         per = {}
+        flush = L2Flush()
         for n in range(1, 6):
-            r = measure(n, max(3, args.steps // 2), 2)
+            # the small workload and the ring share's merge are latency / HBM
+            # bound: also timed with L2 and MALL flushed
+            r = measure(n, max(3, args.steps // 2), 2, flush=flush if n in (1, 5) else None)
             per[r["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in r.items() if k not in ("workload", "kernels")}
             per[r["workload"]]["kernels_ms"] = {k: round(v["mean_ms"], 4)

@@ -102,8 +102,9 @@ def test_varlen_ragged_unequal_segments(vca):
     # lq != lk per segment, zero-query and zero-key segments, lq > lk (empty rows)
     lens_q = [5, 0, 130, 70, 0, 3, 33]
     lens_k = [9, 40, 100, 70, 12, 0, 65]
-    for causal in (True, False):
-        run_varlen(vca, lens_q, lens_k, 8, 2, 128, 128, causal, seed=21 + causal)
+    for d in (128, 512):
+        for causal in (True, False):
+            run_varlen(vca, lens_q, lens_k, 8, 2, d, d, causal, seed=21 + causal + d)
 
 
 def test_varlen_gqa_group_sizes(vca):

@@ -52,31 +52,11 @@ __device__ __forceinline__ void dma4(const float* g, lds_void* lds_base) {
       : "memory");
 }
 
-// Every MFMA of this kernel is written out, so operands can sit in the
-// accumulation registers (AGPRs): the K/V fragments (B operands of S / dP)
-// and the 64x128 dV/dK accumulators live there, leaving the VGPRs to the
-// score tiles, staged fragments and softmax. The compiler does not see these
-// as MFMAs, so they carry their own wait states: mfma_a's s_nop gives the 2 a
-// VALU write of an A/B operand needs before the MFMA reads it (back-to-back
-// MFMAs on one accumulator need none), and mfma_results_ready() waits out an
-// MFMA before anything else reads or overwrites its result or C operand.
-// S / dP: A from an LDS read, B from AGPRs (no VALU-written operand, so no
-// wait states); C starts at zero (mfma_v0) or accumulates (mfma_v).
-__device__ __forceinline__ void mfma_v0(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b_agpr));
-}
-__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_agpr));
-}
-__device__ __forceinline__ void mfma_a(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Orders the wait after the MFMAs that produced `x` (an asm with x as an
-// in/out operand cannot move above them).
-__device__ __forceinline__ void mfma_results_ready(f32x16& x0, f32x16& x1) {
-  if (&x0 == &x1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0));
-  else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
-}
+// The S / dP products, the dV / dK accumulation and the AGPR helpers are the
+// hand-written MFMAs of attn_common.hpp (mfma_v0, mfma_v, mfma_a, in_agprs):
+// the K/V fragments (B operands of S / dP) and the 64x128 dV/dK
+// accumulators live in the accumulation registers, leaving the VGPRs to the
+// score tiles, staged fragments and softmax.
 // The accumulators are in/out operands, so their reads stay below the wait.
 __device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[4][2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -87,20 +67,6 @@ __device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[4][1]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0][0]), "+a"(acc[1][0]), "+a"(acc[2][0]), "+a"(acc[3][0]));
 }
-// Move a value into AGPRs at its definition, so the loop-carried value is
-// allocated there (instead of living in VGPRs and being copied around every
-// MFMA that takes it from an AGPR).
-__device__ __forceinline__ f32x16 in_agprs(f32x16 x) {
-  f32x16 r;
-  asm volatile("; in agprs" : "=a"(r) : "0"(x));
-  return r;
-}
-__device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
-  bf16x8 r;
-  asm volatile("; in agprs" : "=a"(r) : "0"(x));
-  return r;
-}
-
 // KT: 32-key tiles per wave (2: four waves, one per SIMD; 1: eight waves,
 // two per SIMD, whose softmax work then overlaps the other wave's MFMAs).
 template <bool CAUSAL, int KT>

@@ -87,6 +87,43 @@ __device__ __forceinline__ void pipeline_mfma_reads() {
 }
 
 // Partner lane across the two wave halves (l ^ 32).
+// Hand-written MFMAs, for kernels whose operands or accumulators sit in the
+// accumulation registers (AGPRs). The compiler does not see these
+// as MFMAs, so they carry their own wait states: mfma_a's s_nop gives the 2 a
+// VALU write of an A/B operand needs before the MFMA reads it (back-to-back
+// MFMAs on one accumulator need none), and mfma_results_ready() waits out an
+// MFMA before anything else reads or overwrites its result or C operand.
+// S / dP: A from an LDS read, B from AGPRs (no VALU-written operand, so no
+// wait states); C starts at zero (mfma_v0) or accumulates (mfma_v).
+__device__ __forceinline__ void mfma_v0(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_agpr));
+}
+__device__ __forceinline__ void mfma_a(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Orders the wait after the MFMAs that produced `x` (an asm with x as an
+// in/out operand cannot move above them).
+__device__ __forceinline__ void mfma_results_ready(f32x16& x0, f32x16& x1) {
+  if (&x0 == &x1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0));
+  else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x0), "+v"(x1));
+}
+// Move a value into AGPRs at its definition, so the loop-carried value is
+// allocated there (instead of living in VGPRs and being copied around every
+// MFMA that takes it from an AGPR).
+__device__ __forceinline__ f32x16 in_agprs(f32x16 x) {
+  f32x16 r;
+  asm volatile("; in agprs" : "=a"(r) : "0"(x));
+  return r;
+}
+__device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
+  bf16x8 r;
+  asm volatile("; in agprs" : "=a"(r) : "0"(x));
+  return r;
+}
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // Wait until every outstanding global load of this wave has landed
@@ -128,6 +165,64 @@ __device__ __forceinline__ void dma16(const uint16_t* g, lds_void* lds_base) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(g), "s"(m0)
+      : "memory");
+}
+// The same load addressed as a wave-uniform base (SGPRs) plus a 32-bit
+// per-lane byte offset: one VGPR per distinct offset instead of a 64-bit
+// address per load.
+__device__ __forceinline__ void dma16s(const uint16_t* sbase, uint32_t voff_bytes,
+                                       lds_void* lds_base) {
+  uint32_t saved;
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff_bytes), "s"(sbase), "s"(m0)
+      : "memory");
+}
+// Eight rows at once: row i's 16 bytes per lane come from p[i] + voff_bytes
+// and land at LDS byte address m0[i] + 16*l (wave-uniform LDS addresses as
+// integers). Counts as eight operations for vmcnt.
+__device__ __forceinline__ void dma16_rows8(const uint16_t* const (&p)[8], uint32_t voff_bytes,
+                                            const uint32_t (&m0)[8]) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %11\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %12\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %4\n\t"
+      "s_mov_b32 m0, %13\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %14\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
+      "s_mov_b32 m0, %15\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %7\n\t"
+      "s_mov_b32 m0, %16\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %8\n\t"
+      "s_mov_b32 m0, %17\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %9\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff_bytes), "s"(p[0]), "s"(p[1]), "s"(p[2]), "s"(p[3]), "s"(p[4]), "s"(p[5]),
+        "s"(p[6]), "s"(p[7]), "s"(m0[0]), "s"(m0[1]), "s"(m0[2]), "s"(m0[3]), "s"(m0[4]),
+        "s"(m0[5]), "s"(m0[6]), "s"(m0[7])
       : "memory");
 }
 // Global stores whose vmcnt footprint is exactly one operation each (used

@@ -1,5 +1,6 @@
 // Forward launcher: instantiates the forward kernel for every compiled
 // head-dim pair and both mask modes.
+#include "attn_fwd_wide.hpp"
 #include "attn_launch.hpp"
 #include "attn_timing.hpp"
 
@@ -22,6 +23,14 @@ hipError_t fwd_dims(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
   else
     hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false>), grid,
                        dim3(256 * DS), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t fwd_wide(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
+  TimedLaunch timer("attn_fwd", st);
+  if (causal)
+    hipLaunchKernelGGL(attn_fwd_wide_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_wide_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 }  // namespace
@@ -60,7 +69,7 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   if (dqk == 128 && dv == 128) return fwd_dims<128, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 256 && dv == 256) return fwd_dims<256, 256, 64, 1, 2, 1, true>(a, causal, grid, st);
-  return fwd_dims<512, 512, 32, 2, 1, 1, false>(a, causal, grid, st);
+  return fwd_wide(a, causal, grid, st);
 }
 
 }  // namespace vca

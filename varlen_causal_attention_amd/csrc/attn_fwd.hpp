@@ -50,11 +50,11 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   // range [ds*VR, (ds+1)*VR); the partial score tiles are summed through LDS
   // in a fixed order, so every wave of the group sees bitwise-identical scores.
   // NBUF = 2 double-buffers the K/V tiles in LDS (one barrier per tile);
-  // NBUF = 1 keeps one buffer (two barriers per tile) to fit Dqk = 512.
-  // PF = the next tile's global loads are issued a tile ahead into registers
-  // (off where the registers are needed for the accumulators).
+  // NBUF = 1 keeps one buffer (two barriers per tile).
+  // PF = outside DMA mode, the next tile's global loads are issued a tile
+  // ahead into registers (off where the registers are needed for the
+  // accumulators).
   static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
-  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 256 * DS;      // threads
   constexpr int DR = DQK / DS, VR = DV / DS;
   // LDS row strides (elements). K is only read row-wise (b128 per lane, 16
@@ -67,13 +67,20 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   constexpr int NKB = BN / 32;
   constexpr int NDB = VR / 32;
   constexpr int NKS = DR / 16;
-  // Head dim 128 (one wave per 32-row block, 64-key tiles, two buffers): K
-  // and V tiles go straight from global memory into LDS (global_load_lds),
-  // 256-byte rows in the swizzled layout of rtile_off, one tile ahead;
-  // no staging through registers and no LDS stores.
-  constexpr bool DMA = DQK == kTileD && DV == kTileD && DS == 1 && NBUF == 2 && BN == 64;
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * kTileD : BN * KS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * kTileD : BN * VS];
+  // DMA mode (Dqk = Dv a multiple of 128, two buffers): K and V tiles go
+  // straight from global memory into LDS (global_load_lds), one tile ahead,
+  // with no staging through registers and no LDS stores. A tile is stored as
+  // CB column blocks [CB][BN][128], each block in the swizzled 256-byte-row
+  // layout of rtile_off. The tile's BN/4 * CB groups of 4 rows x 256 bytes
+  // are split evenly over the waves, NG (a multiple of 4) per wave.
+  constexpr int CB = DQK / kTileD;
+  constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * DS) : 0;
+  constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NBUF == 2 && NG >= 4 && NG % 4 == 0 &&
+                       NG * 4 * 4 * DS == BN * CB;
+  static_assert(DMA || PF || NBUF == 1, "double buffering relies on the register prefetch");
+  constexpr int KBLK = BN * kTileD;  // elements per column block of a DMA tile
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * DQK : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * DV : BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -110,30 +117,37 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   }
   wait_global_loads();
 
-  // DMA: wave w loads K and V rows 16w..16w+15 of a tile (4 loads each):
-  // load jj covers rows 16w + 4jj + l/16; stored piece l%16 of row r holds
-  // global piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ jj.
+  // DMA: group g = NG*w + jj of a tile is rows 4*(g % (BN/4)) + l/16 of
+  // column block g / (BN/4), at LDS element offset 512*g; stored piece l%16
+  // of row r holds block piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ (jj%4).
+  // A full tile is addressed as a uniform base (its first row of the group,
+  // column block) plus one of four per-lane byte offsets (row l/16, piece).
   const int dl = lane >> 4, p0 = (lane & 15) ^ (dl << 2);
-  const int64_t kr0 = (int64_t)(16 * w + dl) * a.k.sn, vr0 = (int64_t)(16 * w + dl) * a.v.sn;
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    koff[j] = (uint32_t)(dl * a.k.sn + (p0 ^ j) * 8) * 2u;
+    voff[j] = (uint32_t)(dl * a.v.sn + (p0 ^ j) * 8) * 2u;
+  }
   auto issue_kv = [&](int tt) {
     const int b = tt & 1, kt0 = tt * BN;
     if (kt0 + BN <= lk) {
-      const uint16_t* kt = kb + (int64_t)kt0 * a.k.sn + kr0;
-      const uint16_t* vt = vb + (int64_t)kt0 * a.v.sn + vr0;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int pc = (p0 ^ jj) * 8;
-        dma16(kt + (int64_t)(4 * jj) * a.k.sn + pc, lds_ptr(&sk[b][(4 * w + jj) * 512]));
-        dma16(vt + (int64_t)(4 * jj) * a.v.sn + pc, lds_ptr(&sv[b][(4 * w + jj) * 512]));
+      for (int jj = 0; jj < NG; ++jj) {
+        const int g = NG * w + jj;
+        const int c = g / (BN / 4), r0 = kt0 + 4 * (g % (BN / 4));
+        dma16s(kb + (int64_t)r0 * a.k.sn + c * kTileD, koff[jj & 3], lds_ptr(&sk[b][g * 512]));
+        dma16s(vb + (int64_t)r0 * a.v.sn + c * kTileD, voff[jj & 3], lds_ptr(&sv[b][g * 512]));
       }
     } else {
       // the segment's last tile: rows past its end re-read its last row
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rr = min(kt0 + 16 * w + 4 * jj + dl, lk - 1);
-        const int pc = (p0 ^ jj) * 8;
-        dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][(4 * w + jj) * 512]));
-        dma16(vb + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][(4 * w + jj) * 512]));
+      for (int jj = 0; jj < NG; ++jj) {
+        const int g = NG * w + jj;
+        const int c = g / (BN / 4), rr = min(kt0 + 4 * (g % (BN / 4)) + dl, lk - 1);
+        const int pc = c * kTileD + (p0 ^ (jj & 3)) * 8;
+        dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][g * 512]));
+        dma16(vb + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][g * 512]));
       }
     }
   };
@@ -194,7 +208,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int kbk = 0; kbk < NKB; ++kbk)
-          sacc[kbk] = mfma32(DMA ? rtile_row(sk[buf], kbk * 32 + col, 2 * ks + half)
+          sacc[kbk] = mfma32(DMA ? rtile_row(&sk[buf][((ds * DR + ks * 16) / kTileD) * KBLK],
+                                             kbk * 32 + col, ((ds * DR + ks * 16) % kTileD) / 8 + half)
                                  : lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 +
                                                      ks * 16]),
                              qf[ks], sacc[kbk]);
@@ -271,7 +286,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          o[db] = mfma32(DMA ? rtile_col(sv[buf], kk * 16, db * 32, lane)
+          o[db] = mfma32(DMA ? rtile_col(&sv[buf][((ds * VR + db * 32) / kTileD) * KBLK], kk * 16,
+                                         (ds * VR + db * 32) % kTileD, lane)
                              : tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane),
                          pf[kk], o[db]);
       pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();

@@ -185,6 +185,21 @@ __device__ __forceinline__ void dma16s(const uint16_t* sbase, uint32_t voff_byte
       : "v"(voff_bytes), "s"(sbase), "s"(m0)
       : "memory");
 }
+// One row: lane l's 16 bytes from sbase + voff_bytes land at LDS byte
+// address m0 + 16*l (m0 a wave-uniform LDS address as an integer).
+__device__ __forceinline__ void dma16m(const uint16_t* sbase, uint32_t voff_bytes, uint32_t m0) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff_bytes), "s"(sbase), "s"(m0)
+      : "memory");
+}
 // Eight rows at once: row i's 16 bytes per lane come from p[i] + voff_bytes
 // and land at LDS byte address m0[i] + 16*l (wave-uniform LDS addresses as
 // integers). Counts as eight operations for vmcnt.

@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   constexpr int KS = D + 8;           // K row stride (elements)
   constexpr int VS = D + 32;          // V row stride (elements)
   constexpr int NSLOT = 2 * NKS;     // MFMA slots of a pipelined iteration
-  constexpr int LEAD = 2;            // LDS fragments read ahead of their MFMA
+  constexpr int LEAD = 4;            // LDS fragments read ahead of their MFMA
   static_assert(2 * NDB * 2 == NSLOT, "one product MFMA per score MFMA");
   __shared__ __attribute__((aligned(1024))) uint16_t sk[2][BN * KS];
   __shared__ __attribute__((aligned(1024))) uint16_t sv[2][BN * VS];
@@ -114,19 +114,18 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   float alpha = 1.f;      // rescale of O found by the latest softmax
   bool rescale = false;
 
-  // softmax of the scores of tile tt (scale, mask, lazy max, exp2, row sum,
-  // bf16 P^T fragments), split into steps so the pipelined iteration can
+  // softmax of the scores of tile tt, in place (scale, mask, lazy max, exp2,
+  // row sum, bf16 P^T fragments), split into steps so the pipelined iteration can
   // place one between MFMAs: steps 0-15 scale and mask, 16 the row max, 17-32
   // exp2, 33-34 pack.
-  float x[16];
   float mx = kNegInf, m_use = 0.f;
-  auto sm_step = [&](int c, const f32x16& sc, int tt, bf16x8* pf) {
+  auto sm_step = [&](int c, f32x16& sc, int tt, bf16x8* pf) {
     if (c < 16) {
       const int r = c;
       const int key = tt * BN + (r >> 2) * 8 + half * 4 + (r & 3);
       const bool vis = key < lk && (!CAUSAL || key <= row + shift);
-      x[r] = vis ? sc[r] * a.scale_log2 : kNegInf;
-      mx = c == 0 ? x[r] : fmaxf(mx, x[r]);
+      sc[r] = vis ? sc[r] * a.scale_log2 : kNegInf;
+      mx = c == 0 ? sc[r] : fmaxf(mx, sc[r]);
     } else if (c == 16) {
       mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_ref, mx);
@@ -139,13 +138,16 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
       m_use = m_ref == kNegInf ? 0.f : m_ref;
     } else if (c < 33) {
       const int r = c - 17;
-      x[r] = fast_exp2(x[r] - m_use);
-      lsum += x[r];
+      sc[r] = fast_exp2(sc[r] - m_use);
+      lsum += sc[r];
     } else if (c < 35) {
-      pf[c - 33] = to_frag(x + 8 * (c - 33));
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = sc[8 * (c - 33) + i];
+      pf[c - 33] = to_frag(e);
     }
   };
-  auto softmax = [&](const f32x16& sc, int tt, bf16x8* pf) {
+  auto softmax = [&](f32x16& sc, int tt, bf16x8* pf) {
 #pragma unroll
     for (int c = 0; c < 35; ++c) sm_step(c, sc, tt, pf);
   };
@@ -206,8 +208,13 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   for (int t = 1; t < nt; ++t) {
     wait_vmcnt<0>();  // this wave's share of K tile t+1 and V tile t-1 has landed
     __syncthreads();  // everyone's; nobody still reads K tile t or V tile t-2
-    if (t + 2 < nt) issue(kb, a.k.sn, lds_k, KS, t + 2);
-    issue(vb, a.v.sn, lds_v, VS, t);
+    // loads of K tile t+2 and V tile t: one row after each of the first 16
+    // products, so the memory pipe's queue never stalls the MFMA stream (past
+    // the last tile the K loads re-read the segment's last row into the free
+    // buffer)
+    const int rk0 = (t + 2) * BN + 8 * w, rv0 = t * BN + 8 * w;
+    const uint32_t mk0 = lds_k + (uint32_t)(((t & 1) * BN + 8 * w) * KS * 2);
+    const uint32_t mv0 = lds_v + (uint32_t)(((t & 1) * BN + 8 * w) * VS * 2);
     // S of tile t+1 (even slots; on the last tile it reads a stale buffer and
     // is discarded) and O += V^T P^T of tile t-1 (odd slots), the softmax of
     // tile t between them
@@ -221,8 +228,16 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
     for (int c = 0; c < NSLOT; ++c) {
       if (c + LEAD < NSLOT)
         fr[c + LEAD] = ((c + LEAD) & 1) ? vfrag(Vp, (c + LEAD) >> 1) : kfrag(Kn, (c + LEAD) >> 1);
-      if (c & 1) mfma_a(o[(c >> 1) & 15], fr[c], pf_prev[c >> 5]);
-      else s_next = mfma32(fr[c], qf[c >> 1], s_next);
+      if (c & 1) {
+        mfma_a(o[(c >> 1) & 15], fr[c], pf_prev[c >> 5]);
+        const int j = c >> 1, i = j & 7;
+        if (j < 8)
+          dma16m(kb + (int64_t)min(rk0 + i, lk - 1) * a.k.sn, loff, mk0 + (uint32_t)(i * KS * 2));
+        else if (j < 16)
+          dma16m(vb + (int64_t)min(rv0 + i, lk - 1) * a.v.sn, loff, mv0 + (uint32_t)(i * VS * 2));
+      } else {
+        s_next = mfma32(fr[c], qf[c >> 1], s_next);
+      }
       sm_step(c, s_cur, t, pf_cur);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -316,6 +316,18 @@ def test_merge_kernel_against_oracle(vca):
     torch.cuda.synchronize()
     assert np.abs(host(acc) - ro).max() < 1e-5
     check_lse(lacc, rl)
+    # a head dim that is not a multiple of 8 takes the element-wise kernel
+    rows, H, Dv = 77, 3, 20
+    oa, ob = rand((rows, H, Dv), g), rand((rows, H, Dv), g)
+    la = torch.randn((H, rows), generator=g) * 3
+    lb = torch.randn((H, rows), generator=g) * 3
+    lb[2, :9] = -math.inf
+    ro, rl = orc.merge(oa, la, ob, lb)
+    mo, ml, mob = vca.merge(dev(oa), dev(la), dev(ob), dev(lb), bf16_copy=True)
+    torch.cuda.synchronize()
+    assert np.abs(host(mo) - ro).max() < 1e-5
+    check_lse(ml, rl)
+    assert torch.equal(mob, mo.to(torch.bfloat16))
 
 
 # ---------------------------------------------------------------- robustness

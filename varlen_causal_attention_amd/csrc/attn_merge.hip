@@ -38,12 +38,84 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const MergeArgs a) {
 }
 
 
+// Head dims that are a multiple of 8 with 16-byte aligned buffers: one thread
+// per 8 consecutive elements of a (row, head), 16- and 32-byte loads and
+// stores; each thread recomputes its row's weights from the two lse values.
+__device__ __forceinline__ void load8(const void* p, int f32, int64_t i, float (&v)[8]) {
+  if (f32) {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = x0[j];
+      v[4 + j] = x1[j];
+    }
+  } else {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(x[j] << 16);
+      v[2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) attn_merge8_kernel(const MergeArgs a) {
+  const int cpp = a.Dv >> 3;  // 8-element chunks per (row, head)
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (int64_t)a.rows * a.H * cpp) return;
+  const int64_t pair = c / cpp;  // row * H + h
+  const int d0 = int(c - pair * cpp) * 8;
+  const int row = int(pair / a.H), h = int(pair - (int64_t)row * a.H);
+  const int64_t li = (int64_t)h * a.rows + row;
+  const float la = a.lse_a[li], lb = a.lse_b[li];
+  const float mx = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, l = kNegInf;
+  if (mx != kNegInf) {
+    const float ea = expf(la - mx), eb = expf(lb - mx);
+    const float sum = ea + eb;
+    wa = ea / sum;
+    wb = eb / sum;
+    l = mx + logf(sum);
+  }
+  const int64_t e = pair * a.Dv + d0;
+  float va[8], vb[8], v[8];
+  load8(a.out_a, a.a_f32, e, va);
+  load8(a.out_b, a.b_f32, e, vb);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = wa * va[j] + wb * vb[j];
+  f32x4 o0, o1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o0[j] = v[j];
+    o1[j] = v[4 + j];
+  }
+  *reinterpret_cast<f32x4*>(a.out + e) = o0;
+  *reinterpret_cast<f32x4*>(a.out + e + 4) = o1;
+  if (a.out_bf16) {
+    u32x4 b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[2 * j]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v[2 * j + 1]);
+      b[j] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(a.out_bf16 + e) = b;
+  }
+  if (d0 == 0) a.lse[li] = l;
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int64_t pairs = (int64_t)a.rows * a.H;
   if (pairs == 0) return hipSuccess;
-  const dim3 grid((unsigned)((pairs + 3) / 4));
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   TimedLaunch timer("attn_merge", st);
-  hipLaunchKernelGGL(attn_merge_kernel, grid, dim3(256), 0, st, a);
+  if (a.Dv % 8 == 0 && al16(a.out_a) && al16(a.out_b) && al16(a.out) && al16(a.out_bf16)) {
+    const int64_t chunks = pairs * (a.Dv / 8);
+    hipLaunchKernelGGL(attn_merge8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -516,7 +516,9 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
   const int qg = w / DS, ds = w % DS;
-  const int item = blockIdx.x / a.Hq, h = blockIdx.x - item * a.Hq, g = h / a.G;
+  int item, h;
+  xcd_item_head(blockIdx.x, a.Hq, a.G, item, h);
+  const int g = h / a.G;
   if (item >= *a.count_q) return;
   const int2 st = a.items_q[item];
   const int s = st.x;

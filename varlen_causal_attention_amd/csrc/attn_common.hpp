@@ -389,6 +389,26 @@ __device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Workgroup -> (work item, q-head) for passes whose grid is items x H q-heads
+// (GQA group size G). Consecutive workgroup ids are dispatched to the 8 XCDs
+// in turn; when the kv heads divide evenly over the XCDs, XCD x gets every
+// q-head of kv heads x, x+8, ..., so the workgroups that stream one kv head's
+// K/V share that XCD's L2, items in list (heavy-first) order. Otherwise
+// items outermost, heads innermost.
+constexpr int kXcdCount = 8;
+__device__ __forceinline__ void xcd_item_head(int bid, int H, int G, int& item, int& h) {
+  if ((H / G) % kXcdCount == 0) {
+    const int x = bid % kXcdCount, k = bid / kXcdCount;
+    const int per = H / kXcdCount;  // q-heads per XCD
+    item = k / per;
+    const int j = k - item * per;
+    h = (x + kXcdCount * (j / G)) * G + j % G;
+  } else {
+    item = bid / H;
+    h = bid - item * H;
+  }
+}
+
 // Segment geometry: query rows [q_row0, q_row0 + lq) and key rows
 // [k_row0, k_row0 + lk) of the packed tensors. cu arrays are clamped into
 // [0, T] so a malformed table can never index outside the tensors.

@@ -88,7 +88,9 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int qg = w / DS, ds = w % DS;
   const int col = lane & 31, half = lane >> 5;
-  const int item = blockIdx.x / a.H, h = blockIdx.x - item * a.H, kvh = h / a.G;
+  int item, h;
+  xcd_item_head(blockIdx.x, a.H, a.G, item, h);
+  const int kvh = h / a.G;
   if (item >= *a.item_count) return;
   const int2 st = a.items[item];
   const int s = st.x, tile = st.y;

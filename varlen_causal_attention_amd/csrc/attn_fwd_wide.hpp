@@ -48,7 +48,9 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int item = blockIdx.x / a.H, h = blockIdx.x - item * a.H, kvh = h / a.G;
+  int item, h;
+  xcd_item_head(blockIdx.x, a.H, a.G, item, h);
+  const int kvh = h / a.G;
   if (item >= *a.item_count) return;
   const int2 st = a.items[item];
   const int s = st.x, tile = st.y;

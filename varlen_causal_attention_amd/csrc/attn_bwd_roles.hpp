@@ -140,9 +140,13 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   }
   wait_global_loads();
 
-  // step it -> (q-head, first query); stage of step it (it >= -2)
-  auto step_head = [&](int it) { return g * a.G + it / nq; };
-  auto step_q0 = [&](int it) { return q_begin + (it % nq) * kRBQ; };
+  // step it -> (q-head, first query); stage of step it (it >= -2). Query
+  // steps run from the segment's end down, the group's q-heads innermost:
+  // every key block of a segment starts on the same Q/dO tiles and walks
+  // them in lockstep until it reaches its own first visible query, so the
+  // workgroups sharing a tile read it from L2 at about the same time.
+  auto step_head = [&](int it) { return g * a.G + it % a.G; };
+  auto step_q0 = [&](int it) { return q_begin + (nq - 1 - it / a.G) * kRBQ; };
   auto stage = [](int it) { return (it + NS) % NS; };
   // Hand-issued loads of step it: SPW of the Q tile's 8 four-row slices, SPW
   // of dO's, and 16 of the 64 lse*log2(e) | delta values. Lane l of slice j

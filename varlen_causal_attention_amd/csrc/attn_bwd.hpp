@@ -46,6 +46,7 @@ struct BwdArgs {
   uint16_t* tile_ds;
   int tile_nkb;        // key tiles per row slot
   int tile_nqb_dense;  // dense: query tiles per batch; 0 for varlen
+  int nq_items, nk_items;  // list capacities (grid sizes) of the two-phase passes
 };
 
 // ---------------------------------------------------------------------------

@@ -19,6 +19,8 @@ hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_
   a.tile_nqb_dense = tg.nqb_dense;
   const unsigned q_items = (unsigned)((q_rows + kBlk - 1) / kBlk + nseg);
   const unsigned k_items = (unsigned)((k_rows + kBlk - 1) / kBlk + nseg);
+  a.nq_items = (int)q_items;
+  a.nk_items = (int)k_items;
   if (q_rows > 0 && k_rows > 0) {
     TimedLaunch timer("attn_bwd_scores", st);
     hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>),

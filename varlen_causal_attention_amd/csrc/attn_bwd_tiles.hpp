@@ -81,6 +81,25 @@ __device__ __forceinline__ void xcd_work(int bid, int& group, int& part) {
   part = j % PARTS;
   group = (j / PARTS) * kXcds + xcd;
 }
+// Group -> (work item, head) for H heads in GQA groups of G (G = 1 for a
+// kv-head pass). When the kv heads divide evenly over the XCDs, XCD x takes
+// kv heads x, x+8, ... one after the other, and for each of them every item
+// in list (heavy-first) order with the group's q-heads innermost: the groups
+// that run together on an XCD are neighbouring items of one kv head and read
+// the same K/V (and Q/dO) blocks through its L2. Otherwise items outermost.
+__device__ __forceinline__ void xcd_item_head_major(int grp, int nitems, int H, int G, int& item,
+                                                    int& h) {
+  if ((H / G) % kXcds == 0) {
+    const int x = grp % kXcds, k = grp / kXcds;
+    const int per = nitems * G;  // groups per kv head on this XCD
+    const int m = k / per, r = k - m * per;
+    item = r / G;
+    h = (x + kXcds * m) * G + (r - item * G);
+  } else {
+    item = grp / H;
+    h = grp - item * H;
+  }
+}
 template <int PARTS>
 inline unsigned xcd_grid(unsigned groups) {
   return (groups + kXcds - 1) / kXcds * kXcds * PARTS;
@@ -369,7 +388,8 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   const int wm = w / S::WN, wn = w % S::WN;
   int grp, part;
   xcd_work<PARTS>(blockIdx.x, grp, part);
-  const int item = grp / a.Hkv, hk = grp - item * a.Hkv;
+  int item, hk;
+  xcd_item_head_major(grp, a.nk_items, a.Hkv, 1, item, hk);
   if (item >= *a.count_k) return;
   const bool is_dk = WHICH == 2 ? (part & 1) != 0 : WHICH == 1;
   const int dh = WHICH == 2 ? part >> 1 : part;
@@ -472,7 +492,9 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
   const int wm = w / S::WN, wn = w % S::WN;
   int grp, dh;
   xcd_work<NDH>(blockIdx.x, grp, dh);
-  const int item = grp / a.Hq, h = grp - item * a.Hq, g = h / a.G;
+  int item, h;
+  xcd_item_head_major(grp, a.nq_items, a.Hq, a.G, item, h);
+  const int g = h / a.G;
   if (item >= *a.count_q) return;
   const int2 st = a.items_q[item];
   const int s = st.x;

@@ -38,10 +38,8 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
   sa.list = list_q;
   sa.count = counts;
   sa.max_items = (int)list_capacity(q_rows, nseg);
-  {
-    TimedLaunch timer("attn_schedule", st);
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
-  }
+  SchedArgs2 s2{};
+  s2.list[0] = sa;
   // key blocks, cost = query steps walked
   sa.by_keys = 1;
   sa.tile = k_tile;
@@ -49,9 +47,10 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
   sa.list = list_k;
   sa.count = counts + 1;
   sa.max_items = (int)list_capacity(k_rows, nseg);
+  s2.list[1] = sa;
   {
     TimedLaunch timer("attn_schedule", st);
-    hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);
+    hipLaunchKernelGGL(attn_schedule2_kernel, dim3(2), dim3(1024), 0, st, s2);
   }
   a.lse2 = reinterpret_cast<float*>(w + wl.lse2);
   a.items_q = list_q;

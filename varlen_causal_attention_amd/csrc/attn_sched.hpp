@@ -44,7 +44,7 @@ __device__ __forceinline__ int sched_cost(const SchedArgs& a, const SegGeom& g, 
 // scan, scatter. Wave w takes segments w, w+16, ...; its lanes split the
 // segment's tiles. Items of equal cost land in an arbitrary order; every item
 // writes only its own outputs, so the order never changes a result.
-static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedArgs a) {
+__device__ __forceinline__ void schedule_list(const SchedArgs& a) {
   constexpr int NT = 1024, PER = kSchedBuckets / NT;  // buckets per thread
   __shared__ int hist[kSchedBuckets];
   __shared__ int wave_sum[NT / 64];
@@ -99,6 +99,19 @@ static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedA
       if (pos < a.max_items) a.list[pos] = make_int2(s, t);
     }
   }
+}
+
+static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedArgs a) {
+  schedule_list(a);
+}
+
+// Two independent lists in one launch (workgroup i builds list i): the
+// backward's query-tile and key-block lists.
+struct SchedArgs2 {
+  SchedArgs list[2];
+};
+static __global__ void __launch_bounds__(1024) attn_schedule2_kernel(const SchedArgs2 a) {
+  schedule_list(a.list[blockIdx.x]);
 }
 
 }  // namespace vca

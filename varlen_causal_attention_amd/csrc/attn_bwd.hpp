@@ -28,7 +28,7 @@ struct BwdArgs {
   ViewW dq, dk, dv;
   const float* lse;
   float* delta;            // workspace, same indexing as lse
-  float* lse2;             // workspace: lse * log2(e), same indexing
+  float* lse2;             // workspace: lse * log2(e) (+inf where lse = -inf), same indexing
   int64_t lse_sb, lse_sh;  // index = b*lse_sb + h*lse_sh + (q_row0 + i)
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -83,7 +83,11 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
   if (ok && li == 0) {
     const int64_t idx = s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row;
     a.delta[idx] = acc;
-    a.lse2[idx] = a.lse[idx] * kLog2e;
+    // a row with lse = -inf attends nothing: +inf makes its P = exp2(s - lse2)
+    // exactly zero on every key, masked or not (the dense cross chunk of a
+    // ring sees its padding queries' keys)
+    const float l = a.lse[idx];
+    a.lse2[idx] = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
 }
 

@@ -179,6 +179,35 @@ int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_l
                       int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
                       int max_segments, int* num_segments);
 
+/* Dense routing of one ring chunk ("gemma4_moe cp_attention" page: the
+ * dense-routing flags of the packed ring segments and the per-chunk dense
+ * eligibility entry). Host-only, no GPU work. Same doc_ids, ranges and modes
+ * as attn_doc_segments. *eligible receives 1 when the chunk can run on the
+ * dense kernels over the raw [B, H, S, D] rows (queries = positions
+ * [q_start, q_start + q_len), keys = [k_start, k_start + k_len); causal for
+ * mode 0, non-causal for mode 1) and give the document-causal result on every
+ * non-padding query:
+ *  mode 0: the key range ends where the query range ends, and every row's
+ *  keys are one document with padding (id 0) only as a suffix;
+ *  mode 1: every row's keys are exactly one document without padding, and
+ *  the row's queries are that document with padding only as a suffix (or all
+ *  padding).
+ * pad_rows (optional, host uint8 [B, q_len]) receives 1 for padding queries:
+ * after a dense run their out rows must be zeroed and lse set to -inf
+ * (attn_zero_rows), which the backward then treats as attending nothing.
+ * Returns ATTN_E_INVALID on bad ranges (the attn_doc_segments conditions). */
+int attn_dense_route(const int32_t* doc_ids, int B, int S, int q_start, int q_len, int k_start,
+                     int k_len, int mode, uint8_t* pad_rows, int* eligible);
+
+/* Zero the rows a dense ring chunk must not produce: for every (b, i) with
+ * rows[b * S + i] != 0 (device uint8 [B, S]), out[b, h, i, :] = 0 (ATTN_BF16
+ * or ATTN_F32 per dtype) and lse[b*lse_sb + h*lse_sh + i] = -inf for all H
+ * heads. out is a [B, H, S, D] view with element strides (ob, oh, on) and
+ * unit innermost stride; lse may be NULL. Enqueued on stream; no workspace. */
+int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, float* lse,
+                   int64_t lse_sb, int64_t lse_sh, const uint8_t* rows, int B, int H, int S, int D,
+                   hipStream_t stream);
+
 /* Opt-in kernel timing, for profiling on the caller's own streams. While
  * enabled (per calling thread), every kernel this library launches from that
  * thread is bracketed by two HIP events recorded on its stream. Returns the

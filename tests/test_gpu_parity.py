@@ -295,6 +295,72 @@ def test_ring_share_workload(vca):
     assert torch.all(dq[pad] == 0)
 
 
+@pytest.mark.parametrize("d", [128, 512])
+def test_ring_share_dense_route(vca, d):
+    """Ring share whose rows are single documents (one with a pad tail): both
+    chunks pass dense_route, run on the dense kernels over the raw
+    [B, H, S, D] rows, get their padding queries zeroed (zero_rows), merge in
+    the flattened dense layout, and run the dense backwards from the merged
+    out/lse; every result matches the document-causal oracle."""
+    g = torch.Generator().manual_seed(95 + d)
+    B, S, Hq, Hkv = 2, 160, 4, 2
+    ids = np.zeros((B, 2 * S), dtype=np.int32)
+    ids[0, :] = 3
+    ids[1, :2 * S - 60] = 4
+    ok_l, pad = vca.dense_route(ids, S, S, S, S, 0)
+    ok_x, pad_x = vca.dense_route(ids, S, S, 0, S, 1)
+    assert ok_l and ok_x and np.array_equal(pad, pad_x) and pad.sum() == 60
+    q, do = rand((B, Hq, S, d), g), rand((B, Hq, S, d), g)
+    kl, vl, ke, ve = (rand((B, Hkv, S, d), g) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    rows = dev(torch.from_numpy(pad))
+    o1, l1 = vca.fwd_dense(dev(q), dev(kl), dev(vl), scale, True)
+    vca.zero_rows(o1, l1, rows)
+    o2, l2 = vca.fwd_dense(dev(q), dev(ke), dev(ve), scale, False)
+    vca.zero_rows(o2, l2, rows)
+    n = B * Hq * S
+    mo, ml, mob = vca.merge(o1.view(n, 1, d), l1.view(1, n), o2.view(n, 1, d), l2.view(1, n),
+                            bf16_copy=True)
+    mo4, ml4, mob4 = mo.view(B, Hq, S, d), ml.view(B, Hq, S), mob.view(B, Hq, S, d)
+    dq, dkl, dvl = vca.bwd_dense(dev(do), dev(q), dev(kl), dev(vl), mob4, ml4, scale, True)
+    _, dke, dve = vca.bwd_dense(dev(do), dev(q), dev(ke), dev(ve), mob4, ml4, scale, False,
+                                dq_accumulate=dq)
+    torch.cuda.synchronize()
+    qpos, kpos = np.arange(S, 2 * S), np.arange(0, 2 * S)
+    for b in range(B):
+        qb, dob = q[b].transpose(0, 1), do[b].transpose(0, 1)
+        k_all = torch.cat([ke[b], kl[b]], dim=1).transpose(0, 1)
+        v_all = torch.cat([ve[b], vl[b]], dim=1).transpose(0, 1)
+        r1 = orc.fwd_doc_causal(qb, kl[b].transpose(0, 1), vl[b].transpose(0, 1), ids[b, qpos],
+                                qpos, ids[b, qpos], qpos, scale)
+        check_out(o1[b].transpose(0, 1), r1[0])
+        check_lse(l1[b], r1[1])
+        ro, rl = orc.fwd_doc_causal(qb, k_all, v_all, ids[b, qpos], qpos, ids[b, kpos], kpos, scale)
+        check_out(mo4[b].transpose(0, 1), ro)
+        check_lse(ml4[b], rl)
+        rdq, rdk, rdv = orc.bwd_doc_causal(dob, qb, k_all, v_all, ro, rl, ids[b, qpos], qpos,
+                                           ids[b, kpos], kpos, scale)
+        check_grad("dq", dq[b].transpose(0, 1), rdq)
+        check_grad("dk_early", dke[b].transpose(0, 1), rdk[:S])
+        check_grad("dv_early", dve[b].transpose(0, 1), rdv[:S])
+        check_grad("dk_local", dkl[b].transpose(0, 1), rdk[S:])
+        check_grad("dv_local", dvl[b].transpose(0, 1), rdv[S:])
+    # padding queries: out 0, lse -inf, dq 0
+    assert torch.all(mo4[1, :, S - 60:] == 0) and torch.all(torch.isneginf(ml4[1, :, S - 60:]))
+    assert torch.all(dq[1, :, S - 60:] == 0)
+
+
+def test_zero_rows_fp32_and_no_lse(vca):
+    out = torch.ones((2, 3, 5, 7), device="cuda")
+    rows = torch.zeros((2, 5), dtype=torch.bool, device="cuda")
+    rows[1, 2] = True
+    vca.zero_rows(out, None, rows)
+    torch.cuda.synchronize()
+    ref = torch.ones((2, 3, 5, 7))
+    ref[1, :, 2] = 0
+    assert torch.equal(out.cpu(), ref)
+
+
 def test_merge_kernel_against_oracle(vca):
     g = torch.Generator().manual_seed(71)
     rows, H, Dv = 300, 4, 512

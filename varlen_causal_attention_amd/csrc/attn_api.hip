@@ -337,4 +337,30 @@ int attn_merge(const void* out_a, int dtype_a, const float* lse_a, const void* o
   return hip_status(vca::launch_merge(a, stream), "attn_merge launch");
 }
 
+int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, float* lse,
+                   int64_t lse_sb, int64_t lse_sh, const uint8_t* rows, int B, int H, int S, int D,
+                   hipStream_t stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || S < 0 || D < 0) return fail(ATTN_E_INVALID, "B, H, S, D >= 0 required");
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32)
+    return fail(ATTN_E_UNSUPPORTED, "zero_rows: out must be ATTN_BF16 or ATTN_F32");
+  if (B == 0 || H == 0 || S == 0) return ok();
+  if (!out || !rows) return fail(ATTN_E_INVALID, "zero_rows pointer is NULL");
+  vca::ZeroRowsArgs a{};
+  a.out = out;
+  a.f32 = dtype == ATTN_F32;
+  a.ob = ob;
+  a.oh = oh;
+  a.on = on;
+  a.lse = lse;
+  a.lse_sb = lse_sb;
+  a.lse_sh = lse_sh;
+  a.rows = rows;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.D = D;
+  return hip_status(vca::launch_zero_rows(a, stream), "attn_zero_rows launch");
+}
+
 }  // extern "C"

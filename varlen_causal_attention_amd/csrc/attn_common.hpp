@@ -385,7 +385,6 @@ __device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, i
   const uint16_t* p1 = X + rtile_off(row + 8, c >> 3) + (c & 7);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

@@ -113,4 +113,16 @@ hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, i
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
+// rows a dense ring chunk must not produce: out rows to 0, lse to -inf
+struct ZeroRowsArgs {
+  void* out;
+  int f32;
+  int64_t ob, oh, on;
+  float* lse;
+  int64_t lse_sb, lse_sh;
+  const uint8_t* rows;  // [B, S]
+  int B, H, S, D;
+};
+hipError_t launch_zero_rows(const ZeroRowsArgs& a, hipStream_t stream);
+
 }  // namespace vca

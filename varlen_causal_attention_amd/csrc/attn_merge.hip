@@ -105,6 +105,33 @@ __global__ void __launch_bounds__(256) attn_merge8_kernel(const MergeArgs a) {
   if (d0 == 0) a.lse[li] = l;
 }
 
+// Zero the out rows (and set lse to -inf) of the (batch, position) rows a
+// dense ring chunk must not produce. One workgroup per (row, batch), one
+// wave per head in turn, lanes over the head dim.
+__global__ void __launch_bounds__(256) attn_zero_rows_kernel(const ZeroRowsArgs a) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  if (!a.rows[(int64_t)b * a.S + i]) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int h = w; h < a.H; h += 4) {
+    const int64_t base = b * a.ob + h * a.oh + (int64_t)i * a.on;
+    if (a.f32) {
+      float* o = reinterpret_cast<float*>(a.out) + base;
+      for (int d = lane; d < a.D; d += 64) o[d] = 0.f;
+    } else {
+      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + base;
+      for (int d = lane; d < a.D; d += 64) o[d] = 0;
+    }
+    if (a.lse && lane == 0) a.lse[b * a.lse_sb + h * a.lse_sh + i] = kNegInf;
+  }
+}
+
+hipError_t launch_zero_rows(const ZeroRowsArgs& a, hipStream_t st) {
+  if (a.B == 0 || a.S == 0 || a.H == 0) return hipSuccess;
+  TimedLaunch timer("attn_zero_rows", st);
+  hipLaunchKernelGGL(attn_zero_rows_kernel, dim3((unsigned)a.S, (unsigned)a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int64_t pairs = (int64_t)a.rows * a.H;
   if (pairs == 0) return hipSuccess;

@@ -101,7 +101,8 @@ __device__ __forceinline__ void schedule_list(const SchedArgs& a) {
   }
 }
 
-static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedArgs a) {
+[[maybe_unused]] static __global__ void __launch_bounds__(1024)
+attn_schedule_kernel(const SchedArgs a) {
   schedule_list(a);
 }
 
@@ -110,7 +111,8 @@ static __global__ void __launch_bounds__(1024) attn_schedule_kernel(const SchedA
 struct SchedArgs2 {
   SchedArgs list[2];
 };
-static __global__ void __launch_bounds__(1024) attn_schedule2_kernel(const SchedArgs2 a) {
+[[maybe_unused]] static __global__ void __launch_bounds__(1024)
+attn_schedule2_kernel(const SchedArgs2 a) {
   schedule_list(a.list[blockIdx.x]);
 }
 

@@ -116,3 +116,70 @@ extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_sta
   }
   return ATTN_OK;
 }
+
+// Dense routing of one ring chunk ("gemma4_moe cp_attention" page: the
+// dense-routing flags of the packed ring segments and the per-chunk dense
+// eligibility entry; the single-document row predicates).
+namespace {
+
+// Positions [a, b) of one row hold one document id d > 0, then optionally
+// padding (id 0) to b. Returns d, 0 when [a, b) is all padding, -1 otherwise.
+int single_doc_prefix(const int32_t* ids, int a, int b) {
+  if (a >= b || ids[a] == 0) {
+    for (int p = a; p < b; ++p)
+      if (ids[p] != 0) return -1;
+    return 0;
+  }
+  const int d = ids[a];
+  int p = a;
+  while (p < b && ids[p] == d) ++p;
+  while (p < b && ids[p] == 0) ++p;
+  return p == b ? d : -1;
+}
+
+}  // namespace
+
+extern "C" int attn_dense_route(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                                int k_start, int k_len, int mode, uint8_t* pad_rows,
+                                int* eligible) {
+  vca::set_last_error("");
+  if (!doc_ids || !eligible || B < 0 || S < 0 || q_len < 0 || k_len < 0 || q_start < 0 ||
+      k_start < 0 || q_start + q_len > S || k_start + k_len > S || (mode != 0 && mode != 1)) {
+    vca::set_last_error("attn_dense_route: invalid arguments");
+    return ATTN_E_INVALID;
+  }
+  const int q_end = q_start + q_len, k_end = k_start + k_len;
+  if (mode == 0 && !(k_start <= q_start && q_end <= k_end)) {
+    vca::set_last_error("attn_dense_route: causal mode needs the key range to cover the query range");
+    return ATTN_E_INVALID;
+  }
+  if (mode == 1 && k_end > q_start) {
+    vca::set_last_error("attn_dense_route: cross mode needs every key before every query");
+    return ATTN_E_INVALID;
+  }
+  // Bottom-right causal alignment equals position causality only when the
+  // key range ends where the query range ends.
+  bool ok = mode == 1 || k_end == q_end;
+  for (int b = 0; b < B && ok; ++b) {
+    const int32_t* ids = doc_ids + (size_t)b * S;
+    if (mode == 0) {
+      // one document, padding only as a suffix: a query then sees exactly its
+      // document's keys up to its own position; padding queries are zeroed
+      ok = single_doc_prefix(ids, k_start, k_end) >= 0;
+    } else {
+      // keys: exactly one document, no padding; queries: that document, with
+      // padding only as a suffix
+      const int dk = single_doc_prefix(ids, k_start, k_end);
+      bool kfull = dk > 0;
+      for (int p = k_start; p < k_end && kfull; ++p) kfull = ids[p] == dk;
+      const int dq = single_doc_prefix(ids, q_start, q_end);
+      ok = kfull && (dq == dk || dq == 0);
+    }
+  }
+  *eligible = ok ? 1 : 0;
+  if (pad_rows)
+    for (int b = 0; b < B; ++b)
+      for (int i = 0; i < q_len; ++i)
+        pad_rows[(size_t)b * q_len + i] = doc_ids[(size_t)b * S + q_start + i] == 0 ? 1 : 0;
+  return ATTN_OK;
+}

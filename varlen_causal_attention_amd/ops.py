@@ -260,6 +260,44 @@ def doc_layout(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode
             int(max(sq, default=0)), int(max(sk, default=0)))
 
 
+def dense_route(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int):
+    """(eligible, pad_rows bool [B, q_len]) of one ring chunk: whether it can
+    run on the dense kernels over the raw [B, H, S, D] rows (mode 0 causal
+    local chunk, mode 1 non-causal cross chunk), and which of its queries are
+    padding (to zero with zero_rows after the dense forward)."""
+    ids = np.ascontiguousarray(np.asarray(doc_ids, dtype=np.int32))
+    if ids.ndim != 2:
+        raise ValueError("doc_ids is [B, S]")
+    B, S = ids.shape
+    pad = np.zeros((B, max(q_len, 0)), dtype=np.uint8)
+    ok = C.c_int(0)
+    check(load().attn_dense_route(ids.ctypes.data_as(C.POINTER(C.c_int32)), B, S, q_start, q_len,
+                                  k_start, k_len, mode, pad.ctypes.data_as(C.c_void_p),
+                                  C.byref(ok)), "attn_dense_route")
+    return bool(ok.value), pad.astype(bool)
+
+
+def zero_rows(out, lse, rows):
+    """In place: out[b, :, i, :] = 0 and lse[b, :, i] = -inf where rows[b, i]
+    (out a [B, H, S, D] bf16 or fp32 view, lse contiguous [B, H, S] fp32 or
+    None, rows bool/uint8 [B, S] on the same GPU)."""
+    if out.dim() != 4 or out.stride(3) != 1 or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be a [B, H, S, D] bf16/fp32 view with unit last stride")
+    B, H, S, D = out.shape
+    if tuple(rows.shape) != (B, S) or rows.device != out.device:
+        raise ValueError("rows must be [B, S] on the device of out")
+    r = rows.to(torch.uint8).contiguous()
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [B, H, S]")
+    dt = ATTN_F32 if out.dtype == torch.float32 else ATTN_BF16
+    ls = (H * S, S) if lse is not None else (0, 0)
+    check(load().attn_zero_rows(_ptr(out), dt, out.stride(0), out.stride(1), out.stride(2),
+                                _ptr(lse), ls[0], ls[1], _ptr(r), B, H, S, D, _stream(out)),
+          "attn_zero_rows")
+    return out, lse
+
+
 # ---------------------------------------------------------------------------
 # kernel timing (profiling aid)
 # ---------------------------------------------------------------------------

@@ -5,8 +5,9 @@ one MI355X. Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload N] [--all]
 
 The default workload is the packed-varlen document-causal D=128 problem
-(T=16384, Hq=32, Hkv=8); ``--workload`` picks another of the five
-(1 small dense, 2 varlen D128, 3 dense D512, 4 varlen 192/128, 5 ring share),
+(T=16384, Hq=32, Hkv=8); ``--workload`` picks another of the six
+(1 small dense, 2 varlen D128, 3 dense D512, 4 varlen 192/128, 5 ring share,
+6 ring share of a single-document row, whose chunks take the dense route),
 ``--all`` adds per-workload numbers for every one of them to the line.
 Throughput is causal-adjusted: FLOPs count only visible (query, key) pairs,
 forward 2*pairs*(Dqk+Dv), backward 2*pairs*(3*Dqk+2*Dv).
@@ -50,8 +51,17 @@ class Problem:
         elif w.kind == "ring":
             ids = w.row_doc_ids()
             S = w.shard
-            self.local = vca.doc_layout(ids, S, S, S, S, 0, "cuda")
-            self.cross = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
+            # dense routing when both chunks qualify (single-document row):
+            # the dense kernels run on [1, H, S, D] views of the shard tensors
+            ok_l, pad = vca.dense_route(ids, S, S, S, S, 0)
+            ok_x, _ = vca.dense_route(ids, S, S, 0, S, 1)
+            self.dense = ok_l and ok_x
+            if self.dense:
+                self.pad = torch.from_numpy(pad).to("cuda")
+                self.d = {k: x.unsqueeze(0).transpose(1, 2) for k, x in self.t.items()}
+            else:
+                self.local = vca.doc_layout(ids, S, S, S, S, 0, "cuda")
+                self.cross = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
         self.out = self.lse = None
 
     def fwd(self):
@@ -61,16 +71,27 @@ class Problem:
         elif w.kind == "varlen":
             self.out, self.lse = v.fwd_varlen(t["q"], t["k"], t["v"], self.cu, self.cu, self.mx,
                                               self.mx, w.scale, w.causal)
+        elif self.dense:
+            o1, l1, o2, l2 = self.partials()
+            _, lse, out = v.merge(o1, l1, o2, l2, bf16_copy=True)
+            self.out = out.view(1, w.Hq, w.shard, w.Dv)
+            self.lse = lse.view(1, w.Hq, w.shard)
         else:
-            cq, ck, mq, mk = self.local
-            o1, l1 = v.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
-            cq, ck, mq, mk = self.cross
-            o2, l2 = v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False)
+            o1, l1, o2, l2 = self.partials()
             _, self.lse, self.out = v.merge(o1, l1, o2, l2, bf16_copy=True)
 
     def partials(self):
-        """Ring share: the two partial forward results the merge combines."""
+        """Ring share: the two partial forward results the merge combines
+        (dense route: [1, H, S, D] results with padding rows zeroed, flattened
+        to the merge's [rows, 1, D] / [1, rows] layout)."""
         v, w, t = self.vca, self.w, self.t
+        if self.dense:
+            d, n = self.d, w.Hq * w.shard
+            o1, l1 = v.fwd_dense(d["q"], d["k_local"], d["v_local"], w.scale, True)
+            v.zero_rows(o1, l1, self.pad)
+            o2, l2 = v.fwd_dense(d["q"], d["k_early"], d["v_early"], w.scale, False)
+            v.zero_rows(o2, l2, self.pad)
+            return o1.view(n, 1, w.Dv), l1.view(1, n), o2.view(n, 1, w.Dv), l2.view(1, n)
         cq, ck, mq, mk = self.local
         o1, l1 = v.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
         cq, ck, mq, mk = self.cross
@@ -84,6 +105,13 @@ class Problem:
         if w.kind == "varlen":
             return v.bwd_varlen(t["do"], t["q"], t["k"], t["v"], self.out, self.lse, self.cu,
                                 self.cu, self.mx, self.mx, w.scale, w.causal)
+        if self.dense:
+            d = self.d
+            dq, dkl, dvl = v.bwd_dense(d["do"], d["q"], d["k_local"], d["v_local"], self.out,
+                                       self.lse, w.scale, True)
+            _, dke, dve = v.bwd_dense(d["do"], d["q"], d["k_early"], d["v_early"], self.out,
+                                      self.lse, w.scale, False, dq_accumulate=dq)
+            return dq, dkl, dvl, dke, dve
         cq, ck, mq, mk = self.local
         dq, dkl, dvl = v.bwd_varlen(t["do"], t["q"], t["k_local"], t["v_local"], self.out,
                                     self.lse, cq, ck, mq, mk, w.scale, True)
@@ -231,6 +259,8 @@ def kernel_work(w: "workloads.Workload", name: str):
         return "hbm", rows * w.Hq * (2 * w.Dv * 2 + 4), "B"
     if name == "attn_merge":
         return "hbm", rows * w.Hq * (w.Dv * (2 + 2 + 4 + 2) + 4 * 3), "B"
+    if name == "attn_zero_rows":
+        return "hbm", w.pad_tail * w.Hq * (w.Dv * 2 + 4), "B"
     return None
 
 
@@ -425,10 +455,10 @@ def main():
     if args.all:
         per = {}
         flush = L2Flush()
-        for n in range(1, 6):
+        for n in range(1, 7):
             # the small workload and the ring share's merge are latency / HBM
             # bound: also timed with L2 and MALL flushed
-            r = measure(n, max(3, args.steps // 2), 2, flush=flush if n in (1, 5) else None)
+            r = measure(n, max(3, args.steps // 2), 2, flush=flush if n in (1, 5, 6) else None)
             per[r["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in r.items() if k not in ("workload", "kernels")}
             per[r["workload"]]["kernels_ms"] = {k: round(v["mean_ms"], 4)

@@ -255,10 +255,40 @@ def ring_share(vca, w, t):
     return (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve)
 
 
-def test_ring_share_workload(vca):
-    w = workloads.workload(5)
+def ring_share_dense(vca, w, t):
+    """ring_share over the dense route ([1, H, S, D] views of the shard
+    tensors, padding rows zeroed, merge in the flattened dense layout); the
+    results come back in the packed [S, H, D] / [H, S] layout."""
+    ids, S, H, D = w.row_doc_ids(), w.shard, w.Hq, w.Dv
+    ok_l, pad = vca.dense_route(ids, S, S, S, S, 0)
+    ok_x, _ = vca.dense_route(ids, S, S, 0, S, 1)
+    assert ok_l and ok_x
+    rows = dev(torch.from_numpy(pad))
+    d = {k: dev(x).unsqueeze(0).transpose(1, 2) for k, x in t.items()}
+    o1, l1 = vca.fwd_dense(d["q"], d["k_local"], d["v_local"], w.scale, True)
+    vca.zero_rows(o1, l1, rows)
+    o2, l2 = vca.fwd_dense(d["q"], d["k_early"], d["v_early"], w.scale, False)
+    vca.zero_rows(o2, l2, rows)
+    n = H * S
+    mo, ml, mob = vca.merge(o1.view(n, 1, D), l1.view(1, n), o2.view(n, 1, D), l2.view(1, n),
+                            bf16_copy=True)
+    mob4, ml4 = mob.view(1, H, S, D), ml.view(1, H, S)
+    dq, dkl, dvl = vca.bwd_dense(d["do"], d["q"], d["k_local"], d["v_local"], mob4, ml4, w.scale,
+                                 True)
+    _, dke, dve = vca.bwd_dense(d["do"], d["q"], d["k_early"], d["v_early"], mob4, ml4, w.scale,
+                                False, dq_accumulate=dq)
+    thd = lambda x: x[0].transpose(0, 1)  # noqa: E731  [1, H, S, D] -> [S, H, D]
+    return ((thd(o1), l1[0]), (thd(o2), l2[0]), (mo.view(H, S, D).transpose(0, 1), ml.view(H, S)),
+            tuple(thd(x) for x in (dq, dkl, dvl, dke, dve)))
+
+
+@pytest.mark.parametrize("n", [5, 6])
+def test_ring_share_workload(vca, n):
+    # 5: packed documents (varlen route); 6: one document per row (dense route)
+    w = workloads.workload(n)
     t = w.tensors()
-    (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve) = ring_share(vca, w, t)
+    share = ring_share_dense if w.single_doc else ring_share
+    (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve) = share(vca, w, t)
     torch.cuda.synchronize()
     ids = w.row_doc_ids()[0]
     S = w.shard

@@ -81,6 +81,7 @@ class Workload:
     pad_tail: int = 0
     doc_lo: int = 0
     doc_hi: int = 0
+    single_doc: bool = False  # ring: the row is one document (then the pad tail)
 
     @property
     def scale(self) -> float:
@@ -114,6 +115,8 @@ class Workload:
 
     # ---- ring workload: document ids of the global row -----------------
     def ring_docs(self) -> list[int]:
+        if self.single_doc:
+            return [2 * self.shard - self.pad_tail]
         return doc_lengths(2 * self.shard - self.pad_tail, self.doc_lo, self.doc_hi, self.seed)
 
     def row_doc_ids(self) -> np.ndarray:
@@ -169,8 +172,9 @@ def ring_pairs(row_ids: np.ndarray, shard: int) -> int:
 
 
 def workload(n: int) -> Workload:
-    """The five named workloads (1: small dense, 2: varlen D128, 3: dense D512,
-    4: varlen 192/128, 5: one rank of a two-rank ring at D512)."""
+    """The named workloads (1: small dense, 2: varlen D128, 3: dense D512,
+    4: varlen 192/128, 5: one rank of a two-rank ring at D512, 6: the same
+    rank when its row is a single document, the dense-routed ring chunks)."""
     if n == 1:
         return Workload("dense_causal_b1_h4kv2_n256_d128", "dense", 1, Hq=4, Hkv=2, Dqk=128,
                         Dv=128, B=1, Nq=256, Nk=256)
@@ -186,6 +190,9 @@ def workload(n: int) -> Workload:
     if n == 5:
         return Workload("ring_rank1_of2_q4096_h16kv8_d512", "ring", 5, Hq=16, Hkv=8, Dqk=512,
                         Dv=512, shard=4096, pad_tail=128, doc_lo=256, doc_hi=4096)
+    if n == 6:
+        return Workload("ring_rank1_of2_single_doc_q4096_h16kv8_d512", "ring", 6, Hq=16, Hkv=8,
+                        Dqk=512, Dv=512, shard=4096, pad_tail=128, single_doc=True)
     raise ValueError(f"no workload {n}")
 
 

@@ -68,13 +68,14 @@ def rand(shape, g):
 
 
 # ---------------------------------------------------------------- varlen
-def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed):
+def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed, scale=None):
     g = torch.Generator().manual_seed(seed)
     cu_q, cu_k = workloads.cumulative(lens_q), workloads.cumulative(lens_k)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
     q, k, v = rand((Tq, Hq, Dqk), g), rand((Tk, Hkv, Dqk), g), rand((Tk, Hkv, Dv), g)
     do = rand((Tq, Hq, Dv), g)
-    scale = 1.0 / math.sqrt(Dqk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
     ro, rl = orc.fwd_varlen(q, k, v, cu_q, cu_k, scale, causal)
     rdq, rdk, rdv = orc.bwd_varlen(do, q, k, v, ro, rl, cu_q, cu_k, scale, causal)
     cq, ck = dev(torch.from_numpy(cu_q)), dev(torch.from_numpy(cu_k))
@@ -96,6 +97,13 @@ def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed):
 def test_varlen_every_head_dim(vca, dqk, dv, causal):
     lens = [1, 37, 200, 129, 64, 300]
     run_varlen(vca, lens, lens, 4, 2, dqk, dv, causal, seed=11 + dqk + dv + causal)
+
+
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
+def test_varlen_negative_scale(vca, dqk, dv):
+    # the caller's scale may be negative: the softmax is then over -|scale| q.k
+    lens = [1, 100, 257, 64]
+    run_varlen(vca, lens, lens, 4, 2, dqk, dv, True, seed=41 + dqk, scale=-0.7 / math.sqrt(dqk))
 
 
 def test_varlen_ragged_unequal_segments(vca):

@@ -393,8 +393,9 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
     qst.template store<QS>(sq[b], tid);
     ost.template store<QS>(sdo[b], tid);
     if (tid < BQ) {
-      // rows past the segment end or with lse = -inf: -inf, so P = 0
-      slse[b][tid] = (row_ok && lse_r != kNegInf) ? -lse_r * kLog2e * inv_c : kNegInf;
+      // rows past the segment end or with lse = -inf: a seed whose product
+      // with c is -inf (-inf / c carries the sign of c), so P = 0
+      slse[b][tid] = (row_ok && lse_r != kNegInf) ? -lse_r * kLog2e * inv_c : kNegInf * inv_c;
       sdel[b][tid] = row_ok ? -del_r : 0.f;
     }
   };

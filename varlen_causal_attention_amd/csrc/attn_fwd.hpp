@@ -110,12 +110,18 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
+  // Scores are kept unscaled until the exponent: the row max is taken over
+  // raw q.k and scaled once, and exp2(sl2 * s - m) is one fma per element. A
+  // negative scale is folded into Q instead (negating bf16 is exact), so the
+  // factor sl2 applied to the scores is always positive.
+  const float sl2 = fabsf(a.scale_log2);
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   bf16x8 qf[NKS];
   {
     const bool ok = row < lq;
     const uint16_t* src = qb + (int64_t)(ok ? row : 0) * a.q.sn + ds * DR + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_frag(ok ? ldg16(src + ks * 16) : zero_u32x4());
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_frag((ok ? ldg16(src + ks * 16) : zero_u32x4()) ^ qsign);
   }
   wait_global_loads();
 
@@ -235,24 +241,25 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
         }
     }
     if (live) {
-      // scale, mask, row max
+      // mask (diagonal and tail tiles only), then the row max of the raw
+      // scores, scaled once (sl2 > 0; a fully masked row keeps -inf)
       const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift);
-      float mx = kNegInf;
+      if (need_mask) {
 #pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk) {
+        for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kbk][r] * a.scale_log2;
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int key = k0 + kbk * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
             const bool vis = key < lk && (!CAUSAL || key <= row + shift);
-            x = vis ? x : kNegInf;
+            sacc[kbk][r] = vis ? sacc[kbk][r] : kNegInf;
           }
-          sacc[kbk][r] = x;
-          mx = fmaxf(mx, x);
-        }
       }
-      mx = fmaxf(mx, xor32(mx));
+      float mx = kNegInf;
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
+      mx = fmaxf(mx, xor32(mx)) * sl2;
 
       // lazy rescale of the running reference
       const float m_new = fmaxf(m_ref, mx);
@@ -276,7 +283,7 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(sacc[kbk][r] - m_use);
+          p[r] = fast_exp2(fmaf(sacc[kbk][r], sl2, -m_use));
           lsum += p[r];
         }
         pf[2 * kbk] = to_frag(p);

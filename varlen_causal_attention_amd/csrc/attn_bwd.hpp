@@ -18,6 +18,8 @@
 // larger head dims use DS = 2 or 4 to keep the accumulators in registers.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn_fwd.hpp"
 
@@ -677,25 +679,31 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
     if (live) {
       // rows past the segment end carry l2 = +inf (P = 0); the key mask is only
       // needed on tiles that cross the diagonal or the segment end
+      // (one uniform branch picks a masked or an unmasked copy of the loop, so
+      // the mask costs no per-element branch on the other tiles)
       const bool need_mask = k0 + BN > lk || (CAUSAL && k0 + BN - 1 > wq0 + shift);
       bf16x8 sf[2 * NKB];
+      auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float dsv[16];
+        for (int kb = 0; kb < NKB; ++kb) {
+          float dsv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sacc[kb][r] * a.scale_log2 - l2);
-          if (need_mask) {
-            const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            bool vis = kj < lk;
-            if (CAUSAL) vis = vis && kj <= qi + shift;
-            p = vis ? p : 0.f;
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(sacc[kb][r] * a.scale_log2 - l2);
+            if constexpr (decltype(masked)::value) {
+              const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+              bool vis = kj < lk;
+              if (CAUSAL) vis = vis && kj <= qi + shift;
+              p = vis ? p : 0.f;
+            }
+            dsv[r] = p * (pacc[kb][r] - dl);
           }
-          dsv[r] = p * (pacc[kb][r] - dl);
+          sf[2 * kb] = to_frag(dsv);
+          sf[2 * kb + 1] = to_frag(dsv + 8);
         }
-        sf[2 * kb] = to_frag(dsv);
-        sf[2 * kb + 1] = to_frag(dsv + 8);
-      }
+      };
+      if (need_mask) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
       // dQ^T[d][q] += K^T dS^T (K^T read down the K tile's columns)
 #pragma unroll
       for (int kk = 0; kk < 2 * NKB; ++kk)

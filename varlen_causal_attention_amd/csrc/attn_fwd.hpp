@@ -43,8 +43,8 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdBM = 32 * kFwdWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL>
-__global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a) {
+template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL, int HPW = 1>
+__global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const FwdArgs a) {
   // DS waves share one 32-row query block: wave `ds` of the group holds the
   // Q fragments of Dqk range [ds*DR, (ds+1)*DR) and accumulates O^T for Dv
   // range [ds*VR, (ds+1)*VR); the partial score tiles are summed through LDS
@@ -54,8 +54,12 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   // PF = outside DMA mode, the next tile's global loads are issued a tile
   // ahead into registers (off where the registers are needed for the
   // accumulators).
+  // HPW = 2 runs two q-heads of one GQA group over the same query rows (four
+  // waves each): every K/V tile brought into LDS feeds both, half the tile
+  // loads per unit of work, with the same causal work per wave.
   static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
-  constexpr int NT = 256 * DS;      // threads
+  static_assert(HPW == 1 || DS == 1, "head pairs with a split head dim");
+  constexpr int NT = 256 * DS * HPW;  // threads
   constexpr int DR = DQK / DS, VR = DV / DS;
   // LDS row strides (elements). K is only read row-wise (b128 per lane, 16
   // lanes per LDS cycle): a stride of 16 bytes mod 256 puts 16 consecutive
@@ -74,9 +78,10 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   // layout of rtile_off. The tile's BN/4 * CB groups of 4 rows x 256 bytes
   // are split evenly over the waves, NG (a multiple of 4) per wave.
   constexpr int CB = DQK / kTileD;
-  constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * DS) : 0;
-  constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NBUF == 2 && NG >= 4 && NG % 4 == 0 &&
-                       NG * 4 * 4 * DS == BN * CB;
+  constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * DS * HPW) : 0;
+  constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NBUF == 2 && NG >= 1 &&
+                       (NG % 4 == 0 || 4 % NG == 0) && NG * 4 * 4 * DS * HPW == BN * CB;
+  static_assert(DMA || HPW == 1, "head pairs load their tiles with global_load_lds");
   static_assert(DMA || PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int KBLK = BN * kTileD;  // elements per column block of a DMA tile
   __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * DQK : BN * KS];
@@ -86,10 +91,12 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-  const int qg = w / DS, ds = w % DS;
+  const int wl = w % (4 * DS);                               // wave within its q-head
+  const int qg = wl / DS, ds = wl % DS;
   const int col = lane & 31, half = lane >> 5;
   int item, h;
-  xcd_item_head(blockIdx.x, a.H, a.G, item, h);
+  xcd_item_head(blockIdx.x, a.H / HPW, a.G / HPW, item, h);
+  h = h * HPW + w / (4 * DS);
   const int kvh = h / a.G;
   if (item >= *a.item_count) return;
   const int2 st = a.items[item];
@@ -127,15 +134,19 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
 
   // DMA: group g = NG*w + jj of a tile is rows 4*(g % (BN/4)) + l/16 of
   // column block g / (BN/4), at LDS element offset 512*g; stored piece l%16
-  // of row r holds block piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ (jj%4).
+  // of row r holds block piece (l%16) ^ 4*(r%4) ^ (r/4)%4 = p0 ^ (g%4).
   // A full tile is addressed as a uniform base (its first row of the group,
-  // column block) plus one of four per-lane byte offsets (row l/16, piece).
+  // column block) plus one of KO per-lane byte offsets (row l/16, piece):
+  // g%4 runs through jj%4 when NG is a multiple of 4, else through
+  // (NG*w + jj)%4 for the wave's NG groups.
+  constexpr int KO = NG % 4 == 0 ? 4 : (NG > 0 ? NG : 1);
   const int dl = lane >> 4, p0 = (lane & 15) ^ (dl << 2);
-  uint32_t koff[4], voff[4];
+  uint32_t koff[KO], voff[KO];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    koff[j] = (uint32_t)(dl * a.k.sn + (p0 ^ j) * 8) * 2u;
-    voff[j] = (uint32_t)(dl * a.v.sn + (p0 ^ j) * 8) * 2u;
+  for (int j = 0; j < KO; ++j) {
+    const int pc = p0 ^ ((NG * w + j) & 3);
+    koff[j] = (uint32_t)(dl * a.k.sn + pc * 8) * 2u;
+    voff[j] = (uint32_t)(dl * a.v.sn + pc * 8) * 2u;
   }
   auto issue_kv = [&](int tt) {
     const int b = tt & 1, kt0 = tt * BN;
@@ -144,8 +155,8 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int jj = 0; jj < NG; ++jj) {
         const int g = NG * w + jj;
         const int c = g / (BN / 4), r0 = kt0 + 4 * (g % (BN / 4));
-        dma16s(kb + (int64_t)r0 * a.k.sn + c * kTileD, koff[jj & 3], lds_ptr(&sk[b][g * 512]));
-        dma16s(vb + (int64_t)r0 * a.v.sn + c * kTileD, voff[jj & 3], lds_ptr(&sv[b][g * 512]));
+        dma16s(kb + (int64_t)r0 * a.k.sn + c * kTileD, koff[jj % KO], lds_ptr(&sk[b][g * 512]));
+        dma16s(vb + (int64_t)r0 * a.v.sn + c * kTileD, voff[jj % KO], lds_ptr(&sv[b][g * 512]));
       }
     } else {
       // the segment's last tile: rows past its end re-read its last row
@@ -153,7 +164,7 @@ __global__ void __launch_bounds__(256 * DS, WPE) attn_fwd_kernel(const FwdArgs a
       for (int jj = 0; jj < NG; ++jj) {
         const int g = NG * w + jj;
         const int c = g / (BN / 4), rr = min(kt0 + 4 * (g % (BN / 4)) + dl, lk - 1);
-        const int pc = c * kTileD + (p0 ^ (jj & 3)) * 8;
+        const int pc = c * kTileD + (p0 ^ ((NG * w + jj) & 3)) * 8;
         dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][g * 512]));
         dma16(vb + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][g * 512]));
       }

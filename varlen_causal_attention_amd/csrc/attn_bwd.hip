@@ -12,11 +12,12 @@ namespace {
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
 // Work lists (query tiles of q_tile rows with key steps of q_step, key blocks
-// of k_tile keys with query steps of k_step) and the delta pre-pass.
+// of k_tile keys with query steps of k_step) and, when delta_pass, the delta
+// pre-pass (the fused path's dQ pass computes delta itself).
 template <int DV>
 void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
                   int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step, int k_tile,
-                  int k_step, void* ws, hipStream_t st) {
+                  int k_step, void* ws, hipStream_t st, bool delta_pass = true) {
   char* w = static_cast<char*>(ws);
   const size_t delta_bytes = wl.list_q - 256;
   int* counts = reinterpret_cast<int*>(w + delta_bytes);
@@ -62,7 +63,7 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
 
   constexpr int LPR = DV / 8 >= 64 ? 64 : DV / 8;
   constexpr int rows_per_block = 4 * (64 / LPR);
-  if (max_q > 0) {
+  if (delta_pass && max_q > 0) {
     TimedLaunch timer("attn_bwd_delta", st);
     const dim3 g((max_q + rows_per_block - 1) / rows_per_block, Hq, nseg);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<DV>), g, dim3(256), 0, st, a);
@@ -79,7 +80,20 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
   constexpr int q_tile = 32 * (NWQ / DS);
   bwd_prologue<DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, BN, key_block, 32,
-                   ws, st);
+                   ws, st,
+                   /*delta_pass=*/false);
+  // the dQ pass first: it writes the delta and lse*log2(e) rows the dK/dV
+  // pass reads
+  if (q_rows > 0) {
+    TimedLaunch timer("attn_bwd_dq", st);
+    const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true>), g,
+                         dim3(64 * NWQ), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false>), g,
+                         dim3(64 * NWQ), 0, st, a);
+  }
   if (k_rows > 0) {
     TimedLaunch timer("attn_bwd_dkdv", st);
     const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
@@ -99,16 +113,6 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
         hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false>), g, dim3(64 * NWK),
                            0, st, a);
     }
-  }
-  if (q_rows > 0) {
-    TimedLaunch timer("attn_bwd_dq", st);
-    const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
-    if (causal)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true>), g,
-                         dim3(64 * NWQ), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false>), g,
-                         dim3(64 * NWQ), 0, st, a);
   }
   return hipGetLastError();
 }

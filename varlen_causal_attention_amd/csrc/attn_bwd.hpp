@@ -557,11 +557,34 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
     for (int i = 0; i < NVS; ++i) df[i] = as_frag(qok ? ldg16(dp + i * 16) : zero_u32x4());
   }
   const int64_t lidx = s * a.lse_sb + h * a.lse_sh + sg.q_row0 + (qok ? qi : 0);
+  // This pass runs first and computes delta = rowsum(dO * O) of its own
+  // queries: a lane holds the dO elements {16i + 8*half .. +7} of its query
+  // row, sums their products with the same elements of O, and adds the
+  // partner lane's half. The row's delta and lse*log2(e) (+inf for lse = -inf,
+  // so P = 0 on every key) are stored for the dK/dV pass that follows.
+  static_assert(DS == 1, "delta from whole dO rows");
   float l2 = __builtin_inff(), dl = 0.f;
-  if (qok) {
-    const float l = a.lse[lidx];
-    l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    dl = a.delta[lidx];
+  {
+    const uint16_t* op = a.o.p + s * a.o.sb + (int64_t)(sg.q_row0 + (qok ? qi : 0)) * a.o.sn +
+                         h * a.o.sh + half * 8;
+    u32x4 ov[NVS];
+#pragma unroll
+    for (int i = 0; i < NVS; ++i) ov[i] = qok ? ldg16(op + i * 16) : zero_u32x4();
+    float l = kNegInf;
+    if (qok) l = a.lse[lidx];
+#pragma unroll
+    for (int i = 0; i < NVS; ++i) {
+      const u32x4 dv4 = __builtin_bit_cast(u32x4, df[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dl += __uint_as_float(bf16_at(ov[i], e) << 16) * __uint_as_float(bf16_at(dv4, e) << 16);
+    }
+    dl += xor32(dl);
+    if (qok) l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    if (qok && half == 0) {
+      a.delta[lidx] = dl;
+      a.lse2[lidx] = l2;
+    }
   }
   wait_global_loads();
 

@@ -58,6 +58,9 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   sa.count = reinterpret_cast<int*>(w);
   sa.list = reinterpret_cast<int2*>(w + 256);
   sa.max_items = (int)list_capacity(q_rows, nseg);
+  // segment-major: a segment's query tiles start together and share its K/V
+  // tiles in L2 (192/128 varlen forward 2.90 -> 2.60 ms; about 2% at D=128)
+  sa.seg_major = 1;
   {
     TimedLaunch timer("attn_schedule", st);
     hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(1024), 0, st, sa);

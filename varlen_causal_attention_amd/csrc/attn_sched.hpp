@@ -26,6 +26,7 @@ struct SchedArgs {
   int2* list;    // out: (segment, tile) in heavy-first order
   int* count;    // out: number of items
   int max_items; // capacity of list (a malformed table may ask for more)
+  int seg_major; // 1 (query tiles): segments in table order, each one's tiles heaviest first
 };
 
 __device__ __forceinline__ int sched_cost(const SchedArgs& a, const SegGeom& g, int t) {
@@ -101,9 +102,50 @@ __device__ __forceinline__ void schedule_list(const SchedArgs& a) {
   }
 }
 
+// Segment-major order (query tiles only): the tiles of segment 0, heaviest
+// (last) first, then those of segment 1, ... The tiles of one segment and
+// head then start close together and walk the same K/V tiles in step, so a
+// tile read from HBM by one workgroup is still in L2 for the others; under a
+// global heavy-first order they start far apart in time and, without a GQA
+// group sharing the stream, miss L2. A segment's last tile walks all of its
+// keys and is emitted first, so each segment's long tiles still start first.
+__device__ __forceinline__ void schedule_seg_major(const SchedArgs& a) {
+  constexpr int NT = 1024;
+  __shared__ int wave_sum[NT / 64];
+  __shared__ int carry;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < a.nseg; base += NT) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < a.nseg) {
+      const SegGeom g = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+      n = (g.lq + a.tile - 1) / a.tile;
+    }
+    int incl = n;  // inclusive scan over the block
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_sum[w] = incl;
+    __syncthreads();
+    int pos = carry + incl - n;
+    for (int i = 0; i < w; ++i) pos += wave_sum[i];
+    for (int j = 0; j < n; ++j, ++pos)
+      if (pos < a.max_items) a.list[pos] = make_int2(s, n - 1 - j);
+    __syncthreads();  // every thread has read carry and wave_sum
+    if (tid == NT - 1) carry = pos;
+    __syncthreads();
+  }
+  if (tid == 0) *a.count = min(carry, a.max_items);
+}
+
 [[maybe_unused]] static __global__ void __launch_bounds__(1024)
 attn_schedule_kernel(const SchedArgs a) {
-  schedule_list(a);
+  if (a.seg_major) schedule_seg_major(a);
+  else schedule_list(a);
 }
 
 // Two independent lists in one launch (workgroup i builds list i): the

@@ -152,6 +152,10 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
                                                            q_rows, k_rows, wl, ws, st)
   if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
   if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
+  // 192/128: the fused passes at one wave per SIMD (dK/dV 360, dQ 285 registers) beat the
+  // two-phase backward, whose P/dS stores and re-reads make it HBM-bound at these head dims
+  // (14.0 -> 11.7 ms on the 32K-token varlen problem)
+  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 1, 2, true, 32, 2, true, 1, 4, 4);
 #undef VCA_BWD
   return hipErrorInvalidValue;
 }

@@ -2,7 +2,8 @@
 // "ffpa_attention" page, dense and varlen backward entries: the ring feeds a
 // globally merged out/lse, so the backward never uses a chunk-local one).
 //
-//   delta[i]  = sum_d dO[i,d] * O[i,d]                       (delta kernel)
+//   delta[i]  = sum_d dO[i,d] * O[i,d]         (dQ kernel prologue; delta kernel
+//                                                for the two-phase head dims)
 //   P[i,j]    = exp(scale * q_i.k_j - lse_i) on visible (i,j), 0 elsewhere and
 //               on rows with lse = -inf
 //   dV[j]    += sum_i P[i,j] dO[i]                            (dK/dV kernel)
@@ -14,8 +15,10 @@
 // Both main kernels split a 32-row block across DS waves by head-dim range:
 // each wave of the group computes a partial score tile over its share of Dqk
 // (and of Dv for dP), the partials are summed through LDS, and each wave then
-// accumulates its own share of the output columns. DS = 1 needs no exchange;
-// larger head dims use DS = 2 or 4 to keep the accumulators in registers.
+// accumulates its own share of the output columns. DS = 1 needs no exchange
+// and is what the library compiles: head dims 64 and 128 at two waves per
+// SIMD, 192/128 at one (dK and dV accumulators of 32 keys plus the K and V
+// fragments take ~360 registers); 256 and 512 take the two-phase backward.
 #pragma once
 
 #include <type_traits>

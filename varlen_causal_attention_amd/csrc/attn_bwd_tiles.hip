@@ -64,7 +64,6 @@ hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, i
 #define VCA_TILES(DQK, DV)                                                                       \
   if (dqk == DQK && dv == DV)                                                                    \
     return bwd_tiles_any<DQK, DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st);
-  VCA_TILES(192, 128)
   VCA_TILES(256, 256)
   VCA_TILES(512, 512)
 #undef VCA_TILES

@@ -57,7 +57,7 @@ inline TileGeom tile_geom_varlen(int Tq, int nseg, int max_k) {
 }
 // Head-dim pairs whose backward runs in two phases through stored blocks.
 inline bool bwd_uses_tiles(int dqk, int dv) {
-  return (dqk == dv && (dqk == 256 || dqk == 512)) || (dqk == 192 && dv == 128);
+  return dqk == dv && (dqk == 256 || dqk == 512);
 }
 struct BwdWorkspace {
   size_t list_q, list_k, lse2, tile_p, tile_ds, total;

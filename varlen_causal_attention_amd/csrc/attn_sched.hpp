@@ -155,7 +155,8 @@ struct SchedArgs2 {
 };
 [[maybe_unused]] static __global__ void __launch_bounds__(1024)
 attn_schedule2_kernel(const SchedArgs2 a) {
-  schedule_list(a.list[blockIdx.x]);
+  if (a.list[blockIdx.x].seg_major) schedule_seg_major(a.list[blockIdx.x]);
+  else schedule_list(a.list[blockIdx.x]);
 }
 
 }  // namespace vca

@@ -13,16 +13,17 @@ namespace {
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
 // Work lists (query tiles of q_tile rows with key steps of q_step, key blocks
 // of k_tile keys with query steps of k_step) and, when delta_pass, the delta
-// pre-pass (the fused path's dQ pass computes delta itself). q_seg_major puts
-// the query-tile list in segment-major order: the tiles of one segment and
-// head then read its K/V in step and share them in L2, which pays where no
-// GQA group of q-heads already shares each K/V stream (192/128 backward -2%,
-// D=512 -1%; with a group of four at D=128 heavy-first stays faster).
+// pre-pass (the fused path's dQ pass computes delta itself). seg_major_lists puts
+// both lists in segment-major order: the query tiles (key blocks) of one
+// segment and head then read its K/V (Q/dO) in step and share them in L2,
+// which pays where no GQA group of q-heads already shares each stream
+// (192/128 backward -3.5%, D=512 -1%; with a group of four at D=128 the
+// heavy-first order stays faster).
 template <int DV>
 void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
                   int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step, int k_tile,
                   int k_step, void* ws, hipStream_t st, bool delta_pass = true,
-                  int q_seg_major = 1) {
+                  int seg_major_lists = 1) {
   char* w = static_cast<char*>(ws);
   const size_t delta_bytes = wl.list_q - 256;
   int* counts = reinterpret_cast<int*>(w + delta_bytes);
@@ -44,10 +45,9 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
   sa.list = list_q;
   sa.count = counts;
   sa.max_items = (int)list_capacity(q_rows, nseg);
-  sa.seg_major = q_seg_major;
+  sa.seg_major = seg_major_lists;
   SchedArgs2 s2{};
   s2.list[0] = sa;
-  sa.seg_major = 0;
   // key blocks, cost = query steps walked
   sa.by_keys = 1;
   sa.tile = k_tile;
@@ -88,7 +88,7 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   constexpr int q_tile = 32 * (NWQ / DS);
   bwd_prologue<DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, BN, key_block, 32,
                    ws, st,
-                   /*delta_pass=*/false, /*q_seg_major=*/(Hq / Hkv) % 2 == 0 ? 0 : 1);
+                   /*delta_pass=*/false, /*seg_major_lists=*/(Hq / Hkv) % 2 == 0 ? 0 : 1);
   // the dQ pass first: it writes the delta and lse*log2(e) rows the dK/dV
   // pass reads
   if (q_rows > 0) {

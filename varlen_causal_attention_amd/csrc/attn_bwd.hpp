@@ -172,9 +172,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   float lse_r = 0.f, del_r = 0.f;  // threads < BQ carry one row's lse / delta
   bool row_ok = false;
 
+  // step it -> (q-head, first query): query steps from the segment's end
+  // down, the group's q-heads innermost, so the key blocks of a segment read
+  // each Q/dO tile at about the same time (shared in L2)
   auto step_ptrs = [&](int it, const uint16_t*& qp, const uint16_t*& dop, int64_t& lb, int& q0) {
-    const int hh = it / nq;
-    q0 = q_begin + (it - hh * nq) * BQ;
+    const int hh = it % a.G;
+    q0 = q_begin + (nq - 1 - it / a.G) * BQ;
     const int h = g * a.G + hh;
     qp = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
     dop = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + h * a.dout.sh;
@@ -214,7 +217,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
 
   for (int it = 0; it < total; ++it) {
     const int buf = NBUF == 2 ? (it & 1) : 0;
-    const int q0 = q_begin + (it % nq) * BQ;
+    const int q0 = q_begin + (nq - 1 - it / a.G) * BQ;
     __syncthreads();  // step `it` is in LDS; nobody still reads the other buffer
     if (NBUF == 2 && it + 1 < total) {
       store_rows(buf ^ 1);

@@ -26,7 +26,7 @@ struct SchedArgs {
   int2* list;    // out: (segment, tile) in heavy-first order
   int* count;    // out: number of items
   int max_items; // capacity of list (a malformed table may ask for more)
-  int seg_major; // 1 (query tiles): segments in table order, each one's tiles heaviest first
+  int seg_major; // 1: segments in table order, each one's items heaviest first
 };
 
 __device__ __forceinline__ int sched_cost(const SchedArgs& a, const SegGeom& g, int t) {
@@ -102,8 +102,8 @@ __device__ __forceinline__ void schedule_list(const SchedArgs& a) {
   }
 }
 
-// Segment-major order (query tiles only): the tiles of segment 0, heaviest
-// (last) first, then those of segment 1, ... The tiles of one segment and
+// Segment-major order: the items of segment 0, heaviest first (query tiles:
+// the last one; key blocks: the first one), then those of segment 1, ... The tiles of one segment and
 // head then start close together and walk the same K/V tiles in step, so a
 // tile read from HBM by one workgroup is still in L2 for the others; under a
 // global heavy-first order they start far apart in time and, without a GQA
@@ -121,7 +121,7 @@ __device__ __forceinline__ void schedule_seg_major(const SchedArgs& a) {
     int n = 0;
     if (s < a.nseg) {
       const SegGeom g = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
-      n = (g.lq + a.tile - 1) / a.tile;
+      n = ((a.by_keys ? g.lk : g.lq) + a.tile - 1) / a.tile;
     }
     int incl = n;  // inclusive scan over the block
 #pragma unroll
@@ -134,7 +134,7 @@ __device__ __forceinline__ void schedule_seg_major(const SchedArgs& a) {
     int pos = carry + incl - n;
     for (int i = 0; i < w; ++i) pos += wave_sum[i];
     for (int j = 0; j < n; ++j, ++pos)
-      if (pos < a.max_items) a.list[pos] = make_int2(s, n - 1 - j);
+      if (pos < a.max_items) a.list[pos] = make_int2(s, a.by_keys ? j : n - 1 - j);
     __syncthreads();  // every thread has read carry and wave_sum
     if (tid == NT - 1) carry = pos;
     __syncthreads();

@@ -106,13 +106,15 @@ def test_varlen_negative_scale(vca, dqk, dv):
     run_varlen(vca, lens, lens, 4, 2, dqk, dv, True, seed=41 + dqk, scale=-0.7 / math.sqrt(dqk))
 
 
-def test_varlen_ragged_unequal_segments(vca):
-    # lq != lk per segment, zero-query and zero-key segments, lq > lk (empty rows)
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4)])
+def test_varlen_ragged_unequal_segments(vca, dqk, dv, hq, hkv):
+    # lq != lk per segment, zero-query and zero-key segments, lq > lk (empty
+    # rows); an even GQA group and none (the two work-list orders)
     lens_q = [5, 0, 130, 70, 0, 3, 33]
     lens_k = [9, 40, 100, 70, 12, 0, 65]
-    for d in (128, 512):
-        for causal in (True, False):
-            run_varlen(vca, lens_q, lens_k, 8, 2, d, d, causal, seed=21 + causal + d)
+    for causal in (True, False):
+        run_varlen(vca, lens_q, lens_k, hq, hkv, dqk, dv, causal, seed=21 + causal + dqk + hkv)
 
 
 def test_varlen_gqa_group_sizes(vca):
@@ -169,8 +171,9 @@ def test_dense_small_causal_workload(vca):
 
 
 @pytest.mark.parametrize("Nq,Nk", [(130, 300), (300, 130), (257, 257)])
-def test_dense_bottom_right_alignment(vca, Nq, Nk):
-    run_dense(vca, 2, 4, 2, Nq, Nk, 128, 128, True, seed=51 + Nq)
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128)])
+def test_dense_bottom_right_alignment(vca, Nq, Nk, dqk, dv):
+    run_dense(vca, 2, 4, 2, Nq, Nk, dqk, dv, True, seed=51 + Nq + dqk)
 
 
 def test_dense_bshd_views_and_d512(vca):

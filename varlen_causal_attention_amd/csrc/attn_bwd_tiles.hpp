@@ -189,7 +189,11 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
   const int wm = w >> 1, wn = w & 1;
   int grp, part;
   xcd_work<kScoreSplit>(blockIdx.x, grp, part);
-  const int item = grp / a.Hq, h = grp - item * a.Hq, g = h / a.G;
+  // kv-head-major: the q-heads of a GQA group run side by side on one XCD
+  // and stream the same K/V blocks through its L2 (D=512 backward -1.8%)
+  int item, h;
+  xcd_item_head_major(grp, a.nq_items, a.Hq, a.G, item, h);
+  const int g = h / a.G;
   if (item >= *a.count_q) return;
   const int2 st = a.items_q[item];
   const int s = st.x;

@@ -93,8 +93,9 @@ int attn_is_supported(int dtype, int dqk, int dv);
  *  strides[12] = element strides (b, h, n) of q, k, v, out, in that order
  *  (so both BHND- and BSHD-contiguous storage work). Nq may differ from Nk;
  *  with causal = 1 the mask is bottom-right aligned (query i sees keys
- *  j <= i + Nk - Nq). Needs a small workspace (the work list the call
- *  orders heaviest tile first); query its size with workspace = NULL. */
+ *  j <= i + Nk - Nq). Needs a small workspace (the call's list of query
+ *  tiles, segment by segment with each one's heaviest tile first); query
+ *  its size with workspace = NULL. */
 int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void* out,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv,
                    const int64_t* strides, float scale, int causal, void* workspace,
@@ -216,10 +217,12 @@ int attn_timing_enable(int enable);
 
 /* Waits for and reads the recorded launches (in launch order) of the calling
  * thread, then clears the record. Up to max_records entries: names receives
- * NUL-terminated kernel labels in slots of name_len bytes ("attn_fwd",
- * "attn_schedule", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq",
- * "attn_merge"), ms the elapsed milliseconds; *count receives the total number
- * recorded. Returns ATTN_E_HIP if an event could not be read. */
+ * NUL-terminated kernel labels in slots of name_len bytes ("attn_schedule",
+ * "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"; for head dims 256 and 512
+ * "attn_bwd_delta", "attn_bwd_scores", "attn_bwd_dkdv_tiles",
+ * "attn_bwd_dq_tiles"; "attn_merge", "attn_zero_rows"), ms the elapsed
+ * milliseconds; *count receives the total number recorded. Returns
+ * ATTN_E_HIP if an event could not be read. */
 int attn_timing_read(int max_records, char* names, int name_len, float* ms, int* count);
 
 #ifdef __cplusplus

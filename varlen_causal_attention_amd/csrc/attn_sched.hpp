@@ -103,15 +103,20 @@ __device__ __forceinline__ void schedule_list(const SchedArgs& a) {
 }
 
 // Segment-major order: the items of segment 0, heaviest first (query tiles:
-// the last one; key blocks: the first one), then those of segment 1, ... The tiles of one segment and
-// head then start close together and walk the same K/V tiles in step, so a
-// tile read from HBM by one workgroup is still in L2 for the others; under a
-// global heavy-first order they start far apart in time and, without a GQA
-// group sharing the stream, miss L2. A segment's last tile walks all of its
-// keys and is emitted first, so each segment's long tiles still start first.
+// the last one; key blocks: the first one), then those of segment 1, ...
+// The tiles of one segment and head then start close together and walk the
+// same K/V tiles in step, so a tile read from HBM by one workgroup is still
+// in L2 for the others; under a global heavy-first order they start far
+// apart in time and, without a GQA group sharing the stream, miss L2. A
+// segment's last tile walks all of its keys and is emitted first, so each
+// segment's long tiles still start first.
+// Segments are taken 1024 at a time: a block-wide scan of their item counts
+// gives each one's first list position, then wave w writes segments w,
+// w+16, ... of the chunk with its lanes splitting a segment's items.
 __device__ __forceinline__ void schedule_seg_major(const SchedArgs& a) {
   constexpr int NT = 1024;
   __shared__ int wave_sum[NT / 64];
+  __shared__ int seg_pos[NT], seg_n[NT];
   __shared__ int carry;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) carry = 0;
@@ -133,11 +138,17 @@ __device__ __forceinline__ void schedule_seg_major(const SchedArgs& a) {
     __syncthreads();
     int pos = carry + incl - n;
     for (int i = 0; i < w; ++i) pos += wave_sum[i];
-    for (int j = 0; j < n; ++j, ++pos)
-      if (pos < a.max_items) a.list[pos] = make_int2(s, a.by_keys ? j : n - 1 - j);
-    __syncthreads();  // every thread has read carry and wave_sum
-    if (tid == NT - 1) carry = pos;
-    __syncthreads();
+    seg_pos[tid] = pos;
+    seg_n[tid] = n;
+    __syncthreads();  // positions published; every thread has read carry
+    if (tid == NT - 1) carry = pos + n;
+    const int len = min(NT, a.nseg - base);
+    for (int k = w; k < len; k += NT / 64) {
+      const int p0 = seg_pos[k], nk = seg_n[k];
+      for (int j = lane; j < nk; j += 64)
+        if (p0 + j < a.max_items) a.list[p0 + j] = make_int2(base + k, a.by_keys ? j : nk - 1 - j);
+    }
+    __syncthreads();  // carry written; seg_pos / seg_n free for the next chunk
   }
   if (tid == 0) *a.count = min(carry, a.max_items);
 }

@@ -117,6 +117,17 @@ def test_varlen_ragged_unequal_segments(vca, dqk, dv, hq, hkv):
         run_varlen(vca, lens_q, lens_k, hq, hkv, dqk, dv, causal, seed=21 + causal + dqk + hkv)
 
 
+@pytest.mark.parametrize("hq,hkv", [(2, 1), (1, 1)])
+def test_varlen_long_segment_and_many_segments(vca, hq, hkv):
+    # work lists with more than 64 items in one segment (a 9000-token
+    # document: 71 query tiles, 71 key blocks) and with more than 1024
+    # segments (1100 short documents), in both list orders (an even GQA group
+    # keeps the backward lists heavy-first)
+    run_varlen(vca, [9000], [9000], hq, hkv, 64, 64, True, seed=71 + hq)
+    lens = [1 + (7 * i) % 5 for i in range(1100)]
+    run_varlen(vca, lens, lens, hq, hkv, 128, 128, True, seed=73 + hq)
+
+
 def test_varlen_gqa_group_sizes(vca):
     lens = [77, 300, 5]
     for hq, hkv in [(1, 1), (8, 1), (8, 8), (6, 2)]:

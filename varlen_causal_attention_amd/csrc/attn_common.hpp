@@ -124,7 +124,15 @@ __device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
   return r;
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Through the gfx950 VALU half swap instead of an LDS permute: the swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes
+// of its second, so with both = x a lane of the lower half finds x[l + 32]
+// in the second result and a lane of the upper half x[l - 32] in the first.
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
 
 // Wait until every outstanding global load of this wave has landed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at "no wait"). Used once,

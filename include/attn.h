@@ -180,6 +180,16 @@ int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_l
                       int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
                       int max_segments, int* num_segments);
 
+/* The attn_doc_segments layout as cumulative offsets, ready for the varlen
+ * calls (host-only, no GPU work): cu_q, cu_k (host int32, room for
+ * max_segments + 1 entries) receive cu_x[0] = 0 and cu_x[s + 1] = cu_x[s] +
+ * the length of segment s; *num_segments the segment count; *max_q / *max_k
+ * the longest query / key segment (the max_q / max_k arguments of the varlen
+ * calls). Same arguments, modes and errors as attn_doc_segments. */
+int attn_doc_cu_seqlens(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                        int k_start, int k_len, int mode, int32_t* cu_q, int32_t* cu_k,
+                        int max_segments, int* num_segments, int* max_q, int* max_k);
+
 /* Dense routing of one ring chunk ("gemma4_moe cp_attention" page: the
  * dense-routing flags of the packed ring segments and the per-chunk dense
  * eligibility entry). Host-only, no GPU work. Same doc_ids, ranges and modes

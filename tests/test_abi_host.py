@@ -11,7 +11,8 @@ import pytest
 import workloads
 from oracle import attention as orc
 from varlen_causal_attention_amd import _lib
-from varlen_causal_attention_amd.ops import doc_segments
+from varlen_causal_attention_amd import ops
+from varlen_causal_attention_amd.ops import doc_cu_seqlens, doc_segments
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
 
@@ -109,6 +110,70 @@ def test_backward_workspace_query_and_shortage(lib):
     assert st == _lib.ATTN_E_INVALID
 
 
+def _fwd_varlen(lib, **kw):
+    a = dict(Tq=100, Tk=120, Hq=8, Hkv=2, nseg=3, max_q=50, max_k=60)
+    a.update(kw)
+    strides = _lib.i64_array([8 * 128, 128] * 4)
+    need = C.c_size_t(0)
+    st = lib.attn_fwd_varlen(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["nseg"], a["max_q"],
+                             a["max_k"], a["Tq"], a["Tk"], a["Hq"], a["Hkv"], 128, 128, strides,
+                             0.1, 1, None, C.byref(need), None)
+    return st, need.value
+
+
+def test_varlen_forward_bounds_must_cover_tokens(lib):
+    assert _fwd_varlen(lib)[0] == 0
+    assert _fwd_varlen(lib, max_q=0)[0] == _lib.ATTN_E_INVALID
+    assert _fwd_varlen(lib, max_k=0)[0] == _lib.ATTN_E_INVALID
+    # no keys at all: max_k may be 0
+    assert _fwd_varlen(lib, Tk=0, max_k=0)[0] == 0
+
+
+def _cpu(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("which", ["k_batch", "k_dim", "v_rows", "v_heads", "rank"])
+def test_dense_backward_rejects_mismatched_kv_before_any_launch(which):
+    """Shape checks run before the device checks, so they hold on the CPU."""
+    q, dout = _cpu(2, 4, 8, 64), _cpu(2, 4, 8, 64)
+    k, v = _cpu(2, 2, 8, 64), _cpu(2, 2, 8, 64)
+    if which == "k_batch":
+        k = _cpu(1, 2, 8, 64)
+    elif which == "k_dim":
+        k = _cpu(2, 2, 8, 128)
+    elif which == "v_rows":
+        v = _cpu(2, 2, 9, 64)
+    elif which == "v_heads":
+        v = _cpu(2, 1, 8, 64)
+    else:
+        v = _cpu(2, 2, 8)
+    with pytest.raises(ValueError, match="q/k/v shapes disagree|are \\[B, H, N, D\\]"):
+        ops.bwd_dense(dout, q, k, v, dout, None, 0.1, True)
+    with pytest.raises(ValueError, match="q/k/v shapes disagree|are \\[B, H, N, D\\]"):
+        ops.fwd_dense(q, k, v, 0.1, True)
+
+
+@pytest.mark.parametrize("which", ["k_dim", "v_rows", "v_heads", "rank"])
+def test_varlen_backward_rejects_mismatched_kv_before_any_launch(which):
+    q, dout = _cpu(16, 4, 64), _cpu(16, 4, 64)
+    k, v = _cpu(20, 2, 64), _cpu(20, 2, 64)
+    if which == "k_dim":
+        k = _cpu(20, 2, 128)
+    elif which == "v_rows":
+        v = _cpu(21, 2, 64)
+    elif which == "v_heads":
+        v = _cpu(20, 1, 64)
+    else:
+        k = _cpu(20, 2, 64, 1)
+    cu = _cpu(2)
+    with pytest.raises(ValueError, match="q/k/v shapes disagree|are \\[T, H, D\\]"):
+        ops.bwd_varlen(dout, q, k, v, dout, None, cu, cu, 16, 20, 0.1, True)
+    with pytest.raises(ValueError, match="q/k/v shapes disagree|are \\[T, H, D\\]"):
+        ops.fwd_varlen(q, k, v, cu, cu, 16, 20, 0.1, True)
+
+
 def test_merge_rejects_bad_arguments(lib):
     assert lib.attn_merge(FAKE, 2, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 4, 2, 8, None) == _lib.ATTN_E_UNSUPPORTED
     assert lib.attn_merge(FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, -1, 2, 8, None) == _lib.ATTN_E_INVALID
@@ -184,6 +249,35 @@ def test_ring_workload_layout():
     sq, sk = doc_segments(ids, 4096, 4096, 0, 4096, 1)
     assert list(np.cumsum([0] + sq)) == [0, 0, 2084, 2427, 3968, 4096]
     assert list(np.cumsum([0] + sk)) == [0, 2832, 4096, 4096, 4096, 4096]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_cu_seqlens_are_the_running_sums_of_the_segments(mode):
+    """attn_doc_cu_seqlens writes the layout attn_doc_segments describes, as
+    offsets starting at 0, with the longest segments as max_q / max_k."""
+    w = workloads.workload(5)
+    ids = w.row_doc_ids()
+    k_start = 4096 if mode == 0 else 0
+    sq, sk = doc_segments(ids, 4096, 4096, k_start, 4096, mode)
+    cu_q, cu_k, mq, mk = doc_cu_seqlens(ids, 4096, 4096, k_start, 4096, mode)
+    assert cu_q.dtype == np.int32 and len(cu_q) == len(sq) + 1 == len(cu_k)
+    assert cu_q[0] == 0 and cu_k[0] == 0
+    assert list(np.diff(cu_q)) == sq and list(np.diff(cu_k)) == sk
+    assert mq == max(sq) and mk == max(sk)
+    if mode == 0:
+        assert list(cu_q) == [0, 2084, 2427, 3968, 4096, 4096]
+    else:
+        assert list(cu_k) == [0, 2832, 4096, 4096, 4096, 4096]
+
+
+def test_cu_seqlens_reports_a_short_buffer(lib):
+    ids = np.array([[1, 1, 2, 2, 3, 0]], dtype=np.int32)
+    cu_q = (C.c_int32 * 2)()
+    cu_k = (C.c_int32 * 2)()
+    n, mq, mk = C.c_int(0), C.c_int(0), C.c_int(0)
+    st = lib.attn_doc_cu_seqlens(ids.ctypes.data_as(C.POINTER(C.c_int32)), 1, 6, 0, 6, 0, 6, 0,
+                                 cu_q, cu_k, 1, C.byref(n), C.byref(mq), C.byref(mk))
+    assert st == _lib.ATTN_E_INVALID and n.value == 5  # docs 1, 2, 3 and the pad pair
 
 
 def test_segment_builder_rejects_bad_ranges():

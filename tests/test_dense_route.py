@@ -20,8 +20,9 @@ vca = pytest.importorskip("varlen_causal_attention_amd")
 
 
 def single_doc_with_pad_suffix(row):
-    """Real (>0) tokens are one document forming a contiguous prefix; padding
-    (0), if any, is a trailing suffix. An all-padding row qualifies."""
+    """Row predicate of the "gemma4_moe cp_attention" page's single-document
+    check with a pad tail: the ids > 0 form one run that starts at position 0
+    and carries one id; any zeros come after that run. A row of zeros passes."""
     real = row[row > 0]
     if real.size == 0:
         return True

@@ -325,3 +325,47 @@ def test_sampled_rows_and_columns_match_full():
         rk, rv = orc.bwd_varlen_cols(do, q, k, v, o, l, cu_q, cu_k, 0.6, causal, kt, kh)
         np.testing.assert_allclose(rk, dk[kt, kh], atol=1e-12)
         np.testing.assert_allclose(rv, dv[kt, kh], atol=1e-12)
+
+
+def test_doc_causal_gqa_equals_mha_on_repeated_kv():
+    """GQA in the document-causal functions ("ffpa_attention" page: the forward
+    handles GQA, the backward reduces dK/dV to the Hkv heads): with Hq = 4 and
+    Hkv = 2, q-head h reads kv-head h // 2, so the result must equal the same
+    call on K/V whose heads are repeated (Hkv = Hq, one q-head per kv-head),
+    with dk/dv summed over each group of two. The equivalent hand-written
+    segments through the varlen functions must give the same numbers."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, D, Dv = 4, 2, 3, 2
+    # keys: positions 0..11; queries: the shard 5..11 (earlier keys are a
+    # second chunk for the later queries of document 2)
+    ids = np.array([1, 1, 2, 2, 2, 2, 2, 3, 3, 3, 0, 0])
+    k_pos, q_pos = np.arange(12), np.arange(5, 12)
+    q, do = _rand(rng, 7, Hq, D), _rand(rng, 7, Hq, Dv)
+    k, v = _rand(rng, 12, Hkv, D), _rand(rng, 12, Hkv, Dv)
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    args = (ids[q_pos], q_pos, ids, k_pos, 0.7)
+    o, l = orc.fwd_doc_causal(q, k, v, *args)
+    orr, lr = orc.fwd_doc_causal(q, kr, vr, *args)
+    np.testing.assert_allclose(o, orr, atol=1e-13)
+    np.testing.assert_array_equal(l, lr)
+    # heads of one group read the same keys but differ through q: the two
+    # q-heads of kv-head 0 must not coincide (guards against a collapsed map)
+    assert np.abs(o[:, 0] - o[:, 1]).max() > 1e-3
+    dq, dk, dv = orc.bwd_doc_causal(do, q, k, v, o, l, *args)
+    dqr, dkr, dvr = orc.bwd_doc_causal(do, q, kr, vr, orr, lr, *args)
+    np.testing.assert_allclose(dq, dqr, atol=1e-12)
+    np.testing.assert_allclose(dk, dkr.reshape(12, Hkv, Hq // Hkv, D).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dv, dvr.reshape(12, Hkv, Hq // Hkv, Dv).sum(axis=2), atol=1e-12)
+    # the same problem as varlen segments, written out by hand: doc 2 has its
+    # queries 5, 6 against keys 2..6 (bottom-right causal), doc 3 queries 7..9
+    # against keys 7..9, the padding queries 10, 11 against nothing; doc 1 is
+    # keys only. Query rows of the shard are 0..6, keys 0..11 in order.
+    cu_q = [0, 0, 2, 5, 7, 7]
+    cu_k = [0, 2, 7, 10, 10, 12]
+    ov, lv = orc.fwd_varlen(q, k, v, cu_q, cu_k, 0.7, True)
+    np.testing.assert_allclose(ov, o, atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(lv), np.isinf(l))
+    np.testing.assert_allclose(lv[np.isfinite(lv)], l[np.isfinite(l)], atol=1e-13)
+    gv = orc.bwd_varlen(do, q, k, v, o, l, cu_q, cu_k, 0.7, True)
+    for a, b in zip(gv, (dq, dk, dv)):
+        np.testing.assert_allclose(a, b, atol=1e-12)

@@ -23,6 +23,9 @@ MUTATIONS = {
     "dv_uses_dp": ("dv += p.T @ do[r0:r1]", "dv += (p * 0.5).T @ do[r0:r1]"),
     "merge_wrong_weight": ("wb = np.where(live, np.exp(lse_b - safe), 0.0)", "wb = np.where(live, np.exp(lse_a - safe), 0.0)"),
     "doc_ignores_pad": ("& (q_doc[:, None] > 0)", "& (q_doc[:, None] >= 0)"),
+    "doc_fwd_gqa_modulo": ("o, l = attend(q[:, h], k[:, h // G], v[:, h // G], vis, scale)", "o, l = attend(q[:, h], k[:, h % k.shape[1]], v[:, h % k.shape[1]], vis, scale)"),
+    "doc_bwd_gqa_modulo": ("a, b, c = attend_backward(do[:, h], q[:, h], k[:, h // G], v[:, h // G], o[:, h],", "a, b, c = attend_backward(do[:, h], q[:, h], k[:, h % k.shape[1]], v[:, h % k.shape[1]], o[:, h],"),
+    "doc_bwd_group_sum": ("        dk[:, h // G] += b\n", "        dk[:, h % k.shape[1]] += b\n"),
     "doc_future_keys": ("(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None])", "(np.asarray(k_pos)[None, :] >= 0)"),
 }
 

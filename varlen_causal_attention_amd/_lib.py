@@ -22,7 +22,8 @@ ATTN_DQ_ACCUMULATE = 1
 
 EXPORTED = (
     "attn_last_error", "attn_version", "attn_is_supported", "attn_fwd_dense", "attn_fwd_varlen",
-    "attn_bwd_dense", "attn_bwd_varlen", "attn_merge", "attn_doc_segments", "attn_dense_route",
+    "attn_bwd_dense", "attn_bwd_varlen", "attn_merge", "attn_doc_segments", "attn_doc_cu_seqlens",
+    "attn_dense_route",
     "attn_zero_rows", "attn_timing_enable", "attn_timing_read",
 )
 
@@ -48,6 +49,8 @@ _SIGS = {
     "attn_merge": (_I, [_P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
     "attn_doc_segments": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,
                                C.POINTER(C.c_int)]),
+    "attn_doc_cu_seqlens": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,
+                                 C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     "attn_dense_route": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _P, C.POINTER(C.c_int)]),
     "attn_zero_rows": (_I, [_P, _I, C.c_int64, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int64, _P,
                             _I, _I, _I, _I, _P]),

@@ -167,6 +167,7 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
   if (num_segments == 0 && (Tq > 0 || Tk > 0))
     return fail(ATTN_E_INVALID, "tokens given but no segments");
   if (Tq > 0 && max_q < 1) return fail(ATTN_E_INVALID, "max_q must be >= 1 when Tq > 0");
+  if (Tk > 0 && max_k < 1) return fail(ATTN_E_INVALID, "max_k must be >= 1 when Tk > 0");
   if ((st = check_tensor("q", q, Tq > 0, strides + 0, 2))) return st;
   if ((st = check_tensor("k", k, Tk > 0, strides + 2, 2))) return st;
   if ((st = check_tensor("v", v, Tk > 0, strides + 4, 2))) return st;

@@ -137,7 +137,14 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   if (pairs == 0) return hipSuccess;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   TimedLaunch timer("attn_merge", st);
-  if (a.Dv % 8 == 0 && al16(a.out_a) && al16(a.out_b) && al16(a.out) && al16(a.out_bf16)) {
+  // The 8-wide kernel writes a row's lse from the thread of its first chunk
+  // while the other chunks' threads read lse_a. When lse aliases lse_a that is
+  // only ordered if all chunks of a (row, head) sit in one wave: 64 must be a
+  // multiple of the chunk count Dv/8. Otherwise one wave per (row, head).
+  const int cpp = a.Dv / 8;
+  const bool one_wave = cpp >= 1 && cpp <= 64 && 64 % cpp == 0;
+  if (a.Dv % 8 == 0 && al16(a.out_a) && al16(a.out_b) && al16(a.out) && al16(a.out_bf16) &&
+      (one_wave || a.lse != a.lse_a)) {
     const int64_t chunks = pairs * (a.Dv / 8);
     hipLaunchKernelGGL(attn_merge8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, a);
   } else {

@@ -29,25 +29,26 @@ std::vector<Run> runs_of(const int32_t* ids, int a, int b) {
 
 }  // namespace
 
-extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
-                                 int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
-                                 int max_segments, int* num_segments) {
-  vca::set_last_error("");
-  if (!doc_ids || !num_segments || B < 0 || S < 0 || q_len < 0 || k_len < 0 || q_start < 0 ||
+namespace {
+
+// Per-segment query and key lengths of the layout (the attn_doc_segments
+// rules); ATTN_OK or ATTN_E_INVALID with the error text set.
+int build_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_len, int k_start,
+                   int k_len, int mode, std::vector<int32_t>& sq, std::vector<int32_t>& sk) {
+  if (!doc_ids || B < 0 || S < 0 || q_len < 0 || k_len < 0 || q_start < 0 ||
       k_start < 0 || q_start + q_len > S || k_start + k_len > S || (mode != 0 && mode != 1)) {
-    vca::set_last_error("attn_doc_segments: invalid arguments");
+    vca::set_last_error("doc layout: invalid arguments");
     return ATTN_E_INVALID;
   }
   const int q_end = q_start + q_len, k_end = k_start + k_len;
   if (mode == 0 && !(k_start <= q_start && q_end <= k_end)) {
-    vca::set_last_error("attn_doc_segments: causal mode needs the key range to cover the query range");
+    vca::set_last_error("doc layout: causal mode needs the key range to cover the query range");
     return ATTN_E_INVALID;
   }
   if (mode == 1 && k_end > q_start) {
-    vca::set_last_error("attn_doc_segments: cross mode needs every key before every query");
+    vca::set_last_error("doc layout: cross mode needs every key before every query");
     return ATTN_E_INVALID;
   }
-  std::vector<int32_t> sq, sk;
   for (int b = 0; b < B; ++b) {
     const int32_t* ids = doc_ids + (size_t)b * S;
     if (mode == 0) {
@@ -104,6 +105,22 @@ extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_sta
       }
     }
   }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                                 int k_start, int k_len, int mode, int32_t* seg_q, int32_t* seg_k,
+                                 int max_segments, int* num_segments) {
+  vca::set_last_error("");
+  if (!num_segments) {
+    vca::set_last_error("attn_doc_segments: invalid arguments");
+    return ATTN_E_INVALID;
+  }
+  std::vector<int32_t> sq, sk;
+  const int st = build_segments(doc_ids, B, S, q_start, q_len, k_start, k_len, mode, sq, sk);
+  if (st != ATTN_OK) return st;
   *num_segments = (int)sq.size();
   if ((int)sq.size() > max_segments || !seg_q || !seg_k) {
     vca::set_last_error("attn_doc_segments: max_segments too small, " + std::to_string(sq.size()) +
@@ -114,6 +131,38 @@ extern "C" int attn_doc_segments(const int32_t* doc_ids, int B, int S, int q_sta
     seg_q[i] = sq[i];
     seg_k[i] = sk[i];
   }
+  return ATTN_OK;
+}
+
+// The same layout as cumulative offsets, ready for the varlen calls:
+// cu_q[0] = cu_k[0] = 0 and cu_x[s + 1] = cu_x[s] + length of segment s.
+extern "C" int attn_doc_cu_seqlens(const int32_t* doc_ids, int B, int S, int q_start, int q_len,
+                                   int k_start, int k_len, int mode, int32_t* cu_q, int32_t* cu_k,
+                                   int max_segments, int* num_segments, int* max_q, int* max_k) {
+  vca::set_last_error("");
+  if (!num_segments || !max_q || !max_k) {
+    vca::set_last_error("attn_doc_cu_seqlens: invalid arguments");
+    return ATTN_E_INVALID;
+  }
+  std::vector<int32_t> sq, sk;
+  const int st = build_segments(doc_ids, B, S, q_start, q_len, k_start, k_len, mode, sq, sk);
+  if (st != ATTN_OK) return st;
+  *num_segments = (int)sq.size();
+  if ((int)sq.size() > max_segments || !cu_q || !cu_k) {
+    vca::set_last_error("attn_doc_cu_seqlens: max_segments too small, " +
+                        std::to_string(sq.size()) + " needed");
+    return ATTN_E_INVALID;
+  }
+  int mq = 0, mk = 0;
+  cu_q[0] = cu_k[0] = 0;
+  for (size_t i = 0; i < sq.size(); ++i) {
+    cu_q[i + 1] = cu_q[i] + sq[i];
+    cu_k[i + 1] = cu_k[i] + sk[i];
+    mq = sq[i] > mq ? sq[i] : mq;
+    mk = sk[i] > mk ? sk[i] : mk;
+  }
+  *max_q = mq;
+  *max_k = mk;
   return ATTN_OK;
 }
 

@@ -41,6 +41,28 @@ def _need_gpu_bf16(**tensors):
     return dev
 
 
+def _dense_shapes(q, k, v):
+    """(B, Hq, Hkv, Nq, Nk, Dqk, Dv) of dense [B, H, N, D] q/k/v, or ValueError."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("dense tensors are [B, H, N, D]")
+    B, Hq, Nq, Dqk = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if Bk != B or Dk != Dqk or tuple(v.shape[:3]) != tuple(k.shape[:3]):
+        raise ValueError("q/k/v shapes disagree")
+    return B, Hq, Hkv, Nq, Nk, Dqk, v.shape[3]
+
+
+def _varlen_shapes(q, k, v):
+    """(Tq, Tk, Hq, Hkv, Dqk, Dv) of packed [T, H, D] q/k/v, or ValueError."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("varlen tensors are [T, H, D]")
+    Tq, Hq, Dqk = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Dk != Dqk or tuple(v.shape[:2]) != tuple(k.shape[:2]):
+        raise ValueError("q/k/v shapes disagree")
+    return Tq, Tk, Hq, Hkv, Dqk, v.shape[2]
+
+
 def _workspace(size: int, device) -> torch.Tensor:
     return torch.empty(max(size, 16), dtype=torch.uint8, device=device)
 
@@ -58,14 +80,8 @@ def version() -> int:
 # ---------------------------------------------------------------------------
 def fwd_dense(q, k, v, scale: float, causal: bool):
     """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log)."""
+    B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     dev = _need_gpu_bf16(q=q, k=k, v=v)
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("dense tensors are [B, H, N, D]")
-    B, Hq, Nq, Dqk = q.shape
-    Bk, Hkv, Nk, Dk = k.shape
-    if Bk != B or Dk != Dqk or v.shape[:3] != k.shape[:3]:
-        raise ValueError("q/k/v shapes disagree")
-    Dv = v.shape[3]
     out = torch.empty((B, Hq, Nq, Dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     strides = i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
@@ -84,12 +100,10 @@ def fwd_dense(q, k, v, scale: float, causal: bool):
 def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate=None):
     """(dq, dk, dv) from the caller's out/lse; dk/dv have Hkv heads.
     dq_accumulate: an existing dq tensor to add this call's dq into."""
-    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
-    B, Hq, Nq, Dqk = q.shape
-    _, Hkv, Nk, _ = k.shape
-    Dv = v.shape[3]
+    B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     if tuple(out.shape) != (B, Hq, Nq, Dv) or tuple(dout.shape) != (B, Hq, Nq, Dv):
         raise ValueError("out/dout must be [B, Hq, Nq, Dv]")
+    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, Hq, Nq]")
     if lse.device != dev:
@@ -129,16 +143,10 @@ def _cu(cu, dev):
 
 def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool):
     """out [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 (natural log)."""
-    dev = _need_gpu_bf16(q=q, k=k, v=v)
-    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
-        raise ValueError("varlen tensors are [T, H, D]")
-    Tq, Hq, Dqk = q.shape
-    Tk, Hkv, Dk = k.shape
-    if Dk != Dqk or v.shape[:2] != k.shape[:2]:
-        raise ValueError("q/k/v shapes disagree")
+    Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if cu_q.numel() != cu_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
-    Dv = v.shape[2]
+    dev = _need_gpu_bf16(q=q, k=k, v=v)
     out = torch.empty((Tq, Hq, Dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
     strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
@@ -158,12 +166,10 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
 def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float,
                causal: bool, dq_accumulate=None):
     """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse."""
-    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
-    Tq, Hq, Dqk = q.shape
-    Tk, Hkv, _ = k.shape
-    Dv = v.shape[2]
+    Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if tuple(out.shape) != (Tq, Hq, Dv) or tuple(dout.shape) != (Tq, Hq, Dv):
         raise ValueError("out/dout must be [Tq, Hq, Dv]")
+    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [Hq, Tq]")
     if lse.device != dev:
@@ -251,13 +257,29 @@ def doc_segments(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mo
     return list(sq[:n.value]), list(sk[:n.value])
 
 
+def doc_cu_seqlens(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int):
+    """(cu_q, cu_k host int32 numpy arrays, max_q, max_k) of doc_segments'
+    layout, as the library writes them."""
+    ids = np.ascontiguousarray(np.asarray(doc_ids, dtype=np.int32))
+    if ids.ndim != 2:
+        raise ValueError("doc_ids is [B, S]")
+    B, S = ids.shape
+    cap = 2 * S * max(B, 1) + 2
+    cu_q = np.zeros(cap + 1, dtype=np.int32)
+    cu_k = np.zeros(cap + 1, dtype=np.int32)
+    n, mq, mk = C.c_int(0), C.c_int(0), C.c_int(0)
+    i32p = C.POINTER(C.c_int32)
+    st = load().attn_doc_cu_seqlens(ids.ctypes.data_as(i32p), B, S, q_start, q_len, k_start, k_len,
+                                    mode, cu_q.ctypes.data_as(i32p), cu_k.ctypes.data_as(i32p),
+                                    cap, C.byref(n), C.byref(mq), C.byref(mk))
+    check(st, "attn_doc_cu_seqlens")
+    return cu_q[:n.value + 1].copy(), cu_k[:n.value + 1].copy(), mq.value, mk.value
+
+
 def doc_layout(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int, device):
     """(cu_q, cu_k int32 on device, max_q, max_k) of doc_segments' layout."""
-    sq, sk = doc_segments(doc_ids, q_start, q_len, k_start, k_len, mode)
-    cu_q = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
-    cu_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
-    return (torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_k).to(device),
-            int(max(sq, default=0)), int(max(sk, default=0)))
+    cu_q, cu_k, mq, mk = doc_cu_seqlens(doc_ids, q_start, q_len, k_start, k_len, mode)
+    return torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_k).to(device), mq, mk
 
 
 def dense_route(doc_ids, q_start: int, q_len: int, k_start: int, k_len: int, mode: int):

@@ -4,11 +4,14 @@ one MI355X. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload N] [--all]
 
-The default workload is the packed-varlen document-causal D=128 problem
-(T=16384, Hq=32, Hkv=8); ``--workload`` picks another of the six
-(1 small dense, 2 varlen D128, 3 dense D512, 4 varlen 192/128, 5 ring share,
-6 ring share of a single-document row, whose chunks take the dense route),
-``--all`` adds per-workload numbers for every one of them to the line.
+The headline (``value``) is the largest workload that fits one GPU: packed
+varlen document-causal attention with unequal head dims (T=32768, H=32,
+Dqk=192, Dv=128; 8.2 TFLOP per step). The same line carries, under
+``configs``, forward/backward TFLOP/s, % of peak and a roofline entry for each
+of the four large workloads (2 varlen D128, 3 dense D512, 4 varlen 192/128,
+5 ring share D512). ``--workload`` moves the headline to another of the six
+(1 small dense, 2, 3, 4, 5, 6 ring share of a single-document row, whose
+chunks take the dense route); ``--all`` adds every workload's full record.
 Throughput is causal-adjusted: FLOPs count only visible (query, key) pairs,
 forward 2*pairs*(Dqk+Dv), backward 2*pairs*(3*Dqk+2*Dv).
 """
@@ -401,12 +404,35 @@ def blas_name() -> str:
         return "unknown"
 
 
+LARGE_WORKLOADS = (2, 3, 4, 5)
+
+
+def config_entry(w: "workloads.Workload", r: dict) -> dict:
+    """Per-config summary: step, forward and backward throughput against the
+    bf16 MFMA peak, per-call medians, and the dominant kernel's roofline."""
+    pct = lambda x: round(100 * x / PEAK_BF16_TFLOPS, 2)  # noqa: E731
+    e = {"ms_per_step": round(r["ms_per_step"], 4), "tflops_step": round(r["tflops_step"], 2),
+         "pct_of_peak": pct(r["tflops_step"]),
+         "fwd": {"ms": round(r["fwd_ms"], 4), "tflops": round(r["fwd_tflops"], 2),
+                 "pct_of_peak": pct(r["fwd_tflops"])},
+         "bwd": {"ms": round(r["bwd_ms"], 4), "tflops": round(r["bwd_tflops"], 2),
+                 "pct_of_peak": pct(r["bwd_tflops"])},
+         "pairs": r["pairs"], "roofline": roofline(w, r["kernels"]),
+         "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in r["kernels"].items()}}
+    for k in ("fwd_calls", "bwd_calls", "merge_calls"):
+        if k in r:
+            e[k] = r[k]
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config entries of the other large workloads")
     ap.add_argument("--all", action="store_true", help="also report every workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -452,6 +478,13 @@ def main():
         "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in m["kernels"].items()},
         "wall_ms_per_step": round(m["wall_ms_per_step"], 4),
     }
+    if not args.no_configs:
+        # forward / backward throughput and the roofline of each large workload
+        configs = {}
+        for n in LARGE_WORKLOADS:
+            r = m if n == args.workload else measure(n, max(5, args.steps // 2), 3)
+            configs[r["workload"]] = config_entry(workloads.workload(n), r)
+        line["configs"] = configs
     if args.all:
         per = {}
         flush = L2Flush()

@@ -194,16 +194,108 @@ def test_dense_bshd_views_and_d512(vca):
 
 
 # ---------------------------------------------------------------- full-size workloads
-def _segment_slice_check(vca, w, t, seg, kv_heads):
+def nan_like(shape, dtype=torch.bfloat16):
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def assert_all_written(**tensors):
+    """Outputs start NaN-filled, so an element no work item wrote (a dropped or
+    misrouted tile) is still NaN."""
+    for name, x in tensors.items():
+        assert not torch.isnan(x).any().item(), f"{name}: elements left unwritten"
+
+
+def run_full_varlen(vca, w, t):
+    """The whole varlen workload on the GPU, into NaN-filled outputs."""
+    cq = dev(torch.from_numpy(w.cu()))
+    mx = max(w.lengths)
+    T = w.T
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    out, lse = nan_like((T, w.Hq, w.Dv)), nan_like((w.Hq, T), torch.float32)
+    vca.fwd_varlen(q, k, v, cq, cq, mx, mx, w.scale, w.causal, out=out, lse=lse)
+    dq, dk, dv = nan_like((T, w.Hq, w.Dqk)), nan_like((T, w.Hkv, w.Dqk)), nan_like((T, w.Hkv, w.Dv))
+    vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, mx, mx, w.scale, w.causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert_all_written(out=out, lse=lse, dq=dq, dk=dk, dv=dv)
+    return out, lse, (dq, dk, dv)
+
+
+class _Lookup:
+    """Indexable stand-in for an oracle-side array of which only a few entries
+    are known (the oracle's sampled rows): x[i, j] returns the stored entry."""
+
+    def __init__(self, keys, values):
+        self.d = {tuple(int(e) for e in k): v for k, v in zip(keys, values)}
+
+    def __getitem__(self, idx):
+        return self.d[tuple(int(e) for e in idx)]
+
+
+def check_sampled(vca_out, t, cu, Hq, Hkv, scale, causal, seed, rows_per=2):
+    """Every segment x q-head: `rows_per` seeded query rows (out, lse, dq);
+    every non-empty segment x kv-head: one seeded key row (dk, dv), in the last
+    eighth of the segment when causal (few queries see it, so the oracle's
+    sub-problem stays small), plus per segment one key anywhere for one kv-head
+    (rotating). The oracle side is computed from the inputs alone: sampled
+    rows through its row samplers, key rows from the forward and backward of
+    exactly the queries that see the key."""
+    out, lse, (dq, dk, dv) = vca_out
+    rng = np.random.default_rng(seed)
+    G = Hq // Hkv
+    # the row samplers slice k / v per row: upcast them once
+    t = dict(t, k=orc.f64(t["k"]), v=orc.f64(t["v"]))
+    toks, heads = [], []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in range(Hq):
+            pick = rng.integers(a, b, size=rows_per)
+            pick[0] = a if h % 2 == 0 else b - 1  # segment edges on alternate heads
+            toks += [int(x) for x in pick]
+            heads += [h] * rows_per
+    toks, heads = np.array(toks), np.array(heads)
+    it, ih = torch.from_numpy(toks).to(out.device), torch.from_numpy(heads).to(out.device)
+    ro, rl = orc.fwd_varlen_rows(t["q"], t["k"], t["v"], cu, cu, scale, causal, toks, heads)
+    check_out(out[it, ih], ro)
+    check_lse(lse[ih, it], rl)
+    rdq = orc.bwd_varlen_rows(t["do"], t["q"], t["k"], t["v"],
+                              _Lookup(zip(toks, heads), ro), _Lookup(zip(heads, toks), rl),
+                              cu, cu, scale, causal, toks, heads)
+    check_grad("dq rows", dq[it, ih], rdq)
+    gk, gv, rk, rv = [], [], [], []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        L = b - a
+        anywhere = s % Hkv
+        for g in range(Hkv):
+            lo = 0 if (not causal or g == anywhere) else (7 * L) // 8
+            j = int(rng.integers(lo, L))
+            i0 = j if causal else 0  # first query that sees key j (lq = lk)
+            hs = list(range(g * G, (g + 1) * G))
+            qq, dd = t["q"][a + i0:b][:, hs], t["do"][a + i0:b][:, hs]
+            kk, vv = t["k"][a:b][:, [g]], t["v"][a:b][:, [g]]
+            # bottom-right alignment keeps the visibility of the kept rows:
+            # row i - i0 of L - i0 rows sees keys <= (i - i0) + L - (L - i0) = i
+            cq1, ck1 = [0, L - i0], [0, L]
+            so, sl = orc.fwd_varlen(qq, kk, vv, cq1, ck1, scale, causal)
+            k1, v1 = orc.bwd_varlen_cols(dd, qq, kk, vv, so, sl, cq1, ck1, scale, causal,
+                                         [j], [0])
+            rk.append(k1[0])
+            rv.append(v1[0])
+            gk.append(dk[a + j, g])
+            gv.append(dv[a + j, g])
+    check_grad("dk rows", torch.stack(gk), np.array(rk))
+    check_grad("dv rows", torch.stack(gv), np.array(rv))
+
+
+def _segment_slice_check(vca, w, t, seg, kv_heads, res=None):
     """Run the whole workload on the GPU; check one segment x kv-head groups
     against the oracle, computed fully for that slice."""
     cu = w.cu()
-    cq = dev(torch.from_numpy(cu))
-    mx = max(w.lengths)
-    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
-    out, lse = vca.fwd_varlen(q, k, v, cq, cq, mx, mx, w.scale, w.causal)
-    dq, dk, dv = vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, mx, mx, w.scale, w.causal)
-    torch.cuda.synchronize()
+    out, lse, (dq, dk, dv) = res if res is not None else run_full_varlen(vca, w, t)
     a, b = int(cu[seg]), int(cu[seg + 1])
     G = w.Hq // w.Hkv
     for g in kv_heads:
@@ -224,27 +316,43 @@ def _segment_slice_check(vca, w, t, seg, kv_heads):
 def test_varlen_d128_workload_full_size(vca):
     w = workloads.workload(2)
     t = w.tensors()
-    out, lse, grads = _segment_slice_check(vca, w, t, seg=0, kv_heads=[0, 7])
-    _segment_slice_check(vca, w, t, seg=7, kv_heads=[3])
+    res = run_full_varlen(vca, w, t)
+    out, lse, grads = _segment_slice_check(vca, w, t, seg=0, kv_heads=[0, 7], res=res)
+    _segment_slice_check(vca, w, t, seg=7, kv_heads=[3], res=res)
     # properties at full size: finite everywhere, no empty row in causal self-attention
     assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
     for gtn in grads:
         assert torch.isfinite(gtn.float()).all()
+    check_sampled(res, t, w.cu(), w.Hq, w.Hkv, w.scale, True, seed=202)
 
 
 def test_varlen_192_128_workload_full_size(vca):
     w = workloads.workload(4)
     t = w.tensors()
-    _segment_slice_check(vca, w, t, seg=4, kv_heads=[13])
+    res = run_full_varlen(vca, w, t)
+    _segment_slice_check(vca, w, t, seg=4, kv_heads=[13], res=res)
+    check_sampled(res, t, w.cu(), w.Hq, w.Hkv, w.scale, True, seed=204)
 
 
 def test_dense_d512_workload_full_size(vca):
     w = workloads.workload(3)
     t = w.tensors()
     q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
-    out, lse = vca.fwd_dense(q, k, v, w.scale, True)
-    dq, dk, dv = vca.bwd_dense(do, q, k, v, out, lse, w.scale, True)
+    B, N = w.B, w.Nq
+    out, lse = nan_like((B, w.Hq, N, w.Dv)), nan_like((B, w.Hq, N), torch.float32)
+    vca.fwd_dense(q, k, v, w.scale, True, out=out, lse=lse)
+    dq, dk, dv = (nan_like((B, w.Hq, N, w.Dqk)), nan_like((B, w.Hkv, N, w.Dqk)),
+                  nan_like((B, w.Hkv, N, w.Dv)))
+    vca.bwd_dense(do, q, k, v, out, lse, w.scale, True, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
+    assert_all_written(out=out, lse=lse, dq=dq, dk=dk, dv=dv)
+    # every batch x head through the row samplers: the dense problem is the
+    # varlen one with one segment per batch entry ([B, H, N, D] -> [B*N, H, D])
+    thd = lambda x: x.transpose(1, 2).reshape(B * N, x.shape[1], x.shape[3])  # noqa: E731
+    tt = {n: thd(t[n]) for n in ("q", "k", "v", "do")}
+    res = (thd(out), lse.reshape(B, w.Hq, N).transpose(0, 1).reshape(w.Hq, B * N),
+           (thd(dq), thd(dk), thd(dv)))
+    check_sampled(res, tt, np.array([0, N, 2 * N]), w.Hq, w.Hkv, w.scale, True, seed=203)
     b, g = 1, 5
     G = w.Hq // w.Hkv
     hs = list(range(g * G, (g + 1) * G))
@@ -268,12 +376,20 @@ def ring_share(vca, w, t):
     xq_cu, xk_cu, xmq, xmk = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
     q, do = dev(t["q"]), dev(t["do"])
     kl, vl, ke, ve = (dev(t[n]) for n in ("k_local", "v_local", "k_early", "v_early"))
-    o1, l1 = vca.fwd_varlen(q, kl, vl, lq_cu, lk_cu, lmq, lmk, w.scale, True)
-    o2, l2 = vca.fwd_varlen(q, ke, ve, xq_cu, xk_cu, xmq, xmk, w.scale, False)
+    H, Hkv = w.Hq, w.Hkv
+    o1, l1 = nan_like((S, H, w.Dv)), nan_like((H, S), torch.float32)
+    o2, l2 = nan_like((S, H, w.Dv)), nan_like((H, S), torch.float32)
+    vca.fwd_varlen(q, kl, vl, lq_cu, lk_cu, lmq, lmk, w.scale, True, out=o1, lse=l1)
+    vca.fwd_varlen(q, ke, ve, xq_cu, xk_cu, xmq, xmk, w.scale, False, out=o2, lse=l2)
     mo, ml, mob = vca.merge(o1, l1, o2, l2, bf16_copy=True)
-    dq, dkl, dvl = vca.bwd_varlen(do, q, kl, vl, mob, ml, lq_cu, lk_cu, lmq, lmk, w.scale, True)
-    _, dke, dve = vca.bwd_varlen(do, q, ke, ve, mob, ml, xq_cu, xk_cu, xmq, xmk, w.scale, False,
-                                 dq_accumulate=dq)
+    dq, dkl, dvl = nan_like((S, H, w.Dqk)), nan_like((S, Hkv, w.Dqk)), nan_like((S, Hkv, w.Dv))
+    dke, dve = nan_like((S, Hkv, w.Dqk)), nan_like((S, Hkv, w.Dv))
+    vca.bwd_varlen(do, q, kl, vl, mob, ml, lq_cu, lk_cu, lmq, lmk, w.scale, True, dq=dq, dk=dkl,
+                   dv=dvl)
+    vca.bwd_varlen(do, q, ke, ve, mob, ml, xq_cu, xk_cu, xmq, xmk, w.scale, False,
+                   dq_accumulate=dq, dk=dke, dv=dve)
+    torch.cuda.synchronize()
+    assert_all_written(o1=o1, l1=l1, o2=o2, l2=l2, dq=dq, dkl=dkl, dvl=dvl, dke=dke, dve=dve)
     return (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve)
 
 
@@ -340,6 +456,57 @@ def test_ring_share_workload(vca, n):
         check_grad("dv_early", dve[:, [g]], rdv[:S])
         check_grad("dk_local", dkl[:, [g]], rdk[S:])
         check_grad("dv_local", dvl[:, [g]], rdv[S:])
+    # every other kv-head group: seeded query rows (merged out, lse, dq) and
+    # key rows of both chunks (dk, dv), the oracle computing each from the
+    # inputs over exactly the rows involved
+    rng = np.random.default_rng(205 + n)
+    all_pos = np.arange(0, 2 * S)
+    k_all_t = torch.cat([t["k_early"], t["k_local"]])
+    v_all_t = torch.cat([t["v_early"], t["v_local"]])
+    gq, rq, go, ro_s, gl, rl_s = [], [], [], [], [], []
+    gk, rk, gv, rv = [], [], [], []
+    for g in range(w.Hkv):
+        if g in (0, 6):
+            continue
+        hs = list(range(g * G, (g + 1) * G))
+        rows = rng.choice(S, size=12, replace=False)
+        q, do = t["q"][rows][:, hs], t["do"][rows][:, hs]
+        ka, va = k_all_t[:, [g]], v_all_t[:, [g]]
+        o_r, l_r = orc.fwd_doc_causal(q, ka, va, ids[q_pos[rows]], q_pos[rows], ids, all_pos,
+                                      w.scale)
+        dq_r = orc.bwd_doc_causal(do, q, ka, va, o_r, l_r, ids[q_pos[rows]], q_pos[rows], ids,
+                                  all_pos, w.scale)[0]
+        ir = torch.from_numpy(rows).cuda()
+        go.append(mo[ir][:, hs].float().cpu())
+        ro_s.append(o_r)
+        gl.append(ml[hs][:, ir].cpu())
+        rl_s.append(l_r)
+        gq.append(dq[ir][:, hs].float().cpu())
+        rq.append(dq_r)
+        for j in rng.choice(2 * S, size=4, replace=False):
+            j = int(j)
+            seen = np.nonzero((ids[q_pos] == ids[j]) & (ids[j] > 0) & (q_pos >= j))[0]
+            got_k = (dke if j < S else dkl)[j % S, g].float().cpu()
+            got_v = (dve if j < S else dvl)[j % S, g].float().cpu()
+            if len(seen) == 0:
+                exp_k, exp_v = np.zeros(w.Dqk), np.zeros(w.Dv)
+            else:
+                qs, ds = t["q"][seen][:, hs], t["do"][seen][:, hs]
+                o_s, l_s = orc.fwd_doc_causal(qs, ka, va, ids[q_pos[seen]], q_pos[seen], ids,
+                                              all_pos, w.scale)
+                _, bk, bv = orc.bwd_doc_causal(ds, qs, ka[[j]], va[[j]], o_s, l_s,
+                                               ids[q_pos[seen]], q_pos[seen], ids[[j]], [j],
+                                               w.scale)
+                exp_k, exp_v = bk[0, 0], bv[0, 0]
+            gk.append(got_k)
+            rk.append(exp_k)
+            gv.append(got_v)
+            rv.append(exp_v)
+    check_out(torch.stack(go), np.stack(ro_s))
+    check_lse(torch.stack(gl), np.stack(rl_s))
+    check_grad("dq rows", torch.stack(gq), np.stack(rq))
+    check_grad("dk rows", torch.stack(gk), np.stack(rk))
+    check_grad("dv rows", torch.stack(gv), np.stack(rv))
     # padding queries: out 0, lse -inf, dq 0
     pad = np.nonzero(ids[q_pos] == 0)[0]
     assert len(pad) == w.pad_tail
@@ -510,3 +677,56 @@ def test_dq_accumulate_adds(vca):
     torch.cuda.synchronize()
     ref = dq1.float() * 2
     assert (acc.float() - ref).abs().max().item() <= 2 ** -7 * ref.abs().max().item() + 1e-6
+
+
+def test_varlen_and_gradient_outputs_stay_inside_their_views(vca):
+    """Guard bands for the varlen forward and both backward entries: out, dq,
+    dk and dv written through strided views of larger NaN-filled buffers leave
+    every element outside the view untouched and match plain outputs."""
+    g = torch.Generator().manual_seed(92)
+    lens = [70, 1, 200, 33]
+    cu = workloads.cumulative(lens)
+    T, Hq, Hkv = int(cu[-1]), 4, 2
+    cq = dev(torch.from_numpy(cu))
+    for dqk, dv_ in [(128, 128), (192, 128), (512, 512)]:
+        q, do = dev(rand((T, Hq, dqk), g)), dev(rand((T, Hq, dv_), g))
+        k, v = dev(rand((T, Hkv, dqk), g)), dev(rand((T, Hkv, dv_), g))
+        scale = 1 / math.sqrt(dqk)
+
+        def banded(h, d):
+            big = nan_like((T + 9, h + 1, d + 48))
+            return big, big[5:5 + T, 1:, 16:16 + d]
+
+        bo, out = banded(Hq, dv_)
+        vca.fwd_varlen(q, k, v, cq, cq, 200, 200, scale, True, out=out)
+        bq, dq = banded(Hq, dqk)
+        bk, dk = banded(Hkv, dqk)
+        bv, dv = banded(Hkv, dv_)
+        ref_o, lse = vca.fwd_varlen(q, k, v, cq, cq, 200, 200, scale, True)
+        vca.bwd_varlen(do, q, k, v, ref_o, lse, cq, cq, 200, 200, scale, True, dq=dq, dk=dk, dv=dv)
+        ref = vca.bwd_varlen(do, q, k, v, ref_o, lse, cq, cq, 200, 200, scale, True)
+        torch.cuda.synchronize()
+        for big, view, want in ((bo, out, ref_o), (bq, dq, ref[0]), (bk, dk, ref[1]),
+                                (bv, dv, ref[2])):
+            mask = torch.ones_like(big, dtype=torch.bool)
+            mask[5:5 + T, 1:, 16:16 + view.shape[2]] = False
+            assert torch.isnan(big[mask].float()).all(), f"write outside the view ({dqk})"
+            assert torch.equal(view, want), f"view result differs ({dqk})"
+
+
+def test_merge_in_place_with_head_dims_that_split_waves(vca):
+    """In-place merge (lse aliasing lse_a) at head dims whose 8-element chunks
+    do not tile a wave (Dv/8 not a divisor of 64, or above 64): every row's
+    lse must still be combined from the original lse_a."""
+    g = torch.Generator().manual_seed(72)
+    for rows, H, Dv in ((97, 3, 96), (64, 2, 192), (40, 2, 1024)):
+        oa, ob = rand((rows, H, Dv), g).float(), rand((rows, H, Dv), g)
+        la = torch.randn((H, rows), generator=g) * 3
+        lb = torch.randn((H, rows), generator=g) * 3
+        la[0, :7] = -math.inf
+        ro, rl = orc.merge(oa, la, ob, lb)
+        acc, lacc = dev(oa.clone()), dev(la.clone())
+        vca.merge(acc, lacc, dev(ob), dev(lb), out=acc, lse=lacc)
+        torch.cuda.synchronize()
+        assert np.abs(host(acc) - ro).max() < 1e-5, Dv
+        check_lse(lacc, rl)

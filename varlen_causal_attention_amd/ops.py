@@ -63,6 +63,27 @@ def _varlen_shapes(q, k, v):
     return Tq, Tk, Hq, Hkv, Dqk, v.shape[2]
 
 
+def _output(t, shape, dtype, dev, name):
+    """A caller-supplied output (any strides with a unit last one), checked, or
+    a new tensor. The library writes every element of an output, so a caller
+    may pass e.g. a view into a larger buffer."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != dev:
+        raise ValueError(f"{name} must be a {dtype} tensor on {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return t
+
+
+def _lse_output(t, shape, dev):
+    if t is not None and not t.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    return _output(t, shape, torch.float32, dev, "lse")
+
+
 def _workspace(size: int, device) -> torch.Tensor:
     return torch.empty(max(size, 16), dtype=torch.uint8, device=device)
 
@@ -78,12 +99,13 @@ def version() -> int:
 # ---------------------------------------------------------------------------
 # dense [B, H, N, D]
 # ---------------------------------------------------------------------------
-def fwd_dense(q, k, v, scale: float, causal: bool):
-    """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log)."""
+def fwd_dense(q, k, v, scale: float, causal: bool, out=None, lse=None):
+    """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log). out / lse
+    may be given (out as any view with a unit last stride, lse contiguous)."""
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     dev = _need_gpu_bf16(q=q, k=k, v=v)
-    out = torch.empty((B, Hq, Nq, Dv), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    out = _output(out, (B, Hq, Nq, Dv), torch.bfloat16, dev, "out")
+    lse = _lse_output(lse, (B, Hq, Nq), dev)
     strides = i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
                         + list(out.stride()[:3]))
     lib = load()
@@ -97,9 +119,11 @@ def fwd_dense(q, k, v, scale: float, causal: bool):
     return out, lse
 
 
-def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate=None):
+def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate=None,
+              dq=None, dk=None, dv=None):
     """(dq, dk, dv) from the caller's out/lse; dk/dv have Hkv heads.
-    dq_accumulate: an existing dq tensor to add this call's dq into."""
+    dq_accumulate: an existing dq tensor to add this call's dq into.
+    dq / dk / dv: optional output views (unit last stride)."""
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     if tuple(out.shape) != (B, Hq, Nq, Dv) or tuple(dout.shape) != (B, Hq, Nq, Dv):
         raise ValueError("out/dout must be [B, Hq, Nq, Dv]")
@@ -113,12 +137,14 @@ def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate
         _need_gpu_bf16(dq=dq_accumulate)
         if tuple(dq_accumulate.shape) != tuple(q.shape):
             raise ValueError("dq_accumulate must have q's shape")
+        if dq is not None:
+            raise ValueError("give dq or dq_accumulate, not both")
         dq = dq_accumulate
         flags |= ATTN_DQ_ACCUMULATE
     else:
-        dq = torch.empty((B, Hq, Nq, Dqk), dtype=torch.bfloat16, device=dev)
-    dk = torch.empty((B, Hkv, Nk, Dqk), dtype=torch.bfloat16, device=dev)
-    dv = torch.empty((B, Hkv, Nk, Dv), dtype=torch.bfloat16, device=dev)
+        dq = _output(dq, (B, Hq, Nq, Dqk), torch.bfloat16, dev, "dq")
+    dk = _output(dk, (B, Hkv, Nk, Dqk), torch.bfloat16, dev, "dk")
+    dv = _output(dv, (B, Hkv, Nk, Dv), torch.bfloat16, dev, "dv")
     strides = i64_array(sum((list(t.stride()[:3]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
     lib = load()
     args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
@@ -141,14 +167,16 @@ def _cu(cu, dev):
     return C.c_void_p(cu.data_ptr())
 
 
-def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool):
-    """out [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 (natural log)."""
+def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool,
+               out=None, lse=None):
+    """out [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 (natural log). out / lse may
+    be given (out as any view with a unit last stride, lse contiguous)."""
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if cu_q.numel() != cu_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     dev = _need_gpu_bf16(q=q, k=k, v=v)
-    out = torch.empty((Tq, Hq, Dv), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    out = _output(out, (Tq, Hq, Dv), torch.bfloat16, dev, "out")
+    lse = _lse_output(lse, (Hq, Tq), dev)
     strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
                         + list(out.stride()[:2]))
     lib = load()
@@ -164,8 +192,9 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
 
 
 def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float,
-               causal: bool, dq_accumulate=None):
-    """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse."""
+               causal: bool, dq_accumulate=None, dq=None, dk=None, dv=None):
+    """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse.
+    dq / dk / dv: optional output views (unit last stride)."""
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if tuple(out.shape) != (Tq, Hq, Dv) or tuple(dout.shape) != (Tq, Hq, Dv):
         raise ValueError("out/dout must be [Tq, Hq, Dv]")
@@ -181,12 +210,14 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
         _need_gpu_bf16(dq=dq_accumulate)
         if tuple(dq_accumulate.shape) != tuple(q.shape):
             raise ValueError("dq_accumulate must have q's shape")
+        if dq is not None:
+            raise ValueError("give dq or dq_accumulate, not both")
         dq = dq_accumulate
         flags |= ATTN_DQ_ACCUMULATE
     else:
-        dq = torch.empty((Tq, Hq, Dqk), dtype=torch.bfloat16, device=dev)
-    dk = torch.empty((Tk, Hkv, Dqk), dtype=torch.bfloat16, device=dev)
-    dv = torch.empty((Tk, Hkv, Dv), dtype=torch.bfloat16, device=dev)
+        dq = _output(dq, (Tq, Hq, Dqk), torch.bfloat16, dev, "dq")
+    dk = _output(dk, (Tk, Hkv, Dqk), torch.bfloat16, dev, "dk")
+    dv = _output(dv, (Tk, Hkv, Dv), torch.bfloat16, dev, "dv")
     strides = i64_array(sum((list(t.stride()[:2]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
     lib = load()
     args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),

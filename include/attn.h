@@ -119,6 +119,24 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
                     const int64_t* strides, float scale, int causal, void* workspace,
                     size_t* workspace_bytes, hipStream_t stream);
 
+/* The varlen forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments, results and errors as attn_fwd_varlen, without
+ * a workspace. The work list lives in a static device array of
+ * 256 + 8 * ATTN_NOALLOC_MAX_ITEMS bytes (4 MiB) that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing.
+ * It needs ceil(Tq / 32) + num_segments <= ATTN_NOALLOC_MAX_ITEMS, else
+ * ATTN_E_WORKSPACE before any launch. Every call on one GPU shares that
+ * GPU's array and the array keeps the last call's contents: calls that
+ * overlap on one GPU (e.g. on two streams without ordering) race and give
+ * wrong results; calls ordered on one stream are safe. */
+#define ATTN_NOALLOC_MAX_ITEMS 524256
+int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void* v, void* out,
+                            float* lse, const int32_t* cu_q, const int32_t* cu_k,
+                            int num_segments, int max_q, int max_k, int Tq, int Tk, int Hq,
+                            int Hkv, int Dqk, int Dv, const int64_t* strides, float scale,
+                            int causal, hipStream_t stream);
+
 /* Dense backward from the caller's out/lse ("ffpa_attention" page, dense
  * backward entry). dout, out [B,Hq,Nq,Dv]; lse [B,Hq,Nq] fp32 contiguous;
  * dq [B,Hq,Nq,Dqk]; dk [B,Hkv,Nk,Dqk]; dv [B,Hkv,Nk,Dv] (dk/dv summed over the

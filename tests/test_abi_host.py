@@ -298,3 +298,21 @@ def test_timing_toggle_and_empty_read(lib):
     ms = (C.c_float * 2)()
     assert lib.attn_timing_read(2, names, 32, ms, C.byref(n)) == 0 and n.value == 0
     assert lib.attn_timing_read(2, names, 1, ms, C.byref(n)) == _lib.ATTN_E_INVALID
+
+
+def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
+    """attn_fwd_varlen_noalloc checks its static scratch limit on the host,
+    before any device call: ceil(Tq/32) + segments work-list entries."""
+    strides = _lib.i64_array([8 * 128, 128] * 4)
+    cap = _lib.ATTN_NOALLOC_MAX_ITEMS
+
+    def call(Tq, nseg):
+        return lib.attn_fwd_varlen_noalloc(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nseg,
+                                           Tq, Tq, Tq, Tq, 8, 2, 128, 128, strides, 0.1, 1, None)
+
+    st = call(32 * (cap - 10) + 1, 10)  # one entry too many
+    assert st == _lib.ATTN_E_WORKSPACE
+    assert "static scratch" in lib.attn_last_error().decode()
+    assert call(100, 0) == _lib.ATTN_E_INVALID  # the ordinary argument checks still apply
+    # the header's limit and the library's agree
+    assert f"ATTN_NOALLOC_MAX_ITEMS {cap}" in open(HEADER).read()

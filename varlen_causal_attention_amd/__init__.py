@@ -6,11 +6,13 @@ libvca_attn.so (built in-tree by ``python -m varlen_causal_attention_amd.build``
 this package only marshals torch tensors into its C ABI.
 """
 from ._lib import EXPORTED, LIB_PATH, AttnError, load
-from .ops import (bwd_dense, bwd_varlen, dense_route, doc_layout, doc_segments, fwd_dense,
-                  fwd_varlen, is_supported, merge, timing_enable, timing_read, version, zero_rows)
+from .ops import (bwd_dense, bwd_varlen, dense_route, doc_cu_seqlens, doc_layout, doc_segments,
+                  fwd_dense, fwd_varlen, fwd_varlen_noalloc, is_supported, merge, timing_enable,
+                  timing_read, version, zero_rows)
 
 __all__ = [
-    "AttnError", "EXPORTED", "LIB_PATH", "load", "fwd_dense", "fwd_varlen", "bwd_dense",
-    "bwd_varlen", "merge", "doc_segments", "doc_layout", "dense_route", "zero_rows",
+    "AttnError", "EXPORTED", "LIB_PATH", "load", "fwd_dense", "fwd_varlen", "fwd_varlen_noalloc",
+    "bwd_dense", "bwd_varlen", "merge", "doc_segments", "doc_cu_seqlens", "doc_layout",
+    "dense_route", "zero_rows",
     "is_supported", "version", "timing_enable", "timing_read",
 ]

@@ -19,9 +19,11 @@ ATTN_E_HIP = -4
 ATTN_BF16 = 0
 ATTN_F32 = 1
 ATTN_DQ_ACCUMULATE = 1
+ATTN_NOALLOC_MAX_ITEMS = 524256  # work-list entries the no-allocation forward's static scratch holds
 
 EXPORTED = (
     "attn_last_error", "attn_version", "attn_is_supported", "attn_fwd_dense", "attn_fwd_varlen",
+    "attn_fwd_varlen_noalloc",
     "attn_bwd_dense", "attn_bwd_varlen", "attn_merge", "attn_doc_segments", "attn_doc_cu_seqlens",
     "attn_dense_route",
     "attn_zero_rows", "attn_timing_enable", "attn_timing_read",
@@ -42,6 +44,8 @@ _SIGS = {
                             _P, _SZP, _P]),
     "attn_fwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                              _I64P, _F, _I, _P, _SZP, _P]),
+    "attn_fwd_varlen_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                     _I, _I, _I64P, _F, _I, _P]),
     "attn_bwd_dense": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                             _I64P, _F, _I, _I, _P, _SZP, _P]),
     "attn_bwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,

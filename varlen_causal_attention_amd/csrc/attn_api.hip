@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -99,6 +100,88 @@ vca::ViewW vieww(void* p, int64_t sb, int64_t sh, int64_t sn) {
   return vca::ViewW{static_cast<uint16_t*>(p), sb, sh, sn};
 }
 
+// Argument checks of the varlen forward (everything visible on the host).
+int fwd_varlen_checks(int dtype, const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const int32_t* cu_q, const int32_t* cu_k,
+                      int num_segments, int max_q, int max_k, int Tq, int Tk, int Hq, int Hkv,
+                      int Dqk, int Dv, const int64_t* strides, float scale) {
+  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  if (st) return st;
+  if (num_segments < 0 || Tq < 0 || Tk < 0 || max_q < 0 || max_k < 0)
+    return fail(ATTN_E_INVALID, "sizes must be >= 0");
+  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
+  if (num_segments > 0 && (!cu_q || !cu_k)) return fail(ATTN_E_INVALID, "cu_seqlens is NULL");
+  if (num_segments == 0 && (Tq > 0 || Tk > 0))
+    return fail(ATTN_E_INVALID, "tokens given but no segments");
+  if (Tq > 0 && max_q < 1) return fail(ATTN_E_INVALID, "max_q must be >= 1 when Tq > 0");
+  if (Tk > 0 && max_k < 1) return fail(ATTN_E_INVALID, "max_k must be >= 1 when Tk > 0");
+  if ((st = check_tensor("q", q, Tq > 0, strides + 0, 2))) return st;
+  if ((st = check_tensor("k", k, Tk > 0, strides + 2, 2))) return st;
+  if ((st = check_tensor("v", v, Tk > 0, strides + 4, 2))) return st;
+  if ((st = check_tensor("out", out, Tq > 0, strides + 6, 2))) return st;
+  if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+  return ATTN_OK;
+}
+
+// The varlen forward on checked arguments with a workspace of at least
+// fwd_workspace_bytes (the scheduler writes every byte it later reads).
+int fwd_varlen_run(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                   int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                   const int64_t* strides, float scale, int causal, void* ws, hipStream_t stream,
+                   const char* what) {
+  int st;
+  if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
+    return st;
+  vca::FwdArgs a{};
+  a.q = view(q, 0, strides[1], strides[0]);
+  a.k = view(k, 0, strides[3], strides[2]);
+  a.v = view(v, 0, strides[5], strides[4]);
+  a.o = vieww(out, 0, strides[7], strides[6]);
+  a.lse = lse;
+  a.lse_sb = 0;
+  a.lse_sh = Tq;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.Nq = a.Nk = 0;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.G = Hq / Hkv;
+  a.scale_log2 = scale * vca::kLog2e;
+  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, ws, stream),
+                    what);
+}
+
+// Static scratch of attn_fwd_varlen_noalloc: the forward's work list lives in
+// this device array (one copy per GPU, held until the process ends) instead
+// of a caller workspace. Host code never passes the array's name to a kernel
+// (on the host it only stands in for the symbol): each device's address is
+// taken with hipGetSymbolAddress on its first call there, with that device
+// current, and kept.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static_assert(kScratchBytes == 256 + ATTN_NOALLOC_MAX_ITEMS * 8, "scratch size vs header");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_E_INVALID, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ATTN_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 void vca::set_last_error(const std::string& msg) { g_last_error = msg; }
@@ -158,45 +241,39 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
                     const int64_t* strides, float scale, int causal, void* workspace,
                     size_t* workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
-  int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
+  int st = fwd_varlen_checks(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq,
+                             Tk, Hq, Hkv, Dqk, Dv, strides, scale);
   if (st) return st;
-  if (num_segments < 0 || Tq < 0 || Tk < 0 || max_q < 0 || max_k < 0)
-    return fail(ATTN_E_INVALID, "sizes must be >= 0");
-  if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
-  if (num_segments > 0 && (!cu_q || !cu_k)) return fail(ATTN_E_INVALID, "cu_seqlens is NULL");
-  if (num_segments == 0 && (Tq > 0 || Tk > 0))
-    return fail(ATTN_E_INVALID, "tokens given but no segments");
-  if (Tq > 0 && max_q < 1) return fail(ATTN_E_INVALID, "max_q must be >= 1 when Tq > 0");
-  if (Tk > 0 && max_k < 1) return fail(ATTN_E_INVALID, "max_k must be >= 1 when Tk > 0");
-  if ((st = check_tensor("q", q, Tq > 0, strides + 0, 2))) return st;
-  if ((st = check_tensor("k", k, Tk > 0, strides + 2, 2))) return st;
-  if ((st = check_tensor("v", v, Tk > 0, strides + 4, 2))) return st;
-  if ((st = check_tensor("out", out, Tq > 0, strides + 6, 2))) return st;
-  if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
   bool query = false;
   const size_t need_ws = vca::fwd_workspace_bytes(Tq, num_segments);
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || Tq == 0) return ok();
-  if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
-    return st;
+  return fwd_varlen_run(q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk, Hq,
+                        Hkv, Dqk, Dv, strides, scale, causal, workspace, stream,
+                        "attn_fwd_varlen launch");
+}
 
-  vca::FwdArgs a{};
-  a.q = view(q, 0, strides[1], strides[0]);
-  a.k = view(k, 0, strides[3], strides[2]);
-  a.v = view(v, 0, strides[5], strides[4]);
-  a.o = vieww(out, 0, strides[7], strides[6]);
-  a.lse = lse;
-  a.lse_sb = 0;
-  a.lse_sh = Tq;
-  a.cu_q = cu_q;
-  a.cu_k = cu_k;
-  a.Nq = a.Nk = 0;
-  a.Tq = Tq;
-  a.Tk = Tk;
-  a.G = Hq / Hkv;
-  a.scale_log2 = scale * vca::kLog2e;
-  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, workspace, stream),
-                    "attn_fwd_varlen launch");
+int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void* v, void* out,
+                            float* lse, const int32_t* cu_q, const int32_t* cu_k,
+                            int num_segments, int max_q, int max_k, int Tq, int Tk, int Hq,
+                            int Hkv, int Dqk, int Dv, const int64_t* strides, float scale,
+                            int causal, hipStream_t stream) {
+  g_last_error.clear();
+  int st = fwd_varlen_checks(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq,
+                             Tk, Hq, Hkv, Dqk, Dv, strides, scale);
+  if (st) return st;
+  const size_t need_ws = vca::fwd_workspace_bytes(Tq, num_segments);
+  if (need_ws > kScratchBytes)
+    return fail(ATTN_E_WORKSPACE, "attn_fwd_varlen_noalloc: the work list needs " +
+                                      std::to_string(need_ws) + " bytes, the static scratch holds " +
+                                      std::to_string(kScratchBytes) +
+                                      " (at most ATTN_NOALLOC_MAX_ITEMS query tiles + segments)");
+  if (Tq == 0) return ok();
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return fwd_varlen_run(q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk, Hq,
+                        Hkv, Dqk, Dv, strides, scale, causal, ws, stream,
+                        "attn_fwd_varlen_noalloc launch");
 }
 
 int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, const void* v,

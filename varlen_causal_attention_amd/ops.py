@@ -191,6 +191,30 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
     return out, lse
 
 
+def fwd_varlen_noalloc(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool,
+                       out, lse):
+    """attn_fwd_varlen_noalloc: the varlen forward into caller-given out
+    [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 with no device allocation at all
+    (its work list uses the library's static scratch). Calls that overlap on
+    one GPU race."""
+    Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
+    if cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given")
+    dev = _need_gpu_bf16(q=q, k=k, v=v)
+    out = _output(out, (Tq, Hq, Dv), torch.bfloat16, dev, "out")
+    lse = _lse_output(lse, (Hq, Tq), dev)
+    strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
+                        + list(out.stride()[:2]))
+    st = load().attn_fwd_varlen_noalloc(
+        ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev), _cu(cu_k, dev),
+        cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale),
+        int(bool(causal)), _stream(q))
+    check(st, "attn_fwd_varlen_noalloc")
+    return out, lse
+
+
 def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float,
                causal: bool, dq_accumulate=None, dq=None, dk=None, dv=None):
     """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse.

@@ -249,7 +249,7 @@ def kernel_work(w: "workloads.Workload", name: str):
         return "mfma", 2 * pairs * (w.Dqk + w.Dv) / chunks, "FLOP"
     if name == "attn_bwd_dkdv":
         return "mfma", 2 * pairs * (2 * w.Dqk + 2 * w.Dv) / chunks, "FLOP"
-    if name == "attn_bwd_dq":
+    if name in ("attn_bwd_dq", "attn_bwd_dq_ds"):
         return "mfma", 2 * pairs * w.Dqk / chunks, "FLOP"
     # two-phase backward (large head dims): scores S and dP, then products
     if name == "attn_bwd_scores":
@@ -267,10 +267,19 @@ def kernel_work(w: "workloads.Workload", name: str):
     return None
 
 
+def chunk_count(w: "workloads.Workload") -> int:
+    """Calls of one pass per step in kernel_work's units (two ring chunks)."""
+    return 2 if w.kind == "ring" else 1
+
+
 def roofline(w: "workloads.Workload", kernels: dict) -> dict:
     """Roofline entry of the kernel that takes the most time per step."""
     name = max(kernels, key=lambda k: kernels[k]["mean_ms"] * kernels[k]["per_step"])
     bound, units, unit = kernel_work(w, name)
+    # a pass split over several launches (the dS-store backward runs one
+    # dK/dV + dQ launch pair per chunk of kv-heads) does its step's work
+    # over all of them: units per launch = step units / launches per step
+    units = units * chunk_count(w) / kernels[name]["per_step"]
     sec = kernels[name]["mean_ms"] * 1e-3
     if bound == "mfma":
         achieved = units / sec / 1e12
@@ -289,6 +298,7 @@ PER_UNIT = {
     "attn_fwd": "2*pairs*(Dqk+Dv) FLOP",
     "attn_bwd_dkdv": "2*pairs*(2*Dqk+2*Dv) FLOP",
     "attn_bwd_dq": "2*pairs*Dqk FLOP",
+    "attn_bwd_dq_ds": "2*pairs*Dqk FLOP",
     "attn_bwd_scores": "2*pairs*(Dqk+Dv) FLOP",
     "attn_bwd_dkdv_tiles": "2*pairs*(Dqk+Dv) FLOP",
     "attn_bwd_dq_tiles": "2*pairs*Dqk FLOP",

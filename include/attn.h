@@ -142,7 +142,12 @@ int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void*
  * dq [B,Hq,Nq,Dqk]; dk [B,Hkv,Nk,Dqk]; dv [B,Hkv,Nk,Dv] (dk/dv summed over the
  * q-heads of each GQA group).
  * strides[24] = (b, h, n) strides of q, k, v, out, dout, dq, dk, dv.
- * Needs a workspace (query it with workspace = NULL). flags: ATTN_DQ_*. */
+ * Needs a workspace (query it with workspace = NULL). flags: ATTN_DQ_*.
+ * Head dims 128 and 192/128: the workspace also holds the dS blocks of the
+ * q-heads of one launch pair (the dK/dV pass stores them, the dQ pass
+ * multiplies them by K instead of recomputing S and dP), at most
+ * ATTN_BWD_DS_MIB MiB (environment variable, default 8192; 0 turns the store
+ * off); when one GQA group's blocks exceed it, the dQ pass recomputes. */
 int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, const void* v,
                    const void* out, const float* lse, void* dq, void* dk, void* dv, int B,
                    int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
@@ -246,7 +251,8 @@ int attn_timing_enable(int enable);
 /* Waits for and reads the recorded launches (in launch order) of the calling
  * thread, then clears the record. Up to max_records entries: names receives
  * NUL-terminated kernel labels in slots of name_len bytes ("attn_schedule",
- * "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"; for head dims 256 and 512
+ * "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_dq_ds" (dQ from stored dS);
+ * for head dims 256 and 512
  * "attn_bwd_delta", "attn_bwd_scores", "attn_bwd_dkdv_tiles",
  * "attn_bwd_dq_tiles"; "attn_merge", "attn_zero_rows"), ms the elapsed
  * milliseconds; *count receives the total number recorded. Returns

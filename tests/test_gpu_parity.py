@@ -730,3 +730,27 @@ def test_merge_in_place_with_head_dims_that_split_waves(vca):
         torch.cuda.synchronize()
         assert np.abs(host(acc) - ro).max() < 1e-5, Dv
         check_lse(lacc, rl)
+
+
+@pytest.mark.parametrize("dqk,dv", [(128, 128), (192, 128)])
+def test_backward_ds_store_modes(vca, monkeypatch, dqk, dv):
+    """Head dims 128 and 192/128 store dS in the dK/dV pass and compute dQ
+    from it. The store's budget (ATTN_BWD_DS_MIB) picks how many kv-heads
+    share one dK/dV + dQ launch pair; below one GQA group's blocks the dQ
+    pass recomputes S and dP instead. Every mode matches the oracle, and the
+    chunked store gives bitwise the same gradients as the single launch."""
+    lens_q = [300, 0, 41, 130, 1]
+    lens_k = [300, 20, 70, 130, 1]
+    Hq, Hkv = 8, 4
+    monkeypatch.delenv("ATTN_BWD_DS_MIB", raising=False)
+    _, _, whole, _ = run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, True, seed=301 + dqk)
+    # about 0.74 MiB of blocks per group of two q-heads: a 1 MiB budget runs
+    # one kv-head per launch pair
+    monkeypatch.setenv("ATTN_BWD_DS_MIB", "1")
+    _, _, chunked, _ = run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, True, seed=301 + dqk)
+    for a, b in zip(whole, chunked):
+        assert torch.equal(a, b)
+    monkeypatch.setenv("ATTN_BWD_DS_MIB", "0")
+    run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, True, seed=301 + dqk)
+    run_dense(vca, 2, 4, 2, 150, 150, dqk, dv, True, seed=303 + dqk)
+    run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, False, seed=305 + dqk)

@@ -296,7 +296,7 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   if (has_q && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
   const vca::TileGeom tg = vca::tile_geom_dense(B, Nq, Nk);
   const size_t need_ws =
-      vca::bwd_workspace(Dqk, Dv, Hq, (int64_t)B * Nq, (int64_t)B * Nk, B, tg).total;
+      vca::bwd_workspace(Dqk, Dv, Hq, Hkv, (int64_t)B * Nq, (int64_t)B * Nk, B, tg).total;
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (!has_q && !has_k)) return ok();
@@ -354,7 +354,7 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
     if ((st = check_tensor(names[i], ptrs[i], need[i], strides + 2 * i, 2))) return st;
   if (Tq > 0 && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
   const vca::TileGeom tg = vca::tile_geom_varlen(Tq, num_segments, max_k);
-  const size_t need_ws = vca::bwd_workspace(Dqk, Dv, Hq, Tq, Tk, num_segments, tg).total;
+  const size_t need_ws = vca::bwd_workspace(Dqk, Dv, Hq, Hkv, Tq, Tk, num_segments, tg).total;
   bool query = false;
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || (Tq == 0 && Tk == 0)) return ok();

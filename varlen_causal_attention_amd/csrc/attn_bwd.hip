@@ -2,6 +2,8 @@
 // either the fused dK/dV and dQ passes (DS = number of waves that split one
 // 32-row block by head-dim range) or the two-phase scores + products passes
 // (their own translation unit, attn_bwd_tiles.hip).
+#include <cstdlib>
+
 #include "attn_launch.hpp"
 #include "attn_timing.hpp"
 
@@ -80,15 +82,80 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
 // DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
+template <int DQK, int DV, int DS, int KN, bool KP, int NWK>
+hipError_t launch_dkdv(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st) {
+  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
+  TimedLaunch timer("attn_bwd_dkdv", st);
+  if constexpr (kPipe && DQK == 128) {
+    const hipError_t e = launch_dkdv_roles(a, causal, grid, st);
+    if (e != hipSuccess) return e;
+  } else if constexpr (kPipe) {
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, false>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true>), dim3(grid),
+                         dim3(64 * NWK), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false>), dim3(grid),
+                         dim3(64 * NWK), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE, int NWK, int NWQ>
 hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
-                    int64_t k_rows, const BwdWorkspace& wl, void* ws, hipStream_t st) {
+                    int64_t k_rows, const TileGeom& tg, const BwdWorkspace& wl, void* ws,
+                    hipStream_t st) {
   constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
   constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
   constexpr int q_tile = 32 * (NWQ / DS);
+  const int seg_major = (Hq / Hkv) % 2 == 0 ? 0 : 1;
+  const int G = Hq / Hkv;
+  a.kvh0 = 0;
+  a.kvh_n = Hkv;
+  a.ds = nullptr;
+  if constexpr (DQK == 128 || DQK == 192) {
+    if (wl.ds_kv_chunk > 0) {
+      // dS store: the delta pre-pass, then per chunk of kv-heads the dK/dV
+      // pass (which writes the chunk's dS blocks) and the dQ pass over them
+      static_assert(key_block == 128, "dS blocks of 32 keys inside 128-key blocks");
+      constexpr int dq_waves = 8;
+      constexpr int dq_tile = 32 * dq_waves;
+      bwd_prologue<DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, dq_tile, 32,
+                       key_block, 32, ws, st, /*delta_pass=*/true, seg_major);
+      a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wl.ds);
+      a.ds_nqt = (int)tg.ds_nqt;
+      a.ds_mkt = tg.ds_mkt;
+      a.ds_qtb = tg.ds_qtb;
+      const unsigned kitems = (unsigned)((k_rows + key_block - 1) / key_block + nseg);
+      const unsigned qitems = (unsigned)((q_rows + dq_tile - 1) / dq_tile + nseg);
+      for (int g0 = 0; g0 < Hkv; g0 += wl.ds_kv_chunk) {
+        const int n = min(wl.ds_kv_chunk, Hkv - g0);
+        a.kvh0 = g0;
+        a.kvh_n = n;
+        a.ds_h0 = g0 * G;
+        a.ds_nh = n * G;
+        hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(a, causal, kitems * n, st);
+        if (e != hipSuccess) return e;
+        TimedLaunch timer("attn_bwd_dq_ds", st);
+        const dim3 g(qitems * (unsigned)(n * G));
+        if (causal)
+          hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<DQK, dq_waves, true>), g, dim3(64 * dq_waves),
+                             0, st, a);
+        else
+          hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<DQK, dq_waves, false>), g, dim3(64 * dq_waves),
+                             0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
   bwd_prologue<DV>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, wl, q_tile, BN, key_block, 32,
                    ws, st,
-                   /*delta_pass=*/false, /*seg_major_lists=*/(Hq / Hkv) % 2 == 0 ? 0 : 1);
+                   /*delta_pass=*/false, seg_major);
   // the dQ pass first: it writes the delta and lse*log2(e) rows the dK/dV
   // pass reads
   if (q_rows > 0) {
@@ -102,29 +169,25 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
                          dim3(64 * NWQ), 0, st, a);
   }
   if (k_rows > 0) {
-    TimedLaunch timer("attn_bwd_dkdv", st);
-    const dim3 g((unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv));
-    if constexpr (kPipe && DQK == 128) {
-      const hipError_t e = launch_dkdv_roles(a, causal, g.x, st);
-      if (e != hipSuccess) return e;
-    } else if constexpr (kPipe) {
-      if (causal)
-        hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, true>), g, dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, false>), g, dim3(256), 0, st, a);
-    } else {
-      if (causal)
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true>), g, dim3(64 * NWK), 0,
-                           st, a);
-      else
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false>), g, dim3(64 * NWK),
-                           0, st, a);
-    }
+    const hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(
+        a, causal, (unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv), st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t ds_budget_bytes() {
+  const char* e = std::getenv("ATTN_BWD_DS_MIB");
+  long long mib = 8192;
+  if (e && *e) {
+    char* end = nullptr;
+    const long long v = std::strtoll(e, &end, 10);
+    if (end && *end == '\0' && v >= 0) mib = v;
+  }
+  return (size_t)mib << 20;
+}
 
 void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                  int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
@@ -148,7 +211,7 @@ void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int
 hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                       int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws, hipStream_t st) {
   if (nseg == 0 || Hq == 0) return hipSuccess;
-  const BwdWorkspace wl = bwd_workspace(dqk, dv, Hq, q_rows, k_rows, nseg, tg);
+  const BwdWorkspace wl = bwd_workspace(dqk, dv, Hq, Hkv, q_rows, k_rows, nseg, tg);
   if (bwd_uses_tiles(dqk, dv))
     return launch_bwd_tiles(a, dqk, dv, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws,
                             st);
@@ -156,7 +219,7 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
 // per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
 #define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \
   bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ>(a, causal, nseg, Hq, Hkv, max_q, \
-                                                           q_rows, k_rows, wl, ws, st)
+                                                           q_rows, k_rows, tg, wl, ws, st)
   if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
   if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
   // 192/128: the fused passes at one wave per SIMD (dK/dV 360, dQ 285 registers) beat the

@@ -52,7 +52,41 @@ struct BwdArgs {
   int tile_nkb;        // key tiles per row slot
   int tile_nqb_dense;  // dense: query tiles per batch; 0 for varlen
   int nq_items, nk_items;  // list capacities (grid sizes) of the two-phase passes
+  // kv-heads of this launch of a dK/dV pass: kvh0 .. kvh0 + kvh_n - 1
+  int kvh0, kvh_n;
+  // dS store (head dims 128 and 192/128): when ds is set, the dK/dV pass
+  // writes every visible 32x32 block of dS (bf16) there and the dQ pass
+  // reads them instead of recomputing S and dP. Block (q-head h, query tile
+  // qt of a segment, key tile kt) sits at element
+  //   (((h - ds_h0) * ds_nqt + qt_flat) * ds_mkt + kt) * 1024,
+  // qt_flat = (first query row of the segment) / 32 + segment + qt (varlen)
+  // or batch * ds_qtb + qt (dense, ds_qtb = ceil(Nq / 32)). A block is kept
+  // in the order the dK/dV pass holds it: two MFMA B fragments of 64 lanes x
+  // 8 bf16 (element 512 j + 8 l + e); lane l holds key l % 32, fragment j
+  // the queries 16j + 4h + e (e < 4) and 16j + 8 + 4h + (e - 4) (e >= 4),
+  // h = l / 32. Each store and load of a fragment moves 1 KB contiguously.
+  uint16_t* ds;
+  int ds_h0, ds_nh, ds_nqt, ds_mkt, ds_qtb;
 };
+
+// Element offset of dS block (h, query tile starting at segment row q0, key
+// tile starting at segment key k0), or -1 when the layout has no room for it
+// (only with cu_seqlens that break their contract: a segment longer than
+// max_k).
+__device__ __forceinline__ int64_t ds_block(const BwdArgs& a, int s, const SegGeom& sg, int h,
+                                            int q0, int k0) {
+  const int qt_flat = a.cu_q ? (sg.q_row0 >> 5) + s + (q0 >> 5) : s * a.ds_qtb + (q0 >> 5);
+  const int kt = k0 >> 5;
+  if (kt >= a.ds_mkt || qt_flat >= a.ds_nqt) return -1;
+  return (((int64_t)(h - a.ds_h0) * a.ds_nqt + qt_flat) * a.ds_mkt + kt) * 1024;
+}
+
+// Store one lane's share of a 32x32 dS block held as the two bf16 B
+// fragments of dK^T += Q^T dS, in that fragment order.
+__device__ __forceinline__ void ds_store(uint16_t* blk, int lane, bf16x8 f0, bf16x8 f1) {
+  *reinterpret_cast<u32x4*>(blk + 8 * lane) = __builtin_bit_cast(u32x4, f0);
+  *reinterpret_cast<u32x4*>(blk + 512 + 8 * lane) = __builtin_bit_cast(u32x4, f1);
+}
 
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O) in fp32. blockIdx = (row block, head, segment); a row
@@ -125,7 +159,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int kg = w / DS, ds = w % DS;
-  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  const int item = blockIdx.x / a.kvh_n, g = a.kvh0 + (blockIdx.x - item * a.kvh_n);
   if (item >= *a.count_k) return;
   const int2 st = a.items_k[item];
   const int s = st.x;
@@ -215,13 +249,26 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
     if (PF && total > 1) load_rows(1);
   }
 
+  // dS block of the previous step, stored after this step's wait for its
+  // prefetched rows and before the next prefetch: the compiler waits for
+  // every outstanding memory operation when loads and stores are mixed, so
+  // a store issued there is waited for only one step later
+  int64_t pend_off = -1;
+  bf16x8 pend0, pend1;
+  auto flush_ds = [&]() {
+    if (pend_off >= 0) ds_store(a.ds + pend_off, lane, pend0, pend1);
+    pend_off = -1;
+  };
   for (int it = 0; it < total; ++it) {
     const int buf = NBUF == 2 ? (it & 1) : 0;
     const int q0 = q_begin + (nq - 1 - it / a.G) * BQ;
     __syncthreads();  // step `it` is in LDS; nobody still reads the other buffer
     if (NBUF == 2 && it + 1 < total) {
       store_rows(buf ^ 1);
+      flush_ds();
       if (it + 2 < total) load_rows(it + 2);
+    } else {
+      flush_ds();
     }
     // this 32-query step is hidden from every key of this wave's group?
     const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + BQ - 1 + shift);
@@ -277,6 +324,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
       }
       const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
       const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+      if (a.ds) {
+        // this step is visible to the wave's key tile: its dS block for the
+        // dQ pass, stored at the next step (see pend_off)
+        pend_off = ds_block(a, s, sg, g * a.G + it % a.G, q0, gk0);
+        pend0 = s0;
+        pend1 = s1;
+      }
       // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
 #pragma unroll
       for (int b = 0; b < NVB; ++b) {
@@ -297,6 +351,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
       if (PF && it + 2 < total) load_rows(it + 2);
     }
   }
+  flush_ds();
 
   if (key < lk) {
     const int64_t r = sg.k_row0 + key;
@@ -351,7 +406,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
-  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  const int item = blockIdx.x / a.kvh_n, g = a.kvh0 + (blockIdx.x - item * a.kvh_n);
   if (item >= *a.count_k) return;
   const int2 st = a.items_k[item];
   const int s = st.x;
@@ -777,6 +832,141 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
         bf16x4 v4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(dqa[b][rr * 4 + c] * a.scale + add[c]);
+        *reinterpret_cast<bf16x4*>(dst) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ from the stored dS blocks: dQ[q] = scale * sum_j dS[q,j] k_j, a plain
+// block GEMM (no recomputation of S or dP). One workgroup = (segment, q-head,
+// 32*NW queries), wave w owns the query tile of rows 32w..32w+31 and walks
+// the key tiles it can see. Per 32-key tile the workgroup stages the K rows
+// (row-major, row stride KS) once for all its waves, and each wave its own
+// 32x32 dS block (rearranged to keys x queries) in LDS; dQ^T[d][q] +=
+// K^T dS^T takes both
+// operands through the transposing LDS read, so the contraction order (keys
+// 4h..4h+3, 8+4h.. of every 16) matches on both sides. The pass is bound by
+// the dS bytes it reads from HBM.
+// ---------------------------------------------------------------------------
+template <int DQK, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int NDB = DQK / 32;
+  constexpr int BQ = 32 * NW;
+  // K is only read through the transposing read (4 rows x 32 bytes per
+  // 16-lane group): a row stride of 64 bytes mod 256 keeps those rows on
+  // distinct banks
+  constexpr int KS = DQK + (((32 - DQK) % 128) + 128) % 128;
+  constexpr int KCH = 32 * DQK / 8;       // 16-byte chunks of a K tile
+  constexpr int KPT = (KCH + NT - 1) / NT;  // per thread
+  static_assert((KS * 2) % 256 == 64, "K row stride");
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][32 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t sds[2][NW][32 * 32];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  int item, hl;
+  xcd_item_head(blockIdx.x, a.ds_nh, a.G, item, hl);
+  const int h = a.ds_h0 + hl, g = h / a.G;
+  if (item >= *a.count_q) return;
+  const int2 st = a.items_q[item];
+  const int s = st.x;
+  const SegGeom sg = seg_geom(a.cu_q, a.cu_k, s, a.Nq, a.Nk, a.Tq, a.Tk);
+  const int m0 = st.y * BQ;
+  if (m0 >= sg.lq) return;
+  const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
+  const int wq0 = m0 + 32 * w;
+  // key tiles this wave's queries see (the blocks the dK/dV pass stored) and
+  // the workgroup's (its last live wave's)
+  auto tiles_upto = [&](int rows_end) {
+    int kv_end = lk;
+    if (CAUSAL) kv_end = min(lk, rows_end + shift);
+    return kv_end > 0 ? min((kv_end + 31) >> 5, a.ds_mkt) : 0;
+  };
+  const int nkt_w = wq0 < lq ? tiles_upto(wq0 + 32) : 0;
+  const int ntiles = tiles_upto(min(m0 + BQ, ((lq + 31) >> 5) << 5));
+  const int64_t blk0 = ds_block(a, s, sg, h, wq0 < lq ? wq0 : m0, 0);  // key tile t at +1024 t
+  const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
+
+  u32x4 kr[KPT], dr[2];
+  auto load = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      // rows past the segment end read as zero (their dS is zero as well)
+      const int c = min(tid + NT * i, KCH - 1);
+      const int row = 32 * t + c / (DQK / 8);
+      kr[i] = row < lk ? ldg16(kbp + (int64_t)row * a.k.sn + (c % (DQK / 8)) * 8) : zero_u32x4();
+    }
+    if (t < nkt_w && blk0 >= 0) {
+      const uint16_t* b = a.ds + blk0 + 1024 * t;
+      dr[0] = ldg16(b + 8 * lane);
+      dr[1] = ldg16(b + 512 + 8 * lane);
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + NT * i;
+      if (c < KCH) sts16(&sk[b][(c / (DQK / 8)) * KS + (c % (DQK / 8)) * 8], kr[i]);
+    }
+    // to keys x queries, row-major: lane l's fragment j goes to key l % 32,
+    // query positions 16j + 8h .. +7 (queries in the order 0-3, 8-11, 4-7,
+    // 12-15 of every 16)
+    uint16_t* row = &sds[b][w][(lane & 31) * 32 + 8 * (lane >> 5)];
+    sts16(row, dr[0]);
+    sts16(row + 16, dr[1]);
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+  dr[0] = dr[1] = zero_u32x4();
+  if (ntiles > 0) {
+    load(0);
+    store(0);
+    if (ntiles > 1) load(1);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
+    if (t + 1 < ntiles) {
+      store(buf ^ 1);
+      if (t + 2 < ntiles) load(t + 2);
+    }
+    if (t < nkt_w && blk0 >= 0) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bfr = tr_frag(sds[buf][w], 32, 16 * ks, 0, lane);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32(tr_frag(sk[buf], KS, 16 * ks, 32 * db, lane), bfr, acc[db]);
+      }
+    }
+  }
+
+  // lane -> query: block column position col holds query perm(col) (the
+  // middle two 4-query groups of every 16 are swapped)
+  const int qi = wq0 + ((col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1));
+  if (qi < lq) {
+    uint16_t* dqp = a.dq.p + s * a.dq.sb + (int64_t)(sg.q_row0 + qi) * a.dq.sn + h * a.dq.sh;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint16_t* dst = dqp + b * 32 + rr * 8 + half * 4;
+        float add[4] = {0.f, 0.f, 0.f, 0.f};
+        if (a.dq_accumulate) {
+          const u32x2 old = *reinterpret_cast<const u32x2*>(dst);
+          add[0] = __uint_as_float(old[0] << 16);
+          add[1] = __uint_as_float(old[0] & 0xffff0000u);
+          add[2] = __uint_as_float(old[1] << 16);
+          add[3] = __uint_as_float(old[1] & 0xffff0000u);
+        }
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(acc[b][rr * 4 + c] * a.scale + add[c]);
         *reinterpret_cast<bf16x4*>(dst) = v4;
       }
   }

@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, h = lane >> 5;
   const int pair = w >> 1, role = w & 1;  // role 0: S, P, dV; role 1: dP, dS, dK
-  const int item = blockIdx.x / a.Hkv, g = blockIdx.x - item * a.Hkv;
+  const int item = blockIdx.x / a.kvh_n, g = a.kvh0 + (blockIdx.x - item * a.kvh_n);
   if (item >= *a.count_k) return;
   const int2 st = a.items_k[item];
   const int s = st.x;
@@ -263,16 +263,18 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     });
     // diagonal blocks and segment tails (a few steps per key block): zero
     // what the mask hides (a select: hidden entries may be inf, e.g. on rows
-    // with lse = -inf)
-    if (q0 + kRBQ > lq || (CAUSAL && kp0 + KP - 1 > q0 + shift)) {
+    // with lse = -inf). Keys past the segment end (their K rows repeat its
+    // last key) get P = 0 too: their dS must be zero in the stored blocks.
+    if (q0 + kRBQ > lq || kp0 + KP > lk || (CAUSAL && kp0 + KP - 1 > q0 + shift)) {
       const int qh = q0 + 4 * h;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const int kmin = kp0 + 32 * kt + col - shift;  // first query that sees the key
+        const int key = kp0 + 32 * kt + col;
+        const int kmin = key - shift;  // first query that sees the key
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = qh + 8 * (r >> 2) + (r & 3);
-          bool vis = qi < lq;
+          bool vis = qi < lq && key < lk;
           if (CAUSAL) vis = vis && qi >= kmin;
           p[kt][r] = vis ? p[kt][r] : 0.f;
         }
@@ -317,6 +319,23 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 #pragma unroll
       for (int j = 0; j < 2; ++j) Dnew[kt][j] = to_frag(&d[kt][8 * j]);
   };
+  // Role 1 at the top of iteration i (after the barrier, before the loads of
+  // step i+3): the dS blocks of step i-2 that its queries can see, for the dQ
+  // pass. Issued ahead of those loads, the stores are covered by the next
+  // iteration's wait for the loads of step i+2 (loads complete in order), a
+  // full iteration later, so the hand-counted waits never stall on them.
+  auto store_ds = [&](int i, const bf16x8 (&D)[KT][2]) {
+    if (!a.ds || i < 2 || i - 2 >= total) return;
+    const int q0 = step_q0(i - 2), hh = step_head(i - 2);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int k0 = kp0 + 32 * kt;
+      if (k0 < lk && (!CAUSAL || k0 <= q0 + kRBQ - 1 + shift)) {
+        const int64_t off = ds_block(a, s, sg, hh, q0, k0);
+        if (off >= 0) ds_store(a.ds + off, lane, D[kt][0], D[kt][1]);
+      }
+    }
+  };
 
   // Prologue: steps 0..2 in flight; role 0 computes S of step 0.
   if (total > 0) issue(0);
@@ -350,6 +369,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
       if (i + 2 < total) wait_vmcnt<NDMA>();
       else wait_vmcnt<0>();
       __syncthreads();
+      if (role == 1) store_ds(i, Told);  // Told: dS of step i-2
       if (i + 3 < total) issue(i + 3);
       body(i, cur, nxt, Told, Tnew);
     };

@@ -47,23 +47,43 @@ struct TileGeom {
   int64_t slots;  // 256-query row slots
   int nkb;        // 256-key blocks per slot
   int nqb_dense;  // dense: query blocks per batch (slot = b*nqb + qb); 0: varlen
+  // dS store (BwdArgs::ds): 32-row query tiles of the layout, 32-key tiles
+  // per query tile, dense query tiles per batch (0: varlen)
+  int64_t ds_nqt;
+  int ds_mkt, ds_qtb;
 };
 inline TileGeom tile_geom_dense(int B, int Nq, int Nk) {
   const int nqb = (Nq + kBlockRows - 1) / kBlockRows;
-  return TileGeom{(int64_t)B * nqb, (Nk + kBlockRows - 1) / kBlockRows, nqb};
+  const int qtb = (Nq + 31) / 32;
+  return TileGeom{(int64_t)B * nqb, (Nk + kBlockRows - 1) / kBlockRows, nqb, (int64_t)B * qtb,
+                  (Nk + 31) / 32, qtb};
 }
 inline TileGeom tile_geom_varlen(int Tq, int nseg, int max_k) {
-  return TileGeom{(int64_t)Tq / kBlockRows + nseg + 1, (max_k + kBlockRows - 1) / kBlockRows, 0};
+  // a segment's query tiles start at (first row) / 32 + segment index: the
+  // tiles of consecutive segments never collide and stay below Tq/32 + nseg
+  return TileGeom{(int64_t)Tq / kBlockRows + nseg + 1, (max_k + kBlockRows - 1) / kBlockRows, 0,
+                  (int64_t)Tq / 32 + nseg, (max_k + 31) / 32, 0};
 }
 // Head-dim pairs whose backward runs in two phases through stored blocks.
 inline bool bwd_uses_tiles(int dqk, int dv) {
   return dqk == dv && (dqk == 256 || dqk == 512);
 }
+// Head-dim pairs whose dQ pass can read dS blocks stored by the dK/dV pass
+// instead of recomputing S and dP.
+inline bool bwd_can_store_ds(int dqk, int dv) {
+  return (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+}
+// Byte budget of the dS store: ATTN_BWD_DS_MIB (MiB; 0 turns the store off),
+// default 8192. The store holds every visible 32x32 block of the q-heads of
+// one launch; when even one GQA group's blocks exceed the budget the dQ pass
+// recomputes S and dP instead.
+size_t ds_budget_bytes();
 struct BwdWorkspace {
-  size_t list_q, list_k, lse2, tile_p, tile_ds, total;
+  size_t list_q, list_k, lse2, tile_p, tile_ds, ds, total;
+  int ds_kv_chunk;  // kv-heads per dK/dV + dQ launch pair of the dS path; 0: no dS store
 };
-inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64_t k_rows, int nseg,
-                                  const TileGeom& tg) {
+inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int Hkv, int64_t q_rows, int64_t k_rows,
+                                  int nseg, const TileGeom& tg) {
   BwdWorkspace w{};
   const size_t delta = align256(sizeof(float) * (size_t)Hq * (size_t)q_rows);
   w.list_q = delta + 256;
@@ -71,6 +91,18 @@ inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int64_t q_rows, int64
   w.lse2 = w.list_k + align256(sizeof(int2) * list_capacity(k_rows, nseg));
   w.tile_p = w.lse2 + delta;
   w.tile_ds = w.tile_p;
+  w.ds = w.tile_p;
+  if (bwd_can_store_ds(dqk, dv) && Hkv > 0 && q_rows > 0 && k_rows > 0 && tg.ds_mkt > 0) {
+    const size_t per_head = sizeof(uint16_t) * 1024 * (size_t)tg.ds_nqt * (size_t)tg.ds_mkt;
+    const size_t group = per_head * (size_t)(Hq / Hkv);
+    const size_t budget = ds_budget_bytes();
+    if (group <= budget) {
+      const size_t n = budget / group;
+      w.ds_kv_chunk = (int)(n < (size_t)Hkv ? n : (size_t)Hkv);
+      w.total = w.ds + align256(group * (size_t)w.ds_kv_chunk);
+      return w;
+    }
+  }
   if (bwd_uses_tiles(dqk, dv)) {
     const size_t blocks = sizeof(uint16_t) * kBlockRows * kBlockRows * (size_t)tg.slots *
                           (size_t)tg.nkb * (size_t)Hq;

@@ -18,8 +18,10 @@
  *    -inf keeps out 0.
  *
  * Conventions shared by every entry point
- *  - dtype: ATTN_BF16 is the only element type of q, k, v, out, dout, dq, dk,
- *    dv. lse is always fp32.
+ *  - dtype: the element type of q, k, v, out, dout, dq, dk, dv: ATTN_BF16 or
+ *    ATTN_F16 (the "ffpa_attention" page's module overview routes both), the
+ *    same for every tensor of a call. Products accumulate in fp32; outputs are
+ *    rounded to nearest even. lse is always fp32.
  *  - lse is the natural log of the sum of exp over the *scaled* scores
  *    (scale * q.k). A query row with no visible key gets out = 0 and
  *    lse = -inf; the backward treats lse = -inf as "row attends nothing".
@@ -69,7 +71,7 @@ enum {
   ATTN_E_HIP = -4          /* a HIP runtime call failed; text has hipGetErrorString */
 };
 
-enum { ATTN_BF16 = 0, ATTN_F32 = 1 };
+enum { ATTN_BF16 = 0, ATTN_F32 = 1, ATTN_F16 = 2 };
 
 /* Backward flags. ATTN_DQ_ACCUMULATE: dq += this call's dq (the sum is taken
  * in fp32 and rounded once to bf16), so per-chunk backward passes of one
@@ -168,15 +170,15 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
 /* Online-softmax merge of two partial results of the same query rows
  * ("gemma4_moe cp_attention" page, -inf-safe merge entry).
  *  out_a, out_b: [rows, H, Dv] contiguous, element type dtype_a / dtype_b
- *  (ATTN_BF16 or ATTN_F32); lse_a, lse_b: [H, rows] fp32.
+ *  (ATTN_BF16, ATTN_F32 or ATTN_F16); lse_a, lse_b: [H, rows] fp32.
  *  out: [rows, H, Dv] fp32 (written); lse: [H, rows] fp32 (written);
- *  out_bf16: optional (may be NULL) bf16 copy of out, RNE, for feeding the
- *  backward. out may alias out_a when dtype_a is ATTN_F32, and lse may alias
- *  lse_a (running-accumulator use). Rows where both lse are -inf get out 0 and
- *  lse -inf. No workspace. */
+ *  out_copy: optional (may be NULL) copy of out in copy_dtype (ATTN_BF16 or
+ *  ATTN_F16), RNE, for feeding the backward. out may alias out_a when dtype_a
+ *  is ATTN_F32, and lse may alias lse_a (running-accumulator use). Rows where
+ *  both lse are -inf get out 0 and lse -inf. No workspace. */
 int attn_merge(const void* out_a, int dtype_a, const float* lse_a, const void* out_b,
-               int dtype_b, const float* lse_b, float* out, float* lse, void* out_bf16,
-               int rows, int H, int Dv, hipStream_t stream);
+               int dtype_b, const float* lse_b, float* out, float* lse, void* out_copy,
+               int copy_dtype, int rows, int H, int Dv, hipStream_t stream);
 
 /* Document-causal segment layout ("fa4" page, module overview and the
  * _varlen_segments / _varlen_layout entries). Host-only, no GPU work.
@@ -234,10 +236,11 @@ int attn_dense_route(const int32_t* doc_ids, int B, int S, int q_start, int q_le
                      int k_len, int mode, uint8_t* pad_rows, int* eligible);
 
 /* Zero the rows a dense ring chunk must not produce: for every (b, i) with
- * rows[b * S + i] != 0 (device uint8 [B, S]), out[b, h, i, :] = 0 (ATTN_BF16
- * or ATTN_F32 per dtype) and lse[b*lse_sb + h*lse_sh + i] = -inf for all H
- * heads. out is a [B, H, S, D] view with element strides (ob, oh, on) and
- * unit innermost stride; lse may be NULL. Enqueued on stream; no workspace. */
+ * rows[b * S + i] != 0 (device uint8 [B, S]), out[b, h, i, :] = 0 (ATTN_BF16,
+ * ATTN_F16 or ATTN_F32 per dtype) and lse[b*lse_sb + h*lse_sh + i] = -inf for
+ * all H heads. out is a [B, H, S, D] view with element strides (ob, oh, on)
+ * and unit innermost stride; lse may be NULL. Enqueued on stream; no
+ * workspace. */
 int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, float* lse,
                    int64_t lse_sb, int64_t lse_sh, const uint8_t* rows, int B, int H, int S, int D,
                    hipStream_t stream);

@@ -34,7 +34,9 @@ def test_version_and_support_table(lib):
     assert lib.attn_version() >= 10000
     for dqk, dv in [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)]:
         assert lib.attn_is_supported(_lib.ATTN_BF16, dqk, dv) == 1
+        assert lib.attn_is_supported(_lib.ATTN_F16, dqk, dv) == 1
     assert lib.attn_is_supported(_lib.ATTN_BF16, 96, 96) == 0
+    assert lib.attn_is_supported(_lib.ATTN_F16, 96, 96) == 0
     assert lib.attn_is_supported(_lib.ATTN_F32, 128, 128) == 0
 
 
@@ -59,6 +61,7 @@ def _dense(lib, **kw):
     (dict(Dqk=96, Dv=96), _lib.ATTN_E_UNSUPPORTED),
     (dict(Dqk=128, Dv=64), _lib.ATTN_E_UNSUPPORTED),
     (dict(dtype=1), _lib.ATTN_E_UNSUPPORTED),
+    (dict(dtype=3), _lib.ATTN_E_UNSUPPORTED),
     (dict(q=FAKE + 2), _lib.ATTN_E_INVALID),
     (dict(q=0), _lib.ATTN_E_INVALID),
     (dict(lse=0), _lib.ATTN_E_INVALID),
@@ -72,6 +75,15 @@ def test_dense_forward_rejects_bad_arguments(lib, kw, status):
     st, _ = _dense(lib, **kw)
     assert st == status
     assert lib.attn_last_error().decode()
+
+
+def test_fp16_calls_pass_the_host_checks(lib):
+    """ATTN_F16 is accepted by every check the dense forward makes on the host
+    (a size query launches nothing)."""
+    st, need = _dense(lib, dtype=_lib.ATTN_F16)
+    assert st == 0 and need > 0
+    st, _ = _dense(lib, dtype=_lib.ATTN_F16, Dqk=192, Dv=128)
+    assert st == 0
 
 
 def test_dense_forward_workspace_query(lib):
@@ -175,9 +187,12 @@ def test_varlen_backward_rejects_mismatched_kv_before_any_launch(which):
 
 
 def test_merge_rejects_bad_arguments(lib):
-    assert lib.attn_merge(FAKE, 2, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 4, 2, 8, None) == _lib.ATTN_E_UNSUPPORTED
-    assert lib.attn_merge(FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, -1, 2, 8, None) == _lib.ATTN_E_INVALID
-    assert lib.attn_merge(FAKE, 0, None, FAKE, 0, FAKE, FAKE, FAKE, None, 4, 2, 8, None) == _lib.ATTN_E_INVALID
+    m = lib.attn_merge
+    assert m(FAKE, 3, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0, 4, 2, 8, None) == _lib.ATTN_E_UNSUPPORTED
+    assert m(FAKE, 0, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, 0, -1, 2, 8, None) == _lib.ATTN_E_INVALID
+    assert m(FAKE, 0, None, FAKE, 0, FAKE, FAKE, FAKE, None, 0, 4, 2, 8, None) == _lib.ATTN_E_INVALID
+    # the copy must be a 16-bit type
+    assert m(FAKE, 2, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 8, None) == _lib.ATTN_E_UNSUPPORTED
 
 
 # ---------------------------------------------------------------- segments

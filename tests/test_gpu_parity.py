@@ -63,17 +63,18 @@ def check_grad(name, g, ref):
     assert num / den <= GRAD_TOL, f"{name} rel-Frobenius {num / den}"
 
 
-def rand(shape, g):
-    return workloads.randn_bf16(shape, g)
+def rand(shape, g, dtype=torch.bfloat16):
+    return workloads.randn_bf16(shape, g, dtype)
 
 
 # ---------------------------------------------------------------- varlen
-def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed, scale=None):
+def run_varlen(vca, lens_q, lens_k, Hq, Hkv, Dqk, Dv, causal, seed, scale=None,
+               dtype=torch.bfloat16):
     g = torch.Generator().manual_seed(seed)
     cu_q, cu_k = workloads.cumulative(lens_q), workloads.cumulative(lens_k)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
-    q, k, v = rand((Tq, Hq, Dqk), g), rand((Tk, Hkv, Dqk), g), rand((Tk, Hkv, Dv), g)
-    do = rand((Tq, Hq, Dv), g)
+    q, k = rand((Tq, Hq, Dqk), g, dtype), rand((Tk, Hkv, Dqk), g, dtype)
+    v, do = rand((Tk, Hkv, Dv), g, dtype), rand((Tq, Hq, Dv), g, dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(Dqk)
     ro, rl = orc.fwd_varlen(q, k, v, cu_q, cu_k, scale, causal)
@@ -144,10 +145,11 @@ def test_empty_rows_are_exact(vca):
 
 
 # ---------------------------------------------------------------- dense
-def run_dense(vca, B, Hq, Hkv, Nq, Nk, Dqk, Dv, causal, seed, layout="bhnd"):
+def run_dense(vca, B, Hq, Hkv, Nq, Nk, Dqk, Dv, causal, seed, layout="bhnd",
+              dtype=torch.bfloat16):
     g = torch.Generator().manual_seed(seed)
-    q, k, v = rand((B, Hq, Nq, Dqk), g), rand((B, Hkv, Nk, Dqk), g), rand((B, Hkv, Nk, Dv), g)
-    do = rand((B, Hq, Nq, Dv), g)
+    q, k = rand((B, Hq, Nq, Dqk), g, dtype), rand((B, Hkv, Nk, Dqk), g, dtype)
+    v, do = rand((B, Hkv, Nk, Dv), g, dtype), rand((B, Hq, Nq, Dv), g, dtype)
     scale = 1.0 / math.sqrt(Dqk)
     ro, rl = orc.fwd_dense(q, k, v, scale, causal)
     rg = orc.bwd_dense(do, q, k, v, ro, rl, scale, causal)
@@ -211,9 +213,11 @@ def run_full_varlen(vca, w, t):
     mx = max(w.lengths)
     T = w.T
     q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
-    out, lse = nan_like((T, w.Hq, w.Dv)), nan_like((w.Hq, T), torch.float32)
+    et = q.dtype
+    out, lse = nan_like((T, w.Hq, w.Dv), et), nan_like((w.Hq, T), torch.float32)
     vca.fwd_varlen(q, k, v, cq, cq, mx, mx, w.scale, w.causal, out=out, lse=lse)
-    dq, dk, dv = nan_like((T, w.Hq, w.Dqk)), nan_like((T, w.Hkv, w.Dqk)), nan_like((T, w.Hkv, w.Dv))
+    dq, dk = nan_like((T, w.Hq, w.Dqk), et), nan_like((T, w.Hkv, w.Dqk), et)
+    dv = nan_like((T, w.Hkv, w.Dv), et)
     vca.bwd_varlen(do, q, k, v, out, lse, cq, cq, mx, mx, w.scale, w.causal, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     assert_all_written(out=out, lse=lse, dq=dq, dk=dk, dv=dv)
@@ -376,14 +380,15 @@ def ring_share(vca, w, t):
     xq_cu, xk_cu, xmq, xmk = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
     q, do = dev(t["q"]), dev(t["do"])
     kl, vl, ke, ve = (dev(t[n]) for n in ("k_local", "v_local", "k_early", "v_early"))
-    H, Hkv = w.Hq, w.Hkv
-    o1, l1 = nan_like((S, H, w.Dv)), nan_like((H, S), torch.float32)
-    o2, l2 = nan_like((S, H, w.Dv)), nan_like((H, S), torch.float32)
+    H, Hkv, et = w.Hq, w.Hkv, q.dtype
+    o1, l1 = nan_like((S, H, w.Dv), et), nan_like((H, S), torch.float32)
+    o2, l2 = nan_like((S, H, w.Dv), et), nan_like((H, S), torch.float32)
     vca.fwd_varlen(q, kl, vl, lq_cu, lk_cu, lmq, lmk, w.scale, True, out=o1, lse=l1)
     vca.fwd_varlen(q, ke, ve, xq_cu, xk_cu, xmq, xmk, w.scale, False, out=o2, lse=l2)
-    mo, ml, mob = vca.merge(o1, l1, o2, l2, bf16_copy=True)
-    dq, dkl, dvl = nan_like((S, H, w.Dqk)), nan_like((S, Hkv, w.Dqk)), nan_like((S, Hkv, w.Dv))
-    dke, dve = nan_like((S, Hkv, w.Dqk)), nan_like((S, Hkv, w.Dv))
+    mo, ml, mob = vca.merge(o1, l1, o2, l2, copy_dtype=et)
+    dq, dkl = nan_like((S, H, w.Dqk), et), nan_like((S, Hkv, w.Dqk), et)
+    dvl, dke = nan_like((S, Hkv, w.Dv), et), nan_like((S, Hkv, w.Dqk), et)
+    dve = nan_like((S, Hkv, w.Dv), et)
     vca.bwd_varlen(do, q, kl, vl, mob, ml, lq_cu, lk_cu, lmq, lmk, w.scale, True, dq=dq, dk=dkl,
                    dv=dvl)
     vca.bwd_varlen(do, q, ke, ve, mob, ml, xq_cu, xk_cu, xmq, xmk, w.scale, False,
@@ -423,8 +428,12 @@ def ring_share_dense(vca, w, t):
 @pytest.mark.parametrize("n", [5, 6])
 def test_ring_share_workload(vca, n):
     # 5: packed documents (varlen route); 6: one document per row (dense route)
+    check_ring_share(vca, n, torch.bfloat16)
+
+
+def check_ring_share(vca, n, dtype):
     w = workloads.workload(n)
-    t = w.tensors()
+    t = w.tensors(dtype)
     share = ring_share_dense if w.single_doc else ring_share
     (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve) = share(vca, w, t)
     torch.cuda.synchronize()
@@ -754,3 +763,76 @@ def test_backward_ds_store_modes(vca, monkeypatch, dqk, dv):
     run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, True, seed=301 + dqk)
     run_dense(vca, 2, 4, 2, 150, 150, dqk, dv, True, seed=303 + dqk)
     run_varlen(vca, lens_q, lens_k, Hq, Hkv, dqk, dv, False, seed=305 + dqk)
+
+
+
+# ---------------------------------------------------------------- fp16
+@pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp16_every_head_dim(vca, dqk, dv, causal):
+    """fp16 inputs ("ffpa_attention" page: bf16 and fp16 take the same path):
+    ragged segments with zero-query and zero-key ones, GQA, every head dim."""
+    lens_q = [1, 37, 0, 200, 129, 64, 3]
+    lens_k = [1, 37, 12, 200, 129, 64, 0]
+    run_varlen(vca, lens_q, lens_k, 8, 2, dqk, dv, causal, seed=401 + dqk + causal,
+               dtype=torch.float16)
+    run_dense(vca, 1, 4, 2, 130, 160, dqk, dv, causal, seed=403 + dqk, dtype=torch.float16)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_fp16_workloads_full_size(vca, n):
+    """Every workload at full size with fp16 inputs (the same draws rounded to
+    float16): NaN-filled outputs all written, and the oracle on seeded rows
+    and key rows of every segment (or batch entry) x head."""
+    w = workloads.workload(n)
+    if w.kind == "ring":
+        check_ring_share(vca, n, torch.float16)
+        return
+    t = w.tensors(torch.float16)
+    if w.kind == "varlen":
+        res = run_full_varlen(vca, w, t)
+        check_sampled(res, t, w.cu(), w.Hq, w.Hkv, w.scale, True, seed=500 + n)
+        return
+    q, k, v, do = (dev(t[x]) for x in ("q", "k", "v", "do"))
+    B, N, et = w.B, w.Nq, q.dtype
+    out, lse = nan_like((B, w.Hq, N, w.Dv), et), nan_like((B, w.Hq, N), torch.float32)
+    vca.fwd_dense(q, k, v, w.scale, True, out=out, lse=lse)
+    dq, dk, dv = (nan_like((B, w.Hq, N, w.Dqk), et), nan_like((B, w.Hkv, N, w.Dqk), et),
+                  nan_like((B, w.Hkv, N, w.Dv), et))
+    vca.bwd_dense(do, q, k, v, out, lse, w.scale, True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert_all_written(out=out, lse=lse, dq=dq, dk=dk, dv=dv)
+    if n == 1:  # small: the whole problem
+        ro, rl = orc.fwd_dense(t["q"], t["k"], t["v"], w.scale, True)
+        rg = orc.bwd_dense(t["do"], t["q"], t["k"], t["v"], ro, rl, w.scale, True)
+        check_out(out, ro)
+        check_lse(lse, rl)
+        for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), rg):
+            check_grad(name, a, b)
+        return
+    thd = lambda x: x.transpose(1, 2).reshape(B * N, x.shape[1], x.shape[3])  # noqa: E731
+    tt = {x: thd(t[x]) for x in ("q", "k", "v", "do")}
+    res = (thd(out), lse.reshape(B, w.Hq, N).transpose(0, 1).reshape(w.Hq, B * N),
+           (thd(dq), thd(dk), thd(dv)))
+    check_sampled(res, tt, np.array([0, N, 2 * N]), w.Hq, w.Hkv, w.scale, True, seed=500 + n)
+
+
+def test_fp16_merge_copy_and_zero_rows(vca):
+    g = torch.Generator().manual_seed(73)
+    rows, H, Dv = 120, 2, 64
+    oa, ob = rand((rows, H, Dv), g, torch.float16), rand((rows, H, Dv), g, torch.float16)
+    la = torch.randn((H, rows), generator=g) * 3
+    lb = torch.randn((H, rows), generator=g) * 3
+    lb[1, :5] = -math.inf
+    ro, rl = orc.merge(oa, la, ob, lb)
+    mo, ml, mc = vca.merge(dev(oa), dev(la), dev(ob), dev(lb), copy_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.abs(host(mo) - ro).max() < 1e-5
+    check_lse(ml, rl)
+    assert mc.dtype == torch.float16 and torch.equal(mc, mo.to(torch.float16))
+    out = torch.ones((1, 2, 4, 8), dtype=torch.float16, device="cuda")
+    r = torch.zeros((1, 4), dtype=torch.bool, device="cuda")
+    r[0, 1] = True
+    vca.zero_rows(out, None, r)
+    torch.cuda.synchronize()
+    assert torch.all(out[0, :, 1] == 0) and torch.all(out[0, :, 0] == 1)

@@ -18,6 +18,7 @@ ATTN_E_WORKSPACE = -3
 ATTN_E_HIP = -4
 ATTN_BF16 = 0
 ATTN_F32 = 1
+ATTN_F16 = 2
 ATTN_DQ_ACCUMULATE = 1
 ATTN_NOALLOC_MAX_ITEMS = 524256  # work-list entries the no-allocation forward's static scratch holds
 
@@ -50,7 +51,7 @@ _SIGS = {
                             _I64P, _F, _I, _I, _P, _SZP, _P]),
     "attn_bwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                              _I, _I, _I, _I, _I64P, _F, _I, _I, _P, _SZP, _P]),
-    "attn_merge": (_I, [_P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "attn_merge": (_I, [_P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_doc_segments": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,
                                C.POINTER(C.c_int)]),
     "attn_doc_cu_seqlens": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,

@@ -20,8 +20,10 @@ LIB = os.path.join(HERE, "libvca_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_bwd_roles.hip",
-               "attn_merge.hip", "attn_api.hip", "attn_timing.hip"]
+# Kernel units are compiled once per element type: bf16 (namespace vca::bf)
+# and fp16 (VCA_ELEM_F16, namespace vca::hf).
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_bwd_roles.hip"]
+HIP_SOURCES = ["attn_merge.hip", "attn_api.hip", "attn_timing.hip"]
 CXX_SOURCES = ["attn_segments.cpp"]
 # -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in VGPRs. The kernels keep
 # their working set under the unified register budget; left to choose, the
@@ -33,10 +35,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(job) -> str:
+    src, f16 = job
+    obj = os.path.join(BUILD, os.path.basename(src) + (".f16" if f16 else "") + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *VGPR_FORM, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    defs = ["-DVCA_ELEM_F16"] if f16 else []
+    cmd = [HIPCC, *COMMON, *VGPR_FORM, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
@@ -49,9 +53,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = HIP_SOURCES + CXX_SOURCES
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = list(ex.map(_compile, srcs))
+    jobs = ([(s, False) for s in KERNEL_SOURCES] + [(s, True) for s in KERNEL_SOURCES]
+            + [(s, False) for s in HIP_SOURCES + CXX_SOURCES])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        objs = list(ex.map(_compile, jobs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -27,7 +27,8 @@ int ok() { return ATTN_OK; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_heads(int dtype, int Hq, int Hkv, int Dqk, int Dv, float scale) {
-  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "dtype must be ATTN_BF16");
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_E_UNSUPPORTED, "dtype must be ATTN_BF16 or ATTN_F16");
   if (Hq <= 0 || Hkv <= 0) return fail(ATTN_E_INVALID, "Hq and Hkv must be positive");
   if (Hq % Hkv != 0) return fail(ATTN_E_INVALID, "Hq must be a multiple of Hkv (GQA)");
   if (!vca::head_dims_supported(Dqk, Dv))
@@ -93,6 +94,10 @@ int hip_status(hipError_t e, const char* what) {
   return fail(ATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// The kernels of the call's element type (validated by check_heads).
+auto fwd_launcher(int dtype) { return dtype == ATTN_F16 ? vca::hf::launch_fwd : vca::bf::launch_fwd; }
+auto bwd_launcher(int dtype) { return dtype == ATTN_F16 ? vca::hf::launch_bwd : vca::bf::launch_bwd; }
+
 vca::View view(const void* p, int64_t sb, int64_t sh, int64_t sn) {
   return vca::View{static_cast<const uint16_t*>(p), sb, sh, sn};
 }
@@ -125,7 +130,7 @@ int fwd_varlen_checks(int dtype, const void* q, const void* k, const void* v, co
 
 // The varlen forward on checked arguments with a workspace of at least
 // fwd_workspace_bytes (the scheduler writes every byte it later reads).
-int fwd_varlen_run(const void* q, const void* k, const void* v, void* out, float* lse,
+int fwd_varlen_run(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
                    const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
                    int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
                    const int64_t* strides, float scale, int causal, void* ws, hipStream_t stream,
@@ -148,8 +153,8 @@ int fwd_varlen_run(const void* q, const void* k, const void* v, void* out, float
   a.Tk = Tk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
-  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, ws, stream),
-                    what);
+  return hip_status(
+      fwd_launcher(dtype)(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, ws, stream), what);
 }
 
 // Static scratch of attn_fwd_varlen_noalloc: the forward's work list lives in
@@ -186,6 +191,23 @@ int scratch_address(void** out) {
 
 void vca::set_last_error(const std::string& msg) { g_last_error = msg; }
 
+bool vca::head_dims_supported(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128) ||
+         (dqk == 256 && dv == 256) || (dqk == 512 && dv == 512);
+}
+
+size_t vca::ds_budget_bytes() {
+  const char* e = std::getenv("ATTN_BWD_DS_MIB");
+  long long mib = 8192;
+  if (e && *e) {
+    char* end = nullptr;
+    const long long v = std::strtoll(e, &end, 10);
+    if (end && *end == '\0' && v >= 0) mib = v;
+  }
+  return (size_t)mib << 20;
+}
+
+
 extern "C" {
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
@@ -193,7 +215,7 @@ const char* attn_last_error(void) { return g_last_error.c_str(); }
 int attn_version(void) { return 10000; }
 
 int attn_is_supported(int dtype, int dqk, int dv) {
-  return dtype == ATTN_BF16 && vca::head_dims_supported(dqk, dv) ? 1 : 0;
+  return (dtype == ATTN_BF16 || dtype == ATTN_F16) && vca::head_dims_supported(dqk, dv) ? 1 : 0;
 }
 
 int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
@@ -231,8 +253,9 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
   a.Tk = Nk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
-  return hip_status(vca::launch_fwd(a, Dqk, Dv, causal != 0, B, Hq, (int64_t)B * Nq, workspace, stream),
-                    "attn_fwd_dense launch");
+  return hip_status(
+      fwd_launcher(dtype)(a, Dqk, Dv, causal != 0, B, Hq, (int64_t)B * Nq, workspace, stream),
+      "attn_fwd_dense launch");
 }
 
 int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
@@ -248,8 +271,8 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
   const size_t need_ws = vca::fwd_workspace_bytes(Tq, num_segments);
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || Tq == 0) return ok();
-  return fwd_varlen_run(q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk, Hq,
-                        Hkv, Dqk, Dv, strides, scale, causal, workspace, stream,
+  return fwd_varlen_run(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk,
+                        Hq, Hkv, Dqk, Dv, strides, scale, causal, workspace, stream,
                         "attn_fwd_varlen launch");
 }
 
@@ -271,8 +294,8 @@ int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void*
   if (Tq == 0) return ok();
   void* ws = nullptr;
   if ((st = scratch_address(&ws))) return st;
-  return fwd_varlen_run(q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk, Hq,
-                        Hkv, Dqk, Dv, strides, scale, causal, ws, stream,
+  return fwd_varlen_run(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk,
+                        Hq, Hkv, Dqk, Dv, strides, scale, causal, ws, stream,
                         "attn_fwd_varlen_noalloc launch");
 }
 
@@ -324,8 +347,8 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   a.scale_log2 = scale * vca::kLog2e;
   a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
-  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
-                                    (int64_t)B * Nk, tg, workspace, stream),
+  return hip_status(bwd_launcher(dtype)(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
+                                        (int64_t)B * Nk, tg, workspace, stream),
                     "attn_bwd_dense launch");
 }
 
@@ -384,31 +407,35 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   a.scale_log2 = scale * vca::kLog2e;
   a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
-  return hip_status(vca::launch_bwd(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq, Tk,
-                                    tg, workspace, stream),
+  return hip_status(bwd_launcher(dtype)(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq,
+                                        Tk, tg, workspace, stream),
                     "attn_bwd_varlen launch");
 }
 
 int attn_merge(const void* out_a, int dtype_a, const float* lse_a, const void* out_b, int dtype_b,
-               const float* lse_b, float* out, float* lse, void* out_bf16, int rows, int H, int Dv,
-               hipStream_t stream) {
+               const float* lse_b, float* out, float* lse, void* out_copy, int copy_dtype, int rows,
+               int H, int Dv, hipStream_t stream) {
   g_last_error.clear();
   if (rows < 0 || H <= 0 || Dv <= 0) return fail(ATTN_E_INVALID, "rows >= 0, H > 0, Dv > 0 required");
-  if ((dtype_a != ATTN_BF16 && dtype_a != ATTN_F32) || (dtype_b != ATTN_BF16 && dtype_b != ATTN_F32))
-    return fail(ATTN_E_UNSUPPORTED, "merge inputs must be ATTN_BF16 or ATTN_F32");
+  auto known = [](int t) { return t == ATTN_BF16 || t == ATTN_F32 || t == ATTN_F16; };
+  if (!known(dtype_a) || !known(dtype_b))
+    return fail(ATTN_E_UNSUPPORTED, "merge inputs must be ATTN_BF16, ATTN_F32 or ATTN_F16");
+  if (out_copy && copy_dtype != ATTN_BF16 && copy_dtype != ATTN_F16)
+    return fail(ATTN_E_UNSUPPORTED, "the merge's copy must be ATTN_BF16 or ATTN_F16");
   if (rows == 0) return ok();
   if (!out_a || !out_b || !lse_a || !lse_b || !out || !lse)
     return fail(ATTN_E_INVALID, "merge pointer is NULL");
   vca::MergeArgs a{};
   a.out_a = out_a;
   a.out_b = out_b;
-  a.a_f32 = dtype_a == ATTN_F32;
-  a.b_f32 = dtype_b == ATTN_F32;
+  a.a_type = dtype_a;
+  a.b_type = dtype_b;
   a.lse_a = lse_a;
   a.lse_b = lse_b;
   a.out = out;
   a.lse = lse;
-  a.out_bf16 = static_cast<uint16_t*>(out_bf16);
+  a.out_copy = static_cast<uint16_t*>(out_copy);
+  a.copy_type = copy_dtype;
   a.rows = rows;
   a.H = H;
   a.Dv = Dv;
@@ -420,8 +447,8 @@ int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, flo
                    hipStream_t stream) {
   g_last_error.clear();
   if (B < 0 || H < 0 || S < 0 || D < 0) return fail(ATTN_E_INVALID, "B, H, S, D >= 0 required");
-  if (dtype != ATTN_BF16 && dtype != ATTN_F32)
-    return fail(ATTN_E_UNSUPPORTED, "zero_rows: out must be ATTN_BF16 or ATTN_F32");
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32 && dtype != ATTN_F16)
+    return fail(ATTN_E_UNSUPPORTED, "zero_rows: out must be ATTN_BF16, ATTN_F32 or ATTN_F16");
   if (B == 0 || H == 0 || S == 0) return ok();
   if (!out || !rows) return fail(ATTN_E_INVALID, "zero_rows pointer is NULL");
   vca::ZeroRowsArgs a{};

@@ -2,12 +2,13 @@
 // either the fused dK/dV and dQ passes (DS = number of waves that split one
 // 32-row block by head-dim range) or the two-phase scores + products passes
 // (their own translation unit, attn_bwd_tiles.hip).
-#include <cstdlib>
-
+#include "attn_bwd.hpp"
 #include "attn_launch.hpp"
+#include "attn_sched.hpp"
 #include "attn_timing.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 namespace {
 
 // DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
@@ -178,16 +179,6 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
 
 }  // namespace
 
-size_t ds_budget_bytes() {
-  const char* e = std::getenv("ATTN_BWD_DS_MIB");
-  long long mib = 8192;
-  if (e && *e) {
-    char* end = nullptr;
-    const long long v = std::strtoll(e, &end, 10);
-    if (end && *end == '\0' && v >= 0) mib = v;
-  }
-  return (size_t)mib << 20;
-}
 
 void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
                  int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
@@ -230,4 +221,5 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   return hipErrorInvalidValue;
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

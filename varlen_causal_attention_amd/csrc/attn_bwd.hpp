@@ -27,47 +27,8 @@
 #include "attn_fwd.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
-struct BwdArgs {
-  View q, k, v, o, dout;
-  ViewW dq, dk, dv;
-  const float* lse;
-  float* delta;            // workspace, same indexing as lse
-  float* lse2;             // workspace: lse * log2(e) (+inf where lse = -inf), same indexing
-  int64_t lse_sb, lse_sh;  // index = b*lse_sb + h*lse_sh + (q_row0 + i)
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  int Nq, Nk, Tq, Tk;
-  int G;
-  float scale, scale_log2, inv_scale;  // inv_scale = 1 / scale (scale != 0)
-  int dq_accumulate;
-  int Hq, Hkv;
-  const int2* items_q;    // (segment, query tile) for the dQ pass, heavy first
-  const int* count_q;
-  const int2* items_k;    // (segment, key block) for the dK/dV pass, heavy first
-  const int* count_k;
-  // two-phase backward only: bf16 P and dS tiles (workspace) and their layout
-  uint16_t* tile_p;
-  uint16_t* tile_ds;
-  int tile_nkb;        // key tiles per row slot
-  int tile_nqb_dense;  // dense: query tiles per batch; 0 for varlen
-  int nq_items, nk_items;  // list capacities (grid sizes) of the two-phase passes
-  // kv-heads of this launch of a dK/dV pass: kvh0 .. kvh0 + kvh_n - 1
-  int kvh0, kvh_n;
-  // dS store (head dims 128 and 192/128): when ds is set, the dK/dV pass
-  // writes every visible 32x32 block of dS (bf16) there and the dQ pass
-  // reads them instead of recomputing S and dP. Block (q-head h, query tile
-  // qt of a segment, key tile kt) sits at element
-  //   (((h - ds_h0) * ds_nqt + qt_flat) * ds_mkt + kt) * 1024,
-  // qt_flat = (first query row of the segment) / 32 + segment + qt (varlen)
-  // or batch * ds_qtb + qt (dense, ds_qtb = ceil(Nq / 32)). A block is kept
-  // in the order the dK/dV pass holds it: two MFMA B fragments of 64 lanes x
-  // 8 bf16 (element 512 j + 8 l + e); lane l holds key l % 32, fragment j
-  // the queries 16j + 4h + e (e < 4) and 16j + 8 + 4h + (e - 4) (e >= 4),
-  // h = l / 32. Each store and load of a fragment moves 1 KB contiguously.
-  uint16_t* ds;
-  int ds_h0, ds_nh, ds_nqt, ds_mkt, ds_qtb;
-};
 
 // Element offset of dS block (h, query tile starting at segment row q0, key
 // tile starting at segment key k0), or -1 when the layout has no room for it
@@ -83,7 +44,7 @@ __device__ __forceinline__ int64_t ds_block(const BwdArgs& a, int s, const SegGe
 
 // Store one lane's share of a 32x32 dS block held as the two bf16 B
 // fragments of dK^T += Q^T dS, in that fragment order.
-__device__ __forceinline__ void ds_store(uint16_t* blk, int lane, bf16x8 f0, bf16x8 f1) {
+__device__ __forceinline__ void ds_store(uint16_t* blk, int lane, frag8 f0, frag8 f1) {
   *reinterpret_cast<u32x4*>(blk + 8 * lane) = __builtin_bit_cast(u32x4, f0);
   *reinterpret_cast<u32x4*>(blk + 512 + 8 * lane) = __builtin_bit_cast(u32x4, f1);
 }
@@ -114,7 +75,7 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
       const u32x4 ov = ldg16(op + d0), dv = ldg16(dp + d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc += __uint_as_float(bf16_at(ov, e) << 16) * __uint_as_float(bf16_at(dv, e) << 16);
+        acc += elem_to_f(elem_at(ov, e)) * elem_to_f(elem_at(dv, e));
     }
   }
 #pragma unroll
@@ -174,7 +135,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
 
   // K and V fragments of this lane's key over this wave's d ranges (B operands)
-  bf16x8 kf[NKS], vf[NVS];
+  frag8 kf[NKS], vf[NVS];
   {
     const bool ok = key < lk;
     const uint16_t* kp = kbp + (int64_t)(ok ? key : 0) * a.k.sn + ds * DR + half * 8;
@@ -254,7 +215,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   // every outstanding memory operation when loads and stores are mixed, so
   // a store issued there is waited for only one step later
   int64_t pend_off = -1;
-  bf16x8 pend0, pend1;
+  frag8 pend0, pend1;
   auto flush_ds = [&]() {
     if (pend_off >= 0) ds_store(a.ds + pend_off, lane, pend0, pend1);
     pend_off = -1;
@@ -322,8 +283,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
         p[r] = x;
         dsv[r] = x * (pacc[r] - sdel[buf][qr]);
       }
-      const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
-      const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+      const frag8 p0 = to_frag(p), p1 = to_frag(p + 8);
+      const frag8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
       if (a.ds) {
         // this step is visible to the wave's key tile: its dS block for the
         // dQ pass, stored at the next step (see pend_off)
@@ -361,19 +322,19 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(dka[b][rr * 4 + c] * a.scale);
-        *reinterpret_cast<bf16x4*>(dkp + b * 32 + rr * 8 + half * 4) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(dka[b][rr * 4 + c] * a.scale);
+        *reinterpret_cast<elem4*>(dkp + b * 32 + rr * 8 + half * 4) = v4;
       }
 #pragma unroll
     for (int b = 0; b < NVB; ++b)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)dva[b][rr * 4 + c];
-        *reinterpret_cast<bf16x4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)dva[b][rr * 4 + c];
+        *reinterpret_cast<elem4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
       }
   }
 }
@@ -521,8 +482,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
       p[r] = x;
       dsv[r] = x * pacc[r];
     }
-    const bf16x8 p0 = to_frag(p), p1 = to_frag(p + 8);
-    const bf16x8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
+    const frag8 p0 = to_frag(p), p1 = to_frag(p + 8);
+    const frag8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
     // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
 #pragma unroll
     for (int b = 0; b < NDB; ++b) {
@@ -543,14 +504,14 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 k4, v4;
+        elem4 k4, v4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          k4[c] = (__bf16)(dka[b][rr * 4 + c] * a.scale);
-          v4[c] = (__bf16)dva[b][rr * 4 + c];
+          k4[c] = (elem_t)(dka[b][rr * 4 + c] * a.scale);
+          v4[c] = (elem_t)dva[b][rr * 4 + c];
         }
-        *reinterpret_cast<bf16x4*>(dkp + b * 32 + rr * 8 + half * 4) = k4;
-        *reinterpret_cast<bf16x4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
+        *reinterpret_cast<elem4*>(dkp + b * 32 + rr * 8 + half * 4) = k4;
+        *reinterpret_cast<elem4*>(dvp + b * 32 + rr * 8 + half * 4) = v4;
       }
   }
 }
@@ -608,7 +569,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  bf16x8 qf[NKS], df[NVS];
+  frag8 qf[NKS], df[NVS];
   {
     const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
     const uint16_t* dp = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + ds * VR + half * 8;
@@ -638,7 +599,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
       const u32x4 dv4 = __builtin_bit_cast(u32x4, df[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        dl += __uint_as_float(bf16_at(ov[i], e) << 16) * __uint_as_float(bf16_at(dv4, e) << 16);
+        dl += elem_to_f(elem_at(ov[i], e)) * elem_to_f(elem_at(dv4, e));
     }
     dl += xor32(dl);
     if (qok) l2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
@@ -766,7 +727,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
       // (one uniform branch picks a masked or an unmasked copy of the loop, so
       // the mask costs no per-element branch on the other tiles)
       const bool need_mask = k0 + BN > lk || (CAUSAL && k0 + BN - 1 > wq0 + shift);
-      bf16x8 sf[2 * NKB];
+      frag8 sf[2 * NKB];
       auto softmax_grad = [&](auto masked) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -824,15 +785,15 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
         float add[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.dq_accumulate) {
           const u32x2 old = *reinterpret_cast<const u32x2*>(dst);
-          add[0] = __uint_as_float(old[0] << 16);
-          add[1] = __uint_as_float(old[0] & 0xffff0000u);
-          add[2] = __uint_as_float(old[1] << 16);
-          add[3] = __uint_as_float(old[1] & 0xffff0000u);
+          add[0] = elem_lo_f(old[0]);
+          add[1] = elem_hi_f(old[0]);
+          add[2] = elem_lo_f(old[1]);
+          add[3] = elem_hi_f(old[1]);
         }
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(dqa[b][rr * 4 + c] * a.scale + add[c]);
-        *reinterpret_cast<bf16x4*>(dst) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(dqa[b][rr * 4 + c] * a.scale + add[c]);
+        *reinterpret_cast<elem4*>(dst) = v4;
       }
   }
 }
@@ -938,7 +899,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
     if (t < nkt_w && blk0 >= 0) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bfr = tr_frag(sds[buf][w], 32, 16 * ks, 0, lane);
+        const frag8 bfr = tr_frag(sds[buf][w], 32, 16 * ks, 0, lane);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           acc[db] = mfma32(tr_frag(sk[buf], KS, 16 * ks, 32 * db, lane), bfr, acc[db]);
@@ -959,17 +920,18 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
         float add[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.dq_accumulate) {
           const u32x2 old = *reinterpret_cast<const u32x2*>(dst);
-          add[0] = __uint_as_float(old[0] << 16);
-          add[1] = __uint_as_float(old[0] & 0xffff0000u);
-          add[2] = __uint_as_float(old[1] << 16);
-          add[3] = __uint_as_float(old[1] & 0xffff0000u);
+          add[0] = elem_lo_f(old[0]);
+          add[1] = elem_hi_f(old[0]);
+          add[2] = elem_lo_f(old[1]);
+          add[3] = elem_hi_f(old[1]);
         }
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(acc[b][rr * 4 + c] * a.scale + add[c]);
-        *reinterpret_cast<bf16x4*>(dst) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(acc[b][rr * 4 + c] * a.scale + add[c]);
+        *reinterpret_cast<elem4*>(dst) = v4;
       }
   }
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

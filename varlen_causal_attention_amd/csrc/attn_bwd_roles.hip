@@ -3,6 +3,7 @@
 #include "attn_launch.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
 // 32-key tiles per wave: 1 -> eight waves (two per SIMD), 2 -> four
 constexpr int kRolesKT = 2;
@@ -16,4 +17,5 @@ hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipSt
   return hipGetLastError();
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

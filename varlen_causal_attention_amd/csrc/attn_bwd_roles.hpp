@@ -27,6 +27,7 @@
 #include "attn_bwd.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
 constexpr int kRD = kTileD;           // head dim
 constexpr int kRBQ = 32;              // queries per step
@@ -109,7 +110,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 
   // this wave's K (role 0) or V (role 1) rows as B fragments (kept in AGPRs):
   // kf[kt][ks] = row kp0 + 32*kt + l%32, head-dim elements 16*ks + 8*h ..+7
-  bf16x8 kf[KT][NKS];
+  frag8 kf[KT][NKS];
   {
     // field-wise selects (a runtime select of a whole View goes to scratch)
     const uint16_t* base = (role == 0 ? a.k.p : a.v.p) + s * (role == 0 ? a.k.sb : a.v.sb) +
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) acc[d][kt] = in_agprs(zero16());
   // P (role 0) or dS (role 1) fragments [kt][j] of two consecutive steps
-  bf16x8 tf0[KT][2], tf1[KT][2];
+  frag8 tf0[KT][2], tf1[KT][2];
   // score tiles S (role 0) or dP (role 1) of two consecutive steps
   f32x16 sc0[KT], sc1[KT];
 #pragma unroll
@@ -218,9 +219,9 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   // one VALU element valu(e), e = 0..31. Fragments are read two MFMA pairs
   // ahead; sched_barrier pins the interleave.
   auto pipe = [&](const uint16_t* Xs, f32x16 (&out)[KT], const uint16_t* Xp,
-                  const bf16x8 (&T)[KT][2], auto&& valu) {
-    bf16x8 af[NKS];
-    bf16x8 cf[2 * NDB];
+                  const frag8 (&T)[KT][2], auto&& valu) {
+    frag8 af[NKS];
+    frag8 cf[2 * NDB];
     af[0] = rtile_row(Xs, col, h);
     af[1] = rtile_row(Xs, col, 2 + h);
     cf[0] = rtile_col(Xp, 0, 0, lane);
@@ -243,8 +244,8 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 
   // Role 0, iteration i: S of step i+1 (into nxt) and dV of step i-1 (Pold),
   // with P of step i from cur (into Pnew, and to role 1 through LDS).
-  auto step_a = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Pold)[KT][2],
-                    bf16x8 (&Pnew)[KT][2]) {
+  auto step_a = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Pold)[KT][2],
+                    frag8 (&Pnew)[KT][2]) {
     const int q0 = step_q0(i);
     float l2[16];
 #pragma unroll
@@ -291,8 +292,8 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   };
   // Role 1, iteration i: dP of step i (into nxt) and dK of step i-2 (Dold),
   // with dS of step i-1 from cur and role 0's P (into Dnew).
-  auto step_b = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Dold)[KT][2],
-                    bf16x8 (&Dnew)[KT][2]) {
+  auto step_b = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Dold)[KT][2],
+                    frag8 (&Dnew)[KT][2]) {
     float dl[16];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -311,7 +312,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     pipe(sdo[stage(i)], nxt, sq[stage(i - 2)], Dold, [&](int e) {
       const int kt = e >> 4, r = e & 15;
       const uint32_t wv = pv[kt][r >> 3][(r & 7) >> 1];
-      const float pe = __uint_as_float(r & 1 ? (wv & 0xffff0000u) : (wv << 16));
+      const float pe = (r & 1 ? elem_hi_f(wv) : elem_lo_f(wv));
       d[kt][r] = pe * (cur[kt][r] - dl[r]);
     });
 #pragma unroll
@@ -324,7 +325,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   // pass. Issued ahead of those loads, the stores are covered by the next
   // iteration's wait for the loads of step i+2 (loads complete in order), a
   // full iteration later, so the hand-counted waits never stall on them.
-  auto store_ds = [&](int i, const bf16x8 (&D)[KT][2]) {
+  auto store_ds = [&](int i, const frag8 (&D)[KT][2]) {
     if (!a.ds || i < 2 || i - 2 >= total) return;
     const int q0 = step_q0(i - 2), hh = step_head(i - 2);
 #pragma unroll
@@ -346,7 +347,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   else wait_vmcnt<0>();
   __syncthreads();
   if (role == 0 && total > 0) {
-    bf16x8 af[NKS];
+    frag8 af[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) af[ks] = rtile_row(sq[0], col, 2 * ks + h);
 #pragma unroll
@@ -364,8 +365,8 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   // loop (same barriers), so values hoisted out of one role's loop do not
   // stay live in the other's.
   auto run = [&](auto&& body) {
-    auto iteration = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
-                         bf16x8 (&Tnew)[KT][2]) {
+    auto iteration = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
+                         frag8 (&Tnew)[KT][2]) {
       if (i + 2 < total) wait_vmcnt<NDMA>();
       else wait_vmcnt<0>();
       __syncthreads();
@@ -379,13 +380,13 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     }
   };
   if (role == 0)
-    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
-            bf16x8 (&Tnew)[KT][2]) {
+    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
+            frag8 (&Tnew)[KT][2]) {
       if (i <= total) step_a(i, cur, nxt, Told, Tnew);
     });
   else
-    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], bf16x8 (&Told)[KT][2],
-            bf16x8 (&Tnew)[KT][2]) { step_b(i, cur, nxt, Told, Tnew); });
+    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
+            frag8 (&Tnew)[KT][2]) { step_b(i, cur, nxt, Told, Tnew); });
 
   // dV (role 0) or dK * scale (role 1) of keys kp0 + 32*kt + l%32
   agpr_results_ready(acc);
@@ -401,12 +402,13 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(acc[d][kt][4 * rr + c] * mul);
-        *reinterpret_cast<bf16x4*>(out + 32 * d + 8 * rr + 4 * h) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(acc[d][kt][4 * rr + c] * mul);
+        *reinterpret_cast<elem4*>(out + 32 * d + 8 * rr + 4 * h) = v4;
       }
   }
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

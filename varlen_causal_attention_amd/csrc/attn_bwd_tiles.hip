@@ -1,9 +1,11 @@
 // Launcher of the two-phase backward (scores, then dV/dK and dQ products).
 #include "attn_bwd_tiles.hpp"
 #include "attn_launch.hpp"
+#include "attn_sched.hpp"
 #include "attn_timing.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 namespace {
 
 template <int DQK, int DV, bool CAUSAL>
@@ -70,4 +72,5 @@ hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, i
   return hipErrorInvalidValue;
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

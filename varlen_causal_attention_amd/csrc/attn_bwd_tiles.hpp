@@ -37,6 +37,7 @@
 #include "attn_bwd.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
 constexpr int kBlk = 256;                            // block rows and columns
 constexpr int kChunk = 64;                           // contraction elements per stage
@@ -109,7 +110,7 @@ inline unsigned xcd_grid(unsigned groups) {
 // Row mode: kBlk rows x kChunk contraction elements, 128-byte rows. The
 // 16-byte piece p of row r sits at position p ^ ((r >> 1) & 7): the 16 rows
 // one ds_read_b128 serves per LDS cycle land on distinct banks.
-__device__ __forceinline__ bf16x8 row_frag(const uint16_t* X, int r, int piece) {
+__device__ __forceinline__ frag8 row_frag(const uint16_t* X, int r, int piece) {
   return lds_frag(X + r * kChunk + ((piece ^ ((r >> 1) & 7)) << 3));
 }
 // Column mode: kChunk contraction rows x W columns (W = 128, 192 or 256).
@@ -127,7 +128,7 @@ __device__ __forceinline__ int col_pos(int r, int u) {
   else return u ^ ((r & 3) << 2);
 }
 template <int W>
-__device__ __forceinline__ bf16x8 col_frag(const uint16_t* X, int k0, int n0, int lane) {
+__device__ __forceinline__ frag8 col_frag(const uint16_t* X, int k0, int n0, int lane) {
   const int g = lane >> 4, s = lane & 15, h = lane >> 5;
   const int row = k0 + 4 * h + (s >> 2);
   const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
@@ -137,7 +138,7 @@ __device__ __forceinline__ bf16x8 col_frag(const uint16_t* X, int k0, int n0, in
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 8 * W)));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // Fill a row-mode operand: rp(r) points at the stage's first element of row
 // r (r < 256). Wave w issues four 8-row loads.
@@ -269,7 +270,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
       const uint16_t* B = stg[stage] + kOpElems;
 #pragma unroll
       for (int ks = 0; ks < kChunk / 16; ++ks) {
-        bf16x8 af[2], bf[4];
+        frag8 af[2], bf[4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) af[t] = row_frag(A, 64 * wm + 32 * t + col, 2 * ks + half);
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
             const int qr = 128 * wn + 32 * u + col, qi = q0 + qr;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-              bf16x8 p8;
+              frag8 p8;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int r = 8 * m + e;
@@ -308,7 +309,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
                   if (CAUSAL) vis = vis && kj <= qi + shift;
                   p = vis ? p : 0.f;
                 }
-                p8[e] = (__bf16)p;
+                p8[e] = (elem_t)p;
               }
               stg16(pb + qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half,
                     __builtin_bit_cast(u32x4, p8));
@@ -337,11 +338,11 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const int off = qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half;
-            const bf16x8 p8 = as_frag(pv[u][m]);
-            bf16x8 d8;
+            const frag8 p8 = as_frag(pv[u][m]);
+            frag8 d8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              d8[e] = (__bf16)((float)p8[e] * acc[t][u][8 * m + e]);
+              d8[e] = (elem_t)((float)p8[e] * acc[t][u][8 * m + e]);
             stg16(db + off, __builtin_bit_cast(u32x4, d8));
           }
         }
@@ -443,7 +444,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
     const uint16_t* B = stg[stage] + kOpElems;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
-      bf16x8 af[S::RT], bf[S::CT];
+      frag8 af[S::RT], bf[S::CT];
 #pragma unroll
       for (int t = 0; t < S::RT; ++t) af[t] = col_frag<OB>(A, 16 * ks, S::RM * wm + 32 * t, lane);
 #pragma unroll
@@ -469,10 +470,10 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
     for (int t = 0; t < S::RT; ++t)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[t][u][rr * 4 + e] * mul);
-        *reinterpret_cast<bf16x4*>(orow + S::RM * wm + 32 * t + rr * 8 + half * 4) = v4;
+        for (int e = 0; e < 4; ++e) v4[e] = (elem_t)(acc[t][u][rr * 4 + e] * mul);
+        *reinterpret_cast<elem4*>(orow + S::RM * wm + 32 * t + rr * 8 + half * 4) = v4;
       }
   }
 }
@@ -535,7 +536,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
     const uint16_t* B = stg[stage] + kOpElems;
 #pragma unroll
     for (int ks = 0; ks < kChunk / 16; ++ks) {
-      bf16x8 af[S::RT], bf[S::CT];
+      frag8 af[S::RT], bf[S::CT];
 #pragma unroll
       for (int t = 0; t < S::RT; ++t) af[t] = col_frag<OB>(A, 16 * ks, S::RM * wm + 32 * t, lane);
 #pragma unroll
@@ -562,17 +563,18 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
         float add[4] = {0.f, 0.f, 0.f, 0.f};
         if (a.dq_accumulate) {
           const u32x2 old = *reinterpret_cast<const u32x2*>(dst);
-          add[0] = __uint_as_float(old[0] << 16);
-          add[1] = __uint_as_float(old[0] & 0xffff0000u);
-          add[2] = __uint_as_float(old[1] << 16);
-          add[3] = __uint_as_float(old[1] & 0xffff0000u);
+          add[0] = elem_lo_f(old[0]);
+          add[1] = elem_hi_f(old[0]);
+          add[2] = elem_lo_f(old[1]);
+          add[3] = elem_hi_f(old[1]);
         }
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[t][u][rr * 4 + e] * a.scale + add[e]);
-        *reinterpret_cast<bf16x4*>(dst) = v4;
+        for (int e = 0; e < 4; ++e) v4[e] = (elem_t)(acc[t][u][rr * 4 + e] * a.scale + add[e]);
+        *reinterpret_cast<elem4*>(dst) = v4;
       }
   }
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the attention kernels (gfx950 only).
 //
-// MFMA conventions used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+// MFMA conventions used throughout (v_mfma_f32_32x32x16_bf16 / _f16, wave64):
 //   A operand: lane l supplies row (l % 32), 8 contraction elements chosen by
 //              the lane half (l / 32);
 //   B operand: lane l supplies column (l % 32), 8 contraction elements chosen
@@ -16,21 +16,61 @@
 #include <limits.h>
 #include <stdint.h>
 
-namespace vca {
+#include "attn_args.hpp"
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// Element type of q, k, v, out, dout, dq, dk, dv: every kernel translation
+// unit is compiled once per type, bf16 into namespace vca::bf and (with
+// VCA_ELEM_F16 defined) fp16 into vca::hf. Everything below depends on it only
+// through elem_t, the 16-bit MFMA operand fragments and the 16-bit -> fp32
+// decode helpers; accumulation is fp32 for both.
+#ifdef VCA_ELEM_F16
+#define VCA_ELEM hf
+#define VCA_MFMA_32x32x16 "v_mfma_f32_32x32x16_f16"
+#else
+#define VCA_ELEM bf
+#define VCA_MFMA_32x32x16 "v_mfma_f32_32x32x16_bf16"
+#endif
+
+namespace vca {
+namespace VCA_ELEM {
+
+#ifdef VCA_ELEM_F16
+typedef _Float16 elem_t;
+#else
+typedef __bf16 elem_t;
+#endif
+typedef elem_t frag8 __attribute__((ext_vector_type(8)));
+typedef elem_t elem4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_inff();
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma32(frag8 a, frag8 b, f32x16 c) {
+#ifdef VCA_ELEM_F16
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+#else
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
+}
+
+// fp32 value of a 16-bit element held in the low bits of b (exact for both
+// types)
+__device__ __forceinline__ float elem_to_f(uint32_t b) {
+#ifdef VCA_ELEM_F16
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu));
+#else
+  return __uint_as_float(b << 16);
+#endif
+}
+// the low / high element of a 32-bit word of two packed elements
+__device__ __forceinline__ float elem_lo_f(uint32_t w) { return elem_to_f(w & 0xffffu); }
+__device__ __forceinline__ float elem_hi_f(uint32_t w) {
+#ifdef VCA_ELEM_F16
+  return elem_to_f(w >> 16);
+#else
+  return __uint_as_float(w & 0xffff0000u);
+#endif
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -51,10 +91,10 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 }
 __device__ __forceinline__ void sts16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void sts8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+__device__ __forceinline__ frag8 lds_frag(const uint16_t* p) {
+  return *reinterpret_cast<const frag8*>(p);
 }
-__device__ __forceinline__ bf16x8 as_frag(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ frag8 as_frag(u32x4 v) { return __builtin_bit_cast(frag8, v); }
 
 __device__ __forceinline__ u32x4 zero_u32x4() {
   u32x4 z = {0u, 0u, 0u, 0u};
@@ -62,7 +102,7 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
 }
 
 // Element e (0..7) of eight packed bf16 values.
-__device__ __forceinline__ uint32_t bf16_at(u32x4 v, int e) {
+__device__ __forceinline__ uint32_t elem_at(u32x4 v, int e) {
   return (v[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
 }
 
@@ -95,14 +135,14 @@ __device__ __forceinline__ void pipeline_mfma_reads() {
 // MFMA before anything else reads or overwrites its result or C operand.
 // S / dP: A from an LDS read, B from AGPRs (no VALU-written operand, so no
 // wait states); C starts at zero (mfma_v0) or accumulates (mfma_v).
-__device__ __forceinline__ void mfma_v0(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b_agpr));
+__device__ __forceinline__ void mfma_v0(f32x16& c, frag8 a, frag8 b_agpr) {
+  asm(VCA_MFMA_32x32x16 " %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b_agpr));
 }
-__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b_agpr) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_agpr));
+__device__ __forceinline__ void mfma_v(f32x16& c, frag8 a, frag8 b_agpr) {
+  asm(VCA_MFMA_32x32x16 " %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b_agpr));
 }
-__device__ __forceinline__ void mfma_a(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma_a(f32x16& acc, frag8 a, frag8 b) {
+  asm("s_nop 1\n\t" VCA_MFMA_32x32x16 " %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // Orders the wait after the MFMAs that produced `x` (an asm with x as an
 // in/out operand cannot move above them).
@@ -118,8 +158,8 @@ __device__ __forceinline__ f32x16 in_agprs(f32x16 x) {
   asm volatile("; in agprs" : "=a"(r) : "0"(x));
   return r;
 }
-__device__ __forceinline__ bf16x8 in_agprs(bf16x8 x) {
-  bf16x8 r;
+__device__ __forceinline__ frag8 in_agprs(frag8 x) {
+  frag8 r;
   asm volatile("; in agprs" : "=a"(r) : "0"(x));
   return r;
 }
@@ -263,11 +303,11 @@ __device__ __forceinline__ void stg8(uint16_t* p, u32x2 v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Eight fp32 values -> eight bf16 (round to nearest even) as one MFMA fragment.
-__device__ __forceinline__ bf16x8 to_frag(const float* x) {
-  bf16x8 r;
+// Eight fp32 values -> eight elements (round to nearest even) as one MFMA fragment.
+__device__ __forceinline__ frag8 to_frag(const float* x) {
+  frag8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  for (int i = 0; i < 8; ++i) r[i] = (elem_t)x[i];
   return r;
 }
 
@@ -349,7 +389,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // rows {k0 + 4h + j, k0 + 8 + 4h + j : j < 4} (h = l / 32), the key/query
 // order in which a 32x32 C tile holds its rows, so the fragment pairs with a
 // C tile reused as the B operand.
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* X, int LS, int k0, int n0, int lane) {
+__device__ __forceinline__ frag8 tr_frag(const uint16_t* X, int LS, int k0, int n0, int lane) {
   const int g = lane >> 4, s = lane & 15, h = lane >> 5;
   const int row = k0 + 4 * h + (s >> 2);
   const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
@@ -360,7 +400,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* X, int LS, int k0, int
       (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)(p + 8 * LS)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(frag8, v);
 }
 
 // ---- swizzled 128-wide tiles ---------------------------------------------
@@ -378,13 +418,13 @@ __device__ __forceinline__ int rtile_off(int r, int u) {
 }
 // A operand of S / dP: lane l gets row l%32 and the 8 head-dim elements of
 // piece `piece` (= 2*ks + l/32).
-__device__ __forceinline__ bf16x8 rtile_row(const uint16_t* X, int r, int piece) {
+__device__ __forceinline__ frag8 rtile_row(const uint16_t* X, int r, int piece) {
   return lds_frag(X + rtile_off(r, piece));
 }
 // A operand of dV^T / dK^T: lane l gets head-dim column n0 + l%32 and query
 // rows {k0 + 4h + j, k0 + 8 + 4h + j : j < 4} (h = l/32) through the
 // transposing read; the row order matches a 32x32 C tile reused as B.
-__device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, int lane) {
+__device__ __forceinline__ frag8 rtile_col(const uint16_t* X, int k0, int n0, int lane) {
   const int g = lane >> 4, s = lane & 15, h = lane >> 5;
   const int row = k0 + 4 * h + (s >> 2);
   const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
@@ -393,7 +433,7 @@ __device__ __forceinline__ bf16x8 rtile_col(const uint16_t* X, int k0, int n0, i
   const uint16_t* p1 = X + rtile_off(row + 8, c >> 3) + (c & 7);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Workgroup -> (work item, q-head) for passes whose grid is items x H q-heads
@@ -416,12 +456,8 @@ __device__ __forceinline__ void xcd_item_head(int bid, int H, int G, int& item, 
   }
 }
 
-// Segment geometry: query rows [q_row0, q_row0 + lq) and key rows
-// [k_row0, k_row0 + lk) of the packed tensors. cu arrays are clamped into
-// [0, T] so a malformed table can never index outside the tensors.
-struct SegGeom {
-  int q_row0, lq, k_row0, lk;
-};
+// Segment geometry (SegGeom): cu arrays are clamped into [0, T] so a
+// malformed table can never index outside the tensors.
 
 __device__ __forceinline__ SegGeom seg_geom(const int32_t* cu_q, const int32_t* cu_k, int s,
                                             int Nq, int Nk, int Tq, int Tk) {
@@ -444,16 +480,5 @@ __device__ __forceinline__ SegGeom seg_geom(const int32_t* cu_q, const int32_t* 
   return g;
 }
 
-// Tensor view: element (seg-or-batch b, row, head h, d) lives at
-// base + b*sb + row*sn + h*sh + d. Varlen views have sb = 0 and rows offset by
-// the segment's first row.
-struct View {
-  const uint16_t* p;
-  int64_t sb, sh, sn;
-};
-struct ViewW {
-  uint16_t* p;
-  int64_t sb, sh, sn;
-};
-
+}  // namespace VCA_ELEM
 }  // namespace vca

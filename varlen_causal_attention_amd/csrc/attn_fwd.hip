@@ -1,15 +1,13 @@
 // Forward launcher: instantiates the forward kernel for every compiled
 // head-dim pair and both mask modes.
+#include "attn_fwd.hpp"
 #include "attn_fwd_wide.hpp"
 #include "attn_launch.hpp"
+#include "attn_sched.hpp"
 #include "attn_timing.hpp"
 
 namespace vca {
-
-bool head_dims_supported(int dqk, int dv) {
-  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128) ||
-         (dqk == 256 && dv == 256) || (dqk == 512 && dv == 512);
-}
+namespace VCA_ELEM {
 
 namespace {
 // BN = keys per tile, DS = waves sharing one 32-row query block, NBUF = LDS
@@ -81,4 +79,5 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   return fwd_wide(a, causal, grid, st);
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

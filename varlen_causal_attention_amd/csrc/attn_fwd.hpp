@@ -23,24 +23,8 @@
 #include "attn_common.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
-struct FwdArgs {
-  View q, k, v;
-  ViewW o;
-  float* lse;
-  int64_t lse_sb, lse_sh;  // lse index = b*lse_sb + h*lse_sh + (q_row0 + i)
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  int Nq, Nk, Tq, Tk;
-  int G;            // Hq / Hkv
-  int H;            // q-heads: blockIdx.x = item * H + head
-  float scale_log2; // scale * log2(e)
-  const int2* items;      // (segment, q tile) heavy first
-  const int* item_count;
-};
-
-constexpr int kFwdWaves = 4;
-constexpr int kFwdBM = 32 * kFwdWaves;
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
 template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL, int HPW = 1>
@@ -123,7 +107,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   // factor sl2 applied to the scores is always positive.
   const float sl2 = fabsf(a.scale_log2);
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  bf16x8 qf[NKS];
+  frag8 qf[NKS];
   {
     const bool ok = row < lq;
     const uint16_t* src = qb + (int64_t)(ok ? row : 0) * a.q.sn + ds * DR + half * 8;
@@ -288,7 +272,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
       // P = exp2(x - m), row sum, pack to bf16 fragments
-      bf16x8 pf[2 * NKB];
+      frag8 pf[2 * NKB];
 #pragma unroll
       for (int kbk = 0; kbk < NKB; ++kbk) {
         float p[16];
@@ -337,10 +321,10 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[db][rr * 4 + c] * inv);
-        *reinterpret_cast<bf16x4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(o[db][rr * 4 + c] * inv);
+        *reinterpret_cast<elem4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
       }
     }
     if (half == 0 && ds == 0) {
@@ -350,4 +334,5 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   }
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

@@ -27,6 +27,7 @@
 #include "attn_fwd.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
 constexpr int kWideD = 512;
 constexpr int kWideBN = 32;  // keys per tile
@@ -72,7 +73,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
 
   // Q fragments of this lane's row (rows past the segment's end read its
   // first row: their results are never stored)
-  bf16x8 qf[NKS];
+  frag8 qf[NKS];
   {
     const uint16_t* src = qb + (int64_t)(row < lq ? row : 0) * a.q.sn + half * 8;
 #pragma unroll
@@ -121,7 +122,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   // place one between MFMAs: steps 0-15 scale and mask, 16 the row max, 17-32
   // exp2, 33-34 pack.
   float mx = kNegInf, m_use = 0.f;
-  auto sm_step = [&](int c, f32x16& sc, int tt, bf16x8* pf) {
+  auto sm_step = [&](int c, f32x16& sc, int tt, frag8* pf) {
     if (c < 16) {
       const int r = c;
       const int key = tt * BN + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -149,7 +150,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
       pf[c - 33] = to_frag(e);
     }
   };
-  auto softmax = [&](f32x16& sc, int tt, bf16x8* pf) {
+  auto softmax = [&](f32x16& sc, int tt, frag8* pf) {
 #pragma unroll
     for (int c = 0; c < 35; ++c) sm_step(c, sc, tt, pf);
   };
@@ -159,7 +160,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
     for (int ks = 0; ks < NKS; ++ks) sc = mfma32(kfrag(K, ks), qf[ks], sc);
     return sc;
   };
-  auto product = [&](const uint16_t* V, const bf16x8* pf) {
+  auto product = [&](const uint16_t* V, const frag8* pf) {
 #pragma unroll
     for (int j = 0; j < 2 * NDB; ++j) mfma_a(o[j & 15], vfrag(V, j), pf[j >> 4]);
   };
@@ -188,7 +189,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   // row sum nor the running max. One code path keeps O in place in the
   // accumulation registers.
   f32x16 s_cur = zero16();
-  bf16x8 pf_prev[2], pf_cur[2];
+  frag8 pf_prev[2], pf_cur[2];
   if (nt > 0) {
     issue(kb, a.k.sn, lds_k, KS, 0);
     if (nt > 1) issue(kb, a.k.sn, lds_k, KS, 1);
@@ -223,7 +224,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
     const uint16_t* Kn = &sk[(t + 1) & 1][0];
     const uint16_t* Vp = &sv[(t + 1) & 1][0];
     f32x16 s_next = zero16();
-    bf16x8 fr[NSLOT];
+    frag8 fr[NSLOT];
 #pragma unroll
     for (int c = 0; c < LEAD; ++c) fr[c] = (c & 1) ? vfrag(Vp, c >> 1) : kfrag(Kn, c >> 1);
 #pragma unroll
@@ -269,10 +270,10 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        bf16x4 v4;
+        elem4 v4;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[db][rr * 4 + c] * inv);
-        *reinterpret_cast<bf16x4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
+        for (int c = 0; c < 4; ++c) v4[c] = (elem_t)(o[db][rr * 4 + c] * inv);
+        *reinterpret_cast<elem4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
       }
     }
     if (half == 0) {
@@ -282,4 +283,5 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   }
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

@@ -3,9 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "attn_bwd.hpp"
-#include "attn_fwd.hpp"
-#include "attn_sched.hpp"
+#include "attn_args.hpp"
 
 namespace vca {
 
@@ -16,12 +14,13 @@ namespace vca {
 struct MergeArgs {
   const void* out_a;
   const void* out_b;
-  int a_f32, b_f32;
+  int a_type, b_type;  // ATTN_BF16, ATTN_F32 or ATTN_F16
   const float* lse_a;
   const float* lse_b;
   float* out;
   float* lse;
-  uint16_t* out_bf16;
+  uint16_t* out_copy;  // optional 16-bit copy of out, of copy_type
+  int copy_type;       // ATTN_BF16 or ATTN_F16
   int rows, H, Dv;
 };
 
@@ -114,6 +113,10 @@ inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int Hkv, int64_t q_ro
   return w;
 }
 
+// Launchers of one element type, defined in the kernel translation units
+// (compiled once per type: vca::bf for bf16, vca::hf for fp16); their
+// arguments are the same for both.
+namespace bf {
 // Scheduler launch + forward kernel. ws: the forward workspace. q_rows: Tq
 // (varlen) or B * Nq (dense), used for the list capacity.
 hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int64_t q_rows,
@@ -142,13 +145,44 @@ hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipSt
 hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
                             int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg,
                             const BwdWorkspace& wl, void* ws, hipStream_t st);
+}  // namespace bf
+namespace hf {
+// Scheduler launch + forward kernel. ws: the forward workspace. q_rows: Tq
+// (varlen) or B * Nq (dense), used for the list capacity.
+hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int64_t q_rows,
+                      void* ws, hipStream_t stream);
+
+// delta pre-pass, then either the fused dK/dV and dQ passes or the two-phase
+// scores + products passes, in that order on one stream. ws: the backward
+// workspace laid out by bwd_workspace (delta first).
+hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
+                      int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg, void* ws,
+                      hipStream_t stream);
+
+// Work lists of the backward (query tiles of q_tile rows costed in q_step
+// keys, key blocks of k_tile keys costed in k_step queries) and the delta
+// pre-pass; fills the list fields of a.
+void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int max_q,
+                 int64_t q_rows, int64_t k_rows, const BwdWorkspace& wl, int q_tile, int q_step,
+                 int k_tile, int k_step, void* ws, hipStream_t st);
+
+// dK/dV pass of head dim 128 with split wave roles (attn_bwd_roles.hip);
+// grid = (128-key blocks + segments) * Hkv.
+hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
+
+// Two-phase backward (the head-dim pairs bwd_uses_tiles names): lists,
+// delta, scores, products.
+hipError_t launch_bwd_tiles(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq, int Hkv,
+                            int max_q, int64_t q_rows, int64_t k_rows, const TileGeom& tg,
+                            const BwdWorkspace& wl, void* ws, hipStream_t st);
+}  // namespace hf
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 // rows a dense ring chunk must not produce: out rows to 0, lse to -inf
 struct ZeroRowsArgs {
   void* out;
-  int f32;
+  int f32;  // 0: 16-bit elements (bf16 or fp16), 1: fp32
   int64_t ob, oh, on;
   float* lse;
   int64_t lse_sb, lse_sh;

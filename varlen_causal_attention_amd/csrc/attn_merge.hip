@@ -1,12 +1,26 @@
 // Merge launcher and kernel.
+#include "attn_common.hpp"
 #include "attn_launch.hpp"
 #include "attn_timing.hpp"
 
 namespace vca {
+using namespace VCA_ELEM;  // vector types and helpers (this unit is built once)
 
-__device__ __forceinline__ float load_elem(const void* p, int f32, int64_t i) {
-  return f32 ? reinterpret_cast<const float*>(p)[i]
-             : __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+// Element types of the merge's inputs and copy (the ABI's dtype codes).
+constexpr int kF32 = 1, kF16 = 2;  // else bf16 (0)
+
+__device__ __forceinline__ float half_bits_to_f(uint32_t b, int type) {
+  return type == kF16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu))
+                      : __uint_as_float(b << 16);
+}
+__device__ __forceinline__ uint32_t f_to_half_bits(float v, int type) {
+  return type == kF16 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v)
+                      : (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int type, int64_t i) {
+  return type == kF32 ? reinterpret_cast<const float*>(p)[i]
+                      : half_bits_to_f(reinterpret_cast<const uint16_t*>(p)[i], type);
 }
 
 __global__ void __launch_bounds__(256) attn_merge_kernel(const MergeArgs a) {
@@ -27,12 +41,10 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const MergeArgs a) {
   }
   const int64_t base = pair * a.Dv;
   for (int d = lane; d < a.Dv; d += 64) {
-    const float v = wa * load_elem(a.out_a, a.a_f32, base + d) + wb * load_elem(a.out_b, a.b_f32, base + d);
+    const float v = wa * load_elem(a.out_a, a.a_type, base + d) +
+                    wb * load_elem(a.out_b, a.b_type, base + d);
     a.out[base + d] = v;
-    if (a.out_bf16) {
-      const __bf16 b = (__bf16)v;
-      a.out_bf16[base + d] = __builtin_bit_cast(uint16_t, b);
-    }
+    if (a.out_copy) a.out_copy[base + d] = (uint16_t)f_to_half_bits(v, a.copy_type);
   }
   if (lane == 0) a.lse[li] = l;
 }
@@ -41,8 +53,8 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const MergeArgs a) {
 // Head dims that are a multiple of 8 with 16-byte aligned buffers: one thread
 // per 8 consecutive elements of a (row, head), 16- and 32-byte loads and
 // stores; each thread recomputes its row's weights from the two lse values.
-__device__ __forceinline__ void load8(const void* p, int f32, int64_t i, float (&v)[8]) {
-  if (f32) {
+__device__ __forceinline__ void load8(const void* p, int type, int64_t i, float (&v)[8]) {
+  if (type == kF32) {
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
     const f32x4 x1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i + 4);
 #pragma unroll
@@ -54,8 +66,8 @@ __device__ __forceinline__ void load8(const void* p, int f32, int64_t i, float (
     const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p) + i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(x[j] << 16);
-      v[2 * j + 1] = __uint_as_float(x[j] & 0xffff0000u);
+      v[2 * j] = half_bits_to_f(x[j], type);
+      v[2 * j + 1] = half_bits_to_f(x[j] >> 16, type);
     }
   }
 }
@@ -80,8 +92,8 @@ __global__ void __launch_bounds__(256) attn_merge8_kernel(const MergeArgs a) {
   }
   const int64_t e = pair * a.Dv + d0;
   float va[8], vb[8], v[8];
-  load8(a.out_a, a.a_f32, e, va);
-  load8(a.out_b, a.b_f32, e, vb);
+  load8(a.out_a, a.a_type, e, va);
+  load8(a.out_b, a.b_type, e, vb);
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = wa * va[j] + wb * vb[j];
   f32x4 o0, o1;
@@ -92,15 +104,12 @@ __global__ void __launch_bounds__(256) attn_merge8_kernel(const MergeArgs a) {
   }
   *reinterpret_cast<f32x4*>(a.out + e) = o0;
   *reinterpret_cast<f32x4*>(a.out + e + 4) = o1;
-  if (a.out_bf16) {
+  if (a.out_copy) {
     u32x4 b;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[2 * j]);
-      const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v[2 * j + 1]);
-      b[j] = lo | (hi << 16);
-    }
-    *reinterpret_cast<u32x4*>(a.out_bf16 + e) = b;
+    for (int j = 0; j < 4; ++j)
+      b[j] = f_to_half_bits(v[2 * j], a.copy_type) | (f_to_half_bits(v[2 * j + 1], a.copy_type) << 16);
+    *reinterpret_cast<u32x4*>(a.out_copy + e) = b;
   }
   if (d0 == 0) a.lse[li] = l;
 }
@@ -143,7 +152,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   // multiple of the chunk count Dv/8. Otherwise one wave per (row, head).
   const int cpp = a.Dv / 8;
   const bool one_wave = cpp >= 1 && cpp <= 64 && 64 % cpp == 0;
-  if (a.Dv % 8 == 0 && al16(a.out_a) && al16(a.out_b) && al16(a.out) && al16(a.out_bf16) &&
+  if (a.Dv % 8 == 0 && al16(a.out_a) && al16(a.out_b) && al16(a.out) && al16(a.out_copy) &&
       (one_wave || a.lse != a.lse_a)) {
     const int64_t chunks = pairs * (a.Dv / 8);
     hipLaunchKernelGGL(attn_merge8_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st, a);

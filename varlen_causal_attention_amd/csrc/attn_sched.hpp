@@ -12,6 +12,7 @@
 #include "attn_common.hpp"
 
 namespace vca {
+namespace VCA_ELEM {
 
 constexpr int kSchedBuckets = 2048;  // cost classes (costs clamp into the last one)
 
@@ -170,4 +171,5 @@ attn_schedule2_kernel(const SchedArgs2 a) {
   else schedule_list(a.list[blockIdx.x]);
 }
 
+}  // namespace VCA_ELEM
 }  // namespace vca

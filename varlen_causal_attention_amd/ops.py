@@ -12,7 +12,10 @@ import ctypes as C
 import numpy as np
 import torch
 
-from ._lib import ATTN_BF16, ATTN_DQ_ACCUMULATE, ATTN_F32, check, i64_array, load
+from ._lib import ATTN_BF16, ATTN_DQ_ACCUMULATE, ATTN_F16, ATTN_F32, check, i64_array, load
+
+# element types of q, k, v, out, dout and the gradients (one per call)
+_DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
 
 def _stream(t: torch.Tensor) -> C.c_void_p:
@@ -23,22 +26,26 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else C.c_void_p(0)
 
 
-def _need_gpu_bf16(**tensors):
-    dev = None
+def _need_gpu_half(**tensors):
+    """(device, torch dtype) of GPU tensors that share one element type,
+    bfloat16 or float16, each with a contiguous last dimension."""
+    dev = dt = None
     for name, t in tensors.items():
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on the GPU")
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16")
+        if t.dtype not in _DTYPES:
+            raise ValueError(f"{name} must be bfloat16 or float16")
         if t.numel() > 0 and t.stride(-1) != 1:
             raise ValueError(f"{name} must have a contiguous last dimension")
         if dev is None:
-            dev = t.device
+            dev, dt = t.device, t.dtype
         elif t.device != dev:
             raise ValueError("all tensors must be on one device")
-    return dev
+        elif t.dtype != dt:
+            raise ValueError("q, k, v (and out, dout, gradients) must share one dtype")
+    return dev, dt
 
 
 def _dense_shapes(q, k, v):
@@ -88,8 +95,8 @@ def _workspace(size: int, device) -> torch.Tensor:
     return torch.empty(max(size, 16), dtype=torch.uint8, device=device)
 
 
-def is_supported(dqk: int, dv: int) -> bool:
-    return bool(load().attn_is_supported(ATTN_BF16, dqk, dv))
+def is_supported(dqk: int, dv: int, dtype=torch.bfloat16) -> bool:
+    return bool(load().attn_is_supported(_DTYPES.get(dtype, -1), dqk, dv))
 
 
 def version() -> int:
@@ -103,13 +110,13 @@ def fwd_dense(q, k, v, scale: float, causal: bool, out=None, lse=None):
     """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log). out / lse
     may be given (out as any view with a unit last stride, lse contiguous)."""
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
-    dev = _need_gpu_bf16(q=q, k=k, v=v)
-    out = _output(out, (B, Hq, Nq, Dv), torch.bfloat16, dev, "out")
+    dev, dt = _need_gpu_half(q=q, k=k, v=v)
+    out = _output(out, (B, Hq, Nq, Dv), dt, dev, "out")
     lse = _lse_output(lse, (B, Hq, Nq), dev)
     strides = i64_array(list(q.stride()[:3]) + list(k.stride()[:3]) + list(v.stride()[:3])
                         + list(out.stride()[:3]))
     lib = load()
-    args = (ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, Dqk, Dv,
+    args = (_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, Dqk, Dv,
             strides, float(scale), int(bool(causal)))
     need = C.c_size_t(0)
     check(lib.attn_fwd_dense(*args, None, C.byref(need), _stream(q)), "attn_fwd_dense")
@@ -127,14 +134,14 @@ def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     if tuple(out.shape) != (B, Hq, Nq, Dv) or tuple(dout.shape) != (B, Hq, Nq, Dv):
         raise ValueError("out/dout must be [B, Hq, Nq, Dv]")
-    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
+    dev, dt = _need_gpu_half(dout=dout, q=q, k=k, v=v, out=out)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, Hq, Nq]")
     if lse.device != dev:
         raise ValueError("lse must be on the GPU with the other tensors")
     flags = 0
     if dq_accumulate is not None:
-        _need_gpu_bf16(dq=dq_accumulate)
+        _need_gpu_half(dq=dq_accumulate, q=q)
         if tuple(dq_accumulate.shape) != tuple(q.shape):
             raise ValueError("dq_accumulate must have q's shape")
         if dq is not None:
@@ -142,12 +149,12 @@ def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate
         dq = dq_accumulate
         flags |= ATTN_DQ_ACCUMULATE
     else:
-        dq = _output(dq, (B, Hq, Nq, Dqk), torch.bfloat16, dev, "dq")
-    dk = _output(dk, (B, Hkv, Nk, Dqk), torch.bfloat16, dev, "dk")
-    dv = _output(dv, (B, Hkv, Nk, Dv), torch.bfloat16, dev, "dv")
+        dq = _output(dq, (B, Hq, Nq, Dqk), dt, dev, "dq")
+    dk = _output(dk, (B, Hkv, Nk, Dqk), dt, dev, "dk")
+    dv = _output(dv, (B, Hkv, Nk, Dv), dt, dev, "dv")
     strides = i64_array(sum((list(t.stride()[:3]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
     lib = load()
-    args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
+    args = (_DTYPES[dt], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
             _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, Dqk, Dv, strides, float(scale),
             int(bool(causal)), flags)
     need = C.c_size_t(0)
@@ -174,13 +181,13 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if cu_q.numel() != cu_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
-    dev = _need_gpu_bf16(q=q, k=k, v=v)
-    out = _output(out, (Tq, Hq, Dv), torch.bfloat16, dev, "out")
+    dev, dt = _need_gpu_half(q=q, k=k, v=v)
+    out = _output(out, (Tq, Hq, Dv), dt, dev, "out")
     lse = _lse_output(lse, (Hq, Tq), dev)
     strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
                         + list(out.stride()[:2]))
     lib = load()
-    args = (ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev),
+    args = (_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev),
             _cu(cu_k, dev), cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv,
             strides, float(scale), int(bool(causal)))
     need = C.c_size_t(0)
@@ -202,14 +209,14 @@ def fwd_varlen_noalloc(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     if out is None or lse is None:
         raise ValueError("out and lse must be given")
-    dev = _need_gpu_bf16(q=q, k=k, v=v)
-    out = _output(out, (Tq, Hq, Dv), torch.bfloat16, dev, "out")
+    dev, dt = _need_gpu_half(q=q, k=k, v=v)
+    out = _output(out, (Tq, Hq, Dv), dt, dev, "out")
     lse = _lse_output(lse, (Hq, Tq), dev)
     strides = i64_array(list(q.stride()[:2]) + list(k.stride()[:2]) + list(v.stride()[:2])
                         + list(out.stride()[:2]))
     st = load().attn_fwd_varlen_noalloc(
-        ATTN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev), _cu(cu_k, dev),
-        cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale),
+        _DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev),
+        _cu(cu_k, dev), cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale),
         int(bool(causal)), _stream(q))
     check(st, "attn_fwd_varlen_noalloc")
     return out, lse
@@ -222,7 +229,7 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if tuple(out.shape) != (Tq, Hq, Dv) or tuple(dout.shape) != (Tq, Hq, Dv):
         raise ValueError("out/dout must be [Tq, Hq, Dv]")
-    dev = _need_gpu_bf16(dout=dout, q=q, k=k, v=v, out=out)
+    dev, dt = _need_gpu_half(dout=dout, q=q, k=k, v=v, out=out)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [Hq, Tq]")
     if lse.device != dev:
@@ -231,7 +238,7 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     flags = 0
     if dq_accumulate is not None:
-        _need_gpu_bf16(dq=dq_accumulate)
+        _need_gpu_half(dq=dq_accumulate, q=q)
         if tuple(dq_accumulate.shape) != tuple(q.shape):
             raise ValueError("dq_accumulate must have q's shape")
         if dq is not None:
@@ -239,12 +246,12 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
         dq = dq_accumulate
         flags |= ATTN_DQ_ACCUMULATE
     else:
-        dq = _output(dq, (Tq, Hq, Dqk), torch.bfloat16, dev, "dq")
-    dk = _output(dk, (Tk, Hkv, Dqk), torch.bfloat16, dev, "dk")
-    dv = _output(dv, (Tk, Hkv, Dv), torch.bfloat16, dev, "dv")
+        dq = _output(dq, (Tq, Hq, Dqk), dt, dev, "dq")
+    dk = _output(dk, (Tk, Hkv, Dqk), dt, dev, "dk")
+    dv = _output(dv, (Tk, Hkv, Dv), dt, dev, "dv")
     strides = i64_array(sum((list(t.stride()[:2]) for t in (q, k, v, out, dout, dq, dk, dv)), []))
     lib = load()
-    args = (ATTN_BF16, _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
+    args = (_DTYPES[dt], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
             _ptr(dk), _ptr(dv), _cu(cu_q, dev), _cu(cu_k, dev), cu_q.numel() - 1, int(max_q),
             int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale), int(bool(causal)), flags)
     need = C.c_size_t(0)
@@ -258,14 +265,17 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
 # ---------------------------------------------------------------------------
 # lse merge of two partial results of the same rows
 # ---------------------------------------------------------------------------
-def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, bf16_copy: bool = False):
-    """fp32 (out [rows, H, Dv], lse [H, rows]) of two partial results; with
-    bf16_copy also a bf16 rounding of out (to feed the backward). out/lse may
-    be given (e.g. aliasing fp32 out_a / lse_a as running accumulators)."""
+def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, bf16_copy: bool = False,
+          copy_dtype=None):
+    """fp32 (out [rows, H, Dv], lse [H, rows]) of two partial results, plus a
+    16-bit copy of out (to feed the backward) in copy_dtype (bfloat16 or
+    float16; bf16_copy=True means bfloat16), else None. out/lse may be given
+    (e.g. aliasing fp32 out_a / lse_a as running accumulators)."""
     rows, H, Dv = out_a.shape
+    codes = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32, torch.float16: ATTN_F16}
     for name, t in (("out_a", out_a), ("out_b", out_b)):
-        if t.device.type != "cuda" or t.dtype not in (torch.bfloat16, torch.float32):
-            raise ValueError(f"{name} must be a bf16 or fp32 GPU tensor")
+        if t.device.type != "cuda" or t.dtype not in codes:
+            raise ValueError(f"{name} must be a bf16, fp16 or fp32 GPU tensor")
         if tuple(t.shape) != (rows, H, Dv) or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [rows, H, Dv]")
     for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
@@ -282,10 +292,14 @@ def merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, bf16_copy: bool = Fals
         raise ValueError("out must be contiguous fp32 [rows, H, Dv]")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (H, rows) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [H, rows]")
-    ob = torch.empty((rows, H, Dv), dtype=torch.bfloat16, device=dev) if bf16_copy else None
-    dt = lambda t: ATTN_F32 if t.dtype == torch.float32 else ATTN_BF16  # noqa: E731
-    st = load().attn_merge(_ptr(out_a), dt(out_a), _ptr(lse_a), _ptr(out_b), dt(out_b),
-                           _ptr(lse_b), _ptr(out), _ptr(lse), _ptr(ob), rows, H, Dv,
+    if copy_dtype is None and bf16_copy:
+        copy_dtype = torch.bfloat16
+    if copy_dtype is not None and copy_dtype not in _DTYPES:
+        raise ValueError("copy_dtype must be bfloat16 or float16")
+    ob = torch.empty((rows, H, Dv), dtype=copy_dtype, device=dev) if copy_dtype else None
+    st = load().attn_merge(_ptr(out_a), codes[out_a.dtype], _ptr(lse_a), _ptr(out_b),
+                           codes[out_b.dtype], _ptr(lse_b), _ptr(out), _ptr(lse), _ptr(ob),
+                           _DTYPES[copy_dtype] if copy_dtype else ATTN_BF16, rows, H, Dv,
                            _stream(out_a))
     check(st, "attn_merge")
     return out, lse, ob
@@ -358,8 +372,9 @@ def zero_rows(out, lse, rows):
     """In place: out[b, :, i, :] = 0 and lse[b, :, i] = -inf where rows[b, i]
     (out a [B, H, S, D] bf16 or fp32 view, lse contiguous [B, H, S] fp32 or
     None, rows bool/uint8 [B, S] on the same GPU)."""
-    if out.dim() != 4 or out.stride(3) != 1 or out.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("out must be a [B, H, S, D] bf16/fp32 view with unit last stride")
+    if out.dim() != 4 or out.stride(3) != 1 or out.dtype not in (torch.bfloat16, torch.float16,
+                                                                     torch.float32):
+        raise ValueError("out must be a [B, H, S, D] bf16/fp16/fp32 view with unit last stride")
     B, H, S, D = out.shape
     if tuple(rows.shape) != (B, S) or rows.device != out.device:
         raise ValueError("rows must be [B, S] on the device of out")
@@ -367,7 +382,7 @@ def zero_rows(out, lse, rows):
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous fp32 [B, H, S]")
-    dt = ATTN_F32 if out.dtype == torch.float32 else ATTN_BF16
+    dt = {torch.float32: ATTN_F32, torch.float16: ATTN_F16}.get(out.dtype, ATTN_BF16)
     ls = (H * S, S) if lse is not None else (0, 0)
     check(load().attn_zero_rows(_ptr(out), dt, out.stride(0), out.stride(1), out.stride(2),
                                 _ptr(lse), ls[0], ls[1], _ptr(r), B, H, S, D, _stream(out)),

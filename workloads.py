@@ -8,7 +8,8 @@ here without sharing any computation.
 
 Tensor recipe: ``g = torch.Generator().manual_seed(seed)``, then each tensor in
 a fixed order is ``torch.randn(shape, generator=g, dtype=float32)`` rounded to
-bfloat16 on the CPU (i.i.d. N(0,1) values, as the workloads state).
+bfloat16 on the CPU (i.i.d. N(0,1) values, as the workloads state); the fp16
+variants round the same draws to float16 instead.
 Document lengths: ``rng = numpy.random.default_rng(seed)``; repeat
 ``L = min(rng.integers(lo, hi + 1), total - used)`` until ``total`` is covered,
 so the last document is truncated to fit.
@@ -34,9 +35,9 @@ def doc_lengths(total: int, lo: int, hi: int, seed: int) -> list[int]:
     return out
 
 
-def randn_bf16(shape, gen: torch.Generator) -> torch.Tensor:
-    """N(0,1) float32 draws rounded to bf16 (CPU tensor)."""
-    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+def randn_bf16(shape, gen: torch.Generator, dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0,1) float32 draws rounded to bf16 (or to `dtype`, e.g. float16; CPU tensor)."""
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(dtype)
 
 
 def cumulative(lengths) -> np.ndarray:
@@ -129,29 +130,34 @@ class Workload:
         return ids[None, :]
 
     # ---- tensors ---------------------------------------------------------
-    def tensors(self) -> dict:
-        """CPU bf16 tensors, drawn in a fixed order from the workload seed."""
+    def tensors(self, dtype=torch.bfloat16) -> dict:
+        """CPU tensors (bf16, or `dtype`), drawn in a fixed order from the
+        workload seed: the same float32 draws rounded to the element type."""
         g = torch.Generator().manual_seed(self.seed)
+
+        def draw(shape, gen):
+            return randn_bf16(shape, gen, dtype)
+
         if self.kind == "dense":
-            q = randn_bf16((self.B, self.Hq, self.Nq, self.Dqk), g)
-            k = randn_bf16((self.B, self.Hkv, self.Nk, self.Dqk), g)
-            v = randn_bf16((self.B, self.Hkv, self.Nk, self.Dv), g)
-            do = randn_bf16((self.B, self.Hq, self.Nq, self.Dv), g)
+            q = draw((self.B, self.Hq, self.Nq, self.Dqk), g)
+            k = draw((self.B, self.Hkv, self.Nk, self.Dqk), g)
+            v = draw((self.B, self.Hkv, self.Nk, self.Dv), g)
+            do = draw((self.B, self.Hq, self.Nq, self.Dv), g)
             return dict(q=q, k=k, v=v, do=do)
         if self.kind == "varlen":
             T = self.T
-            q = randn_bf16((T, self.Hq, self.Dqk), g)
-            k = randn_bf16((T, self.Hkv, self.Dqk), g)
-            v = randn_bf16((T, self.Hkv, self.Dv), g)
-            do = randn_bf16((T, self.Hq, self.Dv), g)
+            q = draw((T, self.Hq, self.Dqk), g)
+            k = draw((T, self.Hkv, self.Dqk), g)
+            v = draw((T, self.Hkv, self.Dv), g)
+            do = draw((T, self.Hq, self.Dv), g)
             return dict(q=q, k=k, v=v, do=do)
         S = self.shard
-        q = randn_bf16((S, self.Hq, self.Dqk), g)
-        k_local = randn_bf16((S, self.Hkv, self.Dqk), g)
-        v_local = randn_bf16((S, self.Hkv, self.Dv), g)
-        k_early = randn_bf16((S, self.Hkv, self.Dqk), g)
-        v_early = randn_bf16((S, self.Hkv, self.Dv), g)
-        do = randn_bf16((S, self.Hq, self.Dv), g)
+        q = draw((S, self.Hq, self.Dqk), g)
+        k_local = draw((S, self.Hkv, self.Dqk), g)
+        v_local = draw((S, self.Hkv, self.Dv), g)
+        k_early = draw((S, self.Hkv, self.Dqk), g)
+        v_early = draw((S, self.Hkv, self.Dv), g)
+        do = draw((S, self.Hq, self.Dv), g)
         return dict(q=q, k_local=k_local, v_local=v_local, k_early=k_early,
                     v_early=v_early, do=do)
 

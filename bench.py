@@ -41,12 +41,13 @@ def _dev(t):
 class Problem:
     """Device-resident inputs of one workload and closures for each stage."""
 
-    def __init__(self, n: int):
+    def __init__(self, n: int, dtype=torch.bfloat16):
         import varlen_causal_attention_amd as vca
 
         self.vca = vca
         self.w = w = workloads.workload(n)
-        t = w.tensors()
+        self.dtype = dtype
+        t = w.tensors(dtype)
         self.t = {k: _dev(v) for k, v in t.items()}
         if w.kind == "varlen":
             cu = torch.from_numpy(w.cu()).to("cuda")
@@ -76,12 +77,12 @@ class Problem:
                                               self.mx, w.scale, w.causal)
         elif self.dense:
             o1, l1, o2, l2 = self.partials()
-            _, lse, out = v.merge(o1, l1, o2, l2, bf16_copy=True)
+            _, lse, out = v.merge(o1, l1, o2, l2, copy_dtype=self.dtype)
             self.out = out.view(1, w.Hq, w.shard, w.Dv)
             self.lse = lse.view(1, w.Hq, w.shard)
         else:
             o1, l1, o2, l2 = self.partials()
-            _, self.lse, self.out = v.merge(o1, l1, o2, l2, bf16_copy=True)
+            _, self.lse, self.out = v.merge(o1, l1, o2, l2, copy_dtype=self.dtype)
 
     def partials(self):
         """Ring share: the two partial forward results the merge combines
@@ -176,8 +177,9 @@ class L2Flush:
         self.buf.fill_(1)
 
 
-def measure(n: int, steps: int, warmup: int, per_call: bool = True, flush=None) -> dict:
-    p = Problem(n)
+def measure(n: int, steps: int, warmup: int, per_call: bool = True, flush=None,
+            dtype=torch.bfloat16) -> dict:
+    p = Problem(n, dtype)
     w = p.w
     for _ in range(warmup):
         p.step()
@@ -205,10 +207,10 @@ def measure(n: int, steps: int, warmup: int, per_call: bool = True, flush=None) 
         if w.kind == "ring":
             # the lse merge alone (HBM-bound elementwise)
             parts = p.partials()
-            r["merge_calls"] = time_calls(lambda: p.vca.merge(*parts, bf16_copy=True))
+            r["merge_calls"] = time_calls(lambda: p.vca.merge(*parts, copy_dtype=p.dtype))
             if flush is not None:
                 r["merge_calls_l2_flushed"] = time_calls(
-                    lambda: p.vca.merge(*parts, bf16_copy=True), flush=flush)
+                    lambda: p.vca.merge(*parts, copy_dtype=p.dtype), flush=flush)
         elif flush is not None:
             r["fwd_calls_l2_flushed"] = time_calls(p.fwd, flush=flush)
             r["bwd_calls_l2_flushed"] = time_calls(p.bwd, flush=flush)
@@ -495,6 +497,13 @@ def main():
             r = m if n == args.workload else measure(n, max(5, args.steps // 2), 3)
             configs[r["workload"]] = config_entry(workloads.workload(n), r)
         line["configs"] = configs
+        # the same workloads with fp16 inputs (same kernels, fp16 MFMA)
+        line["configs_fp16"] = {}
+        for n in LARGE_WORKLOADS:
+            r = measure(n, max(5, args.steps // 2), 3, per_call=False, dtype=torch.float16)
+            e = config_entry(workloads.workload(n), r)
+            line["configs_fp16"][r["workload"]] = {k: e[k] for k in ("ms_per_step", "tflops_step",
+                                                                    "pct_of_peak", "fwd", "bwd")}
     if args.all:
         per = {}
         flush = L2Flush()

@@ -245,6 +245,81 @@ int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, flo
                    int64_t lse_sb, int64_t lse_sh, const uint8_t* rows, int B, int H, int S, int D,
                    hipStream_t stream);
 
+/* ---- Packed ring layout ("gemma4_moe cp_attention" page: per-document
+ * varlen segments with flat gather indices, the [B, H, S, D] <-> packed
+ * [T, H, D] row moves and their lse counterparts, the gradient scatter-add,
+ * the in-place live-row merge and the in-place-versus-scatter predicate). */
+
+/* Segments shared by a query shard and one KV chunk (host-only, no GPU work).
+ *  q_ids: host int32 [B, Sq] document ids of the query shard; k_ids: [B, Sk]
+ *  of the key chunk (1-based, 0 = padding). Every id > 0 found in row b of
+ *  both becomes one segment: its query positions p (in order) as flat indices
+ *  b*Sq + p and its key positions as b*Sk + p. Rows in order; within a row,
+ *  documents in the order they first occur among the queries; ids in only one
+ *  of the two, and padding, form no segment.
+ *  q_index (room for B*Sq), k_index (room for B*Sk): host int32 gather
+ *  indices; cu_q, cu_k (room for max_segments + 1): cumulative offsets into
+ *  them (cu_q[i] pairs cu_k[i]). *num_segments (0: no shared document),
+ *  *Tq / *Tk (live tokens), *max_q / *max_k receive the layout's sizes.
+ *  Run the local (causal) chunk with causal = 1 (a document's keys then end
+ *  where its queries end, so bottom-right alignment is position causality
+ *  when q_ids == k_ids) and a cross chunk of earlier keys with causal = 0.
+ *  ATTN_E_INVALID on bad arguments or when max_segments is too small (then
+ *  *num_segments holds the count needed). */
+int attn_ring_segments(const int32_t* q_ids, int Sq, const int32_t* k_ids, int Sk, int B,
+                       int32_t* q_index, int32_t* k_index, int32_t* cu_q, int32_t* cu_k,
+                       int max_segments, int* num_segments, int* Tq, int* Tk, int* max_q,
+                       int* max_k);
+
+/* 1 when merging a chunk's live_rows packed rows in place (attn_merge_rows)
+ * moves fewer HBM bytes than scattering them into a [B, H, S, D] tensor and
+ * merging every row (attn_scatter_rows + attn_merge); dtype is the chunk
+ * output's type. The pages give no threshold: this is the byte count of the
+ * two routes with this library's kernels. Host-only. */
+int attn_ring_inplace_preferred(int64_t live_rows, int64_t B, int64_t S, int H, int D, int dtype);
+
+/* dst[t, h, :] = src[b, h, s, :] for index[t] = b*S + s (device int32 [T]):
+ * src a [B, H, S, D] view with element strides (sb, sh, sn) and unit innermost
+ * stride, dst contiguous [T, H, D]; dtype ATTN_BF16, ATTN_F16 or ATTN_F32;
+ * dst_dtype = dtype, or ATTN_BF16 / ATTN_F16 for fp32 src (rounded to nearest
+ * even, D a multiple of 8: e.g. the merged fp32 out for a chunk's backward);
+ * D * element size a multiple of 16, pointers 16-byte aligned. Indices must
+ * lie in [0, B*S) (the kernel does not clamp them). */
+int attn_gather_rows(int dtype, const void* src, int64_t sb, int64_t sh, int64_t sn,
+                     const int32_t* index, int B, int H, int S, int D, int T, void* dst,
+                     int dst_dtype, hipStream_t stream);
+
+/* The inverse move: dst view [B, H, S, D] rows index[t] receive src[t, h, :]
+ * (ATTN_ROWS_ASSIGN), or every row is zeroed first (ATTN_ROWS_ASSIGN_ZERO_REST:
+ * rows no index names end as 0), or src is added to them in fp32 and rounded
+ * once (ATTN_ROWS_ADD: the gradient scatter-add; the indices must be distinct,
+ * which attn_ring_segments guarantees). Same layout rules as
+ * attn_gather_rows. */
+enum { ATTN_ROWS_ASSIGN = 0, ATTN_ROWS_ASSIGN_ZERO_REST = 1, ATTN_ROWS_ADD = 2 };
+int attn_scatter_rows(int dtype, const void* src, const int32_t* index, int T, int H, int D,
+                      void* dst, int64_t sb, int64_t sh, int64_t sn, int B, int S, int mode,
+                      hipStream_t stream);
+
+/* lse_packed[h, t] = lse_dense[b, h, s] (both fp32 contiguous, [H, T] and
+ * [B, H, S]) for index[t] = b*S + s; attn_scatter_lse writes the other way,
+ * first setting every dense entry to -inf when fill_rest != 0 (rows no
+ * segment covers are then "attends nothing"). */
+int attn_gather_lse(const float* lse_dense, const int32_t* index, int B, int H, int S, int T,
+                    float* lse_packed, hipStream_t stream);
+int attn_scatter_lse(const float* lse_packed, const int32_t* index, int T, int H, float* lse_dense,
+                     int B, int S, int fill_rest, hipStream_t stream);
+
+/* In-place online-softmax merge of one chunk at its live rows: for every t
+ * and head h, with (b, s) from index[t], the running fp32 accumulators
+ * out_acc[b, h, s, :] (a [B, H, S, D] view, element strides sb, sh, sn) and
+ * lse_acc[b, h, s] (contiguous [B, H, S]) are combined with out_b[t, h, :]
+ * ([T, H, D] contiguous, dtype_b) and lse_b[h, t] ([H, T]) exactly as
+ * attn_merge combines two results (both -inf: out 0, lse -inf). Rows not
+ * named are untouched; indices must be distinct. */
+int attn_merge_rows(float* out_acc, int64_t sb, int64_t sh, int64_t sn, float* lse_acc, int B,
+                    int S, const void* out_b, int dtype_b, const float* lse_b,
+                    const int32_t* index, int T, int H, int D, hipStream_t stream);
+
 /* Opt-in kernel timing, for profiling on the caller's own streams. While
  * enabled (per calling thread), every kernel this library launches from that
  * thread is bracketed by two HIP events recorded on its stream. Returns the
@@ -257,7 +332,8 @@ int attn_timing_enable(int enable);
  * "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_bwd_dq_ds" (dQ from stored dS);
  * for head dims 256 and 512
  * "attn_bwd_delta", "attn_bwd_scores", "attn_bwd_dkdv_tiles",
- * "attn_bwd_dq_tiles"; "attn_merge", "attn_zero_rows"), ms the elapsed
+ * "attn_bwd_dq_tiles"; "attn_merge", "attn_zero_rows", "attn_ring_rows",
+ * "attn_ring_fill", "attn_ring_lse", "attn_merge_rows"), ms the elapsed
  * milliseconds; *count receives the total number recorded. Returns
  * ATTN_E_HIP if an event could not be read. */
 int attn_timing_read(int max_records, char* names, int name_len, float* ms, int* count);

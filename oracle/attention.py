@@ -362,3 +362,42 @@ def merge(out_a, lse_a, out_b, lse_b):
     wb = np.where(live, np.exp(lse_b - safe), 0.0)
     out = wa.T[:, :, None] * out_a + wb.T[:, :, None] * out_b
     return out, np.where(live, lse, NEG_INF)
+
+
+# ---------------------------------------------------------------------------
+# packed ring layout ("gemma4_moe cp_attention" page: rows gathered at flat
+# indices b*S + pos, scattered back, and one chunk merged in place at its live
+# rows only)
+# ---------------------------------------------------------------------------
+def ring_gather(x, flat_index):
+    """[B, H, S, D] -> [T, H, D]: row t is x[b, :, s] for flat_index[t] = b*S + s."""
+    x = f64(x)
+    B, H, S, D = x.shape
+    idx = np.asarray(flat_index, dtype=np.int64)
+    return x.transpose(0, 2, 1, 3).reshape(B * S, H, D)[idx]
+
+
+def ring_scatter(xp, flat_index, B, S, fill=0.0):
+    """[T, H, D] -> [B, H, S, D]: the inverse of ring_gather, `fill` on rows no
+    index names."""
+    xp = f64(xp)
+    T, H, D = xp.shape
+    out = np.full((B * S, H, D), fill)
+    out[np.asarray(flat_index, dtype=np.int64)] = xp
+    return out.reshape(B, S, H, D).transpose(0, 2, 1, 3)
+
+
+def ring_merge_rows(out_acc, lse_acc, out_b, lse_b, flat_index):
+    """Running accumulators out_acc [B, H, S, D] / lse_acc [B, H, S] after
+    merging one chunk's packed rows (out_b [T, H, D], lse_b [H, T]) at its
+    flat-index rows with the -inf-safe merge; other rows unchanged."""
+    out_acc, lse_acc = f64(out_acc).copy(), f64(lse_acc).copy()
+    B, H, S, D = out_acc.shape
+    idx = np.asarray(flat_index, dtype=np.int64)
+    flat_o = out_acc.transpose(0, 2, 1, 3).reshape(B * S, H, D)
+    flat_l = lse_acc.transpose(0, 2, 1).reshape(B * S, H)
+    mo, ml = merge(flat_o[idx], flat_l[idx].T, out_b, lse_b)
+    flat_o[idx] = mo
+    flat_l[idx] = ml.T
+    return (flat_o.reshape(B, S, H, D).transpose(0, 2, 1, 3),
+            flat_l.reshape(B, S, H).transpose(0, 2, 1))

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import workloads
 from oracle import attention as orc
@@ -331,3 +332,68 @@ def test_noalloc_forward_rejects_sizes_beyond_its_scratch(lib):
     assert call(100, 0) == _lib.ATTN_E_INVALID  # the ordinary argument checks still apply
     # the header's limit and the library's agree
     assert f"ATTN_NOALLOC_MAX_ITEMS {cap}" in open(HEADER).read()
+
+
+# ---------------------------------------------------------------- packed ring segments
+def _ring_pairs(seg, q_pos, k_pos, Sq, Sk, causal):
+    """Visible (row, query position, key position) triples of a gather layout."""
+    vis = set()
+    cu_q, cu_k = seg["cu_q"], seg["cu_k"]
+    for i in range(len(cu_q) - 1):
+        qs = seg["q_index"][cu_q[i]:cu_q[i + 1]]
+        ks = seg["k_index"][cu_k[i]:cu_k[i + 1]]
+        v = orc.segment_visible(len(qs), len(ks), causal)
+        for a, fq in enumerate(qs):
+            for c, fk in enumerate(ks):
+                if v[a, c]:
+                    assert fq // Sq == fk // Sk  # one row
+                    vis.add((int(fq // Sq), int(q_pos[fq % Sq]), int(k_pos[fk % Sk])))
+    return vis
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_ring_segments_reproduce_the_document_mask(seed):
+    """attn_ring_segments' gather layout, run causal for the local chunk (keys
+    = the query shard) and non-causal for an earlier chunk, reproduces the
+    document-causal rule on exactly the live tokens: documents split into
+    several runs, padding and documents found on one side only included."""
+    rng = np.random.default_rng(300 + seed)
+    B, S = 2, 40
+    ids = rng.integers(0, 6, size=(B, 2 * S)).astype(np.int32)  # runs of every length
+    ids.sort(axis=1)
+    ids = ids[:, ::-1].copy() if seed % 2 else ids  # padding first or last
+    if seed % 3 == 0:
+        ids[:, 5:9] = 4  # a document in two separate runs
+    q_ids, early = ids[:, S:], ids[:, :S]
+    q_pos, k_pos_loc, k_pos_early = np.arange(S, 2 * S), np.arange(S, 2 * S), np.arange(S)
+    for k_ids, k_pos, causal in ((q_ids, k_pos_loc, True), (early, k_pos_early, False)):
+        seg = ops.ring_segments(q_ids, k_ids)
+        want = set()
+        for b in range(B):
+            v = orc.doc_causal_visible(q_ids[b], q_pos, k_ids[b], k_pos)
+            want |= {(b, int(q_pos[i]), int(k_pos[j])) for i, j in zip(*np.nonzero(v))}
+        if seg is None:
+            assert not want
+            continue
+        assert _ring_pairs(seg, q_pos, k_pos, S, S, causal) == want
+        # only live tokens: every gathered query has a document id > 0 that
+        # the key chunk holds in the same row
+        for fq in seg["q_index"]:
+            b, p = divmod(int(fq), S)
+            assert q_ids[b, p] > 0 and q_ids[b, p] in k_ids[b]
+        assert len(set(seg["q_index"].tolist())) == len(seg["q_index"])
+        assert seg["max_q"] == max(np.diff(seg["cu_q"])) and seg["max_k"] == max(np.diff(seg["cu_k"]))
+
+
+def test_ring_segments_none_when_nothing_shared():
+    assert ops.ring_segments(np.array([[1, 1, 0]]), np.array([[2, 2, 2]])) is None
+    assert ops.ring_segments(np.zeros((1, 4)), np.zeros((1, 4))) is None
+
+
+def test_ring_inplace_preferred_follows_the_byte_count():
+    """In-place live-row merging moves fewer bytes than scatter + dense merge
+    whenever a chunk covers part of the rows; an empty chunk prefers in place."""
+    assert ops.ring_inplace_preferred(0, 1, 4096, 16, 512)
+    assert ops.ring_inplace_preferred(2048, 1, 4096, 16, 512)
+    assert ops.ring_inplace_preferred(4096, 1, 4096, 16, 512, torch.float32)
+    assert not ops.ring_inplace_preferred(10 ** 9, 1, 4096, 16, 512)

@@ -431,10 +431,68 @@ def test_ring_share_workload(vca, n):
     check_ring_share(vca, n, torch.bfloat16)
 
 
-def check_ring_share(vca, n, dtype):
+def ring_share_gather(vca, w, t):
+    """ring_share through the packed gather layout ("gemma4_moe cp_attention"
+    page): each chunk's live tokens (documents shared by the query shard and
+    the chunk) are gathered from [1, H, S, D] views of the shard tensors, run
+    as varlen segments, merged in place at their rows into fp32 accumulators
+    that start as "attends nothing" (out 0, lse -inf), and the backward
+    gathers the merged out/lse, then scatters dq (added over the chunks),
+    dk and dv back. Results come back in the packed [S, H, D] / [H, S] layout
+    of ring_share."""
+    ids, S, H, Hkv = w.row_doc_ids(), w.shard, w.Hq, w.Hkv
+    d = {k: dev(x).unsqueeze(0).transpose(1, 2) for k, x in t.items()}  # [1, H, S, D] views
+    et = d["q"].dtype
+    loc = vca.ring_segments(ids[:, S:], ids[:, S:], device="cuda")
+    crs = vca.ring_segments(ids[:, S:], ids[:, :S], device="cuda")
+    acc = torch.empty((1, H, S, w.Dv), dtype=torch.float32, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    vca.scatter_rows(torch.empty((0, H, w.Dv), dtype=torch.float32, device="cuda"), none, acc,
+                     mode=1)
+    lacc = vca.scatter_lse(torch.empty((H, 0), dtype=torch.float32, device="cuda"), none, 1, S)
+    partial = []
+    chunks = ((loc, "k_local", "v_local", True), (crs, "k_early", "v_early", False))
+    packed = []
+    for seg, kn, vn, causal in chunks:
+        qp = vca.gather_rows(d["q"], seg["q_index"])
+        kp = vca.gather_rows(d[kn], seg["k_index"])
+        vp = vca.gather_rows(d[vn], seg["k_index"])
+        op, lp = vca.fwd_varlen(qp, kp, vp, seg["cu_q"], seg["cu_k"], seg["max_q"], seg["max_k"],
+                                w.scale, causal)
+        vca.merge_rows(acc, lacc, op, lp, seg["q_index"])
+        # the chunk alone, scattered for the per-chunk checks (0 / -inf elsewhere)
+        o_full = torch.empty((1, H, S, w.Dv), dtype=et, device="cuda")
+        vca.scatter_rows(op, seg["q_index"], o_full, mode=1)
+        l_full = vca.scatter_lse(lp, seg["q_index"], 1, S)
+        partial.append((o_full[0].transpose(0, 1), l_full[0]))
+        packed.append((seg, qp, kp, vp))
+    dq = torch.empty((1, H, S, w.Dqk), dtype=et, device="cuda")
+    grads = {}
+    for i, ((seg, qp, kp, vp), (_, kn, vn, causal)) in enumerate(zip(packed, chunks)):
+        mo_p = vca.gather_rows(acc, seg["q_index"], dtype=et)
+        ml_p = vca.gather_lse(lacc, seg["q_index"])
+        do_p = vca.gather_rows(d["do"], seg["q_index"])
+        dqp, dkp, dvp = vca.bwd_varlen(do_p, qp, kp, vp, mo_p, ml_p, seg["cu_q"], seg["cu_k"],
+                                       seg["max_q"], seg["max_k"], w.scale, causal)
+        # dq: the first chunk assigns (zeroing rows it does not hold), later ones add
+        vca.scatter_rows(dqp, seg["q_index"], dq, mode=1 if i == 0 else 2)
+        dk = torch.empty((1, Hkv, S, w.Dqk), dtype=et, device="cuda")
+        dv = torch.empty((1, Hkv, S, w.Dv), dtype=et, device="cuda")
+        vca.scatter_rows(dkp, seg["k_index"], dk, mode=1)
+        vca.scatter_rows(dvp, seg["k_index"], dv, mode=1)
+        grads[kn] = (dk[0].transpose(0, 1), dv[0].transpose(0, 1))
+    torch.cuda.synchronize()
+    mo = acc[0].transpose(0, 1)
+    return (partial[0], partial[1], (mo, lacc[0]),
+            (dq[0].transpose(0, 1), *grads["k_local"], *grads["k_early"]))
+
+
+def check_ring_share(vca, n, dtype, route="auto"):
     w = workloads.workload(n)
     t = w.tensors(dtype)
     share = ring_share_dense if w.single_doc else ring_share
+    if route == "gather":
+        share = ring_share_gather
     (o1, l1), (o2, l2), (mo, ml), (dq, dkl, dvl, dke, dve) = share(vca, w, t)
     torch.cuda.synchronize()
     ids = w.row_doc_ids()[0]
@@ -836,3 +894,70 @@ def test_fp16_merge_copy_and_zero_rows(vca):
     vca.zero_rows(out, None, r)
     torch.cuda.synchronize()
     assert torch.all(out[0, :, 1] == 0) and torch.all(out[0, :, 0] == 1)
+
+
+
+# ---------------------------------------------------------------- packed ring layout
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_ring_row_moves_and_row_merge(vca, dtype):
+    """gather_rows / scatter_rows (assign, assign with zeroed rest, add) /
+    gather_lse / scatter_lse / merge_rows on BSHD-strided [B, H, S, D] views
+    against the oracle's row moves and live-row merge."""
+    g = torch.Generator().manual_seed(75)
+    B, H, S, D = 2, 3, 37, 64
+    store = rand((B, S, H, D), g, dtype)  # BSHD storage, viewed as [B, H, S, D]
+    x = dev(store).transpose(1, 2)
+    idx_np = np.array([5, 40, 0, 73, 36, 12, 50], dtype=np.int32)
+    idx = dev(torch.from_numpy(idx_np))
+    got = vca.gather_rows(x, idx)
+    np.testing.assert_array_equal(host(got), orc.ring_gather(store.transpose(1, 2), idx_np))
+    # assign into a view holding old values: named rows replaced, others kept
+    old = rand((B, S, H, D), g, dtype)
+    dst = dev(old).transpose(1, 2)
+    vca.scatter_rows(got, idx, dst, mode=0)
+    want = orc.f64(old.transpose(1, 2)).copy()
+    named = orc.ring_scatter(orc.f64(got), idx_np, B, S, fill=np.nan)
+    keep = np.isnan(named)
+    np.testing.assert_array_equal(host(dst), np.where(keep, want, named))
+    # assign with the rest zeroed = ring_scatter
+    vca.scatter_rows(got, idx, dst, mode=1)
+    np.testing.assert_array_equal(host(dst), orc.ring_scatter(orc.f64(got), idx_np, B, S))
+    # add: named rows gain src (one rounding of the fp32 sum)
+    base = dev(rand((B, S, H, D), g, dtype)).transpose(1, 2)
+    ref = host(base) + orc.ring_scatter(orc.f64(got), idx_np, B, S)
+    vca.scatter_rows(got, idx, base, mode=2)
+    torch.cuda.synchronize()
+    tol = 0 if dtype == torch.float32 else 2 ** -7 * np.abs(ref).max()
+    assert np.abs(host(base) - ref).max() <= tol + 1e-6
+    # lse moves
+    lse = dev(torch.randn((B, H, S), generator=g))
+    lp = vca.gather_lse(lse, idx)
+    np.testing.assert_array_equal(host(lp), orc.ring_gather(host(lse)[..., None], idx_np)[..., 0].T)
+    ld = vca.scatter_lse(lp, idx, B, S)
+    np.testing.assert_array_equal(
+        host(ld), orc.ring_scatter(host(lp).T[:, :, None], idx_np, B, S, fill=-np.inf)[..., 0])
+    # live-row merge into fp32 accumulators (one live row starts at -inf)
+    acc = dev(torch.randn((B, S, H, D), generator=g)).transpose(1, 2)
+    lacc = dev(torch.randn((B, H, S), generator=g))
+    lacc[0, 1, 5] = -math.inf
+    ob = dev(rand((len(idx_np), H, D), g, dtype))
+    lb = dev(torch.randn((H, len(idx_np)), generator=g))
+    lb[2, 3] = -math.inf
+    ro, rl = orc.ring_merge_rows(host(acc), host(lacc), host(ob), host(lb), idx_np)
+    vca.merge_rows(acc, lacc, ob, lb, idx)
+    torch.cuda.synchronize()
+    assert np.abs(host(acc) - ro).max() < 1e-5
+    check_lse(lacc, rl)
+    # fp32 rows gathered into a 16-bit type round to nearest even
+    if dtype != torch.float32:
+        acc2 = dev(torch.randn((B, S, H, D), generator=g)).transpose(1, 2)
+        r16 = vca.gather_rows(acc2, idx, dtype=dtype)
+        assert torch.equal(r16, vca.gather_rows(acc2, idx).to(dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_ring_share_gather_layout(vca, dtype):
+    """The ring share at full size through the packed gather layout: partial
+    chunk results, the in-place merge and both chunk backwards against the
+    document-causal oracle (every kv-head group sampled)."""
+    check_ring_share(vca, 5, dtype, route="gather")

@@ -369,3 +369,40 @@ def test_doc_causal_gqa_equals_mha_on_repeated_kv():
     gv = orc.bwd_varlen(do, q, k, v, o, l, cu_q, cu_k, 0.7, True)
     for a, b in zip(gv, (dq, dk, dv)):
         np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_ring_gather_scatter_and_row_merge():
+    """The packed ring layout's row moves and live-row merge ("gemma4_moe
+    cp_attention" page): gather then scatter restores the named rows and
+    fills the rest; merging one chunk at its rows equals the full merge of
+    the dense accumulators with a chunk that is -inf (absent) elsewhere."""
+    rng = np.random.default_rng(14)
+    B, H, S, D = 2, 3, 5, 4
+    x = rng.standard_normal((B, H, S, D))
+    idx = np.array([7, 0, 3, 9, 5])  # b*S + s, in any order
+    g = orc.ring_gather(x, idx)
+    assert g.shape == (5, H, D)
+    for t, f in enumerate(idx):
+        np.testing.assert_array_equal(g[t], x[f // S, :, f % S])
+    back = orc.ring_scatter(g, idx, B, S)
+    for f in range(B * S):
+        want = x[f // S, :, f % S] if f in idx else 0.0
+        np.testing.assert_array_equal(back[f // S, :, f % S], want)
+    acc = rng.standard_normal((B, H, S, D))
+    lacc = rng.standard_normal((B, H, S))
+    lacc[0, 1, 3] = -np.inf  # a live row nothing covered yet (flat 3)
+    ob = rng.standard_normal((5, H, D))
+    lb = rng.standard_normal((H, 5))
+    lb[2, 1] = -np.inf
+    mo, ml = orc.ring_merge_rows(acc, lacc, ob, lb, idx)
+    dense_b = orc.ring_scatter(ob, idx, B, S)
+    dense_lb = orc.ring_scatter(lb.T[:, :, None], idx, B, S, fill=-np.inf)[..., 0]
+    flat = lambda a: a.transpose(0, 2, 1, 3).reshape(B * S, H, D)  # noqa: E731
+    fo, fl = orc.merge(flat(acc), lacc.transpose(0, 2, 1).reshape(B * S, H).T, flat(dense_b),
+                       dense_lb.transpose(0, 2, 1).reshape(B * S, H).T)
+    np.testing.assert_allclose(flat(mo), fo, atol=1e-13)
+    np.testing.assert_allclose(ml.transpose(0, 2, 1).reshape(B * S, H).T, fl, atol=1e-13)
+    # rows no index names are untouched
+    untouched = [f for f in range(B * S) if f not in idx]
+    for f in untouched:
+        np.testing.assert_array_equal(mo[f // S, :, f % S], acc[f // S, :, f % S])

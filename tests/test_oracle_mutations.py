@@ -26,6 +26,8 @@ MUTATIONS = {
     "doc_fwd_gqa_modulo": ("o, l = attend(q[:, h], k[:, h // G], v[:, h // G], vis, scale)", "o, l = attend(q[:, h], k[:, h % k.shape[1]], v[:, h % k.shape[1]], vis, scale)"),
     "doc_bwd_gqa_modulo": ("a, b, c = attend_backward(do[:, h], q[:, h], k[:, h // G], v[:, h // G], o[:, h],", "a, b, c = attend_backward(do[:, h], q[:, h], k[:, h % k.shape[1]], v[:, h % k.shape[1]], o[:, h],"),
     "doc_bwd_group_sum": ("        dk[:, h // G] += b\n", "        dk[:, h % k.shape[1]] += b\n"),
+    "ring_gather_wrong_axes": ("return x.transpose(0, 2, 1, 3).reshape(B * S, H, D)[idx]", "return x.transpose(0, 1, 2, 3).reshape(B * S, H, D)[idx]"),
+    "ring_merge_rows_keeps_old_out": ("    flat_o[idx] = mo\n", "    flat_o[idx] = flat_o[idx]\n"),
     "doc_future_keys": ("(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None])", "(np.asarray(k_pos)[None, :] >= 0)"),
 }
 

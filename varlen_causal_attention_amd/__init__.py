@@ -7,12 +7,14 @@ this package only marshals torch tensors into its C ABI.
 """
 from ._lib import EXPORTED, LIB_PATH, AttnError, load
 from .ops import (bwd_dense, bwd_varlen, dense_route, doc_cu_seqlens, doc_layout, doc_segments,
-                  fwd_dense, fwd_varlen, fwd_varlen_noalloc, is_supported, merge, timing_enable,
-                  timing_read, version, zero_rows)
+                  fwd_dense, fwd_varlen, fwd_varlen_noalloc, gather_lse, gather_rows,
+                  is_supported, merge, merge_rows, ring_inplace_preferred, ring_segments,
+                  scatter_lse, scatter_rows, timing_enable, timing_read, version, zero_rows)
 
 __all__ = [
     "AttnError", "EXPORTED", "LIB_PATH", "load", "fwd_dense", "fwd_varlen", "fwd_varlen_noalloc",
     "bwd_dense", "bwd_varlen", "merge", "doc_segments", "doc_cu_seqlens", "doc_layout",
-    "dense_route", "zero_rows",
+    "dense_route", "zero_rows", "ring_segments", "ring_inplace_preferred", "gather_rows",
+    "scatter_rows", "gather_lse", "scatter_lse", "merge_rows",
     "is_supported", "version", "timing_enable", "timing_read",
 ]

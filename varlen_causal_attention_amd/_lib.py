@@ -20,6 +20,9 @@ ATTN_BF16 = 0
 ATTN_F32 = 1
 ATTN_F16 = 2
 ATTN_DQ_ACCUMULATE = 1
+ATTN_ROWS_ASSIGN = 0
+ATTN_ROWS_ASSIGN_ZERO_REST = 1
+ATTN_ROWS_ADD = 2
 ATTN_NOALLOC_MAX_ITEMS = 524256  # work-list entries the no-allocation forward's static scratch holds
 
 EXPORTED = (
@@ -27,7 +30,9 @@ EXPORTED = (
     "attn_fwd_varlen_noalloc",
     "attn_bwd_dense", "attn_bwd_varlen", "attn_merge", "attn_doc_segments", "attn_doc_cu_seqlens",
     "attn_dense_route",
-    "attn_zero_rows", "attn_timing_enable", "attn_timing_read",
+    "attn_zero_rows", "attn_timing_enable", "attn_timing_read", "attn_ring_segments",
+    "attn_ring_inplace_preferred", "attn_gather_rows", "attn_scatter_rows", "attn_gather_lse",
+    "attn_scatter_lse", "attn_merge_rows",
 )
 
 _P = C.c_void_p
@@ -59,6 +64,18 @@ _SIGS = {
     "attn_dense_route": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _P, C.POINTER(C.c_int)]),
     "attn_zero_rows": (_I, [_P, _I, C.c_int64, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int64, _P,
                             _I, _I, _I, _I, _P]),
+    "attn_ring_segments": (_I, [_I32P, _I, _I32P, _I, _I, _I32P, _I32P, _I32P, _I32P, _I,
+                                C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int),
+                                C.POINTER(C.c_int), C.POINTER(C.c_int)]),
+    "attn_ring_inplace_preferred": (_I, [C.c_int64, C.c_int64, C.c_int64, _I, _I, _I]),
+    "attn_gather_rows": (_I, [_I, _P, C.c_int64, C.c_int64, C.c_int64, _P, _I, _I, _I, _I, _I, _P,
+                              _I, _P]),
+    "attn_scatter_rows": (_I, [_I, _P, _P, _I, _I, _I, _P, C.c_int64, C.c_int64, C.c_int64, _I,
+                               _I, _I, _P]),
+    "attn_gather_lse": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
+    "attn_scatter_lse": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _P]),
+    "attn_merge_rows": (_I, [_P, C.c_int64, C.c_int64, C.c_int64, _P, _I, _I, _P, _I, _P, _P, _I,
+                             _I, _I, _P]),
     "attn_timing_enable": (_I, [_I]),
     "attn_timing_read": (_I, [_I, C.c_char_p, _I, C.POINTER(C.c_float), C.POINTER(C.c_int)]),
 }

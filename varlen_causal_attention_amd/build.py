@@ -23,7 +23,7 @@ ARCH = "gfx950"
 # Kernel units are compiled once per element type: bf16 (namespace vca::bf)
 # and fp16 (VCA_ELEM_F16, namespace vca::hf).
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_tiles.hip", "attn_bwd_roles.hip"]
-HIP_SOURCES = ["attn_merge.hip", "attn_api.hip", "attn_timing.hip"]
+HIP_SOURCES = ["attn_merge.hip", "attn_ring.hip", "attn_api.hip", "attn_timing.hip"]
 CXX_SOURCES = ["attn_segments.cpp"]
 # -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in VGPRs. The kernels keep
 # their working set under the unified register budget; left to choose, the

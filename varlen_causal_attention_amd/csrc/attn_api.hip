@@ -469,3 +469,178 @@ int attn_zero_rows(void* out, int dtype, int64_t ob, int64_t oh, int64_t on, flo
 }
 
 }  // extern "C"
+
+// ---- packed ring layout: row movement and the in-place live-row merge ----
+namespace {
+
+int ring_esz(int dtype) {
+  return dtype == ATTN_F32 ? 4 : (dtype == ATTN_BF16 || dtype == ATTN_F16) ? 2 : 0;
+}
+
+// Checks of a [B, H, S, D] view moved in 16-byte pieces.
+int check_rows_view(const char* name, const void* p, int64_t sb, int64_t sh, int64_t sn, int esz,
+                    int D) {
+  if (!p) return fail(ATTN_E_INVALID, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(ATTN_E_INVALID, std::string(name) + " is not 16-byte aligned");
+  const int64_t per = 16 / esz;
+  if (sb < 0 || sh < 0 || sn < 0 || sb % per || sh % per || sn % per)
+    return fail(ATTN_E_INVALID, std::string(name) + " strides must be non-negative multiples of " +
+                                    std::to_string(per));
+  if ((int64_t)D * esz % 16) return fail(ATTN_E_INVALID, "D * element size must be a multiple of 16");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_gather_rows(int dtype, const void* src, int64_t sb, int64_t sh, int64_t sn,
+                     const int32_t* index, int B, int H, int S, int D, int T, void* dst,
+                     int dst_dtype, hipStream_t stream) {
+  g_last_error.clear();
+  const int esz = ring_esz(dtype);
+  if (!esz) return fail(ATTN_E_UNSUPPORTED, "dtype must be ATTN_BF16, ATTN_F16 or ATTN_F32");
+  const bool convert = dst_dtype != dtype;
+  if (convert && !(dtype == ATTN_F32 && (dst_dtype == ATTN_BF16 || dst_dtype == ATTN_F16)))
+    return fail(ATTN_E_UNSUPPORTED, "gather converts only fp32 rows to ATTN_BF16 / ATTN_F16");
+  if (convert && D % 8) return fail(ATTN_E_INVALID, "converting gather needs D % 8 == 0");
+  if (B < 0 || H <= 0 || S < 0 || D <= 0 || T < 0 || (int64_t)T > (int64_t)B * S)
+    return fail(ATTN_E_INVALID, "sizes: B, S, T >= 0, H, D > 0, T <= B * S");
+  if (T == 0) return ok();
+  int st;
+  if ((st = check_rows_view("src", src, sb, sh, sn, esz, D))) return st;
+  if (!index || !dst || !aligned16(dst)) return fail(ATTN_E_INVALID, "index / dst NULL or dst unaligned");
+  vca::RingRowsArgs a{};
+  a.dense = const_cast<void*>(src);
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.packed = dst;
+  a.index = index;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.T = T;
+  a.D = D;
+  a.type = dtype;
+  a.esz = esz;
+  a.dst_type = dst_dtype;
+  a.mode = convert ? 3 : 0;
+  return hip_status(vca::launch_ring_rows(a, vca::kRingRows, stream), "attn_gather_rows launch");
+}
+
+int attn_scatter_rows(int dtype, const void* src, const int32_t* index, int T, int H, int D,
+                      void* dst, int64_t sb, int64_t sh, int64_t sn, int B, int S, int mode,
+                      hipStream_t stream) {
+  g_last_error.clear();
+  const int esz = ring_esz(dtype);
+  if (!esz) return fail(ATTN_E_UNSUPPORTED, "dtype must be ATTN_BF16, ATTN_F16 or ATTN_F32");
+  if (mode != ATTN_ROWS_ASSIGN && mode != ATTN_ROWS_ASSIGN_ZERO_REST && mode != ATTN_ROWS_ADD)
+    return fail(ATTN_E_INVALID, "unknown scatter mode");
+  if (B < 0 || H <= 0 || S < 0 || D <= 0 || T < 0 || (int64_t)T > (int64_t)B * S)
+    return fail(ATTN_E_INVALID, "sizes: B, S, T >= 0, H, D > 0, T <= B * S");
+  if ((int64_t)B * S == 0) return ok();
+  int st;
+  if ((st = check_rows_view("dst", dst, sb, sh, sn, esz, D))) return st;
+  if (T > 0 && (!index || !src || !aligned16(src)))
+    return fail(ATTN_E_INVALID, "index / src NULL or src unaligned");
+  vca::RingRowsArgs a{};
+  a.dense = dst;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.packed = const_cast<void*>(src);
+  a.index = index;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.T = T;
+  a.D = D;
+  a.type = dtype;
+  a.esz = esz;
+  if (mode == ATTN_ROWS_ASSIGN_ZERO_REST &&
+      (st = hip_status(vca::launch_ring_rows(a, vca::kRingFill, stream), "attn_scatter_rows fill")))
+    return st;
+  a.mode = mode == ATTN_ROWS_ADD ? 2 : 1;
+  return hip_status(vca::launch_ring_rows(a, vca::kRingRows, stream), "attn_scatter_rows launch");
+}
+
+int attn_gather_lse(const float* lse_dense, const int32_t* index, int B, int H, int S, int T,
+                    float* lse_packed, hipStream_t stream) {
+  g_last_error.clear();
+  if (B < 0 || H <= 0 || S < 0 || T < 0 || (int64_t)T > (int64_t)B * S)
+    return fail(ATTN_E_INVALID, "sizes: B, S, T >= 0, H > 0, T <= B * S");
+  if (T == 0) return ok();
+  if (!lse_dense || !index || !lse_packed) return fail(ATTN_E_INVALID, "pointer is NULL");
+  vca::RingRowsArgs a{};
+  a.lse_dense = const_cast<float*>(lse_dense);
+  a.lse_packed = lse_packed;
+  a.index = index;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.T = T;
+  a.mode = 0;
+  return hip_status(vca::launch_ring_rows(a, vca::kRingLse, stream), "attn_gather_lse launch");
+}
+
+int attn_scatter_lse(const float* lse_packed, const int32_t* index, int T, int H, float* lse_dense,
+                     int B, int S, int fill_rest, hipStream_t stream) {
+  g_last_error.clear();
+  if (B < 0 || H <= 0 || S < 0 || T < 0 || (int64_t)T > (int64_t)B * S)
+    return fail(ATTN_E_INVALID, "sizes: B, S, T >= 0, H > 0, T <= B * S");
+  if ((int64_t)B * S == 0) return ok();
+  if (!lse_dense || (T > 0 && (!index || !lse_packed)))
+    return fail(ATTN_E_INVALID, "pointer is NULL");
+  vca::RingRowsArgs a{};
+  a.lse_dense = lse_dense;
+  a.lse_packed = const_cast<float*>(lse_packed);
+  a.index = index;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.T = T;
+  a.D = 0;
+  a.esz = 4;
+  int st;
+  if (fill_rest &&
+      (st = hip_status(vca::launch_ring_rows(a, vca::kRingFill, stream), "attn_scatter_lse fill")))
+    return st;
+  a.mode = 1;
+  return hip_status(vca::launch_ring_rows(a, vca::kRingLse, stream), "attn_scatter_lse launch");
+}
+
+int attn_merge_rows(float* out_acc, int64_t sb, int64_t sh, int64_t sn, float* lse_acc, int B,
+                    int S, const void* out_b, int dtype_b, const float* lse_b,
+                    const int32_t* index, int T, int H, int D, hipStream_t stream) {
+  g_last_error.clear();
+  const int esz = ring_esz(dtype_b);
+  if (!esz) return fail(ATTN_E_UNSUPPORTED, "dtype_b must be ATTN_BF16, ATTN_F16 or ATTN_F32");
+  if (B < 0 || H <= 0 || S < 0 || D <= 0 || T < 0 || (int64_t)T > (int64_t)B * S)
+    return fail(ATTN_E_INVALID, "sizes: B, S, T >= 0, H, D > 0, T <= B * S");
+  if (T == 0) return ok();
+  if (!out_acc || !lse_acc || !out_b || !lse_b || !index)
+    return fail(ATTN_E_INVALID, "merge_rows pointer is NULL");
+  if (sb < 0 || sh < 0 || sn < 0) return fail(ATTN_E_INVALID, "strides must be non-negative");
+  vca::RingRowsArgs a{};
+  a.dense = out_acc;
+  a.sb = sb;
+  a.sh = sh;
+  a.sn = sn;
+  a.packed = const_cast<void*>(out_b);
+  a.lse_dense = lse_acc;
+  a.lse_packed = const_cast<float*>(lse_b);
+  a.index = index;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.T = T;
+  a.D = D;
+  a.type = dtype_b;
+  a.esz = esz;
+  return hip_status(vca::launch_ring_rows(a, vca::kRingMerge, stream), "attn_merge_rows launch");
+}
+
+}  // extern "C"
+
+

@@ -191,4 +191,21 @@ struct ZeroRowsArgs {
 };
 hipError_t launch_zero_rows(const ZeroRowsArgs& a, hipStream_t stream);
 
+// Row movement and merges of the packed ring layout (attn_ring.hip).
+struct RingRowsArgs {
+  void* dense;           // [B, H, S, D] view, element strides sb, sh, sn (innermost 1)
+  int64_t sb, sh, sn;
+  void* packed;          // [T, H, D] contiguous
+  const int32_t* index;  // [T] flat rows b*S + s
+  float* lse_dense;      // [B, H, S] contiguous (or NULL)
+  float* lse_packed;     // [H, T] contiguous
+  int B, H, S, T, D;
+  int type, esz;         // dtype code and its byte size
+  int dst_type;          // mode 3: the 16-bit type fp32 rows are gathered into
+  int mode;              // rows: 0 gather, 1 scatter, 2 scatter-add, 3 gather fp32 -> 16-bit;
+                         // lse: 0 gather, 1 scatter
+};
+enum { kRingRows = 0, kRingFill = 1, kRingLse = 2, kRingMerge = 3 };
+hipError_t launch_ring_rows(const RingRowsArgs& a, int op, hipStream_t stream);
+
 }  // namespace vca

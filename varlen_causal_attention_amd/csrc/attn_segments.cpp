@@ -232,3 +232,87 @@ extern "C" int attn_dense_route(const int32_t* doc_ids, int B, int S, int q_star
         pad_rows[(size_t)b * q_len + i] = doc_ids[(size_t)b * S + q_start + i] == 0 ? 1 : 0;
   return ATTN_OK;
 }
+
+// Packed ring segments with gather indices ("gemma4_moe cp_attention" page:
+// the per-document varlen segments shared between a query shard and one KV
+// chunk, returned as flat gather indices into B*S plus cu_seqlens). Every
+// document id > 0 that occurs in both row b of the query shard and row b of
+// the key chunk becomes one segment: its query positions (in order) and its
+// key positions (in order), as flat indices b*Sq + p and b*Sk + p. Segments
+// follow the rows, and within a row the order in which documents first occur
+// among the queries. Documents in only one of the two, and padding, take no
+// part, so only live tokens are gathered.
+extern "C" int attn_ring_segments(const int32_t* q_ids, int Sq, const int32_t* k_ids, int Sk,
+                                  int B, int32_t* q_index, int32_t* k_index, int32_t* cu_q,
+                                  int32_t* cu_k, int max_segments, int* num_segments, int* Tq,
+                                  int* Tk, int* max_q, int* max_k) {
+  vca::set_last_error("");
+  if (!q_ids || !k_ids || !num_segments || !Tq || !Tk || !max_q || !max_k || B < 0 || Sq < 0 ||
+      Sk < 0 || (int64_t)B * Sq > INT32_MAX || (int64_t)B * Sk > INT32_MAX) {
+    vca::set_last_error("attn_ring_segments: invalid arguments");
+    return ATTN_E_INVALID;
+  }
+  std::vector<int32_t> qi, ki, cq{0}, ck{0};
+  int mq = 0, mk = 0;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* qr = q_ids + (size_t)b * Sq;
+    const int32_t* kr = k_ids + (size_t)b * Sk;
+    std::vector<int32_t> order;  // documents in order of first occurrence among the queries
+    for (int p = 0; p < Sq; ++p) {
+      const int32_t d = qr[p];
+      if (d <= 0) continue;
+      bool seen = false;
+      for (int32_t e : order) seen = seen || e == d;
+      if (!seen) order.push_back(d);
+    }
+    for (int32_t d : order) {
+      const size_t k0 = ki.size(), q0 = qi.size();
+      for (int p = 0; p < Sk; ++p)
+        if (kr[p] == d) ki.push_back((int32_t)((int64_t)b * Sk + p));
+      if (ki.size() == k0) continue;  // not in the key chunk: no segment
+      for (int p = 0; p < Sq; ++p)
+        if (qr[p] == d) qi.push_back((int32_t)((int64_t)b * Sq + p));
+      const int lq = (int)(qi.size() - q0), lk = (int)(ki.size() - k0);
+      cq.push_back((int32_t)qi.size());
+      ck.push_back((int32_t)ki.size());
+      mq = lq > mq ? lq : mq;
+      mk = lk > mk ? lk : mk;
+    }
+  }
+  const int n = (int)cq.size() - 1;
+  *num_segments = n;
+  *Tq = (int)qi.size();
+  *Tk = (int)ki.size();
+  *max_q = mq;
+  *max_k = mk;
+  if (n > max_segments || (n > 0 && (!q_index || !k_index || !cu_q || !cu_k))) {
+    vca::set_last_error("attn_ring_segments: max_segments too small, " + std::to_string(n) +
+                        " needed");
+    return ATTN_E_INVALID;
+  }
+  for (size_t i = 0; i < qi.size(); ++i) q_index[i] = qi[i];
+  for (size_t i = 0; i < ki.size(); ++i) k_index[i] = ki[i];
+  for (int i = 0; i <= n && cu_q && cu_k; ++i) {
+    cu_q[i] = cq[i];
+    cu_k[i] = ck[i];
+  }
+  return ATTN_OK;
+}
+
+// In-place merge of a chunk's live rows versus scatter + dense merge ("gemma4_moe
+// cp_attention" page: true when the live-token subset is small enough for
+// in-place updates to beat scatter). The pages give no threshold; this compares
+// the HBM bytes of the two routes with this library's kernels:
+//   in place: per live row, read the fp32 accumulator row and lse, the chunk's
+//             row and lse, write the accumulator row and lse, read its index;
+//   scatter:  fill the [B, H, S, D] chunk tensor and its lse, write the live
+//             rows into it, then merge every one of the B*S rows densely.
+extern "C" int attn_ring_inplace_preferred(int64_t live_rows, int64_t B, int64_t S, int H, int D,
+                                           int dtype) {
+  if (live_rows < 0 || B < 0 || S < 0 || H <= 0 || D <= 0) return 0;
+  const int64_t es = dtype == ATTN_F32 ? 4 : 2;  // chunk output element bytes
+  const int64_t row_in_place = (int64_t)H * (D * (4 + es + 4) + 4 * 3) + 4;
+  const int64_t row_dense = (int64_t)H * (D * (4 + es + 4) + 4 * 3);
+  const int64_t scatter = B * S * (int64_t)H * (D * es + 4) + live_rows * (int64_t)H * (D * 2 * es + 8);
+  return live_rows * row_in_place < scatter + B * S * row_dense ? 1 : 0;
+}

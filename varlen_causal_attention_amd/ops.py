@@ -412,3 +412,144 @@ def timing_read(max_records: int = 4096):
         label = raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
         out.append((label, float(ms[i])))
     return out
+
+
+# ---------------------------------------------------------------------------
+# packed ring layout: gather indices, row moves, live-row merge
+# ---------------------------------------------------------------------------
+_ROW_TYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16, torch.float32: ATTN_F32}
+
+
+def ring_segments(q_ids, k_ids, device=None):
+    """The per-document segments a query shard ([B, Sq] ids) shares with one
+    KV chunk ([B, Sk] ids), as gather indices into B*Sq / B*Sk plus
+    cu_seqlens; None when no document is shared. With `device`, the index and
+    cu arrays come back as int32 tensors there, else as numpy arrays."""
+    qi = np.ascontiguousarray(np.asarray(q_ids, dtype=np.int32))
+    ki = np.ascontiguousarray(np.asarray(k_ids, dtype=np.int32))
+    if qi.ndim != 2 or ki.ndim != 2 or qi.shape[0] != ki.shape[0]:
+        raise ValueError("q_ids [B, Sq] and k_ids [B, Sk] with the same B")
+    B, Sq = qi.shape
+    Sk = ki.shape[1]
+    cap = B * min(Sq, Sk) + 1
+    q_index = np.zeros(max(B * Sq, 1), dtype=np.int32)
+    k_index = np.zeros(max(B * Sk, 1), dtype=np.int32)
+    cu_q = np.zeros(cap + 1, dtype=np.int32)
+    cu_k = np.zeros(cap + 1, dtype=np.int32)
+    n, tq, tk, mq, mk = (C.c_int(0) for _ in range(5))
+    p32 = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
+    check(load().attn_ring_segments(p32(qi), Sq, p32(ki), Sk, B, p32(q_index), p32(k_index),
+                                    p32(cu_q), p32(cu_k), cap, C.byref(n), C.byref(tq),
+                                    C.byref(tk), C.byref(mq), C.byref(mk)), "attn_ring_segments")
+    if n.value == 0:
+        return None
+    seg = dict(q_index=q_index[:tq.value].copy(), k_index=k_index[:tk.value].copy(),
+               cu_q=cu_q[:n.value + 1].copy(), cu_k=cu_k[:n.value + 1].copy(),
+               max_q=mq.value, max_k=mk.value)
+    if device is not None:
+        for key in ("q_index", "k_index", "cu_q", "cu_k"):
+            seg[key] = torch.from_numpy(seg[key]).to(device)
+    return seg
+
+
+def ring_inplace_preferred(live_rows: int, B: int, S: int, H: int, D: int,
+                           dtype=torch.bfloat16) -> bool:
+    """Whether merging a chunk's live rows in place beats scattering them."""
+    return bool(load().attn_ring_inplace_preferred(int(live_rows), int(B), int(S), int(H), int(D),
+                                                   _ROW_TYPES[dtype]))
+
+
+def _index(index, dev):
+    if index.dtype != torch.int32 or index.device != dev or index.dim() != 1 or \
+            not index.is_contiguous():
+        raise ValueError("index must be contiguous int32 [T] on the device")
+    return C.c_void_p(index.data_ptr()) if index.numel() else C.c_void_p(0)
+
+
+def _dense4(x, name):
+    if x.dim() != 4 or x.dtype not in _ROW_TYPES or x.device.type != "cuda" or \
+            (x.numel() and x.stride(3) != 1):
+        raise ValueError(f"{name} must be a [B, H, S, D] GPU view with unit last stride")
+    return x
+
+
+def gather_rows(src, index, dtype=None):
+    """[B, H, S, D] view -> packed [T, H, D] rows at flat indices b*S + s
+    (dtype: the packed type; fp32 rows may be rounded to bf16 / fp16)."""
+    _dense4(src, "src")
+    B, H, S, D = src.shape
+    dt = src.dtype if dtype is None else dtype
+    out = torch.empty((index.numel(), H, D), dtype=dt, device=src.device)
+    check(load().attn_gather_rows(_ROW_TYPES[src.dtype], _ptr(src), src.stride(0), src.stride(1),
+                                  src.stride(2), _index(index, src.device), B, H, S, D,
+                                  index.numel(), _ptr(out), _ROW_TYPES[dt], _stream(src)),
+          "attn_gather_rows")
+    return out
+
+
+def scatter_rows(src, index, dst, mode=0):
+    """In place: dst [B, H, S, D] rows at the flat indices receive the packed
+    rows src [T, H, D] (mode 0), or every other row is zeroed too (mode 1), or
+    src is added to them (mode 2, the gradient scatter-add)."""
+    _dense4(dst, "dst")
+    B, H, S, D = dst.shape
+    if src.dtype != dst.dtype or tuple(src.shape) != (index.numel(), H, D) or \
+            not src.is_contiguous() or src.device != dst.device:
+        raise ValueError("src must be contiguous [T, H, D] of dst's dtype and device")
+    check(load().attn_scatter_rows(_ROW_TYPES[dst.dtype], _ptr(src), _index(index, dst.device),
+                                   index.numel(), H, D, _ptr(dst), dst.stride(0), dst.stride(1),
+                                   dst.stride(2), B, S, int(mode), _stream(dst)),
+          "attn_scatter_rows")
+    return dst
+
+
+def gather_lse(lse, index):
+    """Dense [B, H, S] -> packed [H, T] at the flat indices."""
+    if lse.dtype != torch.float32 or lse.dim() != 3 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, S]")
+    B, H, S = lse.shape
+    out = torch.empty((H, index.numel()), dtype=torch.float32, device=lse.device)
+    check(load().attn_gather_lse(_ptr(lse), _index(index, lse.device), B, H, S, index.numel(),
+                                 _ptr(out), _stream(lse)), "attn_gather_lse")
+    return out
+
+
+def scatter_lse(lse_pack, index, B: int, S: int, out=None):
+    """Packed [H, T] -> dense [B, H, S], -inf on rows no index names (or, with
+    out given, written into out in place with the other rows kept)."""
+    H, T = lse_pack.shape
+    if lse_pack.dtype != torch.float32 or not lse_pack.is_contiguous() or T != index.numel():
+        raise ValueError("lse_pack must be contiguous fp32 [H, T]")
+    fill = out is None
+    if out is None:
+        out = torch.empty((B, H, S), dtype=torch.float32, device=lse_pack.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H, S) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [B, H, S]")
+    check(load().attn_scatter_lse(_ptr(lse_pack), _index(index, lse_pack.device), T, H, _ptr(out),
+                                  B, S, int(fill), _stream(lse_pack)), "attn_scatter_lse")
+    return out
+
+
+def merge_rows(out_acc, lse_acc, out_b, lse_b, index):
+    """In place: merge one chunk's packed rows (out_b [T, H, D], lse_b [H, T])
+    into the running fp32 accumulators out_acc [B, H, S, D] / lse_acc
+    [B, H, S] at its flat-index rows only."""
+    _dense4(out_acc, "out_acc")
+    B, H, S, D = out_acc.shape
+    if out_acc.dtype != torch.float32:
+        raise ValueError("out_acc must be fp32")
+    if lse_acc.dtype != torch.float32 or tuple(lse_acc.shape) != (B, H, S) or \
+            not lse_acc.is_contiguous():
+        raise ValueError("lse_acc must be contiguous fp32 [B, H, S]")
+    T = index.numel()
+    if tuple(out_b.shape) != (T, H, D) or not out_b.is_contiguous() or \
+            out_b.dtype not in _ROW_TYPES:
+        raise ValueError("out_b must be contiguous [T, H, D]")
+    if lse_b.dtype != torch.float32 or tuple(lse_b.shape) != (H, T) or not lse_b.is_contiguous():
+        raise ValueError("lse_b must be contiguous fp32 [H, T]")
+    check(load().attn_merge_rows(_ptr(out_acc), out_acc.stride(0), out_acc.stride(1),
+                                 out_acc.stride(2), _ptr(lse_acc), B, S, _ptr(out_b),
+                                 _ROW_TYPES[out_b.dtype], _ptr(lse_b),
+                                 _index(index, out_acc.device), T, H, D, _stream(out_acc)),
+          "attn_merge_rows")
+    return out_acc, lse_acc

@@ -59,17 +59,67 @@ class Problem:
             # the dense kernels run on [1, H, S, D] views of the shard tensors
             ok_l, pad = vca.dense_route(ids, S, S, S, S, 0)
             ok_x, _ = vca.dense_route(ids, S, S, 0, S, 1)
-            self.dense = ok_l and ok_x
-            if self.dense:
+            self.dense = ok_l and ok_x and w.route != "gather"
+            self.gather = w.route == "gather"
+            if self.gather:
+                # packed live tokens: gather indices of the documents each chunk shares
+                self.d = {k: x.unsqueeze(0).transpose(1, 2) for k, x in self.t.items()}
+                self.segs = (vca.ring_segments(ids[:, S:], ids[:, S:], device="cuda"),
+                             vca.ring_segments(ids[:, S:], ids[:, :S], device="cuda"))
+            elif self.dense:
                 self.pad = torch.from_numpy(pad).to("cuda")
                 self.d = {k: x.unsqueeze(0).transpose(1, 2) for k, x in self.t.items()}
             else:
                 self.local = vca.doc_layout(ids, S, S, S, S, 0, "cuda")
                 self.cross = vca.doc_layout(ids, S, S, 0, S, 1, "cuda")
         self.out = self.lse = None
+        self.gather = getattr(self, "gather", False)
+
+    def fwd_gather(self):
+        """Ring share through the gather layout: per chunk gather its live
+        tokens, varlen forward, merge in place at its rows into fp32
+        accumulators that start as 'attends nothing'."""
+        v, w, d, S, H = self.vca, self.w, self.d, self.w.shard, self.w.Hq
+        none = torch.empty(0, dtype=torch.int32, device="cuda")
+        acc = torch.empty((1, H, S, w.Dv), dtype=torch.float32, device="cuda")
+        v.scatter_rows(torch.empty((0, H, w.Dv), dtype=torch.float32, device="cuda"), none, acc,
+                       mode=1)
+        lacc = v.scatter_lse(torch.empty((H, 0), dtype=torch.float32, device="cuda"), none, 1, S)
+        self.packed = []
+        for seg, kn, vn, causal in zip(self.segs, ("k_local", "k_early"), ("v_local", "v_early"),
+                                       (True, False)):
+            qp = v.gather_rows(d["q"], seg["q_index"])
+            kp = v.gather_rows(d[kn], seg["k_index"])
+            vp = v.gather_rows(d[vn], seg["k_index"])
+            op, lp = v.fwd_varlen(qp, kp, vp, seg["cu_q"], seg["cu_k"], seg["max_q"],
+                                  seg["max_k"], w.scale, causal)
+            v.merge_rows(acc, lacc, op, lp, seg["q_index"])
+            self.packed.append((seg, qp, kp, vp, causal))
+        self.out, self.lse = acc, lacc
+
+    def bwd_gather(self):
+        """Per chunk: gather the merged out/lse and dO at its rows, varlen
+        backward, scatter dq (assigned by the first chunk, added by the next)
+        and the chunk's dk / dv back to [1, H, S, D]."""
+        v, w, d, S = self.vca, self.w, self.d, self.w.shard
+        dq = torch.empty((1, w.Hq, S, w.Dqk), dtype=self.dtype, device="cuda")
+        res = [dq]
+        for i, (seg, qp, kp, vp, causal) in enumerate(self.packed):
+            mo = v.gather_rows(self.out, seg["q_index"], dtype=self.dtype)
+            ml = v.gather_lse(self.lse, seg["q_index"])
+            dop = v.gather_rows(d["do"], seg["q_index"])
+            dqp, dkp, dvp = v.bwd_varlen(dop, qp, kp, vp, mo, ml, seg["cu_q"], seg["cu_k"],
+                                         seg["max_q"], seg["max_k"], w.scale, causal)
+            v.scatter_rows(dqp, seg["q_index"], dq, mode=1 if i == 0 else 2)
+            for src, D in ((dkp, w.Dqk), (dvp, w.Dv)):
+                g = torch.empty((1, w.Hkv, S, D), dtype=self.dtype, device="cuda")
+                res.append(v.scatter_rows(src, seg["k_index"], g, mode=1))
+        return tuple(res)
 
     def fwd(self):
         v, w, t = self.vca, self.w, self.t
+        if w.kind == "ring" and self.gather:
+            return self.fwd_gather()
         if w.kind == "dense":
             self.out, self.lse = v.fwd_dense(t["q"], t["k"], t["v"], w.scale, w.causal)
         elif w.kind == "varlen":
@@ -104,6 +154,8 @@ class Problem:
 
     def bwd(self):
         v, w, t = self.vca, self.w, self.t
+        if w.kind == "ring" and self.gather:
+            return self.bwd_gather()
         if w.kind == "dense":
             return v.bwd_dense(t["do"], t["q"], t["k"], t["v"], self.out, self.lse, w.scale, w.causal)
         if w.kind == "varlen":
@@ -204,7 +256,7 @@ def measure(n: int, steps: int, warmup: int, per_call: bool = True, flush=None,
         # and >= 200 ms
         r["fwd_calls"] = time_calls(p.fwd)
         r["bwd_calls"] = time_calls(p.bwd)
-        if w.kind == "ring":
+        if w.kind == "ring" and not p.gather:
             # the lse merge alone (HBM-bound elementwise)
             parts = p.partials()
             r["merge_calls"] = time_calls(lambda: p.vca.merge(*parts, copy_dtype=p.dtype))
@@ -276,7 +328,8 @@ def chunk_count(w: "workloads.Workload") -> int:
 
 def roofline(w: "workloads.Workload", kernels: dict) -> dict:
     """Roofline entry of the kernel that takes the most time per step."""
-    name = max(kernels, key=lambda k: kernels[k]["mean_ms"] * kernels[k]["per_step"])
+    ranked = sorted(kernels, key=lambda k: -kernels[k]["mean_ms"] * kernels[k]["per_step"])
+    name = next(k for k in ranked if kernel_work(w, k) is not None)
     bound, units, unit = kernel_work(w, name)
     # a pass split over several launches (the dS-store backward runs one
     # dK/dV + dQ launch pair per chunk of kv-heads) does its step's work
@@ -497,6 +550,9 @@ def main():
             r = m if n == args.workload else measure(n, max(5, args.steps // 2), 3)
             configs[r["workload"]] = config_entry(workloads.workload(n), r)
         line["configs"] = configs
+        # workload 5 through the packed gather layout of live tokens
+        r = measure(7, max(5, args.steps // 2), 3, per_call=False)
+        line["ring_gather_layout"] = config_entry(workloads.workload(7), r)
         # the same workloads with fp16 inputs (same kernels, fp16 MFMA)
         line["configs_fp16"] = {}
         for n in LARGE_WORKLOADS:
@@ -507,10 +563,10 @@ def main():
     if args.all:
         per = {}
         flush = L2Flush()
-        for n in range(1, 7):
+        for n in range(1, 8):
             # the small workload and the ring share's merge are latency / HBM
             # bound: also timed with L2 and MALL flushed
-            r = measure(n, max(3, args.steps // 2), 2, flush=flush if n in (1, 5, 6) else None)
+            r = measure(n, max(3, args.steps // 2), 2, flush=flush if n in (1, 5, 6, 7) else None)
             per[r["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in r.items() if k not in ("workload", "kernels")}
             per[r["workload"]]["kernels_ms"] = {k: round(v["mean_ms"], 4)

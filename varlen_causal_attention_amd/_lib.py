@@ -9,7 +9,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvca_attn.so")
+# VCA_ATTN_LIB names another build of the same library (e.g. one with the host
+# code built under AddressSanitizer for the host-side tests).
+LIB_PATH = os.environ.get("VCA_ATTN_LIB") or os.path.join(HERE, "libvca_attn.so")
 
 ATTN_OK = 0
 ATTN_E_INVALID = -1

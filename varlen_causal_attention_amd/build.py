@@ -51,14 +51,29 @@ def _compile(job) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, asan_host_dir: str | None = None) -> str:
+    """Build the library in-tree; with asan_host_dir, build instead a copy
+    whose host code runs under AddressSanitizer (device code unchanged) into
+    that directory, for the host-side tests:
+        python -m varlen_causal_attention_amd.build --asan-host DIR
+        VCA_ATTN_LIB=DIR/libvca_attn.so ASAN_OPTIONS=detect_leaks=0 \
+          LD_PRELOAD=$(clang -print-file-name=libclang_rt.asan-x86_64.so) \
+          python -m pytest tests/test_abi_host.py tests/test_dense_route.py"""
+    global BUILD, LIB, COMMON
+    if asan_host_dir:
+        BUILD = os.path.join(os.path.abspath(asan_host_dir), "_build")
+        LIB = os.path.join(os.path.abspath(asan_host_dir), "libvca_attn.so")
+        COMMON = [c for c in COMMON if c != "-O3"] + [
+            "-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+            "-fno-omit-frame-pointer"]
     os.makedirs(BUILD, exist_ok=True)
     jobs = ([(s, False) for s in KERNEL_SOURCES] + [(s, True) for s in KERNEL_SOURCES]
             + [(s, False) for s in HIP_SOURCES + CXX_SOURCES])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         objs = list(ex.map(_compile, jobs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    san = ["-Xarch_host", "-fsanitize=address"] if asan_host_dir else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
@@ -69,4 +84,7 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) == 3 and sys.argv[1] == "--asan-host":
+        build(asan_host_dir=sys.argv[2])
+    else:
+        build()

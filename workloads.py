@@ -83,6 +83,7 @@ class Workload:
     doc_lo: int = 0
     doc_hi: int = 0
     single_doc: bool = False  # ring: the row is one document (then the pad tail)
+    route: str = "segments"   # ring: "segments" (cu_seqlens tiling the shard) or "gather"
 
     @property
     def scale(self) -> float:
@@ -180,7 +181,8 @@ def ring_pairs(row_ids: np.ndarray, shard: int) -> int:
 def workload(n: int) -> Workload:
     """The named workloads (1: small dense, 2: varlen D128, 3: dense D512,
     4: varlen 192/128, 5: one rank of a two-rank ring at D512, 6: the same
-    rank when its row is a single document, the dense-routed ring chunks)."""
+    rank when its row is a single document, the dense-routed ring chunks,
+    7: workload 5 through the packed gather layout of live tokens)."""
     if n == 1:
         return Workload("dense_causal_b1_h4kv2_n256_d128", "dense", 1, Hq=4, Hkv=2, Dqk=128,
                         Dv=128, B=1, Nq=256, Nk=256)
@@ -199,6 +201,10 @@ def workload(n: int) -> Workload:
     if n == 6:
         return Workload("ring_rank1_of2_single_doc_q4096_h16kv8_d512", "ring", 6, Hq=16, Hkv=8,
                         Dqk=512, Dv=512, shard=4096, pad_tail=128, single_doc=True)
+    if n == 7:
+        return Workload("ring_rank1_of2_q4096_h16kv8_d512_gather", "ring", 5, Hq=16, Hkv=8,
+                        Dqk=512, Dv=512, shard=4096, pad_tail=128, doc_lo=256, doc_hi=4096,
+                        route="gather")
     raise ValueError(f"no workload {n}")
 
 

@@ -52,17 +52,26 @@ def f64(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # visibility
 # ---------------------------------------------------------------------------
-def causal_visible(lq: int, lk: int, rows=None, cols=None) -> np.ndarray:
+def causal_visible(lq: int, lk: int, rows=None, cols=None, window=None) -> np.ndarray:
     """Bottom-right causal visibility of one segment ("fa4" page, document-causal
-    bullets): query i sees key j iff j <= i + (lk - lq)."""
+    bullets): query i sees key j iff j <= i + (lk - lq). A left window W > 0
+    ("attention utils" page, backend metadata: a positive left window counts
+    the visible keys, the current token included) also requires
+    j > i + (lk - lq) - W; None or W <= 0 means unbounded."""
     i = np.arange(lq) if rows is None else np.asarray(rows)
     j = np.arange(lk) if cols is None else np.asarray(cols)
-    return j[None, :] <= i[:, None] + (lk - lq)
+    vis = j[None, :] <= i[:, None] + (lk - lq)
+    if window is not None and window > 0:
+        vis = vis & (j[None, :] > i[:, None] + (lk - lq) - window)
+    return vis
 
 
-def segment_visible(lq: int, lk: int, causal: bool, rows=None, cols=None) -> np.ndarray:
+def segment_visible(lq: int, lk: int, causal: bool, rows=None, cols=None,
+                    window=None) -> np.ndarray:
     if causal:
-        return causal_visible(lq, lk, rows, cols)
+        return causal_visible(lq, lk, rows, cols, window)
+    if window is not None and window > 0:
+        raise ValueError("a left window applies to causal attention only")
     m = lq if rows is None else len(rows)
     n = lk if cols is None else len(cols)
     return np.ones((m, n), dtype=bool)
@@ -80,12 +89,22 @@ def doc_causal_visible(q_doc, q_pos, k_doc, k_pos) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # one head, one segment: the definitions
 # ---------------------------------------------------------------------------
-def attend(q, k, v, vis, scale: float):
+def capped(s, softcap):
+    """Logit soft-capping of the scaled scores ("ffpa_attention" page: the
+    softcap argument of the attention forward): cap * tanh(s / cap); None or
+    0 leaves s unchanged."""
+    if not softcap:
+        return s
+    return softcap * np.tanh(s / softcap)
+
+
+def attend(q, k, v, vis, scale: float, softcap=None):
     """Softmax attention of rows q [m, Dqk] over keys k [n, Dqk] / values v [n, Dv]
     restricted to vis [m, n]. Returns (out [m, Dv], lse [m]).
 
-    S = scale * q k^T; lse = log sum_{visible} exp(S); P = exp(S - lse) on
-    visible entries; out = P v. Rows with nothing visible: out 0, lse -inf.
+    S = scale * q k^T (soft-capped when softcap is set); lse = log
+    sum_{visible} exp(S); P = exp(S - lse) on visible entries; out = P v. Rows
+    with nothing visible: out 0, lse -inf.
     """
     m = q.shape[0]
     out = np.zeros((m, v.shape[1]))
@@ -93,6 +112,7 @@ def attend(q, k, v, vis, scale: float):
     for r0 in range(0, m, _ROW_BLOCK):
         r1 = min(m, r0 + _ROW_BLOCK)
         s = scale * (q[r0:r1] @ k.T)
+        s = capped(s, softcap)
         s = np.where(vis[r0:r1], s, NEG_INF)
         live = vis[r0:r1].any(axis=1)
         mx = np.where(live, s.max(axis=1, initial=NEG_INF), 0.0)
@@ -104,13 +124,15 @@ def attend(q, k, v, vis, scale: float):
     return out, lse
 
 
-def attend_backward(do, q, k, v, o, lse, vis, scale: float):
+def attend_backward(do, q, k, v, o, lse, vis, scale: float, softcap=None):
     """Gradients of sum(do * out) for one head and segment, recomputed from the
     caller-supplied o and lse ("ffpa_attention" page, backward entries).
 
     delta = rowsum(do * o); P = exp(S - lse) on visible entries (0 where lse is
     -inf); dV = P^T do; dP = do v^T; dS = P * (dP - delta);
-    dQ = scale dS k; dK = scale dS^T q.
+    dQ = scale dS k; dK = scale dS^T q. With a softcap, S = cap tanh(X / cap)
+    of the scaled scores X and dS carries the chain-rule factor
+    dS/dX = 1 - tanh(X / cap)^2.
 
     With a subset of keys this still gives exact dK/dV for those keys (P uses
     the supplied lse, not a renormalised one); dQ is then the subset's part.
@@ -122,13 +144,16 @@ def attend_backward(do, q, k, v, o, lse, vis, scale: float):
     live = np.isfinite(lse)
     for r0 in range(0, q.shape[0], _ROW_BLOCK):
         r1 = min(q.shape[0], r0 + _ROW_BLOCK)
-        s = scale * (q[r0:r1] @ k.T)
+        x = scale * (q[r0:r1] @ k.T)
+        s = capped(x, softcap)
         use = vis[r0:r1] & live[r0:r1, None]
         ref = np.where(live[r0:r1], lse[r0:r1], 0.0)
         p = np.exp(np.where(use, s - ref[:, None], NEG_INF))  # 0 where hidden or lse = -inf
         dv += p.T @ do[r0:r1]
         dp = do[r0:r1] @ v.T
         ds = p * (dp - delta[r0:r1, None])
+        if softcap:
+            ds = ds * (1.0 - np.tanh(x / softcap) ** 2)
         dq[r0:r1] = scale * (ds @ k)
         dk += scale * (ds.T @ q[r0:r1])
     return dq, dk, dv
@@ -145,7 +170,7 @@ def _segments(cu_q, cu_k):
             for s in range(len(cu_q) - 1)]
 
 
-def fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
+def fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, window=None, softcap=None):
     """Varlen forward ("ffpa_attention" page, varlen forward entry): returns
     out [Tq, Hq, Dv] and lse [Hq, Tq]; segment s pairs queries cu_q[s]:cu_q[s+1]
     with keys cu_k[s]:cu_k[s+1]."""
@@ -158,16 +183,17 @@ def fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool):
     for qa, qb, ka, kb in _segments(cu_q, cu_k):
         if qb == qa:
             continue
-        vis = segment_visible(qb - qa, kb - ka, causal)
+        vis = segment_visible(qb - qa, kb - ka, causal, window=window)
         for h in range(Hq):
             g = h // G
-            o, l = attend(q[qa:qb, h], k[ka:kb, g], v[ka:kb, g], vis, scale)
+            o, l = attend(q[qa:qb, h], k[ka:kb, g], v[ka:kb, g], vis, scale, softcap)
             out[qa:qb, h] = o
             lse[h, qa:qb] = l
     return out, lse
 
 
-def bwd_varlen(do, q, k, v, o, lse, cu_q, cu_k, scale: float, causal: bool):
+def bwd_varlen(do, q, k, v, o, lse, cu_q, cu_k, scale: float, causal: bool, window=None,
+               softcap=None):
     """Varlen backward from caller out/lse; dk/dv summed over each GQA group."""
     do, q, k, v, o, lse = f64(do), f64(q), f64(k), f64(v), f64(o), f64(lse)
     Hq = q.shape[1]
@@ -179,11 +205,11 @@ def bwd_varlen(do, q, k, v, o, lse, cu_q, cu_k, scale: float, causal: bool):
     for qa, qb, ka, kb in _segments(cu_q, cu_k):
         if qb == qa or kb == ka:
             continue
-        vis = segment_visible(qb - qa, kb - ka, causal)
+        vis = segment_visible(qb - qa, kb - ka, causal, window=window)
         for h in range(Hq):
             g = h // G
             a, b, c = attend_backward(do[qa:qb, h], q[qa:qb, h], k[ka:kb, g], v[ka:kb, g],
-                                      o[qa:qb, h], lse[h, qa:qb], vis, scale)
+                                      o[qa:qb, h], lse[h, qa:qb], vis, scale, softcap)
             dq[qa:qb, h] = a
             dk[ka:kb, g] += b
             dv[ka:kb, g] += c
@@ -193,7 +219,7 @@ def bwd_varlen(do, q, k, v, o, lse, cu_q, cu_k, scale: float, causal: bool):
 # ---------------------------------------------------------------------------
 # dense SDPA layout: q [B, Hq, Nq, Dqk], k [B, Hkv, Nk, Dqk], v [B, Hkv, Nk, Dv]
 # ---------------------------------------------------------------------------
-def fwd_dense(q, k, v, scale: float, causal: bool):
+def fwd_dense(q, k, v, scale: float, causal: bool, window=None, softcap=None):
     """Dense forward ("ffpa_attention" page, dense forward entry): returns
     out [B, Hq, Nq, Dv] and lse [B, Hq, Nq]."""
     q, k, v = f64(q), f64(k), f64(v)
@@ -202,16 +228,16 @@ def fwd_dense(q, k, v, scale: float, causal: bool):
     G = Hq // Hkv
     out = np.zeros((B, Hq, Nq, v.shape[3]))
     lse = np.full((B, Hq, Nq), NEG_INF)
-    vis = segment_visible(Nq, Nk, causal)
+    vis = segment_visible(Nq, Nk, causal, window=window)
     for b in range(B):
         for h in range(Hq):
-            o, l = attend(q[b, h], k[b, h // G], v[b, h // G], vis, scale)
+            o, l = attend(q[b, h], k[b, h // G], v[b, h // G], vis, scale, softcap)
             out[b, h] = o
             lse[b, h] = l
     return out, lse
 
 
-def bwd_dense(do, q, k, v, o, lse, scale: float, causal: bool):
+def bwd_dense(do, q, k, v, o, lse, scale: float, causal: bool, window=None, softcap=None):
     """Dense backward ("ffpa_attention" page, dense backward entry): dq, dk, dv in
     [B, H, N, D] with dk/dv reduced to Hkv."""
     do, q, k, v, o, lse = f64(do), f64(q), f64(k), f64(v), f64(o), f64(lse)
@@ -221,12 +247,12 @@ def bwd_dense(do, q, k, v, o, lse, scale: float, causal: bool):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    vis = segment_visible(Nq, Nk, causal)
+    vis = segment_visible(Nq, Nk, causal, window=window)
     for b in range(B):
         for h in range(Hq):
             g = h // G
             a, c, d = attend_backward(do[b, h], q[b, h], k[b, g], v[b, g], o[b, h], lse[b, h],
-                                      vis, scale)
+                                      vis, scale, softcap)
             dq[b, h] = a
             dk[b, g] += c
             dv[b, g] += d
@@ -242,7 +268,8 @@ def _locate(cu, t):
     return int(np.searchsorted(np.asarray(cu, dtype=np.int64), t, side="right")) - 1
 
 
-def fwd_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, tokens, heads):
+def fwd_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, tokens, heads, window=None,
+                    softcap=None):
     """out [n, Dv] and lse [n] of the listed (token, q-head) rows of the varlen forward."""
     cu_q = np.asarray(cu_q, dtype=np.int64)
     cu_k = np.asarray(cu_k, dtype=np.int64)
@@ -253,15 +280,16 @@ def fwd_varlen_rows(q, k, v, cu_q, cu_k, scale, causal, tokens, heads):
         t, h = int(t), int(h)
         s = _locate(cu_q, t)
         qa, qb, ka, kb = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
-        vis = segment_visible(qb - qa, kb - ka, causal, rows=[t - qa])
+        vis = segment_visible(qb - qa, kb - ka, causal, rows=[t - qa], window=window)
         qq = f64(q[t, h])[None, :]
-        o, l = attend(qq, f64(k[ka:kb, h // G]), f64(v[ka:kb, h // G]), vis, scale)
+        o, l = attend(qq, f64(k[ka:kb, h // G]), f64(v[ka:kb, h // G]), vis, scale, softcap)
         outs.append(o[0])
         lses.append(l[0])
     return np.array(outs), np.array(lses)
 
 
-def bwd_varlen_rows(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, heads):
+def bwd_varlen_rows(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, heads, window=None,
+                    softcap=None):
     """dq [n, Dqk] of the listed (token, q-head) rows, from caller out/lse [Hq, Tq]."""
     cu_q = np.asarray(cu_q, dtype=np.int64)
     cu_k = np.asarray(cu_k, dtype=np.int64)
@@ -272,16 +300,17 @@ def bwd_varlen_rows(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, head
         t, h = int(t), int(h)
         s = _locate(cu_q, t)
         qa, qb, ka, kb = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
-        vis = segment_visible(qb - qa, kb - ka, causal, rows=[t - qa])
+        vis = segment_visible(qb - qa, kb - ka, causal, rows=[t - qa], window=window)
         g = h // G
         a, _, _ = attend_backward(f64(do[t, h])[None], f64(q[t, h])[None], f64(k[ka:kb, g]),
                                   f64(v[ka:kb, g]), f64(o[t, h])[None],
-                                  np.array([float(lse[h, t])]), vis, scale)
+                                  np.array([float(lse[h, t])]), vis, scale, softcap)
         res.append(a[0])
     return np.array(res)
 
 
-def bwd_varlen_cols(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, kv_heads):
+def bwd_varlen_cols(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, kv_heads,
+                    window=None, softcap=None):
     """dk [n, Dqk], dv [n, Dv] of the listed (key token, kv-head) rows, summed over
     the q-heads of the group and over every query that sees the key."""
     cu_q = np.asarray(cu_q, dtype=np.int64)
@@ -296,12 +325,12 @@ def bwd_varlen_cols(do, q, k, v, o, lse, cu_q, cu_k, scale, causal, tokens, kv_h
         dk = np.zeros(k.shape[2])
         dv = np.zeros(v.shape[2])
         if qb > qa:
-            vis = segment_visible(qb - qa, kb - ka, causal, cols=[t - ka])
+            vis = segment_visible(qb - qa, kb - ka, causal, cols=[t - ka], window=window)
             kk = f64(k[t, g])[None]
             vv = f64(v[t, g])[None]
             for h in range(g * G, (g + 1) * G):
                 _, b, c = attend_backward(f64(do[qa:qb, h]), f64(q[qa:qb, h]), kk, vv,
-                                          f64(o[qa:qb, h]), f64(lse[h, qa:qb]), vis, scale)
+                                          f64(o[qa:qb, h]), f64(lse[h, qa:qb]), vis, scale, softcap)
                 dk += b[0]
                 dv += c[0]
         dks.append(dk)

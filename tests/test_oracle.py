@@ -406,3 +406,94 @@ def test_ring_gather_scatter_and_row_merge():
     untouched = [f for f in range(B * S) if f not in idx]
     for f in untouched:
         np.testing.assert_array_equal(mo[f // S, :, f % S], acc[f // S, :, f % S])
+
+
+# ---------------------------------------------------------------- window, softcap
+@pytest.mark.parametrize("lq,lk,W", [(9, 9, 3), (5, 9, 4), (9, 5, 2), (7, 7, 1), (6, 6, 20)])
+def test_left_window_counts_visible_keys(lq, lk, W):
+    """A left window of W ("attention utils" page: a positive left window
+    counts the visible keys, the current token included): with q = 0 every
+    visible score is 0, so lse = ln(#visible) with #visible = the keys
+    j <= i + lk - lq that are also among the last W of them, by brute force."""
+    rng = np.random.default_rng(20 + W)
+    k, v = _rand(rng, lk, 1, 3), _rand(rng, lk, 1, 2)
+    q = np.zeros((lq, 1, 3))
+    o, l = orc.fwd_varlen(q, k, v, [0, lq], [0, lk], 0.5, True, window=W)
+    for i in range(lq):
+        top = i + lk - lq  # last visible key
+        seen = [j for j in range(lk) if j <= top and j >= top - W + 1]
+        if not seen:
+            assert l[0, i] == -np.inf and np.all(o[i] == 0)
+            continue
+        assert abs(l[0, i] - math.log(len(seen))) < 1e-12
+        np.testing.assert_allclose(o[i, 0], v[seen, 0].mean(axis=0), atol=1e-12)
+
+
+def test_window_of_one_sees_only_the_diagonal_key():
+    rng = np.random.default_rng(21)
+    q, k, v = _rand(rng, 6, 2, 4), _rand(rng, 6, 2, 4), _rand(rng, 6, 2, 3)
+    o, l = orc.fwd_varlen(q, k, v, [0, 6], [0, 6], 0.7, True, window=1)
+    np.testing.assert_allclose(o, v, atol=1e-12)
+    np.testing.assert_allclose(l, 0.7 * np.einsum("thd,thd->ht", q, k), atol=1e-12)
+    # a window covering the whole segment is plain causal attention
+    o2, l2 = orc.fwd_varlen(q, k, v, [0, 6], [0, 6], 0.7, True, window=6)
+    o3, l3 = orc.fwd_varlen(q, k, v, [0, 6], [0, 6], 0.7, True)
+    np.testing.assert_allclose(o2, o3, atol=1e-13)
+    np.testing.assert_allclose(l2, l3, atol=1e-13)
+    with pytest.raises(ValueError):
+        orc.fwd_varlen(q, k, v, [0, 6], [0, 6], 0.7, False, window=2)
+
+
+def test_softcap_bounds_scores_and_matches_brute_force():
+    """Soft-capped scores cap * tanh(s / cap): brute force on single rows,
+    identical keys still give the mean of V, and a huge cap changes nothing."""
+    rng = np.random.default_rng(22)
+    q, k, v = 3 * _rand(rng, 5, 1, 4), 3 * _rand(rng, 7, 1, 4), _rand(rng, 7, 1, 2)
+    cap = 2.5
+    o, l = orc.fwd_varlen(q, k, v, [0, 5], [0, 7], 0.9, True, softcap=cap)
+    for i in range(5):
+        keys = [j for j in range(7) if j <= i + 2]
+        sc = [cap * math.tanh(0.9 * float(q[i, 0] @ k[j, 0]) / cap) for j in keys]
+        assert all(abs(x) <= cap for x in sc)
+        w = [math.exp(x) for x in sc]
+        assert abs(l[0, i] - math.log(sum(w))) < 1e-12
+        np.testing.assert_allclose(o[i, 0], sum(wj * v[j, 0] for wj, j in zip(w, keys)) / sum(w),
+                                   atol=1e-12)
+    kk = np.repeat(k[:1], 7, axis=0)
+    o, _ = orc.fwd_varlen(q, kk, v, [0, 5], [0, 7], 0.9, True, softcap=cap)
+    for i in range(5):
+        np.testing.assert_allclose(o[i, 0], v[: i + 3, 0].mean(axis=0), atol=1e-12)
+    o1, l1 = orc.fwd_varlen(q, k, v, [0, 5], [0, 7], 0.9, True, softcap=1e9)
+    o0, l0 = orc.fwd_varlen(q, k, v, [0, 5], [0, 7], 0.9, True)
+    np.testing.assert_allclose(o1, o0, atol=1e-9)
+    np.testing.assert_allclose(l1, l0, atol=1e-9)
+
+
+@pytest.mark.parametrize("window,softcap", [(3, None), (None, 1.7), (4, 2.2)])
+def test_window_softcap_backward_matches_finite_differences(window, softcap):
+    """Gradients of sum(dO * out) with a left window and / or a softcap: the
+    backward from the oracle's own out/lse against central differences."""
+    rng = np.random.default_rng(23)
+    T, H, D = 7, 1, 3
+    q, k, v, do = (_rand(rng, T, H, D) for _ in range(4))
+    cu = [0, 3, 7]
+    kw = dict(window=window, softcap=softcap)
+    o, l = orc.fwd_varlen(q, k, v, cu, cu, 0.8, True, **kw)
+    dq, dk, dv = orc.bwd_varlen(do, q, k, v, o, l, cu, cu, 0.8, True, **kw)
+
+    def f(qq, kk, vv):
+        return float((do * orc.fwd_varlen(qq, kk, vv, cu, cu, 0.8, True, **kw)[0]).sum())
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = {"q": q, "k": k, "v": v}
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (f(**{a[0] + a[0]: b for a, b in args_p.items()}) -
+                        f(**{a[0] + a[0]: b for a, b in args_m.items()})) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name

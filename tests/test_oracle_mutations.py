@@ -12,10 +12,10 @@ from oracle import attention as orc
 SRC = open(orc.__file__).read()
 
 MUTATIONS = {
-    "top_left_causal": ("return j[None, :] <= i[:, None] + (lk - lq)", "return j[None, :] <= i[:, None]"),
+    "top_left_causal": ("vis = j[None, :] <= i[:, None] + (lk - lq)", "vis = j[None, :] <= i[:, None]"),
     "gqa_modulo_map": ("o, l = attend(q[qa:qb, h], k[ka:kb, g]", "o, l = attend(q[qa:qb, h], k[ka:kb, h % Hkv]"),
     "dense_gqa_modulo": ("o, l = attend(q[b, h], k[b, h // G], v[b, h // G]", "o, l = attend(q[b, h], k[b, h % Hkv], v[b, h % Hkv]"),
-    "scale_dropped_fwd": ("        s = scale * (q[r0:r1] @ k.T)\n        s = np.where", "        s = (q[r0:r1] @ k.T)\n        s = np.where"),
+    "scale_dropped_fwd": ("        s = scale * (q[r0:r1] @ k.T)\n        s = capped(s, softcap)", "        s = (q[r0:r1] @ k.T)\n        s = capped(s, softcap)"),
     "lse_base2": ("mx + np.log(np.where(live, tot, 1.0))", "mx + np.log2(np.where(live, tot, 1.0))"),
     "delta_dropped": ("ds = p * (dp - delta[r0:r1, None])", "ds = p * dp"),
     "dk_scale_dropped": ("dk += scale * (ds.T @ q[r0:r1])", "dk += (ds.T @ q[r0:r1])"),
@@ -28,6 +28,9 @@ MUTATIONS = {
     "doc_bwd_group_sum": ("        dk[:, h // G] += b\n", "        dk[:, h % k.shape[1]] += b\n"),
     "ring_gather_wrong_axes": ("return x.transpose(0, 2, 1, 3).reshape(B * S, H, D)[idx]", "return x.transpose(0, 1, 2, 3).reshape(B * S, H, D)[idx]"),
     "ring_merge_rows_keeps_old_out": ("    flat_o[idx] = mo\n", "    flat_o[idx] = flat_o[idx]\n"),
+    "window_off_by_one": ("vis = vis & (j[None, :] > i[:, None] + (lk - lq) - window)", "vis = vis & (j[None, :] >= i[:, None] + (lk - lq) - window)"),
+    "softcap_not_applied": ("    return softcap * np.tanh(s / softcap)", "    return s"),
+    "softcap_grad_factor_dropped": ("            ds = ds * (1.0 - np.tanh(x / softcap) ** 2)", "            ds = ds * 1.0"),
     "doc_future_keys": ("(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None])", "(np.asarray(k_pos)[None, :] >= 0)"),
 }
 

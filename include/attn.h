@@ -167,6 +167,49 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
                     const int64_t* strides, float scale, int causal, int flags,
                     void* workspace, size_t* workspace_bytes, hipStream_t stream);
 
+/* Left sliding window and logit softcap: the four calls above with one more
+ * argument, ext (the "attention utils" page, window argument of its
+ * mask helpers: a positive left window counts the keys a query sees, its own
+ * position included; the "ffpa_attention" page, softcap argument of the
+ * forward entries, which that page pins off).
+ *  ext->window: 0 = none. W > 0 (only with causal = 1, else ATTN_E_INVALID):
+ *  query i of a segment with lq queries and lk keys sees keys j with
+ *  i + (lk - lq) - W < j <= i + (lk - lq), its W most recent keys.
+ *  ext->softcap: 0 = none. c > 0: every scaled score x = scale * q.k is
+ *  replaced by c * tanh(x / c) before the softmax; lse is taken over the
+ *  capped scores, and the backward applies the chain factor
+ *  1 - tanh^2(x / c) to dS.
+ *  Negative window, negative or non-finite softcap: ATTN_E_INVALID. ext =
+ *  NULL (or both fields 0) is exactly the plain call. The backward of a
+ *  problem must get the ext its forward got (its lse depends on it). With ext
+ *  set, the backward takes the generic dK/dV kernel at every head dim (the
+ *  software-pipelined ones are compiled without the options); the workspace
+ *  size is that of the plain call. */
+typedef struct attn_ext {
+  int window;
+  float softcap;
+} attn_ext;
+int attn_fwd_dense_ex(int dtype, const void* q, const void* k, const void* v, void* out,
+                      float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv,
+                      const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                      void* workspace, size_t* workspace_bytes, hipStream_t stream);
+int attn_fwd_varlen_ex(int dtype, const void* q, const void* k, const void* v, void* out,
+                       float* lse, const int32_t* cu_q, const int32_t* cu_k, int num_segments,
+                       int max_q, int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                       const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                       void* workspace, size_t* workspace_bytes, hipStream_t stream);
+int attn_bwd_dense_ex(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
+                      float scale, int causal, const attn_ext* ext, int flags, void* workspace,
+                      size_t* workspace_bytes, hipStream_t stream);
+int attn_bwd_varlen_ex(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, void* dq, void* dk, void* dv,
+                       const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                       int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                       const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                       int flags, void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
 /* Online-softmax merge of two partial results of the same query rows
  * ("gemma4_moe cp_attention" page, -inf-safe merge entry).
  *  out_a, out_b: [rows, H, Dv] contiguous, element type dtype_a / dtype_b

@@ -142,6 +142,55 @@ def test_varlen_forward_bounds_must_cover_tokens(lib):
     assert _fwd_varlen(lib, Tk=0, max_k=0)[0] == 0
 
 
+def _ext_calls(lib, ext, causal=1):
+    """Size queries of the four _ex entry points with the given attn_ext (or
+    None): their statuses and sizes."""
+    e = C.pointer(ext) if ext is not None else None
+    res = []
+    need = C.c_size_t(0)
+    st = lib.attn_fwd_dense_ex(0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 8, 8, 128, 128,
+                               _lib.i64_array([8 * 128 * 4, 8 * 128, 128] * 4), 0.1, causal, e,
+                               None, C.byref(need), None)
+    res.append((st, need.value))
+    need = C.c_size_t(0)
+    st = lib.attn_fwd_varlen_ex(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 50, 60, 100, 120,
+                                8, 2, 128, 128, _lib.i64_array([8 * 128, 128] * 4), 0.1, causal, e,
+                                None, C.byref(need), None)
+    res.append((st, need.value))
+    need = C.c_size_t(0)
+    st = lib.attn_bwd_dense_ex(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 8,
+                               8, 512, 512, _lib.i64_array([8 * 512 * 4, 8 * 512, 512] * 8), 0.1,
+                               causal, e, 0, None, C.byref(need), None)
+    res.append((st, need.value))
+    need = C.c_size_t(0)
+    st = lib.attn_bwd_varlen_ex(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                3, 50, 60, 100, 120, 8, 2, 192, 128,
+                                _lib.i64_array([8 * 256, 256] * 8), 0.1, causal, e, 0, None,
+                                C.byref(need), None)
+    res.append((st, need.value))
+    return res
+
+
+def test_window_and_softcap_argument_checks(lib):
+    """attn_ext: a positive window needs causal = 1; a negative window and a
+    negative or non-finite softcap are rejected before any launch; valid
+    options (and a NULL ext) pass the host checks with the plain call's
+    workspace size."""
+    plain = _ext_calls(lib, None)
+    assert all(st == 0 and need > 0 for st, need in plain)
+    for ext in (_lib.AttnExt(0, 0.0), _lib.AttnExt(64, 0.0), _lib.AttnExt(0, 30.0),
+                _lib.AttnExt(1, 0.5)):
+        assert _ext_calls(lib, ext) == plain
+    # softcap alone works without the causal mask
+    assert all(st == 0 for st, _ in _ext_calls(lib, _lib.AttnExt(0, 30.0), causal=0))
+    bad = [(_lib.AttnExt(16, 0.0), 0), (_lib.AttnExt(-1, 0.0), 1), (_lib.AttnExt(0, -2.0), 1),
+           (_lib.AttnExt(0, float("inf")), 1), (_lib.AttnExt(0, float("nan")), 1)]
+    for ext, causal in bad:
+        for st, _ in _ext_calls(lib, ext, causal=causal):
+            assert st == _lib.ATTN_E_INVALID
+            assert lib.attn_last_error().decode()
+
+
 def _cpu(*shape):
     import torch
     return torch.zeros(shape, dtype=torch.bfloat16)

@@ -34,7 +34,8 @@ EXPORTED = (
     "attn_dense_route",
     "attn_zero_rows", "attn_timing_enable", "attn_timing_read", "attn_ring_segments",
     "attn_ring_inplace_preferred", "attn_gather_rows", "attn_scatter_rows", "attn_gather_lse",
-    "attn_scatter_lse", "attn_merge_rows",
+    "attn_scatter_lse", "attn_merge_rows", "attn_fwd_dense_ex", "attn_fwd_varlen_ex",
+    "attn_bwd_dense_ex", "attn_bwd_varlen_ex",
 )
 
 _P = C.c_void_p
@@ -43,6 +44,13 @@ _F = C.c_float
 _I64P = C.POINTER(C.c_int64)
 _SZP = C.POINTER(C.c_size_t)
 _I32P = C.POINTER(C.c_int32)
+
+
+
+class AttnExt(C.Structure):
+    """struct attn_ext: left window (0 = none) and softcap (0 = none)."""
+    _fields_ = [("window", C.c_int), ("softcap", C.c_float)]
+
 
 _SIGS = {
     "attn_last_error": (C.c_char_p, []),
@@ -58,6 +66,14 @@ _SIGS = {
                             _I64P, _F, _I, _I, _P, _SZP, _P]),
     "attn_bwd_varlen": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                              _I, _I, _I, _I, _I64P, _F, _I, _I, _P, _SZP, _P]),
+    "attn_fwd_dense_ex": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64P, _F, _I,
+                               _P, _P, _SZP, _P]),
+    "attn_fwd_varlen_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                _I, _I64P, _F, _I, _P, _P, _SZP, _P]),
+    "attn_bwd_dense_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                               _I, _I64P, _F, _I, _P, _I, _P, _SZP, _P]),
+    "attn_bwd_varlen_ex": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                _I, _I, _I, _I, _I, _I64P, _F, _I, _P, _I, _P, _SZP, _P]),
     "attn_merge": (_I, [_P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_doc_segments": (_I, [_I32P, _I, _I, _I, _I, _I, _I, _I, _I32P, _I32P, _I,
                                C.POINTER(C.c_int)]),

@@ -105,6 +105,28 @@ vca::ViewW vieww(void* p, int64_t sb, int64_t sh, int64_t sn) {
   return vca::ViewW{static_cast<uint16_t*>(p), sb, sh, sn};
 }
 
+// Window / softcap options: 0 = off. The window needs the causal mask; both
+// must be non-negative and finite.
+int check_ext(const attn_ext* ext, int causal) {
+  if (!ext) return ATTN_OK;
+  if (ext->window < 0) return fail(ATTN_E_INVALID, "window must be >= 0");
+  if (ext->window > 0 && !causal) return fail(ATTN_E_INVALID, "a window needs causal = 1");
+  if (!(ext->softcap >= 0.f) || std::isinf(ext->softcap))
+    return fail(ATTN_E_INVALID, "softcap must be finite and >= 0");
+  return ATTN_OK;
+}
+// Kernel fields of the options. The forward folds a negative scale into Q and
+// works on scale * q.k as |scale| * s, so its tanh argument factor is
+// |scale| / cap; the backward's scores are raw q.k, so its factor is
+// scale / cap. cap_out = cap * log2(e) puts the capped score in base-2 units.
+template <class Args>
+void set_ext(Args& a, const attn_ext* ext, float scale, bool fwd) {
+  a.window = ext ? ext->window : 0;
+  const float cap = ext ? ext->softcap : 0.f;
+  a.cap_in = cap > 0.f ? (fwd ? std::fabs(scale) : scale) / cap : 0.f;
+  a.cap_out = cap > 0.f ? cap * vca::kLog2e : 0.f;
+}
+
 // Argument checks of the varlen forward (everything visible on the host).
 int fwd_varlen_checks(int dtype, const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const int32_t* cu_q, const int32_t* cu_k,
@@ -133,8 +155,8 @@ int fwd_varlen_checks(int dtype, const void* q, const void* k, const void* v, co
 int fwd_varlen_run(int dtype, const void* q, const void* k, const void* v, void* out, float* lse,
                    const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
                    int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
-                   const int64_t* strides, float scale, int causal, void* ws, hipStream_t stream,
-                   const char* what) {
+                   const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                   void* ws, hipStream_t stream, const char* what) {
   int st;
   if (validate_env() && (st = validate_cu(cu_q, cu_k, num_segments, Tq, Tk, max_q, max_k, stream)))
     return st;
@@ -153,6 +175,7 @@ int fwd_varlen_run(int dtype, const void* q, const void* k, const void* v, void*
   a.Tk = Tk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
+  set_ext(a, ext, scale, true);
   return hip_status(
       fwd_launcher(dtype)(a, Dqk, Dv, causal != 0, num_segments, Hq, Tq, ws, stream), what);
 }
@@ -222,9 +245,18 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
                    int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
                    float scale, int causal, void* workspace, size_t* workspace_bytes,
                    hipStream_t stream) {
+  return attn_fwd_dense_ex(dtype, q, k, v, out, lse, B, Hq, Hkv, Nq, Nk, Dqk, Dv, strides, scale,
+                           causal, nullptr, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_dense_ex(int dtype, const void* q, const void* k, const void* v, void* out,
+                      float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv,
+                      const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                      void* workspace, size_t* workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
   if (st) return st;
+  if ((st = check_ext(ext, causal))) return st;
   if (B < 0 || Nq < 0 || Nk < 0) return fail(ATTN_E_INVALID, "B, Nq, Nk must be >= 0");
   if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
   const bool has_q = (int64_t)B * Nq > 0, has_k = (int64_t)B * Nk > 0;
@@ -253,6 +285,7 @@ int attn_fwd_dense(int dtype, const void* q, const void* k, const void* v, void*
   a.Tk = Nk;
   a.G = Hq / Hkv;
   a.scale_log2 = scale * vca::kLog2e;
+  set_ext(a, ext, scale, true);
   return hip_status(
       fwd_launcher(dtype)(a, Dqk, Dv, causal != 0, B, Hq, (int64_t)B * Nq, workspace, stream),
       "attn_fwd_dense launch");
@@ -263,16 +296,27 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
                     int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
                     const int64_t* strides, float scale, int causal, void* workspace,
                     size_t* workspace_bytes, hipStream_t stream) {
+  return attn_fwd_varlen_ex(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq,
+                            Tk, Hq, Hkv, Dqk, Dv, strides, scale, causal, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+int attn_fwd_varlen_ex(int dtype, const void* q, const void* k, const void* v, void* out,
+                       float* lse, const int32_t* cu_q, const int32_t* cu_k, int num_segments,
+                       int max_q, int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                       const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                       void* workspace, size_t* workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = fwd_varlen_checks(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq,
                              Tk, Hq, Hkv, Dqk, Dv, strides, scale);
   if (st) return st;
+  if ((st = check_ext(ext, causal))) return st;
   bool query = false;
   const size_t need_ws = vca::fwd_workspace_bytes(Tq, num_segments);
   if ((st = workspace_step(need_ws, workspace, workspace_bytes, &query))) return st;
   if (query || Tq == 0) return ok();
   return fwd_varlen_run(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk,
-                        Hq, Hkv, Dqk, Dv, strides, scale, causal, workspace, stream,
+                        Hq, Hkv, Dqk, Dv, strides, scale, causal, ext, workspace, stream,
                         "attn_fwd_varlen launch");
 }
 
@@ -295,7 +339,7 @@ int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void*
   void* ws = nullptr;
   if ((st = scratch_address(&ws))) return st;
   return fwd_varlen_run(dtype, q, k, v, out, lse, cu_q, cu_k, num_segments, max_q, max_k, Tq, Tk,
-                        Hq, Hkv, Dqk, Dv, strides, scale, causal, ws, stream,
+                        Hq, Hkv, Dqk, Dv, strides, scale, causal, nullptr, ws, stream,
                         "attn_fwd_varlen_noalloc launch");
 }
 
@@ -304,9 +348,20 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
                    int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides, float scale,
                    int causal, int flags, void* workspace, size_t* workspace_bytes,
                    hipStream_t stream) {
+  return attn_bwd_dense_ex(dtype, dout, q, k, v, out, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, Dqk, Dv,
+                           strides, scale, causal, nullptr, flags, workspace, workspace_bytes,
+                           stream);
+}
+
+int attn_bwd_dense_ex(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,
+                      float scale, int causal, const attn_ext* ext, int flags, void* workspace,
+                      size_t* workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
   if (st) return st;
+  if ((st = check_ext(ext, causal))) return st;
   if (B < 0 || Nq < 0 || Nk < 0) return fail(ATTN_E_INVALID, "B, Nq, Nk must be >= 0");
   if (flags & ~ATTN_DQ_ACCUMULATE) return fail(ATTN_E_INVALID, "unknown flags");
   if (!strides) return fail(ATTN_E_INVALID, "strides is NULL");
@@ -347,6 +402,7 @@ int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, co
   a.scale_log2 = scale * vca::kLog2e;
   a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
+  set_ext(a, ext, scale, false);
   return hip_status(bwd_launcher(dtype)(a, Dqk, Dv, causal != 0, B, Hq, Hkv, Nq, (int64_t)B * Nq,
                                         (int64_t)B * Nk, tg, workspace, stream),
                     "attn_bwd_dense launch");
@@ -358,9 +414,21 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
                     int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
                     const int64_t* strides, float scale, int causal, int flags, void* workspace,
                     size_t* workspace_bytes, hipStream_t stream) {
+  return attn_bwd_varlen_ex(dtype, dout, q, k, v, out, lse, dq, dk, dv, cu_q, cu_k, num_segments,
+                            max_q, max_k, Tq, Tk, Hq, Hkv, Dqk, Dv, strides, scale, causal,
+                            nullptr, flags, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_varlen_ex(int dtype, const void* dout, const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, void* dq, void* dk, void* dv,
+                       const int32_t* cu_q, const int32_t* cu_k, int num_segments, int max_q,
+                       int max_k, int Tq, int Tk, int Hq, int Hkv, int Dqk, int Dv,
+                       const int64_t* strides, float scale, int causal, const attn_ext* ext,
+                       int flags, void* workspace, size_t* workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_heads(dtype, Hq, Hkv, Dqk, Dv, scale);
   if (st) return st;
+  if ((st = check_ext(ext, causal))) return st;
   if (num_segments < 0 || Tq < 0 || Tk < 0 || max_q < 0 || max_k < 0)
     return fail(ATTN_E_INVALID, "sizes must be >= 0");
   if (flags & ~ATTN_DQ_ACCUMULATE) return fail(ATTN_E_INVALID, "unknown flags");
@@ -407,6 +475,7 @@ int attn_bwd_varlen(int dtype, const void* dout, const void* q, const void* k, c
   a.scale_log2 = scale * vca::kLog2e;
   a.inv_scale = 1.f / scale;
   a.dq_accumulate = (flags & ATTN_DQ_ACCUMULATE) ? 1 : 0;
+  set_ext(a, ext, scale, false);
   return hip_status(bwd_launcher(dtype)(a, Dqk, Dv, causal != 0, num_segments, Hq, Hkv, max_q, Tq,
                                         Tk, tg, workspace, stream),
                     "attn_bwd_varlen launch");

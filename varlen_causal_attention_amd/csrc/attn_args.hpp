@@ -44,6 +44,13 @@ struct FwdArgs {
   int G;            // Hq / Hkv
   int H;            // q-heads: blockIdx.x = item * H + head
   float scale_log2; // scale * log2(e)
+  // Left window and logit softcap (FwdArgs and BwdArgs alike): window > 0
+  // keeps only the keys j > i + (lk - lq) - window of a causal row; with
+  // cap_in != 0 the scaled score x = scale * q.k becomes cap * tanh(x / cap),
+  // computed as cap_out * tanh(cap_in * q.k) with cap_in = |scale| / cap (a
+  // negative scale is folded into q) and cap_out = cap * log2(e).
+  int window;
+  float cap_in, cap_out;
   const int2* items;      // (segment, q tile) heavy first
   const int* item_count;
 };
@@ -60,6 +67,8 @@ struct BwdArgs {
   int Nq, Nk, Tq, Tk;
   int G;
   float scale, scale_log2, inv_scale;  // inv_scale = 1 / scale (scale != 0)
+  int window;             // as in FwdArgs
+  float cap_in, cap_out;  // as in FwdArgs, with cap_in = scale / cap (signed)
   int dq_accumulate;
   int Hq, Hkv;
   const int2* items_q;    // (segment, query tile) for the dQ pass, heavy first

@@ -83,11 +83,20 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
 // DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
 // and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
 // BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
+// The left window and the softcap (ext) take the generic dK/dV kernel at
+// every head dim (same 128-key blocks).
 template <int DQK, int DV, int DS, int KN, bool KP, int NWK>
-hipError_t launch_dkdv(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st) {
+hipError_t launch_dkdv(const BwdArgs& a, bool causal, bool ext, unsigned grid, hipStream_t st) {
   constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
   TimedLaunch timer("attn_bwd_dkdv", st);
-  if constexpr (kPipe && DQK == 128) {
+  if (ext) {
+    if (causal)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true, true>), dim3(grid),
+                         dim3(64 * NWK), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false, true>),
+                         dim3(grid), dim3(64 * NWK), 0, st, a);
+  } else if constexpr (kPipe && DQK == 128) {
     const hipError_t e = launch_dkdv_roles(a, causal, grid, st);
     if (e != hipSuccess) return e;
   } else if constexpr (kPipe) {
@@ -112,7 +121,9 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
                     hipStream_t st) {
   constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
   constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
+  static_assert(key_block == 32 * (NWK / DS), "the generic dK/dV kernel takes the same blocks");
   constexpr int q_tile = 32 * (NWQ / DS);
+  const bool ext = a.window > 0 || a.cap_in != 0.f;
   const int seg_major = (Hq / Hkv) % 2 == 0 ? 0 : 1;
   const int G = Hq / Hkv;
   a.kvh0 = 0;
@@ -139,7 +150,7 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
         a.kvh_n = n;
         a.ds_h0 = g0 * G;
         a.ds_nh = n * G;
-        hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(a, causal, kitems * n, st);
+        hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(a, causal, ext, kitems * n, st);
         if (e != hipSuccess) return e;
         TimedLaunch timer("attn_bwd_dq_ds", st);
         const dim3 g(qitems * (unsigned)(n * G));
@@ -162,8 +173,14 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   if (q_rows > 0) {
     TimedLaunch timer("attn_bwd_dq", st);
     const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
-    if (causal)
+    if (causal && ext)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true, true>), g,
+                         dim3(64 * NWQ), 0, st, a);
+    else if (causal)
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true>), g,
+                         dim3(64 * NWQ), 0, st, a);
+    else if (ext)
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false, true>), g,
                          dim3(64 * NWQ), 0, st, a);
     else
       hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false>), g,
@@ -171,7 +188,7 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
   }
   if (k_rows > 0) {
     const hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(
-        a, causal, (unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv), st);
+        a, causal, ext, (unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv), st);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();

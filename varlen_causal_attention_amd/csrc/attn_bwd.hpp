@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
 // operand of S = Q K^T and dP = dO V^T, and column-wise (transposing LDS read)
 // as the A operand of dK^T += Q^T dS and dV^T += dO^T P.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int NBUF, bool PF, int NW, bool CAUSAL>
+template <int DQK, int DV, int DS, int NBUF, bool PF, int NW, bool CAUSAL, bool EXT = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const BwdArgs a) {
   static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 64 * NW;          // threads
@@ -153,11 +153,16 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
 #pragma unroll
   for (int i = 0; i < NVB; ++i) dva[i] = zero16();
 
-  // query steps that can see any key of this block
+  // query steps that can see any key of this block (with a left window, the
+  // rows past the last one whose window still reaches the block's last key
+  // see none of it)
+  const int win = EXT && CAUSAL ? a.window : 0;
+  const bool capped = EXT && a.cap_in != 0.f;
   int q_begin = 0;
   if (CAUSAL) q_begin = max(0, kb0 - shift);
   q_begin &= ~(BQ - 1);
-  const int nq = lq > q_begin ? (lq - q_begin + BQ - 1) / BQ : 0;
+  const int q_end = win > 0 ? max(0, min(lq, kb0 + 32 * KG - 1 - shift + win)) : lq;
+  const int nq = q_end > q_begin ? (q_end - q_begin + BQ - 1) / BQ : 0;
   const int total = a.G * nq;
 
   using QStage = TileStage<BQ, DQK, NT>;
@@ -232,7 +237,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
       flush_ds();
     }
     // this 32-query step is hidden from every key of this wave's group?
-    const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + BQ - 1 + shift);
+    const bool live = gk0 < lk && !(CAUSAL && gk0 > q0 + BQ - 1 + shift) &&
+                      !(win > 0 && gk0 + 31 <= q0 + shift - win);
     f32x16 sacc = zero16(), pacc = zero16();
     if (live) {
       // partial S[q][key] = Q K^T and dP[q][key] = dO V^T over this wave's d ranges
@@ -269,19 +275,27 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
       // past the segment end carry lse = +inf, so their P is 0 without a mask;
       // the key mask is only needed on steps that cross the causal diagonal
       // or hold keys past the segment end.
-      const bool need_mask = gk0 + 31 >= lk || (CAUSAL && gk0 + 31 > q0 + shift);
+      const bool need_mask = gk0 + 31 >= lk || (CAUSAL && gk0 + 31 > q0 + shift) ||
+                             (win > 0 && gk0 <= q0 + BQ - 1 + shift - win);
       float p[16], dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = (r >> 2) * 8 + half * 4 + (r & 3);
-        float x = fast_exp2(sacc[r] * a.scale_log2 - slse[buf][qr]);
+        // softcap: P = exp(cap * tanh(scale * s / cap) - lse), and the score
+        // gradient takes the chain factor 1 - tanh^2
+        float th = 0.f;
+        if (EXT && capped) th = fast_tanh(a.cap_in * sacc[r]);
+        float x = fast_exp2((EXT && capped ? a.cap_out * th : sacc[r] * a.scale_log2) -
+                            slse[buf][qr]);
         if (need_mask) {
           bool vis = key < lk;
           if (CAUSAL) vis = vis && key <= q0 + qr + shift;
+          if (EXT && win > 0) vis = vis && key > q0 + qr + shift - win;
           x = vis ? x : 0.f;
         }
         p[r] = x;
         dsv[r] = x * (pacc[r] - sdel[buf][qr]);
+        if (EXT && capped) dsv[r] *= 1.f - th * th;
       }
       const frag8 p0 = to_frag(p), p1 = to_frag(p + 8);
       const frag8 s0 = to_frag(dsv), s1 = to_frag(dsv + 8);
@@ -521,7 +535,8 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
 // BN-key tile, K and V are staged row-major in LDS; S^T = K Q^T and
 // dP^T = V dO^T read them row-wise, dQ^T += K^T dS^T column-wise.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, int NW, bool CAUSAL>
+template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, int NW, bool CAUSAL,
+          bool EXT = false>
 __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs a) {
   static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 64 * NW;
@@ -568,6 +583,10 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   int kv_end = lk;
   if (CAUSAL) kv_end = min(lk, m0 + 32 * QG + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // left window: key tiles wholly below the first row's window are skipped
+  const int win = EXT && CAUSAL ? a.window : 0;
+  const int t0 = win > 0 ? min(ntiles, max(0, m0 + shift - win + 1) / BN) : 0;
+  const bool capped = EXT && a.cap_in != 0.f;
 
   frag8 qf[NKS], df[NVS];
   {
@@ -630,20 +649,21 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   KStage kst;
   VStage vst;
   if constexpr (DMA) {
-    if (ntiles > 0) issue_kv(0);
-  } else if (ntiles > 0) {
+    if (t0 < ntiles) issue_kv(t0);
+  } else if (t0 < ntiles) {
+    const int b0 = NBUF == 2 ? (t0 & 1) : 0;
     if (PF) {
-      kst.load_clamped(kbp, a.k.sn, 0, lk, tid);
-      vst.load_clamped(vbp, a.v.sn, 0, lk, tid);
-      kst.template store<KS>(sk[0], tid);
-      vst.template store<VS>(sv[0], tid);
-      if (ntiles > 1) {
-        kst.load_clamped(kbp, a.k.sn, BN, lk, tid);
-        vst.load_clamped(vbp, a.v.sn, BN, lk, tid);
+      kst.load_clamped(kbp, a.k.sn, t0 * BN, lk, tid);
+      vst.load_clamped(vbp, a.v.sn, t0 * BN, lk, tid);
+      kst.template store<KS>(sk[b0], tid);
+      vst.template store<VS>(sv[b0], tid);
+      if (t0 + 1 < ntiles) {
+        kst.load_clamped(kbp, a.k.sn, (t0 + 1) * BN, lk, tid);
+        vst.load_clamped(vbp, a.v.sn, (t0 + 1) * BN, lk, tid);
       }
     } else {
-      KStage::template copy<KS>(sk[0], kbp, a.k.sn, 0, lk, tid);
-      VStage::template copy<VS>(sv[0], vbp, a.v.sn, 0, lk, tid);
+      KStage::template copy<KS>(sk[b0], kbp, a.k.sn, t0 * BN, lk, tid);
+      VStage::template copy<VS>(sv[b0], vbp, a.v.sn, t0 * BN, lk, tid);
     }
   }
 
@@ -652,7 +672,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqa[i] = zero16();
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = NBUF == 2 ? (t & 1) : 0;
     if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
@@ -667,7 +687,8 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
         vst.load_clamped(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
       }
     }
-    const bool live = wq0 < lq && !(CAUSAL && k0 > wq0 + 31 + shift);
+    const bool live = wq0 < lq && !(CAUSAL && k0 > wq0 + 31 + shift) &&
+                      !(win > 0 && k0 + BN - 1 <= wq0 + shift - win);
     f32x16 sacc[NKB], pacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -726,7 +747,8 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
       // needed on tiles that cross the diagonal or the segment end
       // (one uniform branch picks a masked or an unmasked copy of the loop, so
       // the mask costs no per-element branch on the other tiles)
-      const bool need_mask = k0 + BN > lk || (CAUSAL && k0 + BN - 1 > wq0 + shift);
+      const bool need_mask = k0 + BN > lk || (CAUSAL && k0 + BN - 1 > wq0 + shift) ||
+                             (win > 0 && k0 <= wq0 + 31 + shift - win);
       frag8 sf[2 * NKB];
       auto softmax_grad = [&](auto masked) {
 #pragma unroll
@@ -734,14 +756,19 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
           float dsv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(sacc[kb][r] * a.scale_log2 - l2);
+            // softcap: P from the capped score, dS times 1 - tanh^2
+            float th = 0.f;
+            if (EXT && capped) th = fast_tanh(a.cap_in * sacc[kb][r]);
+            float p = fast_exp2((EXT && capped ? a.cap_out * th : sacc[kb][r] * a.scale_log2) - l2);
             if constexpr (decltype(masked)::value) {
               const int kj = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
               bool vis = kj < lk;
               if (CAUSAL) vis = vis && kj <= qi + shift;
+              if (EXT && win > 0) vis = vis && kj > qi + shift - win;
               p = vis ? p : 0.f;
             }
             dsv[r] = p * (pacc[kb][r] - dl);
+            if (EXT && capped) dsv[r] *= 1.f - th * th;
           }
           sf[2 * kb] = to_frag(dsv);
           sf[2 * kb + 1] = to_frag(dsv + 8);
@@ -840,14 +867,20 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
   const int wq0 = m0 + 32 * w;
   // key tiles this wave's queries see (the blocks the dK/dV pass stored) and
-  // the workgroup's (its last live wave's)
+  // the workgroup's (its last live wave's); with a left window the tiles
+  // below the wave's first row's window hold no stored block, and the
+  // workgroup starts at its first wave's first tile
   auto tiles_upto = [&](int rows_end) {
     int kv_end = lk;
     if (CAUSAL) kv_end = min(lk, rows_end + shift);
     return kv_end > 0 ? min((kv_end + 31) >> 5, a.ds_mkt) : 0;
   };
+  const int win = CAUSAL ? a.window : 0;
+  auto first_tile = [&](int row0) { return win > 0 ? max(0, row0 + shift - win + 1) >> 5 : 0; };
   const int nkt_w = wq0 < lq ? tiles_upto(wq0 + 32) : 0;
+  const int kf_w = first_tile(wq0);
   const int ntiles = tiles_upto(min(m0 + BQ, ((lq + 31) >> 5) << 5));
+  const int tb = min(ntiles, first_tile(m0));
   const int64_t blk0 = ds_block(a, s, sg, h, wq0 < lq ? wq0 : m0, 0);  // key tile t at +1024 t
   const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
 
@@ -860,7 +893,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
       const int row = 32 * t + c / (DQK / 8);
       kr[i] = row < lk ? ldg16(kbp + (int64_t)row * a.k.sn + (c % (DQK / 8)) * 8) : zero_u32x4();
     }
-    if (t < nkt_w && blk0 >= 0) {
+    if (t >= kf_w && t < nkt_w && blk0 >= 0) {
       const uint16_t* b = a.ds + blk0 + 1024 * t;
       dr[0] = ldg16(b + 8 * lane);
       dr[1] = ldg16(b + 512 + 8 * lane);
@@ -884,19 +917,19 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
   dr[0] = dr[1] = zero_u32x4();
-  if (ntiles > 0) {
-    load(0);
-    store(0);
-    if (ntiles > 1) load(1);
+  if (tb < ntiles) {
+    load(tb);
+    store(tb & 1);
+    if (tb + 1 < ntiles) load(tb + 1);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = tb; t < ntiles; ++t) {
     const int buf = t & 1;
     __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
     if (t + 1 < ntiles) {
       store(buf ^ 1);
       if (t + 2 < ntiles) load(t + 2);
     }
-    if (t < nkt_w && blk0 >= 0) {
+    if (t >= kf_w && t < nkt_w && blk0 >= 0) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const frag8 bfr = tr_frag(sds[buf][w], 32, 16 * ks, 0, lane);

@@ -25,8 +25,15 @@ hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_
   a.nk_items = (int)k_items;
   if (q_rows > 0 && k_rows > 0) {
     TimedLaunch timer("attn_bwd_scores", st);
-    hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>),
-                       dim3(xcd_grid<kScoreSplit>(q_items * Hq)), dim3(kNT), 0, st, a);
+    // the left window and the softcap (ext) take their own scores kernel;
+    // the product passes read the window's block ranges at run time
+    const dim3 grid(xcd_grid<kScoreSplit>(q_items * Hq));
+    if (a.cap_in != 0.f)
+      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 2>), grid, dim3(kNT), 0, st, a);
+    else if (a.window > 0)
+      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 1>), grid, dim3(kNT), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>), grid, dim3(kNT), 0, st, a);
   }
   if (k_rows > 0) {
     TimedLaunch timer("attn_bwd_dkdv_tiles", st);

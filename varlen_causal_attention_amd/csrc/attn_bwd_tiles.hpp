@@ -66,6 +66,20 @@ __device__ __forceinline__ int blk_row_extent(const BwdArgs& a, const SegGeom& g
 __device__ __forceinline__ int blk_col_start(const SegGeom& g, int kb, bool causal) {
   return causal ? max(0, kb * kBlk - (g.lk - g.lq)) / kBlk : 0;
 }
+// Left window (win > 0, causal only): the first key block the rows of the
+// query block starting at q0 can see (the one holding its first row's first
+// visible key; every later block up to the extent is seen by some row)...
+__device__ __forceinline__ int blk_row_first(const SegGeom& g, int q0, int win) {
+  return win > 0 ? max(0, q0 + (g.lk - g.lq) - win + 1) / kBlk : 0;
+}
+// ...and one past the last query block that sees key block kb (its rows end
+// where the window of a row no longer reaches the block's last key)
+__device__ __forceinline__ int blk_col_end(const SegGeom& g, int kb, int win) {
+  const int nqb = (g.lq + kBlk - 1) / kBlk;
+  if (win <= 0) return nqb;
+  const int q_end = min(g.lq, kb * kBlk + kBlk - 1 - (g.lk - g.lq) + win);
+  return q_end > 0 ? min(nqb, (q_end + kBlk - 1) / kBlk) : 0;
+}
 // stored column of key k inside its block (swaps the middle two 4-key groups
 // of every 16; its own inverse)
 __device__ __forceinline__ int key_perm(int k) {
@@ -178,7 +192,8 @@ typedef const __attribute__((address_space(1))) float gfloat;
 // ---------------------------------------------------------------------------
 constexpr int kScoreSplit = 4;
 
-template <int DQK, int DV, bool CAUSAL>
+// EXT: 0 plain, 1 left window, 2 left window and softcap.
+template <int DQK, int DV, bool CAUSAL, int EXT = 0>
 __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a) {
   constexpr int NCQ = DQK / kChunk, NCV = DV / kChunk, NCT = NCQ + NCV;
   static_assert(DQK % kChunk == 0 && DV % kChunk == 0, "head dims stream in 64-element chunks");
@@ -203,7 +218,11 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
   if (q0 >= sg.lq) return;
   const int lq = sg.lq, lk = sg.lk, shift = lk - lq;
   const int ext = blk_row_extent(a, sg, q0, CAUSAL);
-  const int nkt = ext > part ? (ext - part + kScoreSplit - 1) / kScoreSplit : 0;
+  // with a left window the block's key blocks start at kf (EXT only)
+  const int win = EXT && CAUSAL ? a.window : 0;
+  const bool capped = EXT == 2 && a.cap_in != 0.f;
+  const int kf = EXT ? min(ext, blk_row_first(sg, q0, win)) : 0;
+  const int nkt = ext - kf > part ? (ext - kf - part + kScoreSplit - 1) / kScoreSplit : 0;
   if (nkt == 0) return;
   const int64_t slot = blk_slot(a, sg, s, st.y);
 
@@ -232,7 +251,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
   const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
   auto issue = [&](int it, int stage) {
     const int kt = it / NCT, c = it - kt * NCT;
-    const int k0 = (part + kt * kScoreSplit) * kBlk;
+    const int k0 = (kf + part + kt * kScoreSplit) * kBlk;
     const bool sl = c < NCQ;
     const int c0 = (sl ? c : c - NCQ) * kChunk;
     const uint16_t* ab = (sl ? kbp : vbp) + c0;
@@ -286,10 +305,13 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
     // ---- epilogue: lane holds queries 128*wn + 32*u + col and, per 8 values
     // 8m..8m+7 of a result tile, the keys that are stored at columns
     // 64*wm + 32*t + 16*m + 8*half + 0..7 of the block
-    const int kb = part + kt * kScoreSplit, k0 = kb * kBlk;
+    const int kb = kf + part + kt * kScoreSplit, k0 = kb * kBlk;
     const int64_t base = blk_base(a, slot, kb, h);
     if (c == NCQ - 1) {
       uint16_t* pb = a.tile_p + base;
+      // softcap: the chain factor 1 - tanh^2 of each element goes to the dS
+      // block's place for the dS epilogue to pick up
+      uint16_t* gb = a.tile_ds + base;
       auto pstore = [&](auto masked) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -298,25 +320,37 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
             const int qr = 128 * wn + 32 * u + col, qi = q0 + qr;
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-              frag8 p8;
+              frag8 p8, g8;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int r = 8 * m + e;
-                float p = fast_exp2(acc[t][u][r] * a.scale_log2 - l2[u]);
+                float th = 0.f;
+                if (EXT == 2 && capped) th = fast_tanh(a.cap_in * acc[t][u][r]);
+                float p = fast_exp2(
+                    (EXT == 2 && capped ? a.cap_out * th : acc[t][u][r] * a.scale_log2) - l2[u]);
                 if constexpr (decltype(masked)::value) {
                   const int kj = k0 + 64 * wm + 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
                   bool vis = qi < lq && kj < lk;
                   if (CAUSAL) vis = vis && kj <= qi + shift;
+                  if (EXT && win > 0) vis = vis && kj > qi + shift - win;
                   p = vis ? p : 0.f;
                 }
                 p8[e] = (elem_t)p;
+                if constexpr (EXT == 2) g8[e] = (elem_t)(1.f - th * th);
               }
+              // (the offset is spelled out at each store: naming it once
+              // makes the register allocator spill in the plain kernel)
               stg16(pb + qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half,
                     __builtin_bit_cast(u32x4, p8));
+              if (EXT == 2 && capped)
+                stg16(gb + qr * kBlk + 64 * wm + 32 * t + 16 * m + 8 * half,
+                      __builtin_bit_cast(u32x4, g8));
             }
           }
       };
-      const bool full = q0 + kBlk <= lq && k0 + kBlk <= lk && (!CAUSAL || k0 + kBlk - 1 <= q0 + shift);
+      const bool full = q0 + kBlk <= lq && k0 + kBlk <= lk &&
+                        (!CAUSAL || k0 + kBlk - 1 <= q0 + shift) &&
+                        !(win > 0 && k0 <= q0 + kBlk - 1 + shift - win);
       if (full) pstore(std::false_type{});
       else pstore(std::true_type{});
     } else {
@@ -343,6 +377,11 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               d8[e] = (elem_t)((float)p8[e] * acc[t][u][8 * m + e]);
+            if (EXT == 2 && capped) {
+              const frag8 g8 = as_frag(ldg16(db + off));
+#pragma unroll
+              for (int e = 0; e < 8; ++e) d8[e] = (elem_t)((float)d8[e] * (float)g8[e]);
+            }
             stg16(db + off, __builtin_bit_cast(u32x4, d8));
           }
         }
@@ -405,7 +444,8 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   if (k0 >= sg.lk) return;
   const int lq = sg.lq;
   const int qb0 = blk_col_start(sg, kb, CAUSAL);
-  const int nqb = (lq + kBlk - 1) / kBlk;
+  // query blocks qb0 .. nqb-1 see this key block (fewer with a left window)
+  const int nqb = blk_col_end(sg, kb, CAUSAL ? a.window : 0);
   const int per = kb < a.tile_nkb && nqb > qb0 ? (nqb - qb0) * CPB : 0;
   const int total = a.G * per;
 
@@ -507,12 +547,15 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
   const int q0 = st.y * kBlk;
   if (q0 >= sg.lq) return;
   const int lk = sg.lk;
-  const int total = blk_row_extent(a, sg, q0, CAUSAL) * CPB;
+  // key blocks kf .. extent-1 (kf > 0 only with a left window)
+  const int kext = blk_row_extent(a, sg, q0, CAUSAL);
+  const int kf = min(kext, blk_row_first(sg, q0, CAUSAL ? a.window : 0));
+  const int total = (kext - kf) * CPB;
   const int64_t slot = blk_slot(a, sg, s, st.y);
   const uint16_t* kbp =
       a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh + dh * OB;
   auto issue = [&](int it, int stage) {
-    const int kb = it / CPB, c = it % CPB;
+    const int kb = kf + it / CPB, c = it % CPB;
     const int r0 = kb * kBlk + c * kChunk;
     fill_cols<OB>(stg[stage], w, lane,
                   [&](int r) { return kbp + (int64_t)min(r0 + r, lk - 1) * a.k.sn; });

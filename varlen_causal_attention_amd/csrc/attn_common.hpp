@@ -301,6 +301,11 @@ __device__ __forceinline__ void stg8(uint16_t* p, u32x2 v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// tanh(x) = 1 - 2 / (e^(2x) + 1): one exp2 and one reciprocal; saturates to
+// +-1 without overflow (e^(2x) = inf gives 1, 0 gives -1)
+__device__ __forceinline__ float fast_tanh(float x) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(fast_exp2(x * (2.f * 1.4426950408889634f)) + 1.f);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Eight fp32 values -> eight elements (round to nearest even) as one MFMA fragment.

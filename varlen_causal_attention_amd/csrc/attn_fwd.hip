@@ -1,5 +1,7 @@
 // Forward launcher: instantiates the forward kernel for every compiled
-// head-dim pair and both mask modes.
+// head-dim pair and both mask modes, plain and with the left window /
+// softcap extension (a separate instantiation, so the plain kernels carry
+// none of its registers or branches).
 #include "attn_fwd.hpp"
 #include "attn_fwd_wide.hpp"
 #include "attn_launch.hpp"
@@ -18,18 +20,31 @@ template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, int HPW =
 hipError_t fwd_dims(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
   TimedLaunch timer("attn_fwd", st);
   grid.x /= HPW;
-  if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true, HPW>), grid,
-                       dim3(256 * DS * HPW), 0, st, a);
+  const dim3 block(256 * DS * HPW);
+  const bool ext = a.window > 0 || a.cap_in != 0.f;
+  if (causal && ext)
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true, HPW, true>), grid,
+                       block, 0, st, a);
+  else if (causal)
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true, HPW>), grid, block,
+                       0, st, a);
+  else if (ext)
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false, HPW, true>), grid,
+                       block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false, HPW>), grid,
-                       dim3(256 * DS * HPW), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false, HPW>), grid, block,
+                       0, st, a);
   return hipGetLastError();
 }
 hipError_t fwd_wide(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
   TimedLaunch timer("attn_fwd", st);
-  if (causal)
+  const bool ext = a.window > 0 || a.cap_in != 0.f;
+  if (causal && ext)
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<true, true>), grid, dim3(256), 0, st, a);
+  else if (causal)
     hipLaunchKernelGGL(attn_fwd_wide_kernel<true>, grid, dim3(256), 0, st, a);
+  else if (ext)
+    hipLaunchKernelGGL((attn_fwd_wide_kernel<false, true>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(attn_fwd_wide_kernel<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();

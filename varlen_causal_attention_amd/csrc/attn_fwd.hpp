@@ -27,7 +27,8 @@ namespace VCA_ELEM {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL, int HPW = 1>
+template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL, int HPW = 1,
+          bool EXT = false>
 __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const FwdArgs a) {
   // DS waves share one 32-row query block: wave `ds` of the group holds the
   // Q fragments of Dqk range [ds*DR, (ds+1)*DR) and accumulates O^T for Dv
@@ -41,6 +42,9 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   // HPW = 2 runs two q-heads of one GQA group over the same query rows (four
   // waves each): every K/V tile brought into LDS feeds both, half the tile
   // loads per unit of work, with the same causal work per wave.
+  // EXT adds the left window (tiles below every row's window are skipped,
+  // the window's edge masked) and the logit softcap (scores become
+  // cap * tanh(scale * s / cap) before the softmax).
   static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
   static_assert(HPW == 1 || DS == 1, "head pairs with a split head dim");
   constexpr int NT = 256 * DS * HPW;  // threads
@@ -100,6 +104,10 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   int kv_end = lk;
   if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
   const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // left window: key tiles wholly below the first row's window are skipped
+  const int win = EXT && CAUSAL ? a.window : 0;
+  const int t0 = win > 0 ? min(ntiles, max(0, m0 + shift - win + 1) / BN) : 0;
+  const bool capped = EXT && a.cap_in != 0.f;
 
   // Scores are kept unscaled until the exponent: the row max is taken over
   // raw q.k and scaled once, and exp2(sl2 * s - m) is one fma per element. A
@@ -160,20 +168,21 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   KStage kst;
   VStage vst;
   if constexpr (DMA) {
-    if (ntiles > 0) issue_kv(0);
-  } else if (ntiles > 0) {
+    if (t0 < ntiles) issue_kv(t0);
+  } else if (t0 < ntiles) {
+    const int b0 = NBUF == 2 ? (t0 & 1) : 0;
     if (PF) {
-      kst.load_clamped(kb, a.k.sn, 0, lk, tid);
-      vst.load_clamped(vb, a.v.sn, 0, lk, tid);
-      kst.template store<KS>(sk[0], tid);
-      vst.template store<VS>(sv[0], tid);
-      if (ntiles > 1) {
-        kst.load_clamped(kb, a.k.sn, BN, lk, tid);
-        vst.load_clamped(vb, a.v.sn, BN, lk, tid);
+      kst.load_clamped(kb, a.k.sn, t0 * BN, lk, tid);
+      vst.load_clamped(vb, a.v.sn, t0 * BN, lk, tid);
+      kst.template store<KS>(sk[b0], tid);
+      vst.template store<VS>(sv[b0], tid);
+      if (t0 + 1 < ntiles) {
+        kst.load_clamped(kb, a.k.sn, (t0 + 1) * BN, lk, tid);
+        vst.load_clamped(vb, a.v.sn, (t0 + 1) * BN, lk, tid);
       }
     } else {
-      KStage::template copy<KS>(sk[0], kb, a.k.sn, 0, lk, tid);
-      VStage::template copy<VS>(sv[0], vb, a.v.sn, 0, lk, tid);
+      KStage::template copy<KS>(sk[b0], kb, a.k.sn, t0 * BN, lk, tid);
+      VStage::template copy<VS>(sv[b0], vb, a.v.sn, t0 * BN, lk, tid);
     }
   }
 
@@ -184,7 +193,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   float m_ref = kNegInf;  // base-2 running reference max of this row
   float lsum = 0.f;       // this lane half's share of the row sum
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = NBUF == 2 ? (t & 1) : 0;
     if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
@@ -200,7 +209,8 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       }
     }
     // the DS waves of a group take every branch below together
-    const bool live = wrow0 < lq && !(CAUSAL && k0 > wrow0 + 31 + shift);
+    const bool live = wrow0 < lq && !(CAUSAL && k0 > wrow0 + 31 + shift) &&
+                      !(win > 0 && k0 + BN - 1 < wrow0 + shift - win + 1);
 
     // S^T = K Q^T (partial over this wave's Dqk range when DS > 1)
     f32x16 sacc[NKB];
@@ -236,16 +246,31 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
         }
     }
     if (live) {
-      // mask (diagonal and tail tiles only), then the row max of the raw
-      // scores, scaled once (sl2 > 0; a fully masked row keeps -inf)
-      const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift);
+      // softcap first (a masked score must stay -inf): scores then hold
+      // cap * tanh(scale * s / cap) in base-2 units, and the factor below is 1.
+      // Then the mask (diagonal, window-edge and tail tiles only) and the row
+      // max of the raw scores, scaled once (mul > 0; a fully masked row keeps
+      // -inf)
+      if constexpr (EXT) {
+        if (capped) {
+#pragma unroll
+          for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sacc[kbk][r] = a.cap_out * fast_tanh(a.cap_in * sacc[kbk][r]);
+        }
+      }
+      const float mul = capped ? 1.f : sl2;
+      const bool need_mask = (k0 + BN > lk) || (CAUSAL && k0 + BN - 1 > wrow0 + shift) ||
+                             (win > 0 && k0 < wrow0 + 31 + shift - win + 1);
       if (need_mask) {
 #pragma unroll
         for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kbk * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            const bool vis = key < lk && (!CAUSAL || key <= row + shift);
+            bool vis = key < lk && (!CAUSAL || key <= row + shift);
+            if (EXT && win > 0) vis = vis && key > row + shift - win;
             sacc[kbk][r] = vis ? sacc[kbk][r] : kNegInf;
           }
       }
@@ -254,7 +279,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
-      mx = fmaxf(mx, xor32(mx)) * sl2;
+      mx = fmaxf(mx, xor32(mx)) * mul;
 
       // lazy rescale of the running reference
       const float m_new = fmaxf(m_ref, mx);
@@ -278,7 +303,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(fmaf(sacc[kbk][r], sl2, -m_use));
+          p[r] = fast_exp2(fmaf(sacc[kbk][r], mul, -m_use));
           lsum += p[r];
         }
         pf[2 * kbk] = to_frag(p);

@@ -32,7 +32,7 @@ namespace VCA_ELEM {
 constexpr int kWideD = 512;
 constexpr int kWideBN = 32;  // keys per tile
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool EXT = false>
 __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) {
   constexpr int D = kWideD, BN = kWideBN;
   constexpr int NKS = D / 16;        // contraction steps of S
@@ -61,15 +61,23 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
   const int lq = sg.lq, lk = sg.lk;
   const int shift = lk - lq;
 
-  const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
-  const uint16_t* kb = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + kvh * a.k.sh;
-  const uint16_t* vb = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + kvh * a.v.sh;
-
   const int wrow0 = m0 + 32 * w;  // first query row of this wave
   const int row = wrow0 + col;    // this lane's query row
   int kv_end = lk;
   if (CAUSAL) kv_end = min(lk, m0 + kFwdBM + shift);
-  const int nt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;  // tiles the workgroup loads
+  const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // left window: the key tiles below the workgroup's first window are
+  // skipped; the loads start at key kofs, every key index below is absolute
+  const int win = EXT && CAUSAL ? a.window : 0;
+  const int tb = win > 0 ? min(ntiles, max(0, m0 + shift - win + 1) / BN) : 0;
+  const int kofs = tb * BN, lke = lk - kofs;
+  const int nt = ntiles - tb;  // tiles the workgroup loads
+  const bool capped = EXT && a.cap_in != 0.f;
+  const float cin = a.scale_log2 < 0.f ? -a.cap_in : a.cap_in;
+
+  const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + h * a.q.sh;
+  const uint16_t* kb = a.k.p + s * a.k.sb + (int64_t)(sg.k_row0 + kofs) * a.k.sn + kvh * a.k.sh;
+  const uint16_t* vb = a.v.p + s * a.v.sb + (int64_t)(sg.k_row0 + kofs) * a.v.sn + kvh * a.v.sh;
 
   // Q fragments of this lane's row (rows past the segment's end read its
   // first row: their results are never stored)
@@ -91,13 +99,13 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
     const int r0 = tt * BN + 8 * w;
     const uint16_t* p[8];
     uint32_t m[8];
-    if (r0 + 8 <= lk) {
+    if (r0 + 8 <= lke) {
       p[0] = base + (int64_t)r0 * sn;
 #pragma unroll
       for (int i = 1; i < 8; ++i) p[i] = p[i - 1] + sn;
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = base + (int64_t)min(r0 + i, lk - 1) * sn;
+      for (int i = 0; i < 8; ++i) p[i] = base + (int64_t)min(r0 + i, lke - 1) * sn;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) m[i] = lds + (uint32_t)(((tt & 1) * BN + 8 * w + i) * LS * 2);
@@ -119,15 +127,17 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
 
   // softmax of the scores of tile tt, in place (scale, mask, lazy max, exp2,
   // row sum, bf16 P^T fragments), split into steps so the pipelined iteration can
-  // place one between MFMAs: steps 0-15 scale and mask, 16 the row max, 17-32
-  // exp2, 33-34 pack.
+  // place one between MFMAs: steps 0-15 scale (or softcap) and mask, 16 the
+  // row max, 17-32 exp2, 33-34 pack.
   float mx = kNegInf, m_use = 0.f;
   auto sm_step = [&](int c, f32x16& sc, int tt, frag8* pf) {
     if (c < 16) {
       const int r = c;
-      const int key = tt * BN + (r >> 2) * 8 + half * 4 + (r & 3);
-      const bool vis = key < lk && (!CAUSAL || key <= row + shift);
-      sc[r] = vis ? sc[r] * a.scale_log2 : kNegInf;
+      const int key = kofs + tt * BN + (r >> 2) * 8 + half * 4 + (r & 3);
+      bool vis = key < lk && (!CAUSAL || key <= row + shift);
+      if (EXT && win > 0) vis = vis && key > row + shift - win;
+      const float x = EXT && capped ? a.cap_out * fast_tanh(cin * sc[r]) : sc[r] * a.scale_log2;
+      sc[r] = vis ? x : kNegInf;
       mx = c == 0 ? sc[r] : fmaxf(mx, sc[r]);
     } else if (c == 16) {
       mx = fmaxf(mx, xor32(mx));
@@ -235,9 +245,9 @@ __global__ void __launch_bounds__(256, 1) attn_fwd_wide_kernel(const FwdArgs a) 
         mfma_a(o[(c >> 1) & 15], fr[c], pf_prev[c >> 5]);
         const int j = c >> 1, i = j & 7;
         if (j < 8)
-          dma16m(kb + (int64_t)min(rk0 + i, lk - 1) * a.k.sn, loff, mk0 + (uint32_t)(i * KS * 2));
+          dma16m(kb + (int64_t)min(rk0 + i, lke - 1) * a.k.sn, loff, mk0 + (uint32_t)(i * KS * 2));
         else if (j < 16)
-          dma16m(vb + (int64_t)min(rv0 + i, lk - 1) * a.v.sn, loff, mv0 + (uint32_t)(i * VS * 2));
+          dma16m(vb + (int64_t)min(rv0 + i, lke - 1) * a.v.sn, loff, mv0 + (uint32_t)(i * VS * 2));
       } else {
         s_next = mfma32(fr[c], qf[c >> 1], s_next);
       }

@@ -12,7 +12,8 @@ import ctypes as C
 import numpy as np
 import torch
 
-from ._lib import ATTN_BF16, ATTN_DQ_ACCUMULATE, ATTN_F16, ATTN_F32, check, i64_array, load
+from ._lib import (ATTN_BF16, ATTN_DQ_ACCUMULATE, ATTN_F16, ATTN_F32, AttnExt, check, i64_array,
+                   load)
 
 # element types of q, k, v, out, dout and the gradients (one per call)
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -106,9 +107,28 @@ def version() -> int:
 # ---------------------------------------------------------------------------
 # dense [B, H, N, D]
 # ---------------------------------------------------------------------------
-def fwd_dense(q, k, v, scale: float, causal: bool, out=None, lse=None):
+def _ext(window, softcap):
+    """attn_ext pointer for the _ex entry points, or None for the plain call."""
+    window, softcap = int(window), float(softcap)
+    if window == 0 and softcap == 0.0:
+        return None
+    return C.pointer(AttnExt(window, softcap))
+
+
+def _call(lib, name, ext, args, tail):
+    """Call the plain entry point, or its _ex form with ext inserted after the
+    arguments `args` (the causal flag is their last element)."""
+    if ext is None:
+        return getattr(lib, name)(*args, *tail)
+    return getattr(lib, name + "_ex")(*args, ext, *tail)
+
+
+def fwd_dense(q, k, v, scale: float, causal: bool, out=None, lse=None, window: int = 0,
+              softcap: float = 0.0):
     """out [B, Hq, Nq, Dv] bf16 and lse [B, Hq, Nq] fp32 (natural log). out / lse
-    may be given (out as any view with a unit last stride, lse contiguous)."""
+    may be given (out as any view with a unit last stride, lse contiguous).
+    window > 0 (causal only): each query sees its `window` most recent keys;
+    softcap > 0: scores become softcap * tanh(score / softcap)."""
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     dev, dt = _need_gpu_half(q=q, k=k, v=v)
     out = _output(out, (B, Hq, Nq, Dv), dt, dev, "out")
@@ -118,19 +138,23 @@ def fwd_dense(q, k, v, scale: float, causal: bool, out=None, lse=None):
     lib = load()
     args = (_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, Dqk, Dv,
             strides, float(scale), int(bool(causal)))
+    ext = _ext(window, softcap)
     need = C.c_size_t(0)
-    check(lib.attn_fwd_dense(*args, None, C.byref(need), _stream(q)), "attn_fwd_dense")
+    check(_call(lib, "attn_fwd_dense", ext, args, (None, C.byref(need), _stream(q))),
+          "attn_fwd_dense")
     ws = _workspace(need.value, dev)
     have = C.c_size_t(ws.numel())
-    check(lib.attn_fwd_dense(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_fwd_dense")
+    check(_call(lib, "attn_fwd_dense", ext, args, (_ptr(ws), C.byref(have), _stream(q))),
+          "attn_fwd_dense")
     return out, lse
 
 
 def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate=None,
-              dq=None, dk=None, dv=None):
+              dq=None, dk=None, dv=None, window: int = 0, softcap: float = 0.0):
     """(dq, dk, dv) from the caller's out/lse; dk/dv have Hkv heads.
     dq_accumulate: an existing dq tensor to add this call's dq into.
-    dq / dk / dv: optional output views (unit last stride)."""
+    dq / dk / dv: optional output views (unit last stride).
+    window / softcap: as given to the forward that produced out/lse."""
     B, Hq, Hkv, Nq, Nk, Dqk, Dv = _dense_shapes(q, k, v)
     if tuple(out.shape) != (B, Hq, Nq, Dv) or tuple(dout.shape) != (B, Hq, Nq, Dv):
         raise ValueError("out/dout must be [B, Hq, Nq, Dv]")
@@ -156,12 +180,15 @@ def bwd_dense(dout, q, k, v, out, lse, scale: float, causal: bool, dq_accumulate
     lib = load()
     args = (_DTYPES[dt], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
             _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, Dqk, Dv, strides, float(scale),
-            int(bool(causal)), flags)
+            int(bool(causal)))
+    ext = _ext(window, softcap)
     need = C.c_size_t(0)
-    check(lib.attn_bwd_dense(*args, None, C.byref(need), _stream(q)), "attn_bwd_dense")
+    check(_call(lib, "attn_bwd_dense", ext, args, (flags, None, C.byref(need), _stream(q))),
+          "attn_bwd_dense")
     ws = _workspace(need.value, dev)
     have = C.c_size_t(ws.numel())
-    check(lib.attn_bwd_dense(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_bwd_dense")
+    check(_call(lib, "attn_bwd_dense", ext, args, (flags, _ptr(ws), C.byref(have), _stream(q))),
+          "attn_bwd_dense")
     return dq, dk, dv
 
 
@@ -175,9 +202,10 @@ def _cu(cu, dev):
 
 
 def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool,
-               out=None, lse=None):
+               out=None, lse=None, window: int = 0, softcap: float = 0.0):
     """out [Tq, Hq, Dv] bf16 and lse [Hq, Tq] fp32 (natural log). out / lse may
-    be given (out as any view with a unit last stride, lse contiguous)."""
+    be given (out as any view with a unit last stride, lse contiguous).
+    window / softcap: as in fwd_dense, per segment."""
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if cu_q.numel() != cu_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
@@ -190,11 +218,14 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal
     args = (_DTYPES[dt], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _cu(cu_q, dev),
             _cu(cu_k, dev), cu_q.numel() - 1, int(max_q), int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv,
             strides, float(scale), int(bool(causal)))
+    ext = _ext(window, softcap)
     need = C.c_size_t(0)
-    check(lib.attn_fwd_varlen(*args, None, C.byref(need), _stream(q)), "attn_fwd_varlen")
+    check(_call(lib, "attn_fwd_varlen", ext, args, (None, C.byref(need), _stream(q))),
+          "attn_fwd_varlen")
     ws = _workspace(need.value, dev)
     have = C.c_size_t(ws.numel())
-    check(lib.attn_fwd_varlen(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_fwd_varlen")
+    check(_call(lib, "attn_fwd_varlen", ext, args, (_ptr(ws), C.byref(have), _stream(q))),
+          "attn_fwd_varlen")
     return out, lse
 
 
@@ -223,9 +254,11 @@ def fwd_varlen_noalloc(q, k, v, cu_q, cu_k, max_q: int, max_k: int, scale: float
 
 
 def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float,
-               causal: bool, dq_accumulate=None, dq=None, dk=None, dv=None):
+               causal: bool, dq_accumulate=None, dq=None, dk=None, dv=None, window: int = 0,
+               softcap: float = 0.0):
     """(dq [Tq,Hq,Dqk], dk [Tk,Hkv,Dqk], dv [Tk,Hkv,Dv]) from the caller's out/lse.
-    dq / dk / dv: optional output views (unit last stride)."""
+    dq / dk / dv: optional output views (unit last stride).
+    window / softcap: as given to the forward that produced out/lse."""
     Tq, Tk, Hq, Hkv, Dqk, Dv = _varlen_shapes(q, k, v)
     if tuple(out.shape) != (Tq, Hq, Dv) or tuple(dout.shape) != (Tq, Hq, Dv):
         raise ValueError("out/dout must be [Tq, Hq, Dv]")
@@ -253,12 +286,15 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q: int, max_k: int, scal
     lib = load()
     args = (_DTYPES[dt], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq),
             _ptr(dk), _ptr(dv), _cu(cu_q, dev), _cu(cu_k, dev), cu_q.numel() - 1, int(max_q),
-            int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale), int(bool(causal)), flags)
+            int(max_k), Tq, Tk, Hq, Hkv, Dqk, Dv, strides, float(scale), int(bool(causal)))
+    ext = _ext(window, softcap)
     need = C.c_size_t(0)
-    check(lib.attn_bwd_varlen(*args, None, C.byref(need), _stream(q)), "attn_bwd_varlen")
+    check(_call(lib, "attn_bwd_varlen", ext, args, (flags, None, C.byref(need), _stream(q))),
+          "attn_bwd_varlen")
     ws = _workspace(need.value, dev)
     have = C.c_size_t(ws.numel())
-    check(lib.attn_bwd_varlen(*args, _ptr(ws), C.byref(have), _stream(q)), "attn_bwd_varlen")
+    check(_call(lib, "attn_bwd_varlen", ext, args, (flags, _ptr(ws), C.byref(have), _stream(q))),
+          "attn_bwd_varlen")
     return dq, dk, dv
 
 

@@ -99,6 +99,9 @@ hipError_t launch_dkdv(const BwdArgs& a, bool causal, bool ext, unsigned grid, h
   } else if constexpr (kPipe && DQK == 128) {
     const hipError_t e = launch_dkdv_roles(a, causal, grid, st);
     if (e != hipSuccess) return e;
+  } else if constexpr (DQK == 192 && DV == 128 && DS == 1 && NWK == 4) {
+    const hipError_t e = launch_dkdv_roles192(a, causal, grid, st);
+    if (e != hipSuccess) return e;
   } else if constexpr (kPipe) {
     if (causal)
       hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, true>), dim3(grid), dim3(256), 0, st, a);

@@ -139,6 +139,7 @@ void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int
 // dK/dV pass of head dim 128 with split wave roles (attn_bwd_roles.hip);
 // grid = (128-key blocks + segments) * Hkv.
 hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
+hipError_t launch_dkdv_roles192(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
 
 // Two-phase backward (the head-dim pairs bwd_uses_tiles names): lists,
 // delta, scores, products.
@@ -169,6 +170,7 @@ void bwd_prepare(BwdArgs& a, int dv, bool causal, int nseg, int Hq, int Hkv, int
 // dK/dV pass of head dim 128 with split wave roles (attn_bwd_roles.hip);
 // grid = (128-key blocks + segments) * Hkv.
 hipError_t launch_dkdv_roles(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
+hipError_t launch_dkdv_roles192(const BwdArgs& a, bool causal, unsigned grid, hipStream_t st);
 
 // Two-phase backward (the head-dim pairs bwd_uses_tiles names): lists,
 // delta, scores, products.

@@ -149,7 +149,13 @@ int attn_fwd_varlen_noalloc(int dtype, const void* q, const void* k, const void*
  * q-heads of one launch pair (the dK/dV pass stores them, the dQ pass
  * multiplies them by K instead of recomputing S and dP), at most
  * ATTN_BWD_DS_MIB MiB (environment variable, default 8192; 0 turns the store
- * off); when one GQA group's blocks exceed it, the dQ pass recomputes. */
+ * off); when one GQA group's blocks exceed it, the dQ pass recomputes.
+ * Head dims 256 and 512 (two-phase backward): the workspace holds the bf16 P
+ * and dS blocks of as many 256-query row slots as fit in ATTN_BWD_TILES_MIB
+ * MiB (environment variable, default 8192; at least one slot, whose size
+ * grows with the key length only); more slots run as consecutive chunks,
+ * and the workspace then also holds fp32 dK/dV accumulators (4 bytes x key
+ * rows x Hkv x (Dqk + Dv)). The workspace size query reports the total. */
 int attn_bwd_dense(int dtype, const void* dout, const void* q, const void* k, const void* v,
                    const void* out, const float* lse, void* dq, void* dk, void* dv, int B,
                    int Hq, int Hkv, int Nq, int Nk, int Dqk, int Dv, const int64_t* strides,

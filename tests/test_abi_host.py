@@ -191,6 +191,28 @@ def test_window_and_softcap_argument_checks(lib):
             assert lib.attn_last_error().decode()
 
 
+def test_two_phase_workspace_is_bounded_by_its_budget(lib, monkeypatch):
+    """Head dims 256/512 keep P and dS blocks for as many 256-query row slots
+    as ATTN_BWD_TILES_MIB allows: under a budget the workspace grows with the
+    sequence length (one slot's blocks plus fp32 dK/dV rows), not with its
+    square; without one it holds every slot (quadratic)."""
+    def size(N):
+        s = _lib.i64_array([N * 512 * 16, N * 512, 512] * 8)
+        need = C.c_size_t(0)
+        st = lib.attn_bwd_dense(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 8,
+                                N, N, 512, 512, s, 0.1, 1, 0, None, C.byref(need), None)
+        assert st == 0
+        return need.value
+    monkeypatch.setenv("ATTN_BWD_TILES_MIB", "64")
+    small, big = size(8192), size(32768)
+    assert big < 6 * small  # 4x the length: linear growth (quadratic would be 16x)
+    # one slot of 32768 keys: 2 x 128 key blocks x 16 heads x 128 KB = 512 MiB,
+    # over the 64 MiB budget: the store still holds that one slot
+    assert big >= 2 * 128 * 16 * 131072
+    monkeypatch.setenv("ATTN_BWD_TILES_MIB", str(1 << 20))
+    assert size(32768) > 12 * size(8192)
+
+
 def _cpu(*shape):
     import torch
     return torch.zeros(shape, dtype=torch.bfloat16)

@@ -824,6 +824,21 @@ def test_backward_ds_store_modes(vca, monkeypatch, dqk, dv):
 
 
 
+@pytest.mark.parametrize("dqk,dv", [(256, 256), (512, 512)])
+def test_two_phase_backward_in_chunks(vca, monkeypatch, dqk, dv):
+    """Head dims 256/512 under a small ATTN_BWD_TILES_MIB: the P/dS stores
+    hold one (or two) 256-query row slots, the passes run once per chunk of
+    slots and dK/dV meet in fp32 across the chunks. Gradients match the
+    oracle, varlen and dense, causal and not."""
+    lens = [1, 37, 200, 129, 64, 600]
+    for mib in ("1", "8"):
+        monkeypatch.setenv("ATTN_BWD_TILES_MIB", mib)
+        run_varlen(vca, lens, lens, 4, 2, dqk, dv, True, seed=401 + dqk)
+        run_varlen(vca, [5, 0, 130, 70, 0, 3, 33], [9, 40, 100, 70, 12, 0, 65], 4, 4, dqk, dv,
+                   False, seed=403 + dqk)
+        run_dense(vca, 2, 4, 2, 300, 520, dqk, dv, True, seed=405 + dqk)
+
+
 # ---------------------------------------------------------------- fp16
 @pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
 @pytest.mark.parametrize("causal", [True, False])

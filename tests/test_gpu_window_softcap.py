@@ -136,6 +136,15 @@ def test_window_backward_store_modes(vca, monkeypatch, dqk, dv):
                    softcap=2.0)
 
 
+@pytest.mark.parametrize("dqk,dv", [(256, 256), (512, 512)])
+def test_window_two_phase_in_chunks(vca, monkeypatch, dqk, dv):
+    """The two-phase backward run in chunks of 256-query row slots (a 1 MiB
+    store budget): the window's block ranges meet the chunk ranges."""
+    monkeypatch.setenv("ATTN_BWD_TILES_MIB", "1")
+    lens = [3, 700, 260]
+    run_varlen(vca, lens, lens, 4, 2, dqk, dv, True, seed=1350 + dqk, window=300, softcap=2.0)
+
+
 def test_window_fp16(vca):
     lens = [3, 150, 333]
     for dqk, dv in DIMS:

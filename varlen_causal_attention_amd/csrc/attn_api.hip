@@ -219,9 +219,11 @@ bool vca::head_dims_supported(int dqk, int dv) {
          (dqk == 256 && dv == 256) || (dqk == 512 && dv == 512);
 }
 
-size_t vca::ds_budget_bytes() {
-  const char* e = std::getenv("ATTN_BWD_DS_MIB");
-  long long mib = 8192;
+namespace {
+// A MiB count from the environment (non-negative integer), else the default.
+size_t env_mib(const char* name, long long dflt) {
+  const char* e = std::getenv(name);
+  long long mib = dflt;
   if (e && *e) {
     char* end = nullptr;
     const long long v = std::strtoll(e, &end, 10);
@@ -229,6 +231,10 @@ size_t vca::ds_budget_bytes() {
   }
   return (size_t)mib << 20;
 }
+}  // namespace
+
+size_t vca::ds_budget_bytes() { return env_mib("ATTN_BWD_DS_MIB", 8192); }
+size_t vca::tiles_budget_bytes() { return env_mib("ATTN_BWD_TILES_MIB", 8192); }
 
 
 extern "C" {

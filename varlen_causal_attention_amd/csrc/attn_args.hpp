@@ -81,6 +81,17 @@ struct BwdArgs {
   int tile_nkb;        // key tiles per row slot
   int tile_nqb_dense;  // dense: query tiles per batch; 0 for varlen
   int nq_items, nk_items;  // list capacities (grid sizes) of the two-phase passes
+  // The store holds the row slots slot_lo .. slot_hi - 1 of one chunk (slot
+  // s at (s - slot_lo)); the passes of a chunk touch only those query
+  // blocks. acc_mode: 0 one chunk, dK/dV written directly; 1 first chunk,
+  // 2 middle chunk, 3 last chunk: the dK/dV sums of the chunk go to
+  // (1: =, 2: +=) the fp32 rows acc_dk / acc_dv ([key row][kv-head][D],
+  // key row = batch * Nk + segment row), and the last chunk writes acc +
+  // its sums to dk / dv.
+  int slot_lo, slot_hi;
+  int acc_mode;
+  float* acc_dk;
+  float* acc_dv;
   // kv-heads of this launch of a dK/dV pass: kvh0 .. kvh0 + kvh_n - 1
   int kvh0, kvh_n;
   // dS store (head dims 128 and 192/128): when ds is set, the dK/dV pass

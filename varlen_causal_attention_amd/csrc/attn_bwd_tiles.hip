@@ -23,35 +23,49 @@ hipError_t bwd_tiles(BwdArgs a, int nseg, int Hq, int Hkv, int max_q, int64_t q_
   const unsigned k_items = (unsigned)((k_rows + kBlk - 1) / kBlk + nseg);
   a.nq_items = (int)q_items;
   a.nk_items = (int)k_items;
-  if (q_rows > 0 && k_rows > 0) {
-    TimedLaunch timer("attn_bwd_scores", st);
-    // the left window and the softcap (ext) take their own scores kernel;
-    // the product passes read the window's block ranges at run time
-    const dim3 grid(xcd_grid<kScoreSplit>(q_items * Hq));
-    if (a.cap_in != 0.f)
-      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 2>), grid, dim3(kNT), 0, st, a);
-    else if (a.window > 0)
-      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 1>), grid, dim3(kNT), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>), grid, dim3(kNT), 0, st, a);
-  }
-  if (k_rows > 0) {
-    TimedLaunch timer("attn_bwd_dkdv_tiles", st);
-    if constexpr (DQK == DV) {
-      // dV and dK blocks of one launch, side by side
-      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 2>),
-                         dim3(xcd_grid<2 * (DV / OBV)>(k_items * Hkv)), dim3(kNT), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 0>),
-                         dim3(xcd_grid<DV / OBV>(k_items * Hkv)), dim3(kNT), 0, st, a);
-      hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DQK, OBQ, CAUSAL, 1>),
-                         dim3(xcd_grid<DQK / OBQ>(k_items * Hkv)), dim3(kNT), 0, st, a);
+  // The P/dS stores hold wl.tile_chunk_slots row slots: the three passes run
+  // once per chunk of slots; with several chunks the dK/dV sums of each meet
+  // in fp32 (first chunk stores, middle ones add, the last one writes dk/dv).
+  const int64_t chunk = wl.tile_chunk_slots > 0 ? wl.tile_chunk_slots : tg.slots;
+  const int64_t nchunks = tg.slots > 0 ? (tg.slots + chunk - 1) / chunk : 1;
+  a.acc_dk = nchunks > 1 ? reinterpret_cast<float*>(w + wl.tile_acc_dk) : nullptr;
+  a.acc_dv = nchunks > 1 ? reinterpret_cast<float*>(w + wl.tile_acc_dv) : nullptr;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    a.slot_lo = (int)(c * chunk);
+    a.slot_hi = (int)min(tg.slots, (c + 1) * chunk);
+    a.acc_mode = nchunks == 1 ? 0 : (c == 0 ? 1 : (c + 1 < nchunks ? 2 : 3));
+    if (q_rows > 0 && k_rows > 0) {
+      TimedLaunch timer("attn_bwd_scores", st);
+      // the left window and the softcap (ext) take their own scores kernel;
+      // the product passes read the window's block ranges at run time
+      const dim3 grid(xcd_grid<kScoreSplit>(q_items * Hq));
+      if (a.cap_in != 0.f)
+        hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 2>), grid, dim3(kNT), 0, st, a);
+      else if (a.window > 0)
+        hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL, 1>), grid, dim3(kNT), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_scores_kernel<DQK, DV, CAUSAL>), grid, dim3(kNT), 0, st, a);
     }
-  }
-  if (q_rows > 0) {
-    TimedLaunch timer("attn_bwd_dq_tiles", st);
-    hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<DQK, OBQ, CAUSAL>),
-                       dim3(xcd_grid<DQK / OBQ>(q_items * Hq)), dim3(kNT), 0, st, a);
+    if (k_rows > 0) {
+      TimedLaunch timer("attn_bwd_dkdv_tiles", st);
+      if constexpr (DQK == DV) {
+        // dV and dK blocks of one launch, side by side
+        hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 2>),
+                           dim3(xcd_grid<2 * (DV / OBV)>(k_items * Hkv)), dim3(kNT), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DV, OBV, CAUSAL, 0>),
+                           dim3(xcd_grid<DV / OBV>(k_items * Hkv)), dim3(kNT), 0, st, a);
+        hipLaunchKernelGGL((attn_bwd_dkdv_tiles_kernel<DQK, OBQ, CAUSAL, 1>),
+                           dim3(xcd_grid<DQK / OBQ>(k_items * Hkv)), dim3(kNT), 0, st, a);
+      }
+    }
+    if (q_rows > 0) {
+      TimedLaunch timer("attn_bwd_dq_tiles", st);
+      hipLaunchKernelGGL((attn_bwd_dq_tiles_kernel<DQK, OBQ, CAUSAL>),
+                         dim3(xcd_grid<DQK / OBQ>(q_items * Hq)), dim3(kNT), 0, st, a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -50,8 +50,9 @@ __device__ __forceinline__ int64_t blk_slot(const BwdArgs& a, const SegGeom& g, 
   return a.tile_nqb_dense ? (int64_t)s * a.tile_nqb_dense + qb
                           : (int64_t)(g.q_row0 / kBlk) + s + qb;
 }
+// the store holds the slots of one chunk, slot_lo .. slot_hi - 1
 __device__ __forceinline__ int64_t blk_base(const BwdArgs& a, int64_t slot, int kb, int h) {
-  return ((slot * a.tile_nkb + kb) * a.Hq + h) * kBlkElems;
+  return (((slot - a.slot_lo) * a.tile_nkb + kb) * a.Hq + h) * kBlkElems;
 }
 // key blocks the rows of the query block starting at q0 can see (capped by
 // the store's width)
@@ -225,6 +226,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_scores_kernel(const BwdArgs a
   const int nkt = ext - kf > part ? (ext - kf - part + kScoreSplit - 1) / kScoreSplit : 0;
   if (nkt == 0) return;
   const int64_t slot = blk_slot(a, sg, s, st.y);
+  if (slot < a.slot_lo || slot >= a.slot_hi) return;  // another chunk's query block
 
   // lse*log2(e) and delta of the lane's four query columns
   float l2[4], dl[4];
@@ -444,9 +446,12 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   if (k0 >= sg.lk) return;
   const int lq = sg.lq;
   const int qb0 = blk_col_start(sg, kb, CAUSAL);
-  // query blocks qb0 .. nqb-1 see this key block (fewer with a left window)
-  const int nqb = blk_col_end(sg, kb, CAUSAL ? a.window : 0);
-  const int per = kb < a.tile_nkb && nqb > qb0 ? (nqb - qb0) * CPB : 0;
+  // query blocks qb0 .. nqb-1 see this key block (fewer with a left window);
+  // this chunk holds those whose row slot lies in [slot_lo, slot_hi)
+  const int64_t slot0 = blk_slot(a, sg, s, 0);
+  const int qlo = (int)max((int64_t)blk_col_start(sg, kb, CAUSAL), a.slot_lo - slot0);
+  const int nqb = (int)min((int64_t)blk_col_end(sg, kb, CAUSAL ? a.window : 0), a.slot_hi - slot0);
+  const int per = kb < a.tile_nkb && nqb > qlo ? (nqb - qlo) * CPB : 0;
   const int total = a.G * per;
 
   // field-wise selects (a runtime choice between whole View structs sends
@@ -501,19 +506,31 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   uint16_t* op = is_dk ? a.dk.p : a.dv.p;
   const int64_t osb = is_dk ? a.dk.sb : a.dv.sb, osh = is_dk ? a.dk.sh : a.dv.sh;
   const int64_t osn = is_dk ? a.dk.sn : a.dv.sn;
+  float* accp = is_dk ? a.acc_dk : a.acc_dv;
 #pragma unroll
   for (int u = 0; u < S::CT; ++u) {
     const int key = k0 + key_perm(S::RN * wn + 32 * u + col);
     if (key >= sg.lk) continue;
     uint16_t* orow = op + s * osb + (int64_t)(sg.k_row0 + key) * osn + hk * osh + dh * OB;
+    // fp32 accumulator row of this key when the backward runs in chunks
+    float* arow = accp + (((int64_t)s * a.Nk + sg.k_row0 + key) * a.Hkv + hk) * DOUT + dh * OB;
 #pragma unroll
     for (int t = 0; t < S::RT; ++t)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        elem4 v4;
+        const int c0 = S::RM * wm + 32 * t + rr * 8 + half * 4;
+        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = (elem_t)(acc[t][u][rr * 4 + e] * mul);
-        *reinterpret_cast<elem4*>(orow + S::RM * wm + 32 * t + rr * 8 + half * 4) = v4;
+        for (int e = 0; e < 4; ++e) v[e] = acc[t][u][rr * 4 + e] * mul;
+        if (a.acc_mode >= 2) v += *reinterpret_cast<const f32x4*>(arow + c0);
+        if (a.acc_mode == 1 || a.acc_mode == 2) {
+          *reinterpret_cast<f32x4*>(arow + c0) = v;
+        } else {
+          elem4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (elem_t)v[e];
+          *reinterpret_cast<elem4*>(orow + c0) = v4;
+        }
       }
   }
 }
@@ -552,6 +569,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dq_tiles_kernel(const BwdArgs
   const int kf = min(kext, blk_row_first(sg, q0, CAUSAL ? a.window : 0));
   const int total = (kext - kf) * CPB;
   const int64_t slot = blk_slot(a, sg, s, st.y);
+  if (slot < a.slot_lo || slot >= a.slot_hi) return;  // another chunk's query block
   const uint16_t* kbp =
       a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh + dh * OB;
   auto issue = [&](int it, int stage) {

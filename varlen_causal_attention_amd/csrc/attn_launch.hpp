@@ -77,9 +77,16 @@ inline bool bwd_can_store_ds(int dqk, int dv) {
 // one launch; when even one GQA group's blocks exceed the budget the dQ pass
 // recomputes S and dP instead.
 size_t ds_budget_bytes();
+// Byte budget of the two-phase P and dS block stores: ATTN_BWD_TILES_MIB
+// (MiB), default 8192. The stores hold the blocks of as many 256-query row
+// slots as fit (at least one); more slots run as consecutive chunks whose
+// dK/dV sums meet in fp32 accumulators.
+size_t tiles_budget_bytes();
 struct BwdWorkspace {
   size_t list_q, list_k, lse2, tile_p, tile_ds, ds, total;
   int ds_kv_chunk;  // kv-heads per dK/dV + dQ launch pair of the dS path; 0: no dS store
+  int64_t tile_chunk_slots;  // row slots per chunk of the two-phase backward
+  size_t tile_acc_dk, tile_acc_dv;  // fp32 dK / dV accumulators (several chunks only)
 };
 inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int Hkv, int64_t q_rows, int64_t k_rows,
                                   int nseg, const TileGeom& tg) {
@@ -103,10 +110,23 @@ inline BwdWorkspace bwd_workspace(int dqk, int dv, int Hq, int Hkv, int64_t q_ro
     }
   }
   if (bwd_uses_tiles(dqk, dv)) {
-    const size_t blocks = sizeof(uint16_t) * kBlockRows * kBlockRows * (size_t)tg.slots *
-                          (size_t)tg.nkb * (size_t)Hq;
+    // one row slot's P (or dS) blocks over every key block and q-head
+    const size_t per_slot =
+        sizeof(uint16_t) * kBlockRows * kBlockRows * (size_t)tg.nkb * (size_t)Hq;
+    int64_t chunk = tg.slots;
+    if (per_slot > 0) {
+      const int64_t fit = (int64_t)(tiles_budget_bytes() / (2 * per_slot));
+      chunk = fit < 1 ? 1 : (fit < tg.slots ? fit : tg.slots);
+    }
+    w.tile_chunk_slots = chunk;
+    const size_t blocks = per_slot * (size_t)chunk;
     w.tile_ds = w.tile_p + blocks;
     w.total = w.tile_ds + blocks;
+    if (chunk < tg.slots) {
+      w.tile_acc_dk = w.total;
+      w.tile_acc_dv = w.tile_acc_dk + align256(sizeof(float) * (size_t)k_rows * Hkv * dqk);
+      w.total = w.tile_acc_dv + align256(sizeof(float) * (size_t)k_rows * Hkv * dv);
+    }
   } else {
     w.total = w.tile_p;
   }

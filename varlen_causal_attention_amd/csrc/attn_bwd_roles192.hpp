@@ -38,29 +38,6 @@ constexpr int kR2TileA = kRBQ * kTileD;           // Q columns 0..127 of a step
 constexpr int kR2TileB = kRBQ * 64;               // Q columns 128..191
 constexpr int kR2TileQ = kR2TileA + kR2TileB;     // 6144 elements (12 KB)
 
-__device__ __forceinline__ int sw64(int r) {
-  const int x = (r >> 1) & 7;
-  return ((x & 1) << 2) | (x >> 1);
-}
-// element offset of piece u (8 elements) of row r in a 64-column block
-__device__ __forceinline__ int r64_off(int r, int u) { return r * 64 + ((u ^ sw64(r)) << 3); }
-__device__ __forceinline__ frag8 r64_row(const uint16_t* X, int r, int piece) {
-  return lds_frag(X + r64_off(r, piece));
-}
-// rtile_col's operand (head-dim column n0 + l%32, query rows k0 + 4h + j and
-// k0 + 8 + 4h + j) from a 64-column block
-__device__ __forceinline__ frag8 r64_col(const uint16_t* X, int k0, int n0, int lane) {
-  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
-  const int row = k0 + 4 * h + (s >> 2);
-  const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
-  typedef __attribute__((address_space(3))) uint16_t lds_u16;
-  const uint16_t* p0 = X + r64_off(row, c >> 3) + (c & 7);
-  const uint16_t* p1 = X + r64_off(row + 8, c >> 3) + (c & 7);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
-  return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 __device__ __forceinline__ void agpr_results_ready(f32x16 (&acc)[6][2]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[1][0]), "+a"(acc[1][1]),

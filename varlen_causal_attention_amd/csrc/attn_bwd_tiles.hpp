@@ -445,7 +445,6 @@ __global__ void __launch_bounds__(kNT, 1) attn_bwd_dkdv_tiles_kernel(const BwdAr
   const int k0 = kb * kBlk;
   if (k0 >= sg.lk) return;
   const int lq = sg.lq;
-  const int qb0 = blk_col_start(sg, kb, CAUSAL);
   // query blocks qb0 .. nqb-1 see this key block (fewer with a left window);
   // this chunk holds those whose row slot lies in [slot_lo, slot_hi)
   const int64_t slot0 = blk_slot(a, sg, s, 0);

@@ -441,6 +441,35 @@ __device__ __forceinline__ frag8 rtile_col(const uint16_t* X, int k0, int n0, in
   return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// 64-column blocks (head-dim columns 128..191 of 192-wide rows) in 128-byte
+// rows: piece u of row r sits at u ^ sw64(r), sw64(r) = 4*(x%2) + x/2 with
+// x = (r/2) % 8. Two rows share one 256-byte bank line, so 16 consecutive
+// rows reading one piece cover all 64 banks when sw64 permutes the 8
+// positions within each row parity (it does); the transposing read (4 rows
+// x 4 pieces per 32 lanes) puts rows r and r+2 in different 4-piece halves
+// (sw64 differs in bit 2 between them), so it is free of conflicts as well.
+__device__ __forceinline__ int sw64(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+__device__ __forceinline__ int r64_off(int r, int u) { return r * 64 + ((u ^ sw64(r)) << 3); }
+__device__ __forceinline__ frag8 r64_row(const uint16_t* X, int r, int piece) {
+  return lds_frag(X + r64_off(r, piece));
+}
+// rtile_col's operand (head-dim column n0 + l%32, rows k0 + 4h + j and
+// k0 + 8 + 4h + j) from a 64-column block
+__device__ __forceinline__ frag8 r64_col(const uint16_t* X, int k0, int n0, int lane) {
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
+  const int row = k0 + 4 * h + (s >> 2);
+  const int c = n0 + 16 * (g & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint16_t* p0 = X + r64_off(row, c >> 3) + (c & 7);
+  const uint16_t* p1 = X + r64_off(row + 8, c >> 3) + (c & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
+  return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Workgroup -> (work item, q-head) for passes whose grid is items x H q-heads
 // (GQA group size G). Consecutive workgroup ids are dispatched to the 8 XCDs
 // in turn; when the kv heads divide evenly over the XCDs, XCD x gets every

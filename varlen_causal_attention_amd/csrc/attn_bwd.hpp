@@ -837,6 +837,24 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 // 4h..4h+3, 8+4h.. of every 16) matches on both sides. The pass is bound by
 // the dS bytes it reads from HBM.
 // ---------------------------------------------------------------------------
+// Staged dS block in LDS ([key][query position], 64-byte rows): piece p of
+// row r at position p ^ ds_swz(r).
+__device__ __forceinline__ int ds_swz(int r) { return (r >> 2) & 3; }
+// tr_frag's operand (query column n0 + l%32 with n0 = 0, key rows k0 + 4h + j
+// and k0 + 8 + 4h + j) from a staged dS block: the four rows one transposing
+// read covers per 32 lanes share the swizzle, so they still cover all banks.
+__device__ __forceinline__ frag8 ds_frag(const uint16_t* X, int k0, int lane) {
+  const int g = lane >> 4, s = lane & 15, h = lane >> 5;
+  const int row = k0 + 4 * h + (s >> 2);
+  const int c = 16 * (g & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint16_t* p0 = X + row * 32 + (((c >> 3) ^ ds_swz(row)) << 3) + (c & 7);
+  const uint16_t* p1 = X + (row + 8) * 32 + (((c >> 3) ^ ds_swz(row + 8)) << 3) + (c & 7);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u16*)p1));
+  return __builtin_bit_cast(frag8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int DQK, int NW, bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArgs a) {
   constexpr int NT = 64 * NW;
@@ -907,10 +925,13 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
     }
     // to keys x queries, row-major: lane l's fragment j goes to key l % 32,
     // query positions 16j + 8h .. +7 (queries in the order 0-3, 8-11, 4-7,
-    // 12-15 of every 16)
-    uint16_t* row = &sds[b][w][(lane & 31) * 32 + 8 * (lane >> 5)];
-    sts16(row, dr[0]);
-    sts16(row + 16, dr[1]);
+    // 12-15 of every 16), its 16-byte piece p of the 64-byte row at position
+    // p ^ ds_swz(row): 16 consecutive rows writing one piece then cover all
+    // 64 banks (rows of 64 bytes put four rows in one bank line)
+    const int r = lane & 31, sw = ds_swz(r);
+    uint16_t* row = &sds[b][w][r * 32];
+    sts16(row + (((lane >> 5) ^ sw) << 3), dr[0]);
+    sts16(row + (((2 + (lane >> 5)) ^ sw) << 3), dr[1]);
   };
 
   f32x16 acc[NDB];
@@ -932,7 +953,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_bwd_dq_ds_kernel(const BwdArg
     if (t >= kf_w && t < nkt_w && blk0 >= 0) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const frag8 bfr = tr_frag(sds[buf][w], 32, 16 * ks, 0, lane);
+        const frag8 bfr = ds_frag(sds[buf][w], 16 * ks, lane);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           acc[db] = mfma32(tr_frag(sk[buf], KS, 16 * ks, 32 * db, lane), bfr, acc[db]);

@@ -146,11 +146,28 @@ class Problem:
             o2, l2 = v.fwd_dense(d["q"], d["k_early"], d["v_early"], w.scale, False)
             v.zero_rows(o2, l2, self.pad)
             return o1.view(n, 1, w.Dv), l1.view(1, n), o2.view(n, 1, w.Dv), l2.view(1, n)
+        # the two chunks' forwards are independent: the earlier chunk's runs on
+        # a second stream (default priority) beside the local one, so the two
+        # small grids share the CUs instead of running one after the other
+        main = torch.cuda.current_stream()
+        side = self.side_stream()
+        rows, H = t["q"].shape[0], w.Hq
+        o2 = torch.empty((rows, H, w.Dv), dtype=self.dtype, device="cuda")
+        l2 = torch.empty((H, rows), dtype=torch.float32, device="cuda")
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            cq, ck, mq, mk = self.cross
+            v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False,
+                         out=o2, lse=l2)
         cq, ck, mq, mk = self.local
         o1, l1 = v.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
-        cq, ck, mq, mk = self.cross
-        o2, l2 = v.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq, ck, mq, mk, w.scale, False)
+        main.wait_stream(side)
         return o1, l1, o2, l2
+
+    def side_stream(self):
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream()
+        return self._side
 
     def bwd(self):
         v, w, t = self.vca, self.w, self.t
@@ -168,12 +185,27 @@ class Problem:
             _, dke, dve = v.bwd_dense(d["do"], d["q"], d["k_early"], d["v_early"], self.out,
                                       self.lse, w.scale, False, dq_accumulate=dq)
             return dq, dkl, dvl, dke, dve
+        # the two chunks' backwards run side by side as well (each a small
+        # grid); the earlier chunk's dq is then added into the local one's
+        # in fp32 (the library's row scatter-add over every row)
+        main = torch.cuda.current_stream()
+        side = self.side_stream()
+        rows = t["q"].shape[0]
+        dq2 = torch.empty_like(t["q"])
+        dke = torch.empty_like(t["k_early"])
+        dve = torch.empty_like(t["v_early"])
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            cq, ck, mq, mk = self.cross
+            v.bwd_varlen(t["do"], t["q"], t["k_early"], t["v_early"], self.out, self.lse, cq, ck,
+                         mq, mk, w.scale, False, dq=dq2, dk=dke, dv=dve)
         cq, ck, mq, mk = self.local
         dq, dkl, dvl = v.bwd_varlen(t["do"], t["q"], t["k_local"], t["v_local"], self.out,
                                     self.lse, cq, ck, mq, mk, w.scale, True)
-        cq, ck, mq, mk = self.cross
-        _, dke, dve = v.bwd_varlen(t["do"], t["q"], t["k_early"], t["v_early"], self.out,
-                                   self.lse, cq, ck, mq, mk, w.scale, False, dq_accumulate=dq)
+        main.wait_stream(side)
+        if getattr(self, "_all_rows", None) is None:
+            self._all_rows = torch.arange(rows, dtype=torch.int32, device="cuda")
+        v.scatter_rows(dq2, self._all_rows, dq.unsqueeze(0).transpose(1, 2), mode=2)
         return dq, dkl, dvl, dke, dve
 
     def step(self):

@@ -839,6 +839,35 @@ def test_two_phase_backward_in_chunks(vca, monkeypatch, dqk, dv):
         run_dense(vca, 2, 4, 2, 300, 520, dqk, dv, True, seed=405 + dqk)
 
 
+def test_bench_ring_step_runs_chunks_side_by_side(vca):
+    """bench.py's ring share step runs the local and the earlier chunk's
+    forward and backward on two streams and adds the earlier chunk's dq in
+    with the library's row scatter-add: the same out, lse, dk and dv
+    (bitwise) as the two chunks run one after the other, and the same dq up
+    to the one extra rounding of the earlier chunk's dq to bf16."""
+    import bench
+
+    p = bench.Problem(5)
+    dq, dkl, dvl, dke, dve = p.step()
+    out, lse = p.out.clone(), p.lse.clone()
+    t, w = p.t, p.w
+    cq, ck, mq, mk = p.local
+    o1, l1 = vca.fwd_varlen(t["q"], t["k_local"], t["v_local"], cq, ck, mq, mk, w.scale, True)
+    cq2, ck2, mq2, mk2 = p.cross
+    o2, l2 = vca.fwd_varlen(t["q"], t["k_early"], t["v_early"], cq2, ck2, mq2, mk2, w.scale, False)
+    _, rlse, rout = vca.merge(o1, l1, o2, l2, copy_dtype=torch.bfloat16)
+    rdq, rdkl, rdvl = vca.bwd_varlen(t["do"], t["q"], t["k_local"], t["v_local"], rout, rlse, cq,
+                                     ck, mq, mk, w.scale, True)
+    _, rdke, rdve = vca.bwd_varlen(t["do"], t["q"], t["k_early"], t["v_early"], rout, rlse, cq2,
+                                   ck2, mq2, mk2, w.scale, False, dq_accumulate=rdq)
+    torch.cuda.synchronize()
+    assert torch.equal(out, rout) and torch.equal(lse, rlse)
+    for a, b in ((dkl, rdkl), (dvl, rdvl), (dke, rdke), (dve, rdve)):
+        assert torch.equal(a, b)
+    d = (dq.float() - rdq.float()).abs().max().item()
+    assert d <= 2.0 ** -7 * rdq.float().abs().max().item(), f"dq differs by {d}"
+
+
 # ---------------------------------------------------------------- fp16
 @pytest.mark.parametrize("dqk,dv", [(64, 64), (128, 128), (192, 128), (256, 256), (512, 512)])
 @pytest.mark.parametrize("causal", [True, False])

@@ -89,7 +89,7 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
     if (a.G % 2 == 0) return fwd_dims<128, 128, 64, 1, 2, 1, true, 2>(a, causal, grid, st);
     return fwd_dims<128, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   }
-  if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 32, 1, 2, 2, true>(a, causal, grid, st);
+  if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 256 && dv == 256) return fwd_dims<256, 256, 64, 1, 2, 1, true>(a, causal, grid, st);
   return fwd_wide(a, causal, grid, st);
 }

@@ -69,11 +69,20 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * DS * HPW) : 0;
   constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NBUF == 2 && NG >= 1 &&
                        (NG % 4 == 0 || 4 % NG == 0) && NG * 4 * 4 * DS * HPW == BN * CB;
-  static_assert(DMA || HPW == 1, "head pairs load their tiles with global_load_lds");
-  static_assert(DMA || PF || NBUF == 1, "double buffering relies on the register prefetch");
+  // Split-K DMA mode (Dqk = 192, Dv = 128): the same direct loads, with K
+  // stored as a block of columns 0..127 in 256-byte rows (rtile_off) followed
+  // by a block of columns 128..191 in 128-byte rows (r64_off), and V as one
+  // block of 256-byte rows. Per wave and tile: BN/16 groups of 4 rows x 256
+  // bytes of K's first block and of V, BN/32 groups of 8 rows x 128 bytes of
+  // K's second block.
+  constexpr bool SPLITK =
+      DQK == 192 && DV == kTileD && NBUF == 2 && DS == 1 && HPW == 1 && BN % 32 == 0;
+  constexpr bool LDMA = DMA || SPLITK;  // tiles land in LDS by global_load_lds
+  static_assert(LDMA || HPW == 1, "head pairs load their tiles with global_load_lds");
+  static_assert(LDMA || PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int KBLK = BN * kTileD;  // elements per column block of a DMA tile
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * DQK : BN * KS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * DV : BN * VS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][LDMA ? BN * DQK : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][LDMA ? BN * DV : BN * VS];
   __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
@@ -163,12 +172,38 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
     }
   };
 
+  // split-K mode: tile tt into buffer tt & 1; the segment's last tile
+  // re-reads its last row for rows past the end (those keys are masked)
+  auto issue_split = [&](int tt) {
+    const int b = tt & 1, kt0 = tt * BN;
+    const bool full = kt0 + BN <= lk;
+#pragma unroll
+    for (int jj = 0; jj < BN / 16; ++jj) {
+      const int g = (BN / 16) * w + jj;  // rows 4g..4g+3 of K's first block and of V
+      const int r = kt0 + 4 * g + dl;
+      const int rr = full ? r : min(r, lk - 1);
+      const int pc = (p0 ^ (g & 3)) * 8;
+      dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][g * 512]));
+      dma16(vb + (int64_t)rr * a.v.sn + pc, lds_ptr(&sv[b][g * 512]));
+    }
+#pragma unroll
+    for (int jj = 0; jj < BN / 32; ++jj) {
+      const int g = (BN / 32) * w + jj;  // rows 8g..8g+7 of K's second block
+      const int rl = 8 * g + (lane >> 3);
+      const int rr = full ? kt0 + rl : min(kt0 + rl, lk - 1);
+      const int pc = kTileD + ((lane & 7) ^ sw64(rl)) * 8;
+      dma16(kb + (int64_t)rr * a.k.sn + pc, lds_ptr(&sk[b][KBLK + g * 512]));
+    }
+  };
+
   using KStage = TileStage<BN, DQK, NT>;
   using VStage = TileStage<BN, DV, NT>;
   KStage kst;
   VStage vst;
   if constexpr (DMA) {
     if (t0 < ntiles) issue_kv(t0);
+  } else if constexpr (SPLITK) {
+    if (t0 < ntiles) issue_split(t0);
   } else if (t0 < ntiles) {
     const int b0 = NBUF == 2 ? (t0 & 1) : 0;
     if (PF) {
@@ -196,10 +231,12 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   for (int t = t0; t < ntiles; ++t) {
     const int k0 = t * BN;
     const int buf = NBUF == 2 ? (t & 1) : 0;
-    if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
+    if constexpr (LDMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
     __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
     if constexpr (DMA) {
       if (t + 1 < ntiles) issue_kv(t + 1);
+    } else if constexpr (SPLITK) {
+      if (t + 1 < ntiles) issue_split(t + 1);
     } else if (NBUF == 2 && t + 1 < ntiles) {
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
@@ -221,11 +258,14 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int kbk = 0; kbk < NKB; ++kbk)
-          sacc[kbk] = mfma32(DMA ? rtile_row(&sk[buf][((ds * DR + ks * 16) / kTileD) * KBLK],
-                                             kbk * 32 + col, ((ds * DR + ks * 16) % kTileD) / 8 + half)
-                                 : lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 +
-                                                     ks * 16]),
-                             qf[ks], sacc[kbk]);
+          sacc[kbk] = mfma32(
+              SPLITK ? (ks < kTileD / 16
+                            ? rtile_row(&sk[buf][0], kbk * 32 + col, 2 * ks + half)
+                            : r64_row(&sk[buf][KBLK], kbk * 32 + col, 2 * (ks - kTileD / 16) + half))
+              : DMA ? rtile_row(&sk[buf][((ds * DR + ks * 16) / kTileD) * KBLK], kbk * 32 + col,
+                                ((ds * DR + ks * 16) % kTileD) / 8 + half)
+                    : lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 + ks * 16]),
+              qf[ks], sacc[kbk]);
       pipeline_mfma_reads<NKS * NKB, 4>();
     }
     if constexpr (DS > 1) {
@@ -315,7 +355,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          o[db] = mfma32(DMA ? rtile_col(&sv[buf][((ds * VR + db * 32) / kTileD) * KBLK], kk * 16,
+          o[db] = mfma32(LDMA ? rtile_col(&sv[buf][((ds * VR + db * 32) / kTileD) * KBLK], kk * 16,
                                          (ds * VR + db * 32) % kTileD, lane)
                              : tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane),
                          pf[kk], o[db]);

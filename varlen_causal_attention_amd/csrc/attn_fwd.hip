@@ -86,7 +86,7 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   const dim3 grid((unsigned)(items * Hq));
   if (dqk == 64 && dv == 64) return fwd_dims<64, 64, 64, 1, 2, 2, true>(a, causal, grid, st);
   if (dqk == 128 && dv == 128) {
-    if (a.G % 2 == 0) return fwd_dims<128, 128, 64, 1, 2, 1, true, 2>(a, causal, grid, st);
+    if (a.G % 2 == 0) return fwd_dims<128, 128, 128, 1, 2, 1, true, 2>(a, causal, grid, st);
     return fwd_dims<128, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
   }
   if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 1, 2, 2, true>(a, causal, grid, st);

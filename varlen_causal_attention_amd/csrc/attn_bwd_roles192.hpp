@@ -54,9 +54,11 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
   constexpr int KP = 32 * KT;     // keys per pair
   constexpr int NS = kRStages;    // Q/dO/lse/delta stages in LDS
   // hand-issued loads per wave and step: two 4-row slices of Q columns
-  // 0..127, one 8-row slice of columns 128..191, two 4-row slices of dO,
-  // 64 lse*log2(e) | delta values
-  constexpr int NDMA = 6;
+  // 0..127, one 8-row slice of columns 128..191, 64 lse*log2(e) | delta
+  // values, and in role 0 its pair's four 4-row slices of dO (role 1 also
+  // stores the dS blocks: the loads are split so both roles reach the
+  // barrier together)
+  constexpr int NDMA_R0 = 8, NDMA_R1 = 4;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[NS][kR2TileQ];
   __shared__ __attribute__((aligned(1024))) uint16_t sdo[NS][kRTile];
   // lse*log2(e) (waves 0, 1: query rows 0-15, 16-31) | delta (waves 2, 3)
@@ -93,38 +95,44 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
   // l%16 (global piece l%16 ^ swizzle). Q columns 128..191: slice w holds
   // rows 8w..8w+7, lane l row 8w + l/8 at stored piece l%8 (global piece
   // (l%8) ^ sw64(row)).
-  int arow[2], apiece[2];
-#pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int r = 4 * (2 * w + j2) + (lane >> 4);
-    arow[j2] = r;
-    apiece[j2] = ((lane & 15) ^ (((r & 3) << 2) | ((r >> 2) & 3))) * 8;
-  }
-  const int brow = 8 * w + (lane >> 3);
-  const int bpiece = kTileD + ((lane & 7) ^ sw64(brow)) * 8;
-  const float* ldsrc =
-      ((w & 3) < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + 16 * (w & 1) + (lane & 15);
-  auto issue = [&](int it) {
+  // (computed at each issue from a lane id the compiler cannot see through:
+  // held across the loop they would take registers this kernel does not
+  // have, and a reload from scratch waits for every load in flight)
+  auto issue = [&](int it, auto role_c) {
+    constexpr int R = decltype(role_c)::value;
     const int b = stage(it);
     const int hh = step_head(it), q0 = step_q0(it);
     const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + hh * a.q.sh;
     const uint16_t* db = a.dout.p + s * a.dout.sb + (int64_t)sg.q_row0 * a.dout.sn + hh * a.dout.sh;
     // rows past the segment's end (its last step) re-read its last row
     const bool tail = q0 + kRBQ > lq;
+    int ln = lane;
+    asm volatile("; lane" : "+v"(ln));
+    // a 4-row slice sl of Q columns 0..127 or of dO: lane row 4*sl + l/16,
+    // stored piece l%16 = global piece (l%16) ^ swizzle
+    auto slice = [&](const uint16_t* base, int64_t sn, uint16_t* dst, int sl) {
+      const int r = 4 * sl + (ln >> 4);
+      const int qi = tail ? min(q0 + r, lq - 1) : q0 + r;
+      const int pc = ((ln & 15) ^ (((r & 3) << 2) | ((r >> 2) & 3))) * 8;
+      dma16(base + (int64_t)qi * sn + pc, lds_ptr(&dst[sl * 512]));
+    };
 #pragma unroll
-    for (int j2 = 0; j2 < 2; ++j2) {
-      const int qi = tail ? min(q0 + arow[j2], lq - 1) : q0 + arow[j2];
-      dma16(qb + (int64_t)qi * a.q.sn + apiece[j2], lds_ptr(&sq[b][(2 * w + j2) * 512]));
-      dma16(db + (int64_t)qi * a.dout.sn + apiece[j2], lds_ptr(&sdo[b][(2 * w + j2) * 512]));
+    for (int j2 = 0; j2 < 2; ++j2) slice(qb, a.q.sn, sq[b], 2 * w + j2);
+    if constexpr (R == 0) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) slice(db, a.dout.sn, sdo[b], 4 * pair + j4);
     }
     {
+      const int brow = 8 * w + (ln >> 3);
+      const int bpiece = kTileD + ((ln & 7) ^ sw64(brow)) * 8;
       const int qi = tail ? min(q0 + brow, lq - 1) : q0 + brow;
       dma16(qb + (int64_t)qi * a.q.sn + bpiece, lds_ptr(&sq[b][kR2TileA + w * 512]));
     }
     {
-      const int r = 16 * (w & 1) + (lane & 15);
+      const int r = 16 * (w & 1) + (ln & 15);
       const int qi = tail ? min(q0 + r, lq - 1) - r : q0;
-      dma4(ldsrc + hh * a.lse_sh + qi, lds_ptr(&sld[b][w][0]));
+      const float* src = ((w & 3) < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + hh * a.lse_sh;
+      dma4(src + r + qi, lds_ptr(&sld[b][w][0]));
     }
   };
 
@@ -133,6 +141,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
   // copy of the kernel body (the same barriers in the same order).
   auto role_main = [&](auto role_c) {
     constexpr int R = decltype(role_c)::value;
+    constexpr int NDMA = R == 0 ? NDMA_R0 : NDMA_R1;        // this role's loads per step
     constexpr int NKS = R == 0 ? kR2Dq / 16 : kR2Dv / 16;  // contraction steps of S / dP
     constexpr int NPB = R == 0 ? kR2Dv / 32 : kR2Dq / 32;  // 32-column blocks of dV / dK
     constexpr int NSC = NKS * KT, NPR = 2 * NPB * KT;
@@ -323,9 +332,9 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
     };
 
     // Prologue: steps 0..2 in flight; role 0 computes S of step 0.
-    if (total > 0) issue(0);
-    if (total > 1) issue(1);
-    if (total > 2) issue(2);
+    if (total > 0) issue(0, role_c);
+    if (total > 1) issue(1, role_c);
+    if (total > 2) issue(2, role_c);
     if (total > 2) wait_vmcnt<2 * NDMA>();
     else if (total > 1) wait_vmcnt<NDMA>();
     else wait_vmcnt<0>();
@@ -351,7 +360,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
       else wait_vmcnt<0>();
       __syncthreads();
       if (R == 1) store_ds(i, Told);  // Told: dS of step i-2
-      if (i + 3 < total) issue(i + 3);
+      if (i + 3 < total) issue(i + 3, role_c);
       if (R == 0) {
         if (i <= total) step_a(i, cur, nxt, Told, Tnew);
       } else {

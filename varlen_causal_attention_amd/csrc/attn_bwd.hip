@@ -1,7 +1,6 @@
 // Backward launcher: delta pre-pass, then for every compiled head-dim pair
-// either the fused dK/dV and dQ passes (DS = number of waves that split one
-// 32-row block by head-dim range) or the two-phase scores + products passes
-// (their own translation unit, attn_bwd_tiles.hip).
+// either the fused dK/dV and dQ passes or the two-phase scores + products
+// passes (their own translation unit, attn_bwd_tiles.hip).
 #include "attn_bwd.hpp"
 #include "attn_launch.hpp"
 #include "attn_sched.hpp"
@@ -11,9 +10,6 @@ namespace vca {
 namespace VCA_ELEM {
 namespace {
 
-// DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
-// and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
-// BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
 // Work lists (query tiles of q_tile rows with key steps of q_step, key blocks
 // of k_tile keys with query steps of k_step) and, when delta_pass, the delta
 // pre-pass (the fused path's dQ pass computes delta itself). seg_major_lists puts
@@ -80,26 +76,23 @@ void bwd_prologue(BwdArgs& a, bool causal, int nseg, int Hq, int Hkv, int max_q,
   }
 }
 
-// DS: waves splitting one 32-row block by head-dim range; NB/PF: LDS buffers
-// and register prefetch of the dK/dV pass (KN, KP) and the dQ pass (QN, QP);
-// BN keys per dQ tile; WPE waves per SIMD the dQ register budget targets.
-// The left window and the softcap (ext) take the generic dK/dV kernel at
-// every head dim (same 128-key blocks).
-template <int DQK, int DV, int DS, int KN, bool KP, int NWK>
+// NWK waves per dK/dV workgroup. The left window and the softcap (ext) take
+// the generic dK/dV kernel at every head dim (same 128-key blocks).
+template <int DQK, int DV, int NWK>
 hipError_t launch_dkdv(const BwdArgs& a, bool causal, bool ext, unsigned grid, hipStream_t st) {
-  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
+  constexpr bool kPipe = DQK == DV;  // software-pipelined dK/dV
   TimedLaunch timer("attn_bwd_dkdv", st);
   if (ext) {
     if (causal)
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true, true>), dim3(grid),
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, NWK, true, true>), dim3(grid),
                          dim3(64 * NWK), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false, true>),
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, NWK, false, true>),
                          dim3(grid), dim3(64 * NWK), 0, st, a);
   } else if constexpr (kPipe && DQK == 128) {
     const hipError_t e = launch_dkdv_roles(a, causal, grid, st);
     if (e != hipSuccess) return e;
-  } else if constexpr (DQK == 192 && DV == 128 && DS == 1 && NWK == 4) {
+  } else if constexpr (DQK == 192 && DV == 128 && NWK == 4) {
     const hipError_t e = launch_dkdv_roles192(a, causal, grid, st);
     if (e != hipSuccess) return e;
   } else if constexpr (kPipe) {
@@ -109,23 +102,25 @@ hipError_t launch_dkdv(const BwdArgs& a, bool causal, bool ext, unsigned grid, h
       hipLaunchKernelGGL((attn_bwd_dkdv_pipe_kernel<DQK, false>), dim3(grid), dim3(256), 0, st, a);
   } else {
     if (causal)
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, true>), dim3(grid),
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, NWK, true>), dim3(grid),
                          dim3(64 * NWK), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, DS, KN, KP, NWK, false>), dim3(grid),
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DQK, DV, NWK, false>), dim3(grid),
                          dim3(64 * NWK), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <int DQK, int DV, int DS, int KN, bool KP, int BN, int QN, bool QP, int WPE, int NWK, int NWQ>
+// BN keys per dQ tile, WPE waves per SIMD the dQ register budget targets,
+// NWK / NWQ waves per dK/dV / dQ workgroup.
+template <int DQK, int DV, int BN, int WPE, int NWK, int NWQ>
 hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q, int64_t q_rows,
                     int64_t k_rows, const TileGeom& tg, const BwdWorkspace& wl, void* ws,
                     hipStream_t st) {
-  constexpr bool kPipe = DS == 1 && DQK == DV;  // software-pipelined dK/dV
-  constexpr int key_block = kPipe ? 128 : 32 * (NWK / DS);
-  static_assert(key_block == 32 * (NWK / DS), "the generic dK/dV kernel takes the same blocks");
-  constexpr int q_tile = 32 * (NWQ / DS);
+  constexpr bool kPipe = DQK == DV;  // software-pipelined dK/dV
+  constexpr int key_block = kPipe ? 128 : 32 * NWK;
+  static_assert(key_block == 32 * NWK, "the generic dK/dV kernel takes the same blocks");
+  constexpr int q_tile = 32 * NWQ;
   const bool ext = a.window > 0 || a.cap_in != 0.f;
   const int seg_major = (Hq / Hkv) % 2 == 0 ? 0 : 1;
   const int G = Hq / Hkv;
@@ -153,7 +148,7 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
         a.kvh_n = n;
         a.ds_h0 = g0 * G;
         a.ds_nh = n * G;
-        hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(a, causal, ext, kitems * n, st);
+        hipError_t e = launch_dkdv<DQK, DV, NWK>(a, causal, ext, kitems * n, st);
         if (e != hipSuccess) return e;
         TimedLaunch timer("attn_bwd_dq_ds", st);
         const dim3 g(qitems * (unsigned)(n * G));
@@ -177,20 +172,20 @@ hipError_t bwd_dims(BwdArgs a, bool causal, int nseg, int Hq, int Hkv, int max_q
     TimedLaunch timer("attn_bwd_dq", st);
     const dim3 g((unsigned)(((q_rows + q_tile - 1) / q_tile + nseg) * Hq));
     if (causal && ext)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true, true>), g,
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, BN, WPE, NWQ, true, true>), g,
                          dim3(64 * NWQ), 0, st, a);
     else if (causal)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, true>), g,
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, BN, WPE, NWQ, true>), g,
                          dim3(64 * NWQ), 0, st, a);
     else if (ext)
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false, true>), g,
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, BN, WPE, NWQ, false, true>), g,
                          dim3(64 * NWQ), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, DS, BN, QN, QP, WPE, NWQ, false>), g,
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<DQK, DV, BN, WPE, NWQ, false>), g,
                          dim3(64 * NWQ), 0, st, a);
   }
   if (k_rows > 0) {
-    const hipError_t e = launch_dkdv<DQK, DV, DS, KN, KP, NWK>(
+    const hipError_t e = launch_dkdv<DQK, DV, NWK>(
         a, causal, ext, (unsigned)(((k_rows + key_block - 1) / key_block + nseg) * Hkv), st);
     if (e != hipSuccess) return e;
   }
@@ -226,17 +221,16 @@ hipError_t launch_bwd(BwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   if (bwd_uses_tiles(dqk, dv))
     return launch_bwd_tiles(a, dqk, dv, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws,
                             st);
-// arguments: DQK, DV, DS, dK/dV buffers + prefetch, dQ key tile, dQ buffers + prefetch, dQ waves
-// per SIMD, dK/dV waves per workgroup, dQ waves per workgroup
-#define VCA_BWD(DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ)                                 \
-  bwd_dims<DQK, DV, DS, KN, KP, BN, QN, QP, WPE, NWK, NWQ>(a, causal, nseg, Hq, Hkv, max_q, \
-                                                           q_rows, k_rows, tg, wl, ws, st)
-  if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 1, 2, true, 32, 2, true, 2, 4, 4);
-  if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 1, 2, true, 32, 2, true, 2, 4, 4);
+// arguments: DQK, DV, dQ key tile, dQ waves per SIMD, dK/dV waves per
+// workgroup, dQ waves per workgroup
+#define VCA_BWD(DQK, DV, BN, WPE, NWK, NWQ) \
+  bwd_dims<DQK, DV, BN, WPE, NWK, NWQ>(a, causal, nseg, Hq, Hkv, max_q, q_rows, k_rows, tg, wl, ws, st)
+  if (dqk == 64 && dv == 64) return VCA_BWD(64, 64, 32, 2, 4, 4);
+  if (dqk == 128 && dv == 128) return VCA_BWD(128, 128, 32, 2, 4, 4);
   // 192/128: the fused passes at one wave per SIMD (dK/dV 360, dQ 285 registers) beat the
   // two-phase backward, whose P/dS stores and re-reads make it HBM-bound at these head dims
   // (14.0 -> 11.7 ms on the 32K-token varlen problem)
-  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 1, 2, true, 32, 2, true, 1, 4, 4);
+  if (dqk == 192 && dv == 128) return VCA_BWD(192, 128, 32, 1, 4, 4);
 #undef VCA_BWD
   return hipErrorInvalidValue;
 }

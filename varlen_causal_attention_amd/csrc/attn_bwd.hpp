@@ -12,13 +12,11 @@
 //   dQ[i]     = scale * sum_j dS[i,j] k_j                     (dQ kernel)
 // dK/dV sum over the q-heads of each GQA group inside the dK/dV kernel.
 //
-// Both main kernels split a 32-row block across DS waves by head-dim range:
-// each wave of the group computes a partial score tile over its share of Dqk
-// (and of Dv for dP), the partials are summed through LDS, and each wave then
-// accumulates its own share of the output columns. DS = 1 needs no exchange
-// and is what the library compiles: head dims 64 and 128 at two waves per
-// SIMD, 192/128 at one (dK and dV accumulators of 32 keys plus the K and V
-// fragments take ~360 registers); 256 and 512 take the two-phase backward.
+// In the two generic kernels below each wave owns one 32-row block over the
+// whole head dim (dK/dV: 32 keys; dQ: 32 queries). They serve the window /
+// softcap variants and the head dims without a dedicated pass (dQ by
+// recomputation at 64, and at 128 and 192/128 when the dS store is off);
+// 256 and 512 take the two-phase backward.
 #pragma once
 
 #include <type_traits>
@@ -92,34 +90,30 @@ __global__ void __launch_bounds__(256) attn_bwd_delta_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup = (segment, kv-head, block of 32*(4/DS) keys). The
+// dK / dV: one workgroup = (segment, kv-head, block of 32*NW keys). The
 // workgroup walks every (q-head of the group, 32-row query step) that can see
-// its keys; each step's Q and dO rows are staged row-major in LDS (the next
-// step's global loads issued a step ahead when PF), read row-wise as the A
-// operand of S = Q K^T and dP = dO V^T, and column-wise (transposing LDS read)
-// as the A operand of dK^T += Q^T dS and dV^T += dO^T P.
+// its keys; each step's Q and dO rows are staged row-major in two LDS buffers
+// (the next step's global loads issued a step ahead into registers), read
+// row-wise as the A operand of S = Q K^T and dP = dO V^T, and column-wise
+// (transposing LDS read) as the A operand of dK^T += Q^T dS and dV^T += dO^T P.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int NBUF, bool PF, int NW, bool CAUSAL, bool EXT = false>
+template <int DQK, int DV, int NW, bool CAUSAL, bool EXT = false>
 __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const BwdArgs a) {
-  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
-  constexpr int NT = 64 * NW;          // threads
-  constexpr int KG = NW / DS;          // 32-key groups per workgroup
-  constexpr int DR = DQK / DS;         // this wave's share of Dqk
-  constexpr int VR = DV / DS;          // this wave's share of Dv
-  static_assert(DR % 32 == 0 && VR % 32 == 0, "head-dim split");
-  constexpr int NKS = DR / 16, NVS = VR / 16;
-  constexpr int NDB = DR / 32, NVB = VR / 32;
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int KG = NW;       // 32-key groups per workgroup
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "head dims");
+  constexpr int NKS = DQK / 16, NVS = DV / 16;
+  constexpr int NDB = DQK / 32, NVB = DV / 32;
   constexpr int BQ = 32;
   constexpr int QS = DQK + 16, OS = DV + 16;  // LDS row strides (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sq[NBUF][BQ * QS];
-  __shared__ __attribute__((aligned(16))) uint16_t sdo[NBUF][BQ * OS];
-  __shared__ __attribute__((aligned(16))) float slse[NBUF][BQ];
-  __shared__ __attribute__((aligned(16))) float sdel[NBUF][BQ];
-  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? KG * DS * 2 * 16 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][BQ * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t sdo[2][BQ * OS];
+  __shared__ __attribute__((aligned(16))) float slse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sdel[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int kg = w / DS, ds = w % DS;
+  const int kg = w;  // this wave's 32-key group
   const int item = blockIdx.x / a.kvh_n, g = a.kvh0 + (blockIdx.x - item * a.kvh_n);
   if (item >= *a.count_k) return;
   const int2 st = a.items_k[item];
@@ -134,12 +128,12 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   const uint16_t* kbp = a.k.p + s * a.k.sb + (int64_t)sg.k_row0 * a.k.sn + g * a.k.sh;
   const uint16_t* vbp = a.v.p + s * a.v.sb + (int64_t)sg.k_row0 * a.v.sn + g * a.v.sh;
 
-  // K and V fragments of this lane's key over this wave's d ranges (B operands)
+  // K and V fragments of this lane's key (B operands)
   frag8 kf[NKS], vf[NVS];
   {
     const bool ok = key < lk;
-    const uint16_t* kp = kbp + (int64_t)(ok ? key : 0) * a.k.sn + ds * DR + half * 8;
-    const uint16_t* vp = vbp + (int64_t)(ok ? key : 0) * a.v.sn + ds * VR + half * 8;
+    const uint16_t* kp = kbp + (int64_t)(ok ? key : 0) * a.k.sn + half * 8;
+    const uint16_t* vp = vbp + (int64_t)(ok ? key : 0) * a.v.sn + half * 8;
 #pragma unroll
     for (int i = 0; i < NKS; ++i) kf[i] = as_frag(ok ? ldg16(kp + i * 16) : zero_u32x4());
 #pragma unroll
@@ -212,7 +206,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
   if (total > 0) {
     load_rows(0);
     store_rows(0);
-    if (PF && total > 1) load_rows(1);
+    if (total > 1) load_rows(1);
   }
 
   // dS block of the previous step, stored after this step's wait for its
@@ -226,10 +220,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
     pend_off = -1;
   };
   for (int it = 0; it < total; ++it) {
-    const int buf = NBUF == 2 ? (it & 1) : 0;
+    const int buf = it & 1;
     const int q0 = q_begin + (nq - 1 - it / a.G) * BQ;
     __syncthreads();  // step `it` is in LDS; nobody still reads the other buffer
-    if (NBUF == 2 && it + 1 < total) {
+    if (it + 1 < total) {
       store_rows(buf ^ 1);
       flush_ds();
       if (it + 2 < total) load_rows(it + 2);
@@ -241,34 +235,14 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
                       !(win > 0 && gk0 + 31 <= q0 + shift - win);
     f32x16 sacc = zero16(), pacc = zero16();
     if (live) {
-      // partial S[q][key] = Q K^T and dP[q][key] = dO V^T over this wave's d ranges
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T
 #pragma unroll
       for (int i = 0; i < NKS; ++i)
-        sacc = mfma32(lds_frag(&sq[buf][col * QS + ds * DR + half * 8 + i * 16]), kf[i], sacc);
+        sacc = mfma32(lds_frag(&sq[buf][col * QS + half * 8 + i * 16]), kf[i], sacc);
 #pragma unroll
       for (int i = 0; i < NVS; ++i)
-        pacc = mfma32(lds_frag(&sdo[buf][col * OS + ds * VR + half * 8 + i * 16]), vf[i], pacc);
+        pacc = mfma32(lds_frag(&sdo[buf][col * OS + half * 8 + i * 16]), vf[i], pacc);
       pipeline_mfma_reads<NKS + NVS, 4>();
-    }
-    if constexpr (DS > 1) {
-      float* mine = &sx[((kg * DS + ds) * 2) * 16 * 64];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        mine[r * 64 + lane] = sacc[r];
-        mine[16 * 64 + r * 64 + lane] = pacc[r];
-      }
-      __syncthreads();
-      sacc = zero16();
-      pacc = zero16();
-#pragma unroll
-      for (int o = 0; o < DS; ++o) {
-        const float* src = &sx[((kg * DS + o) * 2) * 16 * 64];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[r] += src[r * 64 + lane];
-          pacc[r] += src[16 * 64 + r * 64 + lane];
-        }
-      }
     }
     if (live) {
       // P and dS (rows q = q0 + 8*(r/4) + 4*half + r%4, column = key). Rows
@@ -309,29 +283,23 @@ __global__ void __launch_bounds__(64 * NW, NW / 4) attn_bwd_dkdv_kernel(const Bw
       // dV^T[dv][key] += dO^T P ; dK^T[d][key] += Q^T dS
 #pragma unroll
       for (int b = 0; b < NVB; ++b) {
-        dva[b] = mfma32(tr_frag(sdo[buf], OS, 0, ds * VR + b * 32, lane), p0, dva[b]);
-        dva[b] = mfma32(tr_frag(sdo[buf], OS, 16, ds * VR + b * 32, lane), p1, dva[b]);
+        dva[b] = mfma32(tr_frag(sdo[buf], OS, 0, b * 32, lane), p0, dva[b]);
+        dva[b] = mfma32(tr_frag(sdo[buf], OS, 16, b * 32, lane), p1, dva[b]);
       }
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
-        dka[b] = mfma32(tr_frag(sq[buf], QS, 0, ds * DR + b * 32, lane), s0, dka[b]);
-        dka[b] = mfma32(tr_frag(sq[buf], QS, 16, ds * DR + b * 32, lane), s1, dka[b]);
+        dka[b] = mfma32(tr_frag(sq[buf], QS, 0, b * 32, lane), s0, dka[b]);
+        dka[b] = mfma32(tr_frag(sq[buf], QS, 16, b * 32, lane), s1, dka[b]);
       }
       pipeline_mfma_reads<2 * (NVB + NDB), 4, 2>();
-    }
-    if (NBUF == 1 && it + 1 < total) {
-      __syncthreads();  // everyone is done reading the single buffer
-      if (!PF) load_rows(it + 1);
-      store_rows(0);
-      if (PF && it + 2 < total) load_rows(it + 2);
     }
   }
   flush_ds();
 
   if (key < lk) {
     const int64_t r = sg.k_row0 + key;
-    uint16_t* dkp = a.dk.p + s * a.dk.sb + r * a.dk.sn + g * a.dk.sh + ds * DR;
-    uint16_t* dvp = a.dv.p + s * a.dv.sb + r * a.dv.sn + g * a.dv.sh + ds * VR;
+    uint16_t* dkp = a.dk.p + s * a.dk.sb + r * a.dk.sn + g * a.dk.sh;
+    uint16_t* dvp = a.dv.p + s * a.dv.sb + r * a.dv.sn + g * a.dv.sh;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll
@@ -531,36 +499,33 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_pipe_kernel(const BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = (segment, q-head, block of 32*(4/DS) queries). Per
-// BN-key tile, K and V are staged row-major in LDS; S^T = K Q^T and
-// dP^T = V dO^T read them row-wise, dQ^T += K^T dS^T column-wise.
+// dQ: one workgroup = (segment, q-head, block of 32*NW queries). Per BN-key
+// tile, K and V are staged row-major in two LDS buffers (the next tile's
+// global loads issued a tile ahead into registers, or loaded straight into
+// LDS at head dim 128); S^T = K Q^T and dP^T = V dO^T read them row-wise,
+// dQ^T += K^T dS^T column-wise.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int DS, int BN, int NBUF, bool PF, int WPE, int NW, bool CAUSAL,
-          bool EXT = false>
+template <int DQK, int DV, int BN, int WPE, int NW, bool CAUSAL, bool EXT = false>
 __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs a) {
-  static_assert(PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int NT = 64 * NW;
-  constexpr int QG = NW / DS;
-  constexpr int DR = DQK / DS;
-  constexpr int VR = DV / DS;
-  static_assert(DR % 32 == 0 && VR % 32 == 0 && BN % 32 == 0, "head-dim split");
-  constexpr int NKS = DR / 16, NVS = VR / 16, NDB = DR / 32, NKB = BN / 32;
+  constexpr int QG = NW;  // 32-query groups per workgroup
+  static_assert(DQK % 32 == 0 && DV % 32 == 0 && BN % 32 == 0, "head dims");
+  constexpr int NKS = DQK / 16, NVS = DV / 16, NDB = DQK / 32, NKB = BN / 32;
   // K is read both row-wise and through the transposing read: a stride of
   // 32 bytes mod 256 is the compromise (2-way on the row reads, none on the
   // transposing reads); V is only read row-wise (16 bytes mod 256).
   constexpr int KS = DQK + 16, VS = DV + 8;
-  // Head dim 128 (DS 1, 32-key tiles, two buffers): K and V tiles go straight
-  // from global memory into LDS (global_load_lds) in the swizzled layout of
-  // rtile_off, one tile ahead, instead of through registers.
-  constexpr bool DMA = DQK == kTileD && DV == kTileD && DS == 1 && NBUF == 2 && BN == 32 && NW == 4;
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][DMA ? BN * kTileD : BN * KS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][DMA ? BN * kTileD : BN * VS];
-  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? QG * DS * 2 * NKB * 16 * 64 : 1];
+  // Head dim 128 (32-key tiles): K and V tiles go straight from global
+  // memory into LDS (global_load_lds) in the swizzled layout of rtile_off,
+  // one tile ahead, instead of through registers.
+  constexpr bool DMA = DQK == kTileD && DV == kTileD && BN == 32 && NW == 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[2][DMA ? BN * kTileD : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[2][DMA ? BN * kTileD : BN * VS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31, half = lane >> 5;
-  const int qg = w / DS, ds = w % DS;
+  const int qg = w;  // this wave's 32-query group
   int item, h;
   xcd_item_head(blockIdx.x, a.Hq, a.G, item, h);
   const int g = h / a.G;
@@ -590,8 +555,8 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 
   frag8 qf[NKS], df[NVS];
   {
-    const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + ds * DR + half * 8;
-    const uint16_t* dp = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + ds * VR + half * 8;
+    const uint16_t* qp = qbp + (int64_t)(qok ? qi : 0) * a.q.sn + half * 8;
+    const uint16_t* dp = dobp + (int64_t)(qok ? qi : 0) * a.dout.sn + half * 8;
 #pragma unroll
     for (int i = 0; i < NKS; ++i) qf[i] = as_frag(qok ? ldg16(qp + i * 16) : zero_u32x4());
 #pragma unroll
@@ -603,7 +568,6 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   // row, sums their products with the same elements of O, and adds the
   // partner lane's half. The row's delta and lse*log2(e) (+inf for lse = -inf,
   // so P = 0 on every key) are stored for the dK/dV pass that follows.
-  static_assert(DS == 1, "delta from whole dO rows");
   float l2 = __builtin_inff(), dl = 0.f;
   {
     const uint16_t* op = a.o.p + s * a.o.sb + (int64_t)(sg.q_row0 + (qok ? qi : 0)) * a.o.sn +
@@ -651,19 +615,14 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
   if constexpr (DMA) {
     if (t0 < ntiles) issue_kv(t0);
   } else if (t0 < ntiles) {
-    const int b0 = NBUF == 2 ? (t0 & 1) : 0;
-    if (PF) {
-      kst.load_clamped(kbp, a.k.sn, t0 * BN, lk, tid);
-      vst.load_clamped(vbp, a.v.sn, t0 * BN, lk, tid);
-      kst.template store<KS>(sk[b0], tid);
-      vst.template store<VS>(sv[b0], tid);
-      if (t0 + 1 < ntiles) {
-        kst.load_clamped(kbp, a.k.sn, (t0 + 1) * BN, lk, tid);
-        vst.load_clamped(vbp, a.v.sn, (t0 + 1) * BN, lk, tid);
-      }
-    } else {
-      KStage::template copy<KS>(sk[b0], kbp, a.k.sn, t0 * BN, lk, tid);
-      VStage::template copy<VS>(sv[b0], vbp, a.v.sn, t0 * BN, lk, tid);
+    const int b0 = t0 & 1;
+    kst.load_clamped(kbp, a.k.sn, t0 * BN, lk, tid);
+    vst.load_clamped(vbp, a.v.sn, t0 * BN, lk, tid);
+    kst.template store<KS>(sk[b0], tid);
+    vst.template store<VS>(sv[b0], tid);
+    if (t0 + 1 < ntiles) {
+      kst.load_clamped(kbp, a.k.sn, (t0 + 1) * BN, lk, tid);
+      vst.load_clamped(vbp, a.v.sn, (t0 + 1) * BN, lk, tid);
     }
   }
 
@@ -674,12 +633,12 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 
   for (int t = t0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    const int buf = NBUF == 2 ? (t & 1) : 0;
+    const int buf = t & 1;
     if constexpr (DMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
     __syncthreads();
     if constexpr (DMA) {
       if (t + 1 < ntiles) issue_kv(t + 1);
-    } else if (NBUF == 2 && t + 1 < ntiles) {
+    } else if (t + 1 < ntiles) {
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
@@ -702,7 +661,7 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           sacc[kb] = mfma32(DMA ? rtile_row(sk[buf], kb * 32 + col, 2 * i + half)
-                                : lds_frag(&sk[buf][(kb * 32 + col) * KS + ds * DR + half * 8 +
+                                : lds_frag(&sk[buf][(kb * 32 + col) * KS + half * 8 +
                                                     i * 16]),
                             qf[i], sacc[kb]);
 #pragma unroll
@@ -710,37 +669,10 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           pacc[kb] = mfma32(DMA ? rtile_row(sv[buf], kb * 32 + col, 2 * i + half)
-                                : lds_frag(&sv[buf][(kb * 32 + col) * VS + ds * VR + half * 8 +
+                                : lds_frag(&sv[buf][(kb * 32 + col) * VS + half * 8 +
                                                     i * 16]),
                             df[i], pacc[kb]);
       pipeline_mfma_reads<(NKS + NVS) * NKB, 4>();
-    }
-    if constexpr (DS > 1) {
-      float* mine = &sx[((qg * DS + ds) * 2 * NKB) * 16 * 64];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          mine[(kb * 16 + r) * 64 + lane] = sacc[kb][r];
-          mine[((NKB + kb) * 16 + r) * 64 + lane] = pacc[kb][r];
-        }
-      __syncthreads();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = zero16();
-        pacc[kb] = zero16();
-      }
-#pragma unroll
-      for (int o = 0; o < DS; ++o) {
-        const float* src = &sx[((qg * DS + o) * 2 * NKB) * 16 * 64];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            sacc[kb][r] += src[(kb * 16 + r) * 64 + lane];
-            pacc[kb][r] += src[((NKB + kb) * 16 + r) * 64 + lane];
-          }
-      }
     }
     if (live) {
       // rows past the segment end carry l2 = +inf (P = 0); the key mask is only
@@ -782,28 +714,14 @@ __global__ void __launch_bounds__(64 * NW, WPE) attn_bwd_dq_kernel(const BwdArgs
 #pragma unroll
         for (int b = 0; b < NDB; ++b)
           dqa[b] = mfma32(DMA ? rtile_col(sk[buf], kk * 16, b * 32, lane)
-                              : tr_frag(sk[buf], KS, kk * 16, ds * DR + b * 32, lane),
+                              : tr_frag(sk[buf], KS, kk * 16, b * 32, lane),
                           sf[kk], dqa[b]);
       pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
-    }
-    if (NBUF == 1 && t + 1 < ntiles) {
-      __syncthreads();
-      if (PF) {
-        kst.template store<KS>(sk[0], tid);
-        vst.template store<VS>(sv[0], tid);
-        if (t + 2 < ntiles) {
-          kst.load_clamped(kbp, a.k.sn, k0 + 2 * BN, lk, tid);
-          vst.load_clamped(vbp, a.v.sn, k0 + 2 * BN, lk, tid);
-        }
-      } else {
-        KStage::template copy<KS>(sk[0], kbp, a.k.sn, k0 + BN, lk, tid);
-        VStage::template copy<VS>(sv[0], vbp, a.v.sn, k0 + BN, lk, tid);
-      }
     }
   }
 
   if (qok) {
-    uint16_t* dqp = a.dq.p + s * a.dq.sb + (int64_t)(sg.q_row0 + qi) * a.dq.sn + h * a.dq.sh + ds * DR;
+    uint16_t* dqp = a.dq.p + s * a.dq.sb + (int64_t)(sg.q_row0 + qi) * a.dq.sn + h * a.dq.sh;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
 #pragma unroll

@@ -12,28 +12,25 @@ namespace vca {
 namespace VCA_ELEM {
 
 namespace {
-// BN = keys per tile, DS = waves sharing one 32-row query block, NBUF = LDS
-// buffers for the K/V tiles, WPE = waves per SIMD the register budget targets.
+// BN = keys per tile, WPE = waves per SIMD the register budget targets,
 // HPW = q-heads per workgroup (2: two heads of a GQA group share each K/V
 // tile; the grid then has one workgroup per item and head pair).
-template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, int HPW = 1>
+template <int DQK, int DV, int BN, int WPE, int HPW = 1>
 hipError_t fwd_dims(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
   TimedLaunch timer("attn_fwd", st);
   grid.x /= HPW;
-  const dim3 block(256 * DS * HPW);
+  const dim3 block(256 * HPW);
   const bool ext = a.window > 0 || a.cap_in != 0.f;
   if (causal && ext)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true, HPW, true>), grid,
-                       block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, WPE, true, HPW, true>), grid, block, 0, st,
+                       a);
   else if (causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, true, HPW>), grid, block,
-                       0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, WPE, true, HPW>), grid, block, 0, st, a);
   else if (ext)
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false, HPW, true>), grid,
-                       block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, WPE, false, HPW, true>), grid, block, 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, DS, NBUF, WPE, PF, false, HPW>), grid, block,
-                       0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<DQK, DV, BN, WPE, false, HPW>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 hipError_t fwd_wide(const FwdArgs& a, bool causal, dim3 grid, hipStream_t st) {
@@ -84,13 +81,13 @@ hipError_t launch_fwd(FwdArgs a, int dqk, int dv, bool causal, int nseg, int Hq,
   // at most ceil(q_rows / 128) + nseg query tiles exist
   const int64_t items = (q_rows + kFwdBM - 1) / kFwdBM + nseg;
   const dim3 grid((unsigned)(items * Hq));
-  if (dqk == 64 && dv == 64) return fwd_dims<64, 64, 64, 1, 2, 2, true>(a, causal, grid, st);
+  if (dqk == 64 && dv == 64) return fwd_dims<64, 64, 64, 2>(a, causal, grid, st);
   if (dqk == 128 && dv == 128) {
-    if (a.G % 2 == 0) return fwd_dims<128, 128, 128, 1, 2, 1, true, 2>(a, causal, grid, st);
-    return fwd_dims<128, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
+    if (a.G % 2 == 0) return fwd_dims<128, 128, 128, 1, 2>(a, causal, grid, st);
+    return fwd_dims<128, 128, 64, 2>(a, causal, grid, st);
   }
-  if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 1, 2, 2, true>(a, causal, grid, st);
-  if (dqk == 256 && dv == 256) return fwd_dims<256, 256, 64, 1, 2, 1, true>(a, causal, grid, st);
+  if (dqk == 192 && dv == 128) return fwd_dims<192, 128, 64, 2>(a, causal, grid, st);
+  if (dqk == 256 && dv == 256) return fwd_dims<256, 256, 64, 1>(a, causal, grid, st);
   return fwd_wide(a, causal, grid, st);
 }
 

@@ -7,7 +7,8 @@
 // j <= i + (lk - lq). A row that sees nothing gets out 0 and lse -inf.
 //
 // Work item: one workgroup = one (segment or batch, q-head, 128-row q tile);
-// four 32-row query blocks, each owned by DS waves (DS = 1 below Dqk 512).
+// four 32-row query blocks, one per wave (head dims 64 to 256; 512 has
+// attn_fwd_wide.hpp).
 // Per key tile:
 //   * K tile [BN][Dqk] and V tile [BN][Dv] row-major in LDS;
 //   * each wave computes S^T = K Q^T with Q held in registers, so a lane owns
@@ -27,28 +28,19 @@ namespace VCA_ELEM {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
 
-template <int DQK, int DV, int BN, int DS, int NBUF, int WPE, bool PF, bool CAUSAL, int HPW = 1,
-          bool EXT = false>
-__global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const FwdArgs a) {
-  // DS waves share one 32-row query block: wave `ds` of the group holds the
-  // Q fragments of Dqk range [ds*DR, (ds+1)*DR) and accumulates O^T for Dv
-  // range [ds*VR, (ds+1)*VR); the partial score tiles are summed through LDS
-  // in a fixed order, so every wave of the group sees bitwise-identical scores.
-  // NBUF = 2 double-buffers the K/V tiles in LDS (one barrier per tile);
-  // NBUF = 1 keeps one buffer (two barriers per tile).
-  // PF = outside DMA mode, the next tile's global loads are issued a tile
-  // ahead into registers (off where the registers are needed for the
-  // accumulators).
+template <int DQK, int DV, int BN, int WPE, bool CAUSAL, int HPW = 1, bool EXT = false>
+__global__ void __launch_bounds__(256 * HPW, WPE) attn_fwd_kernel(const FwdArgs a) {
+  // K/V tiles are double-buffered in LDS (one barrier per tile); outside the
+  // direct-load modes below, the next tile's global loads are issued a tile
+  // ahead into registers and stored to LDS after the barrier.
   // HPW = 2 runs two q-heads of one GQA group over the same query rows (four
   // waves each): every K/V tile brought into LDS feeds both, half the tile
   // loads per unit of work, with the same causal work per wave.
   // EXT adds the left window (tiles below every row's window are skipped,
   // the window's edge masked) and the logit softcap (scores become
   // cap * tanh(scale * s / cap) before the softmax).
-  static_assert(DQK % (16 * DS) == 0 && DV % (32 * DS) == 0 && BN % 32 == 0, "tile shape");
-  static_assert(HPW == 1 || DS == 1, "head pairs with a split head dim");
-  constexpr int NT = 256 * DS * HPW;  // threads
-  constexpr int DR = DQK / DS, VR = DV / DS;
+  static_assert(DQK % 16 == 0 && DV % 32 == 0 && BN % 32 == 0, "tile shape");
+  constexpr int NT = 256 * HPW;  // threads
   // LDS row strides (elements). K is only read row-wise (b128 per lane, 16
   // lanes per LDS cycle): a stride of 16 bytes mod 256 puts 16 consecutive
   // rows on distinct banks. V is only read through the transposing read (4
@@ -57,8 +49,8 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   constexpr int KS = DQK + 8;
   constexpr int VS = DV + 32;
   constexpr int NKB = BN / 32;
-  constexpr int NDB = VR / 32;
-  constexpr int NKS = DR / 16;
+  constexpr int NDB = DV / 32;
+  constexpr int NKS = DQK / 16;
   // DMA mode (Dqk = Dv a multiple of 128, two buffers): K and V tiles go
   // straight from global memory into LDS (global_load_lds), one tile ahead,
   // with no staging through registers and no LDS stores. A tile is stored as
@@ -66,9 +58,9 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   // layout of rtile_off. The tile's BN/4 * CB groups of 4 rows x 256 bytes
   // are split evenly over the waves, NG (a multiple of 4) per wave.
   constexpr int CB = DQK / kTileD;
-  constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * DS * HPW) : 0;
-  constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NBUF == 2 && NG >= 1 &&
-                       (NG % 4 == 0 || 4 % NG == 0) && NG * 4 * 4 * DS * HPW == BN * CB;
+  constexpr int NG = DQK % kTileD == 0 ? BN * CB / (4 * 4 * HPW) : 0;
+  constexpr bool DMA = DQK == DV && DQK % kTileD == 0 && NG >= 1 &&
+                       (NG % 4 == 0 || 4 % NG == 0) && NG * 4 * 4 * HPW == BN * CB;
   // Split-K DMA mode (Dqk = 192, Dv = 128): the same direct loads, with K
   // stored as a block of columns 0..127 in 256-byte rows (rtile_off) followed
   // by a block of columns 128..191 in 128-byte rows (r64_off), and V as one
@@ -76,24 +68,21 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   // bytes of K's first block and of V, BN/32 groups of 8 rows x 128 bytes of
   // K's second block.
   constexpr bool SPLITK =
-      DQK == 192 && DV == kTileD && NBUF == 2 && DS == 1 && HPW == 1 && BN % 32 == 0;
+      DQK == 192 && DV == kTileD && HPW == 1 && BN % 32 == 0;
   constexpr bool LDMA = DMA || SPLITK;  // tiles land in LDS by global_load_lds
   static_assert(LDMA || HPW == 1, "head pairs load their tiles with global_load_lds");
-  static_assert(LDMA || PF || NBUF == 1, "double buffering relies on the register prefetch");
   constexpr int KBLK = BN * kTileD;  // elements per column block of a DMA tile
-  __shared__ __attribute__((aligned(1024))) uint16_t sk[NBUF][LDMA ? BN * DQK : BN * KS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sv[NBUF][LDMA ? BN * DV : BN * VS];
-  __shared__ __attribute__((aligned(16))) float sx[DS > 1 ? 4 * DS * NKB * 16 * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk[2][LDMA ? BN * DQK : BN * KS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv[2][LDMA ? BN * DV : BN * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
-  const int wl = w % (4 * DS);                               // wave within its q-head
-  const int qg = wl / DS, ds = wl % DS;
+  const int qg = w % 4;  // query block of this wave within its q-head
   const int col = lane & 31, half = lane >> 5;
   int item, h;
   xcd_item_head(blockIdx.x, a.H / HPW, a.G / HPW, item, h);
-  h = h * HPW + w / (4 * DS);
+  h = h * HPW + w / 4;
   const int kvh = h / a.G;
   if (item >= *a.item_count) return;
   const int2 st = a.items[item];
@@ -127,7 +116,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   frag8 qf[NKS];
   {
     const bool ok = row < lq;
-    const uint16_t* src = qb + (int64_t)(ok ? row : 0) * a.q.sn + ds * DR + half * 8;
+    const uint16_t* src = qb + (int64_t)(ok ? row : 0) * a.q.sn + half * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = as_frag((ok ? ldg16(src + ks * 16) : zero_u32x4()) ^ qsign);
   }
@@ -205,22 +194,16 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   } else if constexpr (SPLITK) {
     if (t0 < ntiles) issue_split(t0);
   } else if (t0 < ntiles) {
-    const int b0 = NBUF == 2 ? (t0 & 1) : 0;
-    if (PF) {
-      kst.load_clamped(kb, a.k.sn, t0 * BN, lk, tid);
-      vst.load_clamped(vb, a.v.sn, t0 * BN, lk, tid);
-      kst.template store<KS>(sk[b0], tid);
-      vst.template store<VS>(sv[b0], tid);
-      if (t0 + 1 < ntiles) {
-        kst.load_clamped(kb, a.k.sn, (t0 + 1) * BN, lk, tid);
-        vst.load_clamped(vb, a.v.sn, (t0 + 1) * BN, lk, tid);
-      }
-    } else {
-      KStage::template copy<KS>(sk[b0], kb, a.k.sn, t0 * BN, lk, tid);
-      VStage::template copy<VS>(sv[b0], vb, a.v.sn, t0 * BN, lk, tid);
+    const int b0 = t0 & 1;
+    kst.load_clamped(kb, a.k.sn, t0 * BN, lk, tid);
+    vst.load_clamped(vb, a.v.sn, t0 * BN, lk, tid);
+    kst.template store<KS>(sk[b0], tid);
+    vst.template store<VS>(sv[b0], tid);
+    if (t0 + 1 < ntiles) {
+      kst.load_clamped(kb, a.k.sn, (t0 + 1) * BN, lk, tid);
+      vst.load_clamped(vb, a.v.sn, (t0 + 1) * BN, lk, tid);
     }
   }
-
 
   f32x16 o[NDB];
 #pragma unroll
@@ -230,14 +213,14 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
 
   for (int t = t0; t < ntiles; ++t) {
     const int k0 = t * BN;
-    const int buf = NBUF == 2 ? (t & 1) : 0;
+    const int buf = t & 1;
     if constexpr (LDMA) wait_vmcnt<0>();  // this wave's share of tile t has landed
     __syncthreads();  // tile t is in LDS; nobody still reads the other buffer
     if constexpr (DMA) {
       if (t + 1 < ntiles) issue_kv(t + 1);
     } else if constexpr (SPLITK) {
       if (t + 1 < ntiles) issue_split(t + 1);
-    } else if (NBUF == 2 && t + 1 < ntiles) {
+    } else if (t + 1 < ntiles) {
       kst.template store<KS>(sk[buf ^ 1], tid);
       vst.template store<VS>(sv[buf ^ 1], tid);
       if (t + 2 < ntiles) {
@@ -245,11 +228,10 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
         vst.load_clamped(vb, a.v.sn, k0 + 2 * BN, lk, tid);
       }
     }
-    // the DS waves of a group take every branch below together
     const bool live = wrow0 < lq && !(CAUSAL && k0 > wrow0 + 31 + shift) &&
                       !(win > 0 && k0 + BN - 1 < wrow0 + shift - win + 1);
 
-    // S^T = K Q^T (partial over this wave's Dqk range when DS > 1)
+    // S^T = K Q^T
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) sacc[kbk] = zero16();
@@ -262,28 +244,11 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
               SPLITK ? (ks < kTileD / 16
                             ? rtile_row(&sk[buf][0], kbk * 32 + col, 2 * ks + half)
                             : r64_row(&sk[buf][KBLK], kbk * 32 + col, 2 * (ks - kTileD / 16) + half))
-              : DMA ? rtile_row(&sk[buf][((ds * DR + ks * 16) / kTileD) * KBLK], kbk * 32 + col,
-                                ((ds * DR + ks * 16) % kTileD) / 8 + half)
-                    : lds_frag(&sk[buf][(kbk * 32 + col) * KS + ds * DR + half * 8 + ks * 16]),
+              : DMA ? rtile_row(&sk[buf][((ks * 16) / kTileD) * KBLK], kbk * 32 + col,
+                                ((ks * 16) % kTileD) / 8 + half)
+                    : lds_frag(&sk[buf][(kbk * 32 + col) * KS + half * 8 + ks * 16]),
               qf[ks], sacc[kbk]);
       pipeline_mfma_reads<NKS * NKB, 4>();
-    }
-    if constexpr (DS > 1) {
-      float* mine = &sx[(w * NKB) * 16 * 64];
-#pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mine[(kbk * 16 + r) * 64 + lane] = sacc[kbk][r];
-      __syncthreads();
-#pragma unroll
-      for (int kbk = 0; kbk < NKB; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = 0.f;
-#pragma unroll
-          for (int o2 = 0; o2 < DS; ++o2) v += sx[((qg * DS + o2) * NKB + kbk) * 16 * 64 + r * 64 + lane];
-          sacc[kbk][r] = v;
-        }
     }
     if (live) {
       // softcap first (a masked score must stay -inf): scores then hold
@@ -355,25 +320,11 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
       for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          o[db] = mfma32(LDMA ? rtile_col(&sv[buf][((ds * VR + db * 32) / kTileD) * KBLK], kk * 16,
-                                         (ds * VR + db * 32) % kTileD, lane)
-                             : tr_frag(sv[buf], VS, kk * 16, ds * VR + db * 32, lane),
+          o[db] = mfma32(LDMA ? rtile_col(&sv[buf][((db * 32) / kTileD) * KBLK], kk * 16,
+                                         (db * 32) % kTileD, lane)
+                             : tr_frag(sv[buf], VS, kk * 16, db * 32, lane),
                          pf[kk], o[db]);
       pipeline_mfma_reads<2 * NKB * NDB, 4, 2>();
-    }
-    if (NBUF == 1 && t + 1 < ntiles) {
-      __syncthreads();  // everyone is done reading the single buffer
-      if (PF) {
-        kst.template store<KS>(sk[0], tid);
-        vst.template store<VS>(sv[0], tid);
-        if (t + 2 < ntiles) {
-          kst.load_clamped(kb, a.k.sn, k0 + 2 * BN, lk, tid);
-          vst.load_clamped(vb, a.v.sn, k0 + 2 * BN, lk, tid);
-        }
-      } else {
-        KStage::template copy<KS>(sk[0], kb, a.k.sn, k0 + BN, lk, tid);
-        VStage::template copy<VS>(sv[0], vb, a.v.sn, k0 + BN, lk, tid);
-      }
     }
   }
 
@@ -381,7 +332,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
   const float ltot = lsum + xor32(lsum);
   if (row < lq) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    uint16_t* ob = a.o.p + s * a.o.sb + (int64_t)(sg.q_row0 + row) * a.o.sn + h * a.o.sh + ds * VR;
+    uint16_t* ob = a.o.p + s * a.o.sb + (int64_t)(sg.q_row0 + row) * a.o.sn + h * a.o.sh;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -392,7 +343,7 @@ __global__ void __launch_bounds__(256 * DS * HPW, WPE) attn_fwd_kernel(const Fwd
         *reinterpret_cast<elem4*>(ob + db * 32 + rr * 8 + half * 4) = v4;
       }
     }
-    if (half == 0 && ds == 0) {
+    if (half == 0) {
       const float l = ltot > 0.f ? (m_ref + log2f(ltot)) * kLn2 : kNegInf;
       a.lse[s * a.lse_sb + h * a.lse_sh + sg.q_row0 + row] = l;
     }

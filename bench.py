@@ -452,6 +452,25 @@ def copy_calibration(gib: int = 1) -> None:
                       "dispatches": 3}), flush=True)
 
 
+def gemm_reference() -> None:
+    """The chip's practical bf16 matrix rate on plain square GEMMs through
+    torch.matmul (hipBLASLt), timed like the bench steps: a reference for the
+    attention kernels' rates beside the published peak, which assumes the
+    2.4 GHz top clock that dense matrix work does not hold."""
+    out = []
+    for n, iters in ((8192, 20), (16384, 5)):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        ms = time_stage(lambda: torch.matmul(a, b), iters)
+        tf = 2.0 * n ** 3 / ms / 1e9
+        out.append({"n": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
+        del a, b
+    print(json.dumps({"gemm_reference": "torch.matmul bf16 n x n x n", "runs": out}), flush=True)
+
+
 def cpu_baseline(n: int, budget_s: float = 12.0) -> dict:
     """The fp64 oracle on the host cores over a bounded sample of the workload:
     whole documents of one q-head group at a time (forward then backward),
@@ -545,6 +564,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB elementwise copy (counter calibration) and exit")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time plain bf16 GEMMs (torch.matmul) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -556,6 +577,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_reference:
+        gemm_reference()
         return
     m = measure(args.workload, args.steps, args.warmup)
     w = workloads.workload(args.workload)

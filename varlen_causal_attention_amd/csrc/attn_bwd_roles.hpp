@@ -79,14 +79,14 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   constexpr int NP = NW / 2;     // wave pairs
   constexpr int KP = 32 * KT;    // keys per pair
   constexpr int SPW = 8 / NW;    // Q (and dO) four-row slices per wave and step
-  constexpr int NDMA = 2 * SPW + 1;  // hand-issued loads per wave per step
+  // hand-issued loads per wave and step: SPW slices of Q and of dO, and in
+  // role 0 the step's 32 lse*log2(e) and 32 delta values (one load)
+  constexpr int NDMA_R0 = 2 * SPW + 1, NDMA_R1 = 2 * SPW;
   constexpr int NS = kRStages;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[NS][kRTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sdo[NS][kRTile];
-  // lse*log2(e) (waves 0, 1: query rows 0-15, 16-31) | delta (waves 2, 3); a
-  // wave's load fills 64 values of which the first 16 are used (waves 4-7
-  // load stand-ins, keeping every wave's load count the same)
-  __shared__ __attribute__((aligned(256))) float sld[NS][NW][64];
+  // per pair: lse*log2(e) of the step's query rows 0-31, then their delta
+  __shared__ __attribute__((aligned(256))) float sld[NS][NP][64];
   __shared__ __attribute__((aligned(16))) u32x4 sp[2][NP][KT][2][64];  // [parity][pair][kt][j][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     for (int i = tid; i < 2 * kRTile / 8; i += NT) q4[i] = z;
     u32x4* d4 = reinterpret_cast<u32x4*>(&sdo[NS - 1][0]);
     for (int i = tid; i < kRTile / 8; i += NT) d4[i] = z;
-    for (int i = tid; i < NW * 64; i += NT) (&sld[NS - 1][0][0])[i] = 0.f;
+    for (int i = tid; i < NP * 64; i += NT) (&sld[NS - 1][0][0])[i] = 0.f;
     u32x4* p1 = &sp[1][0][0][0][0];
     for (int i = tid; i < NP * KT * 2 * 64; i += NT) p1[i] = z;
   }
@@ -162,9 +162,8 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     qoff[j2] = (int64_t)r * a.q.sn + spiece[j2];
     doff[j2] = (int64_t)r * a.dout.sn + spiece[j2];
   }
-  const float* ldsrc =
-      ((w & 3) < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + 16 * (w & 1) + (lane & 15);
-  auto issue = [&](int it) {
+  auto issue = [&](int it, auto role_c) {
+    constexpr int R = decltype(role_c)::value;
     const int b = stage(it);
     const int hh = step_head(it), q0 = step_q0(it);
     const uint16_t* qb = a.q.p + s * a.q.sb + (int64_t)sg.q_row0 * a.q.sn + hh * a.q.sh;
@@ -177,7 +176,10 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
         dma16(qs + qoff[j2], lds_ptr(&sq[b][(SPW * w + j2) * 512]));
         dma16(ds + doff[j2], lds_ptr(&sdo[b][(SPW * w + j2) * 512]));
       }
-      dma4(ldsrc + hh * a.lse_sh + q0, lds_ptr(&sld[b][w][0]));
+      if constexpr (R == 0)
+        dma4((lane < 32 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + hh * a.lse_sh + q0 +
+                 (lane & 31),
+             lds_ptr(&sld[b][pair][0]));
     } else {
       // last step of the segment: rows past its end re-read its last row
 #pragma unroll
@@ -186,10 +188,10 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
         dma16(qb + (int64_t)qi * a.q.sn + spiece[j2], lds_ptr(&sq[b][(SPW * w + j2) * 512]));
         dma16(db + (int64_t)qi * a.dout.sn + spiece[j2], lds_ptr(&sdo[b][(SPW * w + j2) * 512]));
       }
-      {
-        const int r = 16 * (w & 1) + (lane & 15);
-        dma4(ldsrc + hh * a.lse_sh + (min(q0 + r, lq - 1) - r), lds_ptr(&sld[b][w][0]));
-      }
+      if constexpr (R == 0)
+        dma4((lane < 32 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + hh * a.lse_sh +
+                 min(q0 + (lane & 31), lq - 1),
+             lds_ptr(&sld[b][pair][0]));
     }
   };
 
@@ -251,7 +253,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int qo = 8 * rr + 4 * h;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][qo >> 4][qo & 15]);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][pair][qo]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) l2[4 * rr + c] = v[c];
     }
@@ -298,7 +300,7 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int qo = 8 * rr + 4 * h;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][2 + (qo >> 4)][qo & 15]);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][pair][32 + qo]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) dl[4 * rr + c] = v[c];
     }
@@ -339,12 +341,17 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   };
 
   // Prologue: steps 0..2 in flight; role 0 computes S of step 0.
-  if (total > 0) issue(0);
-  if (total > 1) issue(1);
-  if (total > 2) issue(2);
-  if (total > 2) wait_vmcnt<2 * NDMA>();
-  else if (total > 1) wait_vmcnt<NDMA>();
-  else wait_vmcnt<0>();
+  auto prologue = [&](auto role_c) {
+    constexpr int N = decltype(role_c)::value == 0 ? NDMA_R0 : NDMA_R1;
+    if (total > 0) issue(0, role_c);
+    if (total > 1) issue(1, role_c);
+    if (total > 2) issue(2, role_c);
+    if (total > 2) wait_vmcnt<2 * N>();
+    else if (total > 1) wait_vmcnt<N>();
+    else wait_vmcnt<0>();
+  };
+  if (role == 0) prologue(std::integral_constant<int, 0>{});
+  else prologue(std::integral_constant<int, 1>{});
   __syncthreads();
   if (role == 0 && total > 0) {
     frag8 af[NKS];
@@ -364,14 +371,16 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   // alternate between the 0 and 1 copies. Each role runs its own copy of the
   // loop (same barriers), so values hoisted out of one role's loop do not
   // stay live in the other's.
-  auto run = [&](auto&& body) {
+  auto run = [&](auto role_c, auto&& body) {
+    constexpr int R = decltype(role_c)::value;
+    constexpr int N = R == 0 ? NDMA_R0 : NDMA_R1;
     auto iteration = [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
                          frag8 (&Tnew)[KT][2]) {
-      if (i + 2 < total) wait_vmcnt<NDMA>();
+      if (i + 2 < total) wait_vmcnt<N>();
       else wait_vmcnt<0>();
       __syncthreads();
-      if (role == 1) store_ds(i, Told);  // Told: dS of step i-2
-      if (i + 3 < total) issue(i + 3);
+      if constexpr (R == 1) store_ds(i, Told);  // Told: dS of step i-2
+      if (i + 3 < total) issue(i + 3, role_c);
       body(i, cur, nxt, Told, Tnew);
     };
     for (int i = 0; i <= total + 1; i += 2) {
@@ -380,12 +389,14 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
     }
   };
   if (role == 0)
-    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
+    run(std::integral_constant<int, 0>{},
+        [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
             frag8 (&Tnew)[KT][2]) {
-      if (i <= total) step_a(i, cur, nxt, Told, Tnew);
-    });
+          if (i <= total) step_a(i, cur, nxt, Told, Tnew);
+        });
   else
-    run([&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
+    run(std::integral_constant<int, 1>{},
+        [&](int i, f32x16 (&cur)[KT], f32x16 (&nxt)[KT], frag8 (&Told)[KT][2],
             frag8 (&Tnew)[KT][2]) { step_b(i, cur, nxt, Told, Tnew); });
 
   // dV (role 0) or dK * scale (role 1) of keys kp0 + 32*kt + l%32

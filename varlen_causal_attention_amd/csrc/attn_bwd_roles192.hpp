@@ -54,15 +54,15 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
   constexpr int KP = 32 * KT;     // keys per pair
   constexpr int NS = kRStages;    // Q/dO/lse/delta stages in LDS
   // hand-issued loads per wave and step: two 4-row slices of Q columns
-  // 0..127, one 8-row slice of columns 128..191, 64 lse*log2(e) | delta
-  // values, and in role 0 its pair's four 4-row slices of dO (role 1 also
-  // stores the dS blocks: the loads are split so both roles reach the
-  // barrier together)
-  constexpr int NDMA_R0 = 8, NDMA_R1 = 4;
+  // 0..127 and one 8-row slice of columns 128..191; role 0 also its pair's
+  // four 4-row slices of dO and the step's 32 lse*log2(e) and 32 delta
+  // values (one load: lanes 0-31 and 32-63). Role 1 also stores the dS
+  // blocks: the loads are split so both roles reach the barrier together.
+  constexpr int NDMA_R0 = 8, NDMA_R1 = 3;
   __shared__ __attribute__((aligned(1024))) uint16_t sq[NS][kR2TileQ];
   __shared__ __attribute__((aligned(1024))) uint16_t sdo[NS][kRTile];
-  // lse*log2(e) (waves 0, 1: query rows 0-15, 16-31) | delta (waves 2, 3)
-  __shared__ __attribute__((aligned(256))) float sld[NS][NW][64];
+  // per pair: lse*log2(e) of the step's query rows 0-31, then their delta
+  __shared__ __attribute__((aligned(256))) float sld[NS][NP][64];
   __shared__ __attribute__((aligned(16))) u32x4 sp[2][NP][KT][2][64];  // [parity][pair][kt][j][lane]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -128,11 +128,11 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
       const int qi = tail ? min(q0 + brow, lq - 1) : q0 + brow;
       dma16(qb + (int64_t)qi * a.q.sn + bpiece, lds_ptr(&sq[b][kR2TileA + w * 512]));
     }
-    {
-      const int r = 16 * (w & 1) + (ln & 15);
-      const int qi = tail ? min(q0 + r, lq - 1) - r : q0;
-      const float* src = ((w & 3) < 2 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + hh * a.lse_sh;
-      dma4(src + r + qi, lds_ptr(&sld[b][w][0]));
+    if constexpr (R == 0) {
+      const int r = ln & 31;
+      const int qi = tail ? min(q0 + r, lq - 1) : q0 + r;
+      const float* src = (ln < 32 ? a.lse2 : a.delta) + s * a.lse_sb + sg.q_row0 + hh * a.lse_sh;
+      dma4(src + qi, lds_ptr(&sld[b][pair][0]));
     }
   };
 
@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
       for (int i = tid; i < 2 * kR2TileQ / 8; i += NT) q4[i] = z;
       u32x4* d4 = reinterpret_cast<u32x4*>(&sdo[NS - 1][0]);
       for (int i = tid; i < kRTile / 8; i += NT) d4[i] = z;
-      for (int i = tid; i < NW * 64; i += NT) (&sld[NS - 1][0][0])[i] = 0.f;
+      for (int i = tid; i < NP * 64; i += NT) (&sld[NS - 1][0][0])[i] = 0.f;
       u32x4* p1 = &sp[1][0][0][0][0];
       for (int i = tid; i < NP * KT * 2 * 64; i += NT) p1[i] = z;
     }
@@ -248,7 +248,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int qo = 8 * rr + 4 * h;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][qo >> 4][qo & 15]);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i)][pair][qo]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) l2[4 * rr + c] = v[c];
       }
@@ -292,8 +292,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_roles_qk192_kernel(const
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int qo = 8 * rr + 4 * h;
-        const f32x4 v =
-            *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][2 + (qo >> 4)][qo & 15]);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sld[stage(i - 1)][pair][32 + qo]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) dl[4 * rr + c] = v[c];
       }

@@ -149,9 +149,10 @@ __global__ void __launch_bounds__(512 / KT, 1) attn_bwd_dkdv_roles_kernel(const 
   auto step_head = [&](int it) { return g * a.G + it % a.G; };
   auto step_q0 = [&](int it) { return q_begin + (nq - 1 - it / a.G) * kRBQ; };
   auto stage = [](int it) { return (it + NS) % NS; };
-  // Hand-issued loads of step it: SPW of the Q tile's 8 four-row slices, SPW
-  // of dO's, and 16 of the 64 lse*log2(e) | delta values. Lane l of slice j
-  // loads row 4j + l/16, stored piece l%16 (global piece l%16 ^ swizzle).
+  // Hand-issued loads of step it: SPW of the Q tile's 8 four-row slices and
+  // SPW of dO's, and in role 0 the step's lse*log2(e) and delta values. Lane
+  // l of slice j loads row 4j + l/16, stored piece l%16 (global piece l%16 ^
+  // swizzle).
   int srow[SPW], spiece[SPW];
   int64_t qoff[SPW], doff[SPW];
 #pragma unroll
